@@ -1,0 +1,276 @@
+"""CPU oracle for the DSpark draft / schedule / verify round -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package.  The product path (the HIP library and its Python binding) never does,
+and this package never imports anything from the product package.
+
+The arithmetic lives in ``dspark_oracle.c`` (plain C, double precision, one loop per step of
+the definition).  This module only marshals numpy / torch-CPU arrays into that library and
+back.  ``build()`` compiles it with gcc; ``lib()`` loads it, building it once if it is absent.
+
+Every function documents the definition it implements; the C file cites the pages.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dspark_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESIDUAL, STREAM_BONUS = 0, 1, 2, 3
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (-O2, scalar code, OpenMP over requests)."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = C.CDLL(LIB_PATH)
+        p = C.c_void_p
+        i32 = C.c_int
+        u64 = C.c_uint64
+        L.oracle_philox4x32_10.argtypes = [p, p, p]
+        L.oracle_philox_batch.argtypes = [i32, p, p, p]
+        L.oracle_uniform.restype = C.c_double
+        L.oracle_uniform.argtypes = [u64, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32]
+        L.oracle_gumbel.restype = C.c_double
+        L.oracle_gumbel.argtypes = [u64, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32]
+        L.oracle_uniform_batch.argtypes = [i32, u64, p, p, p, C.c_uint32, p]
+        L.oracle_corrected_row.argtypes = [i32, i32, i32, p, i32, p, p, i32, p]
+        L.oracle_draft_block.restype = i32
+        L.oracle_draft_block.argtypes = [i32, i32, i32, i32, i32, p, i32, p, p, p, p, p, p, u64,
+                                         p, i32, p, p, p, p, p]
+        L.oracle_profile.restype = C.c_double
+        L.oracle_profile.argtypes = [i32, p, p, C.c_double]
+        L.oracle_schedule.restype = i32
+        L.oracle_schedule.argtypes = [i32, i32, p, p, i32, p, p, i32, p, p, p]
+        L.oracle_verify.restype = i32
+        L.oracle_verify.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, i32, p, i32, p, p, p, p,
+                                    p, p, u64, p, i32, p, p, p, p]
+        L.oracle_num_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+# ----------------------------------------------------------------------------------------
+# array marshalling
+# ----------------------------------------------------------------------------------------
+
+def _as_logits(a):
+    """Return (contiguous numpy array, dtype code) for float32 or bfloat16 data.
+
+    bfloat16 arrives as a torch tensor (numpy has no bfloat16); its raw 16-bit patterns are
+    handed to C, which widens them exactly."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().contiguous()
+            if a.dtype == torch.bfloat16:
+                return a.view(torch.int16).numpy().view(np.uint16), BF16
+            if a.dtype == torch.float32:
+                return a.numpy(), F32
+            raise TypeError(f"unsupported logits dtype {a.dtype}")
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.uint16:
+        return a, BF16
+    raise TypeError(f"unsupported logits dtype {a.dtype}")
+
+
+def _np(a, dtype):
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a), dtype=dtype)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _subset(a, rows):
+    """Rows of a leading-batch array (keeps bfloat16 tensors as tensors)."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return a.detach().cpu()[torch.as_tensor(rows, dtype=torch.long)].contiguous()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a)[rows])
+
+
+# ----------------------------------------------------------------------------------------
+# random numbers
+# ----------------------------------------------------------------------------------------
+
+def philox(ctrs, key):
+    """Philox4x32-10 blocks for counters ctrs [n,4] (uint32) under key [2] -> [n,4] uint32."""
+    ctrs = _np(ctrs, np.uint32).reshape(-1, 4)
+    key = _np(key, np.uint32).reshape(2)
+    out = np.empty_like(ctrs)
+    lib().oracle_philox_batch(len(ctrs), _ptr(ctrs), _ptr(key), _ptr(out))
+    return out
+
+
+def uniform(seed, req, pos, v, stream):
+    """Uniforms in (0,1) at (request key, position, vocab index) on a stream (broadcasting)."""
+    req, pos, v = np.broadcast_arrays(np.asarray(req), np.asarray(pos), np.asarray(v))
+    shape = req.shape
+    req = _np(req, np.uint32).ravel()
+    pos = _np(pos, np.uint32).ravel()
+    v = _np(v, np.uint32).ravel()
+    out = np.empty(len(req), np.float64)
+    lib().oracle_uniform_batch(len(req), C.c_uint64(seed), _ptr(req), _ptr(pos), _ptr(v),
+                               stream, _ptr(out))
+    return out.reshape(shape)
+
+
+# ----------------------------------------------------------------------------------------
+# the three steps of a round
+# ----------------------------------------------------------------------------------------
+
+def corrected_row(z_row, U, W, prev):
+    """c_v = Z_v + sum_i U[prev][i] * W[v][i] (double accumulation, float result) -> [V]."""
+    z, zdt = _as_logits(z_row)
+    u, udt = _as_logits(U)
+    w, wdt = _as_logits(W)
+    assert udt == wdt
+    V = z.shape[-1]
+    r = u.shape[-1]
+    out = np.empty(V, np.float32)
+    lib().oracle_corrected_row(V, r, zdt, _ptr(z), udt, _ptr(u), _ptr(w), int(prev), _ptr(out))
+    return out
+
+
+def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=None, rows=None,
+                want_corrected=False):
+    """Draft tokens for a block (see oracle_draft_block in dspark_oracle.c).
+
+    Z [B,K,V] (float32 or bfloat16), U [V,r], W [V,r] (row v = column v of the r x V factor),
+    prev_token [B], temperature [B], draft_len [B] or None (= K), req_id [B] or None (= b).
+    rows: optional list of requests to compute; the result arrays then have len(rows) rows.
+    Returns a dict with tokens [n,K] int32, q_tok / q_lse [n,K] float64, gap [n,K] float64
+    and, when asked, corrected [n,K,V] float32.
+    """
+    B = int(Z.shape[0])
+    rows = np.arange(B) if rows is None else np.asarray(rows, dtype=np.int64)
+    n = len(rows)
+    z, zdt = _as_logits(_subset(Z, rows))
+    u, udt = _as_logits(U)
+    w, wdt = _as_logits(W)
+    assert udt == wdt, "U and W must share a dtype"
+    K, V = z.shape[1], z.shape[2]
+    r = u.shape[1]
+    prev = _np(prev_token, np.int32)[rows]
+    temp = _np(temperature, np.float32)[rows]
+    dlen = None if draft_len is None else _np(draft_len, np.int32)[rows]
+    req = (rows.astype(np.uint32) if req_id is None else _np(req_id, np.uint32)[rows])
+    req = np.ascontiguousarray(req, dtype=np.uint32)
+    sub_rows = np.arange(n, dtype=np.int32)
+    tokens = np.empty((n, K), np.int32)
+    q_tok = np.empty((n, K), np.float64)
+    q_lse = np.empty((n, K), np.float64)
+    gap = np.empty((n, K), np.float64)
+    corrected = np.empty((n, K, V), np.float32) if want_corrected else None
+    st = lib().oracle_draft_block(n, K, V, r, zdt, _ptr(z), udt, _ptr(u), _ptr(w), _ptr(prev),
+                                  _ptr(dlen), _ptr(temp), _ptr(req), C.c_uint64(seed),
+                                  _ptr(sub_rows), n, _ptr(tokens), _ptr(q_tok), _ptr(q_lse),
+                                  _ptr(corrected), _ptr(gap))
+    if st != 0:
+        raise ValueError("oracle_draft_block: token index out of range")
+    return dict(tokens=tokens, q_tok=q_tok, q_lse=q_lse, gap=gap, corrected=corrected)
+
+
+def profile(knot_tokens, knot_tps, N):
+    kt = _np(knot_tokens, np.float64)
+    kp = _np(knot_tps, np.float64)
+    return lib().oracle_profile(len(kt), _ptr(kt), _ptr(kp), float(N))
+
+
+def schedule(conf_logits, knot_tokens, knot_tps, enabled=True, draft_len=None):
+    """Per-request verification lengths (see oracle_schedule in dspark_oracle.c).
+
+    Returns dict(verify_len [B] int32, expected_tokens [B] float64, n_star, margin)."""
+    c = _np(conf_logits, np.float32)
+    B, K = c.shape
+    dlen = None if draft_len is None else _np(draft_len, np.int32)
+    kt = _np(knot_tokens, np.float64)
+    kp = _np(knot_tps, np.float64)
+    vl = np.empty(B, np.int32)
+    et = np.empty(B, np.float64)
+    diag = np.empty(2, np.float64)
+    st = lib().oracle_schedule(B, K, _ptr(c), _ptr(dlen), len(kt), _ptr(kt), _ptr(kp),
+                               int(bool(enabled)), _ptr(vl), _ptr(et), _ptr(diag))
+    if st != 0:
+        raise ValueError("oracle_schedule: invalid argument")
+    return dict(verify_len=vl, expected_tokens=et, n_star=int(diag[0]), margin=float(diag[1]))
+
+
+def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature, seed,
+           req_id=None, rows=None):
+    """Rejection-sampling verification (see oracle_verify in dspark_oracle.c).
+
+    Y [B,K+1,V] (float32 or bfloat16); draft_tokens [B,K]; q_tok, q_lse [B,K] (taken as
+    float32, the precision the draft hands over); Z, U, W, prev_token as for draft_block.
+    Returns dict(accept_len [n], next_token [n], p_tok [n,K], accept_margin [n],
+    sample_margin [n]) for the listed rows (all by default)."""
+    B = int(Y.shape[0])
+    rows = np.arange(B) if rows is None else np.asarray(rows, dtype=np.int64)
+    n = len(rows)
+    y, ydt = _as_logits(_subset(Y, rows))
+    z, zdt = _as_logits(_subset(Z, rows))
+    u, udt = _as_logits(U)
+    w, wdt = _as_logits(W)
+    assert udt == wdt
+    K = z.shape[1]
+    V = z.shape[2]
+    r = u.shape[1]
+    assert y.shape[1] == K + 1 and y.shape[2] == V
+    toks = _np(draft_tokens, np.int32)[rows]
+    qt = _np(q_tok, np.float32)[rows]
+    ql = _np(q_lse, np.float32)[rows]
+    prev = _np(prev_token, np.int32)[rows]
+    vl = _np(verify_len, np.int32)[rows]
+    temp = _np(temperature, np.float32)[rows]
+    req = (rows.astype(np.uint32) if req_id is None else _np(req_id, np.uint32)[rows])
+    req = np.ascontiguousarray(req, dtype=np.uint32)
+    sub_rows = np.arange(n, dtype=np.int32)
+    acc = np.empty(n, np.int32)
+    nxt = np.empty(n, np.int32)
+    p_tok = np.zeros((n, K), np.float64)
+    diag = np.empty((n, 2), np.float64)
+    st = lib().oracle_verify(n, K, V, r, ydt, _ptr(y), _ptr(toks), _ptr(qt), _ptr(ql), zdt,
+                             _ptr(z), udt, _ptr(u), _ptr(w), _ptr(prev), _ptr(vl), _ptr(temp),
+                             _ptr(req), C.c_uint64(seed), _ptr(sub_rows), n, _ptr(acc),
+                             _ptr(nxt), _ptr(p_tok), _ptr(diag))
+    if st != 0:
+        raise ValueError("oracle_verify: token index out of range")
+    return dict(accept_len=acc, next_token=nxt, p_tok=p_tok, accept_margin=diag[:, 0],
+                sample_margin=diag[:, 1])
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())

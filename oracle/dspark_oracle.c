@@ -1,0 +1,573 @@
+/*
+ * dspark_oracle.c -- plain CPU oracle for the DSpark draft / schedule / verify round.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct definition that the
+ * GPU library is checked against.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load it.  It shares no code, header, table or constant generator with
+ * the HIP library, and it never takes a value produced by that library.
+ *
+ * Everything floating-point is done in double precision unless a step fixes the precision
+ * itself (the corrected logits are rounded to float once, because that float is the value
+ * both implementations take their argmax decisions on).  Loops are written in the order of
+ * the definitions, with no blocking and no fusion.
+ *
+ * Sources (the pages are web articles about DeepSeek's DSpark; cited by title and section):
+ *  - Markov sequential head: QbitAI, "DSpark in 10 concepts", section "Cheaper serial
+ *    module: the Markov head" (the head looks only at the previous token and is a rank-256
+ *    low-rank factorisation); 10100.com commentary, section "Parallel drafts are fast but may
+ *    turn 'of course' into 'of problem'" (rank-256 low-rank transition correction, added to the
+ *    block of base logits produced by the parallel backbone, left to right).
+ *  - Confidence-scheduled verification length: QbitAI, section "Variable-length drafts and
+ *    hardware-aware scheduling" (per-position survival score, throughput curve measured per
+ *    batch size, per-request verify length); 10100.com, section "DSpark's hardest step: letting
+ *    the GPU decide how much to verify" (survival given all earlier positions passed;
+ *    longer at low load, low-return suffixes cut at high load); wangjunjian.com tag page,
+ *    translated abstract (prefix survival probability and engine throughput profile).
+ *  - Lossless verification: QbitAI, section "Speculative decoding" (accept the longest correct
+ *    prefix, resample at the first divergence, output distribution equals the target's);
+ *    10100.com, section "Speculative decoding is block checking" (rejection rule of
+ *    Leviathan et al., arXiv 2211.17192); wangjunjian.com tag page, post "Speculative
+ *    Decoding" steps 3-4 (accept by comparing the two probabilities with a random number;
+ *    if all guesses pass, sample the next token from the target; else resample the rejected
+ *    position from the adjusted distribution).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - U is [V][r] (row t = left factor of token t); W is stored [V][r] as well: row v holds
+ *    column v of the r x V right factor, so bias_v = sum_i U[t][i] * W[v][i].
+ *  - The corrected logit is purely additive: c_v = Z_v + bias_v.  The first draft position
+ *    uses the last committed token t0.  Temperature T divides the corrected logit; T = 0
+ *    means greedy (argmax).  Ties in every argmax go to the lowest vocabulary index.
+ *  - Random numbers: Philox4x32 with 10 rounds (Salmon et al., SC'11), key = (seed low word,
+ *    seed high word), counter = (v >> 2, position, request key, stream), output word v & 3,
+ *    uniform = ((word >> 8) + 0.5) * 2^-24, which lies strictly inside (0, 1).
+ *    Streams: 0 draft sampling, 1 accept test (v = 0), 2 residual resampling, 3 bonus.
+ *  - Gumbel-max sampling: x = argmax_v (s_v + G_v), G_v = -log(-log u_v).
+ *  - Accept test: u * q(x) < p(x)  (equivalent to u < p/q for q > 0; p >= q always accepts).
+ *  - Residual: r_v = max(0, p_v - q_v); the correction is argmax over r_v > 0 of
+ *    (log r_v + G_v) on the residual stream; if every r_v is 0 the correction is drawn from
+ *    p with the same stream.
+ *  - Schedule: survival s = 1/(1+exp(-C)); P = running product over positions; rank all
+ *    (request, position) items by (P desc, position asc, request asc); for n = 0..sum K_b
+ *    E(n) = B + sum of the top-n P, N(n) = B + n, G(n) = E(n) * T(N(n)) / N(n) with T the
+ *    piecewise-linear throughput profile clamped outside its knots; n* = smallest argmax;
+ *    L_b = number of request b's items in the top n*.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* dtype codes of the arrays handed in (float32 or bfloat16 bit patterns) */
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Philox stream identifiers */
+#define ORACLE_STREAM_DRAFT 0u
+#define ORACLE_STREAM_ACCEPT 1u
+#define ORACLE_STREAM_RESIDUAL 2u
+#define ORACLE_STREAM_BONUS 3u
+
+/* ------------------------------------------------------------------------------------ */
+/* element access                                                                         */
+/* ------------------------------------------------------------------------------------ */
+
+/* A bfloat16 value is the upper half of the float32 with the same sign/exponent/mantissa. */
+static double bf16_bits_to_double(uint16_t h)
+{
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double load_elem(int dtype, const void *base, size_t idx)
+{
+    if (dtype == ORACLE_BF16)
+        return bf16_bits_to_double(((const uint16_t *)base)[idx]);
+    return (double)((const float *)base)[idx];
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Philox4x32-10 and the uniform / Gumbel draws built on it                               */
+/* ------------------------------------------------------------------------------------ */
+
+/* One Philox4x32 round: two 32x32->64 multiplies by the published multipliers, the high
+ * halves mixed with the other counter words and the round key. */
+static void philox_round(uint32_t c[4], uint32_t k0, uint32_t k1)
+{
+    uint64_t prod_a = (uint64_t)0xD2511F53u * (uint64_t)c[0];
+    uint64_t prod_b = (uint64_t)0xCD9E8D57u * (uint64_t)c[2];
+    uint32_t n0 = (uint32_t)(prod_b >> 32) ^ c[1] ^ k0;
+    uint32_t n1 = (uint32_t)prod_b;
+    uint32_t n2 = (uint32_t)(prod_a >> 32) ^ c[3] ^ k1;
+    uint32_t n3 = (uint32_t)prod_a;
+    c[0] = n0;
+    c[1] = n1;
+    c[2] = n2;
+    c[3] = n3;
+}
+
+/* Philox4x32-10: ten rounds; the key is advanced by the Weyl constants before every round
+ * after the first. */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        philox_round(c, k0, k1);
+    }
+    out[0] = c[0];
+    out[1] = c[1];
+    out[2] = c[2];
+    out[3] = c[3];
+}
+
+/* Uniform in (0,1) for vocabulary index v at (request key, position, stream). */
+double oracle_uniform(uint64_t seed, uint32_t req, uint32_t pos, uint32_t v, uint32_t stream)
+{
+    uint32_t ctr[4] = {v >> 2, pos, req, stream};
+    uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    uint32_t w = out[v & 3u];
+    return ((double)(w >> 8) + 0.5) * (1.0 / 16777216.0);
+}
+
+/* Standard Gumbel draw from the uniform above. */
+double oracle_gumbel(uint64_t seed, uint32_t req, uint32_t pos, uint32_t v, uint32_t stream)
+{
+    double u = oracle_uniform(seed, req, pos, v, stream);
+    return -log(-log(u));
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Markov sequential head                                                                 */
+/* ------------------------------------------------------------------------------------ */
+
+/* Corrected logits of one draft row: c_v = Z_v + sum_i U[prev][i] * W[v][i].
+ * The sum is accumulated in double; the result is rounded once to float, which is the
+ * value the argmax and the softmax below start from. */
+void oracle_corrected_row(int V, int r, int z_dtype, const void *z_row, int uw_dtype,
+                          const void *U, const void *W, int prev, float *c_out)
+{
+    for (int v = 0; v < V; ++v) {
+        double bias = 0.0;
+        for (int i = 0; i < r; ++i)
+            bias += load_elem(uw_dtype, U, (size_t)prev * r + i) *
+                    load_elem(uw_dtype, W, (size_t)v * r + i);
+        c_out[v] = (float)(load_elem(z_dtype, z_row, (size_t)v) + bias);
+    }
+}
+
+/* argmax with ties to the lowest index; also reports the gap to the runner-up. */
+static int argmax_double(const double *a, int n, double *gap)
+{
+    int best = 0;
+    for (int v = 1; v < n; ++v)
+        if (a[v] > a[best])
+            best = v;
+    double second = -INFINITY;
+    for (int v = 0; v < n; ++v)
+        if (v != best && a[v] > second)
+            second = a[v];
+    if (gap)
+        *gap = a[best] - second;
+    return best;
+}
+
+/* log of sum_v exp(s_v), with the maximum taken out first */
+static double log_sum_exp(const double *s, int n)
+{
+    double m = -INFINITY;
+    for (int v = 0; v < n; ++v)
+        if (s[v] > m)
+            m = s[v];
+    double acc = 0.0;
+    for (int v = 0; v < n; ++v)
+        acc += exp(s[v] - m);
+    return m + log(acc);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Draft block                                                                            */
+/* ------------------------------------------------------------------------------------ */
+
+/*
+ * Draft tokens for the requests listed in rows[0..n_rows).  For request b and position
+ * k = 0..K_b-1 (K_b = draft_len[b], or K when draft_len is NULL):
+ *   prev = t0_b for k = 0, else x_{b,k-1};
+ *   c = corrected row (above);
+ *   T = 0: x = argmax c, q_tok = 1, q_lse = 0;
+ *   T > 0: s = c / T, lse = log sum exp s, x = argmax (s_v + G_v) with the draft stream,
+ *          q_tok = exp(s_x - lse), q_lse = lse.
+ * Positions k >= K_b get x = -1, q_tok = 0, q_lse = 0.
+ * Arrays are full-size ([B][K] / [B][K][V]); only the listed requests are written.
+ * corrected (optional, [B][K][V]) receives the float corrected logits.
+ * gap (optional, [B][K]) receives the winning score's margin over the runner-up
+ * (c for greedy, s + G for sampling) so that near-ties can be recognised by the tests.
+ * Returns 0, or -1 when a token index is out of range.
+ */
+int oracle_draft_block(int B, int K, int V, int r, int z_dtype, const void *Z, int uw_dtype,
+                       const void *U, const void *W, const int32_t *prev_token,
+                       const int32_t *draft_len, const float *temperature, const uint32_t *req_id,
+                       uint64_t seed, const int32_t *rows, int n_rows, int32_t *draft_tokens,
+                       double *q_tok, double *q_lse, float *corrected, double *gap)
+{
+    (void)B; /* arrays are [B][...]; only the listed rows are touched */
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ri = 0; ri < n_rows; ++ri) {
+        int b = rows[ri];
+        float *c = (float *)malloc(sizeof(float) * (size_t)V);
+        double *s = (double *)malloc(sizeof(double) * (size_t)V);
+        int Kb = draft_len ? draft_len[b] : K;
+        uint32_t req = req_id ? req_id[b] : (uint32_t)b;
+        double T = (double)temperature[b];
+        int prev = prev_token[b];
+        for (int k = 0; k < K; ++k) {
+            size_t bk = (size_t)b * K + k;
+            if (k >= Kb || prev < 0 || prev >= V) {
+                if (k < Kb) {
+#pragma omp atomic write
+                    status = -1;
+                }
+                draft_tokens[bk] = -1;
+                q_tok[bk] = 0.0;
+                q_lse[bk] = 0.0;
+                if (gap)
+                    gap[bk] = INFINITY;
+                continue;
+            }
+            const void *z_row = (z_dtype == ORACLE_BF16)
+                                    ? (const void *)((const uint16_t *)Z + bk * (size_t)V)
+                                    : (const void *)((const float *)Z + bk * (size_t)V);
+            oracle_corrected_row(V, r, z_dtype, z_row, uw_dtype, U, W, prev, c);
+            if (corrected)
+                memcpy(corrected + bk * (size_t)V, c, sizeof(float) * (size_t)V);
+            int x;
+            double g;
+            if (T == 0.0) {
+                for (int v = 0; v < V; ++v)
+                    s[v] = (double)c[v];
+                x = argmax_double(s, V, &g);
+                q_tok[bk] = 1.0;
+                q_lse[bk] = 0.0;
+            } else {
+                for (int v = 0; v < V; ++v)
+                    s[v] = (double)c[v] / T;
+                double lse = log_sum_exp(s, V);
+                double *pert = (double *)malloc(sizeof(double) * (size_t)V);
+                for (int v = 0; v < V; ++v)
+                    pert[v] = s[v] + oracle_gumbel(seed, req, (uint32_t)k, (uint32_t)v,
+                                                   ORACLE_STREAM_DRAFT);
+                x = argmax_double(pert, V, &g);
+                free(pert);
+                q_tok[bk] = exp(s[x] - lse);
+                q_lse[bk] = lse;
+            }
+            draft_tokens[bk] = x;
+            if (gap)
+                gap[bk] = g;
+            prev = x;
+        }
+        free(c);
+        free(s);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Confidence-scheduled verification length                                              */
+/* ------------------------------------------------------------------------------------ */
+
+/* Piecewise-linear throughput profile, clamped to the end knots outside their range. */
+double oracle_profile(int n_knots, const double *knot_tokens, const double *knot_tps, double N)
+{
+    if (N <= knot_tokens[0])
+        return knot_tps[0];
+    if (N >= knot_tokens[n_knots - 1])
+        return knot_tps[n_knots - 1];
+    int i = 0;
+    while (!(N >= knot_tokens[i] && N <= knot_tokens[i + 1]))
+        ++i;
+    double t = (N - knot_tokens[i]) / (knot_tokens[i + 1] - knot_tokens[i]);
+    return knot_tps[i] + (knot_tps[i + 1] - knot_tps[i]) * t;
+}
+
+typedef struct {
+    double P;
+    int k;
+    int b;
+} sched_item;
+
+/* (P desc, position asc, request asc) */
+static int sched_item_cmp(const void *pa, const void *pb)
+{
+    const sched_item *a = (const sched_item *)pa, *b = (const sched_item *)pb;
+    if (a->P > b->P)
+        return -1;
+    if (a->P < b->P)
+        return 1;
+    if (a->k != b->k)
+        return a->k < b->k ? -1 : 1;
+    if (a->b != b->b)
+        return a->b < b->b ? -1 : 1;
+    return 0;
+}
+
+/*
+ * Per-request verification length.  enabled = 0 returns L_b = K_b.
+ * expected_tokens (optional, [B]) = 1 + sum_{k < L_b} P_{b,k}: the expected number of tokens
+ * the round emits for request b (accepted prefix plus the one correction/bonus token).
+ * diag (optional, [2]) = {n*, relative margin of G(n*) over the best other n}.
+ * Returns 0, or -1 on an invalid argument.
+ */
+int oracle_schedule(int B, int K, const float *conf_logits, const int32_t *draft_len,
+                    int n_knots, const double *knot_tokens, const double *knot_tps, int enabled,
+                    int32_t *verify_len, double *expected_tokens, double *diag)
+{
+    if (B < 0 || K < 0 || n_knots < 1)
+        return -1;
+    double *P = (double *)malloc(sizeof(double) * (size_t)(B > 0 ? B : 1) * (size_t)(K > 0 ? K : 1));
+    for (int b = 0; b < B; ++b) {
+        double run = 1.0;
+        for (int k = 0; k < K; ++k) {
+            double C = (double)conf_logits[(size_t)b * K + k];
+            double surv = 1.0 / (1.0 + exp(-C));
+            run = run * surv;
+            P[(size_t)b * K + k] = run;
+        }
+    }
+    if (!enabled) {
+        for (int b = 0; b < B; ++b)
+            verify_len[b] = draft_len ? draft_len[b] : K;
+        if (diag) {
+            diag[0] = -1.0;
+            diag[1] = INFINITY;
+        }
+    } else {
+        int total = 0;
+        for (int b = 0; b < B; ++b)
+            total += draft_len ? draft_len[b] : K;
+        sched_item *items = (sched_item *)malloc(sizeof(sched_item) * (size_t)(total > 0 ? total : 1));
+        int n_items = 0;
+        for (int b = 0; b < B; ++b) {
+            int Kb = draft_len ? draft_len[b] : K;
+            for (int k = 0; k < Kb; ++k) {
+                items[n_items].P = P[(size_t)b * K + k];
+                items[n_items].k = k;
+                items[n_items].b = b;
+                ++n_items;
+            }
+        }
+        qsort(items, (size_t)n_items, sizeof(sched_item), sched_item_cmp);
+        double E = (double)B;
+        double best_G = -INFINITY, second_G = -INFINITY;
+        int best_n = 0;
+        for (int n = 0; n <= n_items; ++n) {
+            if (n > 0)
+                E += items[n - 1].P;
+            double N = (double)B + (double)n;
+            double G = E * oracle_profile(n_knots, knot_tokens, knot_tps, N) / N;
+            if (G > best_G) {
+                second_G = best_G;
+                best_G = G;
+                best_n = n;
+            } else if (G > second_G) {
+                second_G = G;
+            }
+        }
+        for (int b = 0; b < B; ++b)
+            verify_len[b] = 0;
+        for (int i = 0; i < best_n; ++i)
+            verify_len[items[i].b] += 1;
+        if (diag) {
+            diag[0] = (double)best_n;
+            diag[1] = (best_G - second_G) / fabs(best_G);
+        }
+        free(items);
+    }
+    if (expected_tokens) {
+        for (int b = 0; b < B; ++b) {
+            double e = 1.0;
+            for (int k = 0; k < verify_len[b]; ++k)
+                e += P[(size_t)b * K + k];
+            expected_tokens[b] = e;
+        }
+    }
+    free(P);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Lossless rejection-sampling verification                                              */
+/* ------------------------------------------------------------------------------------ */
+
+/*
+ * For every listed request b with L = verify_len[b], temperature T, target rows Y[b][0..K]:
+ *   for k = 0..L-1 (draft position k+1):
+ *     T = 0: accept iff x_k == argmax Y[b][k];
+ *     T > 0: p = softmax(Y[b][k] / T); u = uniform(accept stream, v = 0, position k);
+ *            accept iff u * q_tok[b][k] < p(x_k).
+ *     On the first rejection at k = j: accept_len = j and the correction is
+ *       T = 0: argmax Y[b][j];
+ *       T > 0: q_j(v) = exp(c_{j,v} / T - q_lse[b][j]) with c_j the corrected row of position j
+ *              (previous token t0 for j = 0, else x_{j-1}); r = max(0, p - q_j);
+ *              argmax over r_v > 0 of log r_v + G_v (residual stream, position j);
+ *              if r is identically zero, argmax of log p_v + G_v (same stream).
+ *   If all L pass: accept_len = L and the bonus token is argmax Y[b][L] (T = 0) or
+ *   argmax of Y[b][L]/T + G_v with the bonus stream at position L.
+ * Outputs: accept_len[b], next_token[b]; p_tok (optional, [B][K]) = p(x_k) for the tested
+ * positions (1 for a greedy match, 0 for a greedy mismatch); diag (optional, [B][2]) =
+ * {|u - p/q| of the deciding test (inf for greedy / none), margin of the sampled correction
+ * or bonus over its runner-up}.
+ * Returns 0, or -1 when a token index is out of range.
+ */
+int oracle_verify(int B, int K, int V, int r, int y_dtype, const void *Y,
+                  const int32_t *draft_tokens, const float *q_tok, const float *q_lse,
+                  int z_dtype, const void *Z, int uw_dtype, const void *U, const void *W,
+                  const int32_t *prev_token, const int32_t *verify_len, const float *temperature,
+                  const uint32_t *req_id, uint64_t seed, const int32_t *rows, int n_rows,
+                  int32_t *accept_len, int32_t *next_token, double *p_tok, double *diag)
+{
+    (void)B; /* arrays are [B][...]; only the listed rows are touched */
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ri = 0; ri < n_rows; ++ri) {
+        int b = rows[ri];
+        int L = verify_len[b];
+        double T = (double)temperature[b];
+        uint32_t req = req_id ? req_id[b] : (uint32_t)b;
+        double *y = (double *)malloc(sizeof(double) * (size_t)V);
+        double *p = (double *)malloc(sizeof(double) * (size_t)V);
+        double *score = (double *)malloc(sizeof(double) * (size_t)V);
+        float *c = (float *)malloc(sizeof(float) * (size_t)V);
+        double accept_margin = INFINITY, sample_margin = INFINITY;
+        int a = L, token = -1, rejected = 0;
+
+        for (int k = 0; k < L && !rejected; ++k) {
+            size_t row = (size_t)b * (K + 1) + k;
+            int x = draft_tokens[(size_t)b * K + k];
+            if (x < 0 || x >= V) {
+#pragma omp atomic write
+                status = -1;
+                x = 0;
+            }
+            for (int v = 0; v < V; ++v)
+                y[v] = load_elem(y_dtype, Y, row * V + v);
+            int accept;
+            if (T == 0.0) {
+                int am = argmax_double(y, V, NULL);
+                accept = (x == am);
+                if (p_tok)
+                    p_tok[(size_t)b * K + k] = accept ? 1.0 : 0.0;
+                if (!accept)
+                    token = am;
+            } else {
+                for (int v = 0; v < V; ++v)
+                    score[v] = y[v] / T;
+                double lse_p = log_sum_exp(score, V);
+                for (int v = 0; v < V; ++v)
+                    p[v] = exp(score[v] - lse_p);
+                double u = oracle_uniform(seed, req, (uint32_t)k, 0u, ORACLE_STREAM_ACCEPT);
+                double q = (double)q_tok[(size_t)b * K + k];
+                accept = (u * q < p[x]);
+                if (p_tok)
+                    p_tok[(size_t)b * K + k] = p[x];
+                accept_margin = (q > 0.0) ? fabs(u - p[x] / q) : INFINITY;
+                if (!accept) {
+                    /* recompute the draft distribution of this position */
+                    int prev = (k == 0) ? prev_token[b] : draft_tokens[(size_t)b * K + k - 1];
+                    if (prev < 0 || prev >= V) {
+#pragma omp atomic write
+                        status = -1;
+                        prev = 0;
+                    }
+                    size_t zrow = (size_t)b * K + k;
+                    const void *z_row =
+                        (z_dtype == ORACLE_BF16)
+                            ? (const void *)((const uint16_t *)Z + zrow * (size_t)V)
+                            : (const void *)((const float *)Z + zrow * (size_t)V);
+                    oracle_corrected_row(V, r, z_dtype, z_row, uw_dtype, U, W, prev, c);
+                    double lq = (double)q_lse[(size_t)b * K + k];
+                    int any = 0;
+                    for (int v = 0; v < V; ++v) {
+                        double qv = exp((double)c[v] / T - lq);
+                        double rv = p[v] - qv;
+                        if (rv > 0.0) {
+                            any = 1;
+                            score[v] = log(rv) + oracle_gumbel(seed, req, (uint32_t)k, (uint32_t)v,
+                                                               ORACLE_STREAM_RESIDUAL);
+                        } else {
+                            score[v] = -INFINITY;
+                        }
+                    }
+                    if (!any)
+                        for (int v = 0; v < V; ++v)
+                            score[v] = log(p[v]) + oracle_gumbel(seed, req, (uint32_t)k,
+                                                                 (uint32_t)v, ORACLE_STREAM_RESIDUAL);
+                    token = argmax_double(score, V, &sample_margin);
+                }
+            }
+            if (!accept) {
+                a = k;
+                rejected = 1;
+            }
+        }
+        if (!rejected) {
+            size_t row = (size_t)b * (K + 1) + L;
+            for (int v = 0; v < V; ++v)
+                y[v] = load_elem(y_dtype, Y, row * V + v);
+            if (T == 0.0) {
+                token = argmax_double(y, V, NULL);
+            } else {
+                for (int v = 0; v < V; ++v)
+                    score[v] = y[v] / T + oracle_gumbel(seed, req, (uint32_t)L, (uint32_t)v,
+                                                        ORACLE_STREAM_BONUS);
+                token = argmax_double(score, V, &sample_margin);
+            }
+        }
+        accept_len[b] = a;
+        next_token[b] = token;
+        if (diag) {
+            diag[(size_t)b * 2 + 0] = accept_margin;
+            diag[(size_t)b * 2 + 1] = sample_margin;
+        }
+        free(y);
+        free(p);
+        free(score);
+        free(c);
+    }
+    return status;
+}
+
+/* Number of threads the parallel loops above use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Batch helpers for the tests: n Philox blocks for explicit counters / n uniforms. */
+void oracle_philox_batch(int n, const uint32_t *ctrs, const uint32_t key[2], uint32_t *out)
+{
+    for (int i = 0; i < n; ++i)
+        oracle_philox4x32_10(ctrs + 4 * (size_t)i, key, out + 4 * (size_t)i);
+}
+
+void oracle_uniform_batch(int n, uint64_t seed, const uint32_t *req, const uint32_t *pos,
+                          const uint32_t *v, uint32_t stream, double *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = oracle_uniform(seed, req[i], pos[i], v[i], stream);
+}

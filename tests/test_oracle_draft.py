@@ -1,0 +1,164 @@
+"""Pins for the oracle's draft block (Markov sequential head + fused softmax / sampling).
+
+Each test checks the oracle against something fixed outside it: a library routine run in
+float64 (torch.matmul, torch.argmax, torch.logsumexp), the softmax law of Gumbel-max sampling
+(chi-squared), or the pages' qualitative "of course" / "of problem" example.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+from draft_head_verification_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bias64(U, W, prev):
+    return torch.matmul(U[prev].double(), W.double().T)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_markov_bias_matches_fp64_matmul(dtype):
+    g = torch.Generator().manual_seed(3)
+    V, r = 777, 48
+    U = torch.randn(V, r, generator=g).to(dtype)
+    W = torch.randn(V, r, generator=g).to(dtype)
+    z = (3 * torch.randn(V, generator=g)).to(dtype)
+    for prev in (0, 5, V - 1):
+        c = torch.from_numpy(oracle.corrected_row(z, U, W, prev)).double()
+        ref = (z.double() + _bias64(U, W, prev)).float().double()
+        # the oracle rounds its double sum to float once: equal to the float of the exact sum
+        assert torch.equal(c, ref), (prev, (c - ref).abs().max())
+
+
+def test_greedy_chain_matches_torch_argmax_chain():
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(w, temperature=0.0, strong_bias=True)
+    res = oracle.draft_block(inp["Z"], inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
+                             inp["seed"], req_id=inp["req_id"], want_corrected=True)
+    Z, U, W = inp["Z"], inp["U"], inp["W"]
+    changed = 0
+    for b in range(w.B):
+        prev = int(inp["prev_token"][b])
+        for k in range(w.K):
+            c = (Z[b, k].double() + _bias64(U, W, prev)).float()
+            x = int(torch.argmax(c))  # first maximal index
+            assert res["tokens"][b, k] == x
+            assert res["q_tok"][b, k] == 1.0 and res["q_lse"][b, k] == 0.0
+            np.testing.assert_array_equal(res["corrected"][b, k], c.numpy())
+            changed += int(torch.argmax(Z[b, k]) != x)
+            prev = x
+    assert changed > 0, "strong-bias inputs should let the head change some argmaxes"
+
+
+def test_softmax_normaliser_and_q_tok_match_torch():
+    w = synth.WORKLOADS["tiny"]
+    for T in (1.0, 0.7):
+        inp = synth.make_inputs(w, temperature=T)
+        res = oracle.draft_block(inp["Z"], inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
+                                 inp["seed"], req_id=inp["req_id"], want_corrected=True)
+        c = torch.from_numpy(res["corrected"]).double()
+        s = c / float(np.float32(T))  # the temperature travels as float32
+        lse = torch.logsumexp(s, dim=-1)
+        np.testing.assert_allclose(res["q_lse"], lse.numpy(), rtol=0, atol=1e-12)
+        tok = torch.from_numpy(res["tokens"]).long()
+        logp = torch.log_softmax(s, dim=-1).gather(-1, tok[..., None])[..., 0]
+        np.testing.assert_allclose(res["q_tok"], logp.exp().numpy(), rtol=1e-12, atol=0)
+
+
+def _tiny_block(n_req, V, r, K, seed=0, strong=1.0):
+    g = torch.Generator().manual_seed(seed)
+    U = (strong * torch.randn(V, r, generator=g)).float()
+    W = (strong * torch.randn(V, r, generator=g)).float()
+    zrow = torch.randn(K, V, generator=g)
+    Z = zrow.expand(n_req, K, V).contiguous()
+    return Z, U, W
+
+
+@pytest.mark.parametrize("T", [1.0, 0.6])
+def test_gumbel_max_sampling_follows_softmax(T):
+    """Across 200k request keys, position 1 is distributed as softmax(c_1 / T) and position 2,
+    given x_1 = a, as softmax(c_2(a) / T) -- the chain feeds the sampled token back."""
+    n, V, r, K = 200_000, 16, 4, 2
+    Z, U, W = _tiny_block(n, V, r, K, seed=4, strong=0.8)
+    prev = torch.full((n,), 3, dtype=torch.int32)
+    temp = torch.full((n,), T)
+    res = oracle.draft_block(Z, U, W, prev, temp, seed=77)
+    x1 = res["tokens"][:, 0]
+    T = float(np.float32(T))
+    c1 = (Z[0, 0].double() + _bias64(U, W, 3)).float().double()
+    p1 = torch.softmax(c1 / T, 0).numpy()
+    obs = np.bincount(x1, minlength=V)
+    assert stats.chisquare(obs, p1 * n).pvalue > 1e-4
+    a = int(np.argmax(obs))
+    sel = x1 == a
+    c2 = (Z[0, 1].double() + _bias64(U, W, a)).float().double()
+    p2 = torch.softmax(c2 / T, 0).numpy()
+    obs2 = np.bincount(res["tokens"][sel, 1], minlength=V)
+    assert stats.chisquare(obs2, p2 * sel.sum()).pvalue > 1e-4
+    # the head matters here: a wrong previous token would give a clearly different law
+    c2_wrong = (Z[0, 1].double() + _bias64(U, W, 3)).float().double()
+    p2_wrong = torch.softmax(c2_wrong / T, 0).numpy()
+    assert stats.chisquare(obs2, p2_wrong * sel.sum()).pvalue < 1e-6
+
+
+def test_ragged_draft_lengths_mask_tail():
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(w)
+    dl = torch.tensor([0, 1, 3, 4], dtype=torch.int32)
+    res = oracle.draft_block(inp["Z"], inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
+                             inp["seed"], draft_len=dl, req_id=inp["req_id"])
+    full = oracle.draft_block(inp["Z"], inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
+                              inp["seed"], req_id=inp["req_id"])
+    for b in range(4):
+        kb = int(dl[b])
+        assert np.all(res["tokens"][b, kb:] == -1) and np.all(res["q_tok"][b, kb:] == 0)
+        np.testing.assert_array_equal(res["tokens"][b, :kb], full["tokens"][b, :kb])
+
+
+def test_of_course_worked_example():
+    """The pages' illustration: after "of" the sequential head pushes position 2 towards
+    "course" and away from "problem" (QbitAI, "DSpark = Eagle + DFlash" section; 10100.com,
+    "parallel drafts ... 'of problem'" section).  The fixture is a hand-built V=8 instance."""
+    with open(os.path.join(GOLDEN, "of_course.json")) as f:
+        fx = json.load(f)
+    vocab = fx["vocab"]
+    Z = torch.tensor([fx["base_logits"]], dtype=torch.float32)
+    U = torch.tensor(fx["U"], dtype=torch.float32)
+    W = torch.tensor(fx["W"], dtype=torch.float32)
+    t0 = torch.tensor([vocab.index(fx["context_token"])], dtype=torch.int32)
+    temp = torch.zeros(1)
+    with_head = oracle.draft_block(Z, U, W, t0, temp, 0)["tokens"][0]
+    without = oracle.draft_block(Z, torch.zeros_like(U), W, t0, temp, 0)["tokens"][0]
+    assert [vocab[i] for i in with_head] == fx["expected_with_head"]
+    assert [vocab[i] for i in without] == fx["expected_parallel_only"]
+
+
+def test_greedy_ties_go_to_lowest_index():
+    """Exact ties are resolved to the lowest vocabulary index (torch.argmax's documented rule),
+    in the draft and in the verifier's greedy correction / bonus."""
+    V, K = 40, 2
+    Z = torch.zeros(1, K, V)
+    Z[0, 0, [7, 19, 33]] = 5.0
+    Z[0, 1, [3, 4]] = 2.0
+    U = torch.zeros(V, 2)
+    W = torch.zeros(V, 2)
+    t0 = torch.tensor([0], dtype=torch.int32)
+    d = oracle.draft_block(Z, U, W, t0, torch.zeros(1), 0)
+    assert list(d["tokens"][0]) == [int(torch.argmax(Z[0, 0])), int(torch.argmax(Z[0, 1]))] == [7, 3]
+    Y = torch.zeros(1, K + 1, V)
+    Y[0, 0, [9, 11]] = 1.0
+    Y[0, 2, [20, 30]] = 1.0
+    ones = np.ones((1, K), np.float32)
+    v = oracle.verify(Y, d["tokens"], ones, 0 * ones, Z, U, W, t0,
+                      torch.tensor([K], dtype=torch.int32), torch.zeros(1), 0)
+    assert v["accept_len"][0] == 0 and v["next_token"][0] == 9
+    tokens = torch.tensor([[9, 0]], dtype=torch.int32)
+    v = oracle.verify(Y, tokens, ones, 0 * ones, Z, U, W, t0,
+                      torch.tensor([K], dtype=torch.int32), torch.zeros(1), 0)
+    assert v["accept_len"][0] == K and v["next_token"][0] == 20
