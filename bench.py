@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark: one DSpark round (draft block -> schedule -> verify) per step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload headline]
+
+A step is the whole hot path over one batch of synthetic inputs already resident in HBM:
+the K Markov-head draft steps (gather, bias contraction, base add, temperature, softmax,
+Gumbel-max sample), the confidence schedule, and the rejection-sampling verify (row
+statistics over the target logits, accept scan, residual / bonus draw).  The default workload
+is the headline shape: B=256 requests, K=16 draft positions, V=151936, rank 256, bf16 base
+logits and factors, fp32 target logits, temperature 1, scheduling off.
+
+Prints one JSON line: throughput in drafted positions per second (sum of draft lengths per
+step / step time), the roofline of the dominant kernel (algorithmic bytes per launch over its
+average HIP-event duration inside the timed region, against the MI355X HBM peak), and the
+CPU oracle timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "draft+verify positions/s at V=151936,K=16,B=256; HBM GB/s vs peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters (optional)")
+    return ap.parse_args()
+
+
+def build_targets_on_gpu(inp, tokens, corrected, w):
+    """Target logits for the timed GPU path: the drafter's corrected rows plus the workload's
+    noise; the bonus row adds the bias of the last drafted token to the extra base row."""
+    import torch
+    from draft_head_verification_amd import synth
+    B, K = w.B, w.K
+    corr = inp["Z_ext"].float()
+    corr[:, :K] = corrected
+    last = tokens[:, K - 1].long().clamp(min=0)
+    bias = inp["U"][last].float() @ inp["W"].float().T
+    corr[:, K] += bias
+    Y = synth.target_logits(corr, inp["noise"], w.y_dtype)
+    del corr, bias
+    torch.cuda.empty_cache()
+    return Y
+
+
+def algorithmic_bytes(name, w, inp, vlen_host, n_resid, zb, ub, yb):
+    """Bytes the method must move per launch (reads of base logits, factors and target rows,
+    plus the outputs that leave the kernel); see the design notes for the accounting."""
+    B, K, V, r = w.B, w.K, w.V, w.r
+    if name == "markov_head_step":
+        return B * V * zb + V * r * ub + B * r * ub
+    if name == "verify_rowstats":
+        return int(sum((int(L) + 1) for L in vlen_host)) * V * yb
+    if name == "verify_residual":
+        return n_resid * V * (zb + yb) + (V * r * ub if n_resid else 0) + n_resid * r * ub
+    return None
+
+
+def cpu_baseline(inp, w, n_threads_hint):
+    """The oracle, as it stands, on a bounded sample of requests of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from draft_head_verification_amd import synth
+    threads = oracle.num_threads()
+    n = max(8, min(w.B, 4 * threads))
+    rows = list(range(n))
+    U, W = inp["U"].cpu(), inp["W"].cpu()
+    Zc = inp["Z_ext"][:n, : w.K].cpu().contiguous()
+    prev, temp = inp["prev_token"][:n].cpu(), inp["temperature"][:n].cpu()
+    req, dlen = inp["req_id"][:n].cpu(), inp["draft_len"][:n].cpu()
+    t0 = time.perf_counter()
+    od = oracle.draft_block(Zc, U, W, prev, temp, inp["seed"], draft_len=dlen, req_id=req,
+                            want_corrected=True)
+    t_draft = time.perf_counter() - t0
+    # targets of the sample from the oracle's own chain (not timed)
+    corr = inp["Z_ext"][:n].cpu().float().clone()
+    corr[:, : w.K] = torch.from_numpy(od["corrected"])
+    for i in range(n):
+        kb = int(dlen[i])
+        corr[i, kb] = torch.from_numpy(oracle.corrected_row(inp["Z_ext"][i, kb].cpu(), U, W,
+                                                            int(od["tokens"][i, kb - 1])))
+    Y = synth.target_logits(corr, inp["noise"][:n].cpu(), w.y_dtype)
+    t1 = time.perf_counter()
+    oracle.verify(Y, od["tokens"], od["q_tok"].astype(np.float32), od["q_lse"].astype(np.float32),
+                  Zc, U, W, prev, dlen, temp, inp["seed"], req_id=req, rows=rows)
+    t_verify = time.perf_counter() - t1
+    positions = int(dlen.sum())
+    return {"value": positions / (t_draft + t_verify), "unit": "positions/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {w.B} requests of the same workload ({positions} drafted positions): "
+                      f"oracle draft {t_draft:.2f} s + verify {t_verify:.2f} s, OpenMP over requests"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path shards by "
+              "request with no exchange, so multi-GPU throughput is N x the one-GPU figure; "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from draft_head_verification_amd import dspark as D
+    from draft_head_verification_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    inp = synth.make_inputs(w, device=dev)
+    for k in list(inp):
+        if isinstance(inp[k], torch.Tensor):
+            inp[k] = inp[k].contiguous()
+    Z = inp["Z_ext"][:, : w.K].contiguous()
+    B, K, V, r = w.B, w.K, w.V, w.r
+    zb = 2 if w.z_dtype == torch.bfloat16 else 4
+    ub = 2 if w.uw_dtype == torch.bfloat16 else 4
+    yb = 2 if w.y_dtype == torch.bfloat16 else 4
+
+    # outputs and workspaces, allocated once
+    toks = torch.empty(B, K, dtype=torch.int32, device=dev)
+    q_tok = torch.empty(B, K, device=dev)
+    q_lse = torch.empty(B, K, device=dev)
+    vlen = torch.empty(B, dtype=torch.int32, device=dev)
+    exp_tok = torch.empty(B, dtype=torch.float64, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    ws_d = torch.empty(D.dspark_draft_workspace_size(B, K, V, r), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(max(256, D.dspark_schedule_workspace_size(B, K)), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(D.dspark_verify_workspace_size(B, K, V, r), dtype=torch.uint8, device=dev)
+
+    # one untimed draft gives the chain the target logits are built around
+    corrected = torch.empty(B, K, V, device=dev)
+    D.dspark_draft_block(Z, inp["U"], inp["W"], inp["prev_token"], inp["temperature"], inp["seed"],
+                         toks, q_tok, q_lse, draft_len=inp["draft_len"], req_id=inp["req_id"],
+                         corrected=corrected, workspace=ws_d)
+    Y = build_targets_on_gpu(inp, toks, corrected, w)
+    del corrected
+    torch.cuda.empty_cache()
+
+    def step(trace=None):
+        D.dspark_draft_block(Z, inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
+                             inp["seed"], toks, q_tok, q_lse, draft_len=inp["draft_len"],
+                             req_id=inp["req_id"], workspace=ws_d, trace=trace)
+        D.dspark_schedule(inp["conf_logits"], vlen, inp["knot_tokens"], inp["knot_tps"],
+                          w.schedule, draft_len=inp["draft_len"], expected_tokens=exp_tok,
+                          workspace=ws_s, trace=trace)
+        D.dspark_verify(Y, toks, q_tok, q_lse, Z, inp["U"], inp["W"], inp["prev_token"], vlen,
+                        inp["temperature"], inp["seed"], acc, nxt, req_id=inp["req_id"],
+                        workspace=ws_v, trace=trace)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    trace = D.Trace(capacity=64 * (args.steps + 1) + 64)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step(trace)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    for bits_ws in (ws_d, ws_s, ws_v):
+        bits = D.dspark_query_device_status(bits_ws)
+        assert bits == 0, f"device status {bits:#x}"
+
+    positions = int(inp["draft_len"].sum().item())
+    value = positions * args.steps / (ms_total / 1e3)
+
+    # per-kernel statistics from the HIP events of the timed region
+    per = {}
+    for name, ms in trace.records():
+        s = per.setdefault(name, [0, 0.0])
+        s[0] += 1
+        s[1] += ms
+    vlen_host = vlen.cpu().numpy()
+    n_resid = int(torch.from_numpy(ws_v[256:260].cpu().numpy().copy()).view(torch.int32)[0])
+    kernels = []
+    for name, (cnt, tot) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+        avg_us = tot / cnt * 1e3
+        nbytes = algorithmic_bytes(name, w, inp, vlen_host, n_resid, zb, ub, yb)
+        kernels.append({"kernel": name, "launches_per_step": cnt / args.steps,
+                        "avg_us": round(avg_us, 2), "share": round(tot / max(1e-9, sum(v[1] for v in per.values())), 4),
+                        "algorithmic_bytes": nbytes,
+                        "achieved_GBs": (round(nbytes / (avg_us * 1e-6) / 1e9, 1) if nbytes else None)})
+    dom = next(k for k in kernels if k["algorithmic_bytes"])
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            ent = tj.get(args.workload, {}).get(dom["kernel"])
+            if ent and ent.get("source_hash") == _kernel_source_hash():
+                traffic = ent["hbm_bytes_per_launch"]
+        except Exception:
+            traffic = None
+    roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["achieved_GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": traffic}
+    step_bytes = sum((k["algorithmic_bytes"] or 0) * k["launches_per_step"] for k in kernels)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, w, None)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generator; random factors; no checkpoint)",
+        "config": {"workload": f"{w.name}: B={B} K={K} V={V} r={r} base/factors "
+                               f"{'bf16' if zb == 2 else 'fp32'}, target {'bf16' if yb == 2 else 'fp32'}, "
+                               f"T={','.join(str(t) for t in w.temperature)}, "
+                               f"schedule {'on' if w.schedule else 'off'}",
+                   "B": B, "K": K, "V": V, "r": r, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step_algorithmic_GBs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "wall_s": round(wall, 3),
+        "mean_accept_len": round(float(acc.float().mean().item()), 3),
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "draft_head_verification_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,275 @@
+// api.hip -- the C ABI of libdspark.so: argument checks, workspace carving and the launch
+// sequence of each call.  See include/dspark.h for the contract of every entry point.
+#include <new>
+
+#include "dspark_common.hpp"
+
+using namespace dspark;
+
+struct dspark_trace {
+    int cap = 0, n = 0;
+    hipEvent_t *start = nullptr, *stop = nullptr;
+    const char **names = nullptr;
+};
+
+namespace {
+
+constexpr int kMaxK = 64;
+constexpr int kMaxRank = 1024;
+constexpr int kMaxV = 1 << 30;
+
+bool valid_dtype(int d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
+
+// Records HIP events around one kernel launch when a trace is attached.
+template <typename F>
+hipError_t traced(dspark_trace *t, const char *name, hipStream_t s, F &&launch) {
+    const bool rec = t && t->n < t->cap;
+    if (rec) {
+        hipError_t e = hipEventRecord(t->start[t->n], s);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch();
+    if (e != hipSuccess) return e;
+    if (rec) {
+        e = hipEventRecord(t->stop[t->n], s);
+        if (e != hipSuccess) return e;
+        t->names[t->n] = name;
+        ++t->n;
+    }
+    return hipSuccess;
+}
+
+bool check_ws(const void *ws, size_t ws_bytes, size_t need) {
+    return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0 && ws_bytes >= need;
+}
+
+bool head_sizes_ok(int32_t B, int32_t K, int32_t V, int32_t r) {
+    return B >= 0 && K >= 1 && K <= kMaxK && V >= 8 && V <= kMaxV && V % 8 == 0 && r >= 1 &&
+           r <= kMaxRank;
+}
+
+// draft workspace: status | prev_cur[B] | partials[B][n_slabs]
+size_t draft_layout(int32_t B, int32_t V, DraftWs *ws, char *base) {
+    const int ns = num_vslabs(V, B);
+    size_t off = 0;
+    if (ws) ws->status = reinterpret_cast<uint32_t *>(base + off);
+    off += 256;
+    if (ws) ws->prev_cur = reinterpret_cast<int32_t *>(base + off);
+    off += align256((size_t)B * sizeof(int32_t));
+    if (ws) ws->partials = reinterpret_cast<Partial *>(base + off);
+    off += align256((size_t)B * ns * sizeof(Partial));
+    if (ws) ws->n_slabs = ns;
+    return off;
+}
+
+// verify workspace: status | n_resid | resid_rows[B] | rowstats[B][K+1] | partials[B][n_slabs]
+size_t verify_layout(int32_t B, int32_t K, int32_t V, VerifyWs *ws, char *base) {
+    const int ns = num_vslabs(V, B);
+    size_t off = 0;
+    if (ws) ws->status = reinterpret_cast<uint32_t *>(base + off);
+    off += 256;
+    if (ws) ws->n_resid = reinterpret_cast<int32_t *>(base + off);
+    off += 256;
+    if (ws) ws->resid_rows = reinterpret_cast<int32_t *>(base + off);
+    off += align256((size_t)B * sizeof(int32_t));
+    if (ws) ws->rowstats = reinterpret_cast<float4 *>(base + off);
+    off += align256((size_t)B * (K + 1) * sizeof(float4));
+    if (ws) ws->partials = reinterpret_cast<Partial *>(base + off);
+    off += align256((size_t)B * ns * sizeof(Partial));
+    if (ws) ws->n_slabs = ns;
+    return off;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dspark_version(void) { return "dspark-mi355x 0.1 (gfx950)"; }
+
+const char *dspark_status_string(dspark_status s) {
+    switch (s) {
+        case DSPARK_OK: return "ok";
+        case DSPARK_EINVAL: return "invalid argument";
+        case DSPARK_EDTYPE: return "unsupported dtype";
+        case DSPARK_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case DSPARK_EHIP: return "HIP runtime error";
+        case DSPARK_EDEVICE: return "invalid device data (see device status bits)";
+    }
+    return "unknown status";
+}
+
+size_t dspark_draft_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r) {
+    if (!head_sizes_ok(B, K, V, r)) return 0;
+    return draft_layout(B, V, nullptr, nullptr);
+}
+
+size_t dspark_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r) {
+    if (!head_sizes_ok(B, K, V, r) || B >= (1 << 24)) return 0;
+    return verify_layout(B, K, V, nullptr, nullptr);
+}
+
+size_t dspark_schedule_workspace_size(int32_t B, int32_t K) {
+    if (B < 0 || B > 8192 || K < 1 || K > kMaxK) return 0;
+    return 256;
+}
+
+dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws_bytes,
+                                 void *stream) {
+    if (!a) return DSPARK_EINVAL;
+    if (!head_sizes_ok(a->B, a->K, a->V, a->r)) return DSPARK_EINVAL;
+    if (!valid_dtype(a->z_dtype) || !valid_dtype(a->uw_dtype)) return DSPARK_EDTYPE;
+    if (a->B == 0) return DSPARK_OK;
+    if (!a->Z || !a->U || !a->W || !a->prev_token || !a->temperature || !a->draft_tokens ||
+        !a->q_tok || !a->q_lse)
+        return DSPARK_EINVAL;
+    if (!check_ws(ws, ws_bytes, dspark_draft_workspace_size(a->B, a->K, a->V, a->r)))
+        return DSPARK_EWORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    DraftWs w;
+    draft_layout(a->B, a->V, &w, reinterpret_cast<char *>(ws));
+    hipError_t e = traced(a->trace, "draft_prepare", s,
+                          [&] { return launch_draft_prepare(*a, w, s); });
+    if (e != hipSuccess) return DSPARK_EHIP;
+    DraftStepParams p{};
+    p.B = a->B;
+    p.K = a->K;
+    p.V = a->V;
+    p.r = a->r;
+    p.Z = a->Z;
+    p.U = a->U;
+    p.W = a->W;
+    p.draft_len = a->draft_len;
+    p.temperature = a->temperature;
+    p.req_id = a->req_id;
+    p.key0 = (uint32_t)(a->seed & 0xFFFFFFFFu);
+    p.key1 = (uint32_t)(a->seed >> 32);
+    p.prev_cur = w.prev_cur;
+    p.partials = w.partials;
+    p.corrected = a->corrected;
+    p.status = w.status;
+    p.n_slabs = w.n_slabs;
+    for (int k = 0; k < a->K; ++k) {
+        p.k = k;
+        e = traced(a->trace, "markov_head_step", s,
+                   [&] { return launch_draft_step(p, a->z_dtype, a->uw_dtype, s); });
+        if (e != hipSuccess) return DSPARK_EHIP;
+        e = traced(a->trace, "draft_reduce", s, [&] { return launch_draft_reduce(*a, w, k, s); });
+        if (e != hipSuccess) return DSPARK_EHIP;
+    }
+    return DSPARK_OK;
+}
+
+dspark_status dspark_schedule(const dspark_schedule_args *a, void *ws, size_t ws_bytes,
+                              void *stream) {
+    if (!a) return DSPARK_EINVAL;
+    if (a->B < 0 || a->B > 8192 || a->K < 1 || a->K > kMaxK) return DSPARK_EINVAL;
+    if (a->B == 0) return DSPARK_OK;
+    if (!a->conf_logits || !a->verify_len) return DSPARK_EINVAL;
+    if (a->enabled) {
+        if (!a->knot_tokens || !a->knot_tps || a->n_knots < 1 || a->n_knots > 64)
+            return DSPARK_EINVAL;
+        if ((long long)a->B * a->K > 8192) return DSPARK_EINVAL;
+    }
+    if (!check_ws(ws, ws_bytes, dspark_schedule_workspace_size(a->B, a->K)))
+        return DSPARK_EWORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint32_t *status = reinterpret_cast<uint32_t *>(ws);
+    hipError_t e = traced(a->trace, "schedule", s, [&] { return launch_schedule(*a, status, s); });
+    return e == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+}
+
+dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_bytes, void *stream) {
+    if (!a) return DSPARK_EINVAL;
+    if (!head_sizes_ok(a->B, a->K, a->V, a->r) || a->B >= (1 << 24)) return DSPARK_EINVAL;
+    if (!valid_dtype(a->y_dtype) || !valid_dtype(a->z_dtype) || !valid_dtype(a->uw_dtype))
+        return DSPARK_EDTYPE;
+    if (a->B == 0) return DSPARK_OK;
+    if (!a->Y || !a->draft_tokens || !a->q_tok || !a->q_lse || !a->Z || !a->U || !a->W ||
+        !a->prev_token || !a->verify_len || !a->temperature || !a->accept_len || !a->next_token)
+        return DSPARK_EINVAL;
+    if (!check_ws(ws, ws_bytes, dspark_verify_workspace_size(a->B, a->K, a->V, a->r)))
+        return DSPARK_EWORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    VerifyWs w;
+    verify_layout(a->B, a->K, a->V, &w, reinterpret_cast<char *>(ws));
+    hipError_t e;
+    e = traced(a->trace, "verify_prepare", s, [&] { return launch_verify_prepare(*a, w, s); });
+    if (e != hipSuccess) return DSPARK_EHIP;
+    e = traced(a->trace, "verify_rowstats", s, [&] { return launch_verify_rowstats(*a, w, s); });
+    if (e != hipSuccess) return DSPARK_EHIP;
+    e = traced(a->trace, "verify_finish", s, [&] { return launch_verify_finish(*a, w, s); });
+    if (e != hipSuccess) return DSPARK_EHIP;
+    e = traced(a->trace, "verify_residual", s, [&] { return launch_verify_residual(*a, w, s); });
+    if (e != hipSuccess) return DSPARK_EHIP;
+    e = traced(a->trace, "verify_residual_reduce", s,
+               [&] { return launch_verify_residual_reduce(*a, w, s); });
+    return e == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+}
+
+dspark_status dspark_query_device_status(const void *ws, void *stream, uint32_t *bits) {
+    if (!ws) return DSPARK_EINVAL;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(s) != hipSuccess) return DSPARK_EHIP;
+    uint32_t v = 0;
+    if (hipMemcpy(&v, ws, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return DSPARK_EHIP;
+    if (bits) *bits = v;
+    return v ? DSPARK_EDEVICE : DSPARK_OK;
+}
+
+dspark_trace *dspark_trace_create(int32_t capacity) {
+    if (capacity <= 0) return nullptr;
+    dspark_trace *t = new (std::nothrow) dspark_trace;
+    if (!t) return nullptr;
+    t->cap = capacity;
+    t->start = new (std::nothrow) hipEvent_t[capacity];
+    t->stop = new (std::nothrow) hipEvent_t[capacity];
+    t->names = new (std::nothrow) const char *[capacity];
+    if (!t->start || !t->stop || !t->names) {
+        dspark_trace_destroy(t);
+        return nullptr;
+    }
+    for (int i = 0; i < capacity; ++i) {
+        t->start[i] = nullptr;
+        t->stop[i] = nullptr;
+    }
+    for (int i = 0; i < capacity; ++i) {
+        if (hipEventCreate(&t->start[i]) != hipSuccess || hipEventCreate(&t->stop[i]) != hipSuccess) {
+            dspark_trace_destroy(t);
+            return nullptr;
+        }
+    }
+    return t;
+}
+
+void dspark_trace_destroy(dspark_trace *t) {
+    if (!t) return;
+    if (t->start)
+        for (int i = 0; i < t->cap; ++i)
+            if (t->start[i]) (void)hipEventDestroy(t->start[i]);
+    if (t->stop)
+        for (int i = 0; i < t->cap; ++i)
+            if (t->stop[i]) (void)hipEventDestroy(t->stop[i]);
+    delete[] t->start;
+    delete[] t->stop;
+    delete[] t->names;
+    delete t;
+}
+
+void dspark_trace_reset(dspark_trace *t) {
+    if (t) t->n = 0;
+}
+
+int32_t dspark_trace_count(const dspark_trace *t) { return t ? t->n : 0; }
+
+dspark_status dspark_trace_get(dspark_trace *t, int32_t i, const char **kernel_name,
+                               float *milliseconds) {
+    if (!t || i < 0 || i >= t->n) return DSPARK_EINVAL;
+    if (hipEventSynchronize(t->stop[i]) != hipSuccess) return DSPARK_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t->start[i], t->stop[i]) != hipSuccess) return DSPARK_EHIP;
+    if (kernel_name) *kernel_name = t->names[i];
+    if (milliseconds) *milliseconds = ms;
+    return DSPARK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,684 @@
+// markov_head.hip -- the Markov sequential head and its fused sampling epilogue.
+//
+// One draft step k computes, for every request b, the corrected row
+//     c[b][v] = Z[b][k][v] + sum_i U[prev_b][i] * W[v][i]
+// and folds it straight into softmax statistics and a Gumbel-max (or argmax) candidate,
+// without ever writing c (unless the caller asks for it).  The head looks at the previous
+// token only and is a low-rank (rank r) factorisation of a token-to-token bias (QbitAI "DSpark
+// in 10 concepts", section "Cheaper serial module: the Markov head"; 10100.com commentary,
+// section on parallel drafts and the rank-256 transition correction).  Steps run left to right
+// because position k needs the token sampled at k-1 (QbitAI, section "DSpark = Eagle + DFlash").
+//
+// Matrix-core path (bf16 factors, r % 32 == 0, r <= 256):
+//   GEMM view: rows = vocabulary (M), columns = requests (N), reduction = r (K).
+//   A workgroup of 8 waves owns up to 256 requests (32 per wave, two 16-wide column blocks)
+//   and a contiguous slab of the vocabulary.  Each wave keeps its requests' gathered U rows
+//   in registers as MFMA B fragments for the whole slab.  The slab streams through LDS in
+//   tiles of 64 vocabulary rows of W (double-buffered, one barrier per tile); every wave reads
+//   its A fragments from the shared tile, so W leaves HBM once per 256 requests.
+//   v_mfma_f32_16x16x32_bf16 leaves each lane 4 consecutive vocabulary entries of one
+//   request, which is exactly one Philox4x32 block: the Gumbel noise costs one Philox call
+//   per 4 outputs with no data exchange.
+//   Workgroups are laid out so that the (up to 2) request groups sharing a vocabulary slab
+//   are dispatched to the same XCD and meet the slab's W tiles in that XCD's L2.
+// Vector-ALU path (any other factor dtype / rank): one workgroup per (request, slab).
+#include "dspark_common.hpp"
+
+namespace dspark {
+
+enum class HeadMode { Draft, Residual };
+
+// Everything a Markov-head kernel needs; the residual mode (the verifier's recompute of the
+// draft distribution at the first rejected position) reuses the same GEMM.
+struct HeadParams {
+    int B, K, V, r;
+    int n_rows_max;                 // grid is sized for this many GEMM rows
+    const int32_t *n_rows_dev;      // residual mode: actual row count (device)
+    int k;                          // draft mode: the position of this step
+    const void *Z;                  // [B][K][V]
+    const uint16_t *U, *W;          // [V][r] bf16 (matrix-core path)
+    const float *Uf, *Wf;           // [V][r] f32 (vector path)
+    const int32_t *draft_len;       // [B] or null
+    const float *temperature;       // [B]
+    const uint32_t *req_id;         // [B] or null
+    uint32_t key0, key1;
+    const int32_t *prev_cur;        // draft: [B]
+    const int32_t *resid_rows;      // residual: packed rows
+    const int32_t *prev_token;      // residual: [B]
+    const int32_t *draft_tokens;    // residual: [B][K]
+    const void *Y;                  // residual: [B][K+1][V]
+    const float4 *rowstats;         // residual: [B][K+1]
+    const float *q_lse;             // residual: [B][K]
+    Partial *partials;              // [rows][n_slabs]
+    float *corrected;               // draft: optional [B][K][V]
+    uint32_t *status;
+    int n_slabs;
+};
+
+// Per-row description resolved on the device.
+struct RowInfo {
+    bool valid;
+    int b, pos, prev;
+    size_t zrow, yrow;
+    float T;
+    uint32_t req;
+    float qlse2, lse2p;  // residual mode
+};
+
+template <HeadMode MODE>
+__device__ __forceinline__ RowInfo row_info(const HeadParams &p, int row, int n_rows) {
+    RowInfo ri;
+    ri.valid = false;
+    ri.b = 0;
+    ri.pos = 0;
+    ri.prev = 0;
+    ri.zrow = 0;
+    ri.yrow = 0;
+    ri.T = 0.f;
+    ri.req = 0;
+    ri.qlse2 = 0.f;
+    ri.lse2p = 0.f;
+    if (row >= n_rows) return ri;
+    if constexpr (MODE == HeadMode::Draft) {
+        const int b = row;
+        int kb = p.draft_len ? p.draft_len[b] : p.K;
+        kb = kb < 0 ? 0 : (kb > p.K ? p.K : kb);
+        if (p.k >= kb) return ri;
+        ri.valid = true;
+        ri.b = b;
+        ri.pos = p.k;
+        ri.prev = p.prev_cur[b];  // validated by the prepare / reduce kernels
+        ri.zrow = (size_t)b * p.K + p.k;
+        ri.T = p.temperature[b];
+        if (!(ri.T >= 0.f)) ri.T = 0.f;
+    } else {
+        const int packed = p.resid_rows[row];
+        const int b = packed >> 7, j = packed & 127;
+        ri.valid = true;
+        ri.b = b;
+        ri.pos = j;
+        int prev = (j == 0) ? p.prev_token[b] : p.draft_tokens[(size_t)b * p.K + j - 1];
+        if (prev < 0 || prev >= p.V) prev = 0;  // flagged by the verifier's finish kernel
+        ri.prev = prev;
+        ri.zrow = (size_t)b * p.K + j;
+        ri.yrow = (size_t)b * (p.K + 1) + j;
+        ri.T = p.temperature[b];  // > 0: greedy rows never need a residual
+        const float4 rs = p.rowstats[ri.yrow];
+        ri.lse2p = rs.x + fast_log2(rs.y);
+        ri.qlse2 = p.q_lse[ri.zrow] * kLog2e;
+    }
+    ri.req = p.req_id ? p.req_id[ri.b] : (uint32_t)ri.b;
+    return ri;
+}
+
+// Residual candidates: best score over r = p - q > 0 and, as the fallback when the residual
+// is identically zero, best score over p.  Packed into a Partial as
+// {g: best r-score, idx: its index, m: best p-score, pad: its index}.
+struct ResidState {
+    float gr, gp;
+    int ir, ip;
+};
+
+__device__ __forceinline__ ResidState resid_init() {
+    ResidState s;
+    s.gr = -INFINITY;
+    s.gp = -INFINITY;
+    s.ir = 0x7FFFFFFF;
+    s.ip = 0x7FFFFFFF;
+    return s;
+}
+
+__device__ __forceinline__ ResidState resid_merge(ResidState a, ResidState b) {
+    if ((b.gr > a.gr) || (b.gr == a.gr && b.ir < a.ir)) {
+        a.gr = b.gr;
+        a.ir = b.ir;
+    }
+    if ((b.gp > a.gp) || (b.gp == a.gp && b.ip < a.ip)) {
+        a.gp = b.gp;
+        a.ip = b.ip;
+    }
+    return a;
+}
+
+__device__ __forceinline__ ResidState resid_shfl_xor(ResidState s, int mask) {
+    ResidState r;
+    r.gr = __shfl_xor(s.gr, mask);
+    r.gp = __shfl_xor(s.gp, mask);
+    r.ir = __shfl_xor(s.ir, mask);
+    r.ip = __shfl_xor(s.ip, mask);
+    return r;
+}
+
+// Four consecutive logits of a row starting at v (v % 4 == 0, v + 3 < V when v < V).
+template <typename T>
+__device__ __forceinline__ void load4(const void *base, size_t row, int V, int v, float out[4]);
+
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const void *base, size_t row, int V, int v,
+                                                float out[4]) {
+    const uint2 q = *reinterpret_cast<const uint2 *>(
+        reinterpret_cast<const uint16_t *>(base) + row * (size_t)V + v);
+    out[0] = bf16_lo(q.x);
+    out[1] = bf16_hi(q.x);
+    out[2] = bf16_lo(q.y);
+    out[3] = bf16_hi(q.y);
+}
+
+template <>
+__device__ __forceinline__ void load4<float>(const void *base, size_t row, int V, int v,
+                                             float out[4]) {
+    const float4 q = *reinterpret_cast<const float4 *>(
+        reinterpret_cast<const float *>(base) + row * (size_t)V + v);
+    out[0] = q.x;
+    out[1] = q.y;
+    out[2] = q.z;
+    out[3] = q.w;
+}
+
+// Epilogue for four consecutive corrected logits c[0..3] = entries v..v+3 of one row.
+template <HeadMode MODE, typename YT>
+__device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInfo &ri, int v,
+                                               const float c[4], SampleState &st,
+                                               ResidState &rs) {
+    if constexpr (MODE == HeadMode::Draft) {
+        if (p.corrected) {
+            float4 o;
+            o.x = c[0];
+            o.y = c[1];
+            o.z = c[2];
+            o.w = c[3];
+            *reinterpret_cast<float4 *>(p.corrected + ri.zrow * (size_t)p.V + v) = o;
+        }
+        if (ri.T == 0.f) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) greedy_update(st, c[i], v + i);
+        } else {
+            const float inv = kLog2e / ri.T;
+            float s[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[i] = c[i] * inv;
+            lse_update4(st, s);
+            const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
+                                             kStreamDraft, p.key0, p.key1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gumbel_update(st, s[i], ph.w[i], v + i);
+        }
+    } else {
+        float y[4];
+        load4<YT>(p.Y, ri.yrow, p.V, v, y);
+        const float inv = kLog2e / ri.T;
+        const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
+                                         kStreamResidual, p.key0, p.key1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lp = y[i] * inv - ri.lse2p;        // log2 p_v
+            const float lq = c[i] * inv - ri.qlse2;        // log2 q_v
+            const float rv = fast_exp2(lp) - fast_exp2(lq);
+            const float le = fast_log2(exp_from_word(ph.w[i]));
+            const float gp = lp - le;
+            if (gp > rs.gp) {
+                rs.gp = gp;
+                rs.ip = v + i;
+            }
+            if (rv > 0.f) {
+                const float gr = fast_log2(rv) - le;
+                if (gr > rs.gr) {
+                    rs.gr = gr;
+                    rs.ir = v + i;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Matrix-core kernel
+// ---------------------------------------------------------------------------------------
+
+template <HeadMode MODE, typename ZT, typename YT, int R>
+__global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadParams p) {
+    constexpr int KS = R / 32;               // MFMA k-steps
+    constexpr int LDS_STRIDE = R + 8;        // bf16 elements per LDS row (16-byte pad)
+    constexpr int CHUNKS = kTileV * R / 8;   // 16-byte chunks per W tile
+    constexpr int NT = kMfmaWaves * 64;
+    constexpr int CPT = (CHUNKS + NT - 1) / NT;  // chunks per thread
+    __shared__ __align__(16) uint16_t wt[2][kTileV * LDS_STRIDE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n_groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
+    const int group = slot % n_groups;
+    const int slab = (slot / n_groups) * 8 + xcd;
+    const int n_rows = (MODE == HeadMode::Residual) ? *p.n_rows_dev : p.n_rows_max;
+    if (group * kRowsPerGroup >= n_rows || slab >= p.n_slabs) return;  // uniform exit
+
+    const int n_tiles = (p.V + kTileV - 1) / kTileV;
+    const int t_begin = (int)((long long)slab * n_tiles / p.n_slabs);
+    const int t_end = (int)((long long)(slab + 1) * n_tiles / p.n_slabs);
+
+    // the two 16-request column blocks of this wave; lane & 15 selects the request
+    RowInfo ri[2];
+    bf16x8 ufrag[2][KS];
+    bool any_valid = false;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int row = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + (lane & 15);
+        ri[q] = row_info<MODE>(p, row, n_rows);
+        any_valid |= ri[q].valid;
+        const uint16_t *urow = p.U + (size_t)ri[q].prev * R + 8 * (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            uint4 raw = make_uint4(0, 0, 0, 0);
+            if (ri[q].valid) raw = *reinterpret_cast<const uint4 *>(urow + 32 * kk);
+            ufrag[q][kk] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+    const bool wave_active = __any(any_valid);
+
+    SampleState st[2] = {sample_state_init(), sample_state_init()};
+    ResidState rs[2] = {resid_init(), resid_init()};
+
+    // W tile t -> registers (rows beyond V read as zero)
+    uint4 wreg[CPT];
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT;
+            wreg[i] = make_uint4(0, 0, 0, 0);
+            if (c < CHUNKS) {
+                const int row = c / (R / 8), col = c % (R / 8);
+                const int v = t * kTileV + row;
+                if (v < p.V)
+                    wreg[i] = *reinterpret_cast<const uint4 *>(p.W + (size_t)v * R + col * 8);
+            }
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT;
+            if (c < CHUNKS) {
+                const int row = c / (R / 8), col = c % (R / 8);
+                *reinterpret_cast<uint4 *>(&wt[buf][row * LDS_STRIDE + col * 8]) = wreg[i];
+            }
+        }
+    };
+
+    if (t_begin < t_end) fetch(t_begin);
+    for (int t = t_begin; t < t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        stash(buf);
+        __syncthreads();
+        if (t + 1 < t_end) fetch(t + 1);
+        if (wave_active) {
+            const int v_tile = t * kTileV;
+            // base logits for this tile (issued before the matrix work)
+            float z[4][2][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int v = v_tile + 16 * j + 4 * (lane >> 4);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    if (ri[q].valid && v < p.V) {
+                        load4<ZT>(p.Z, ri[q].zrow, p.V, v, z[j][q]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) z[j][q][i] = 0.f;
+                    }
+                }
+            }
+            floatx4 acc[4][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) acc[j][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 araw = *reinterpret_cast<const uint4 *>(
+                        &wt[buf][(16 * j + (lane & 15)) * LDS_STRIDE + 32 * kk + 8 * (lane >> 4)]);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, araw);
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        acc[j][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ufrag[q][kk],
+                                                                             acc[j][q], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (!ri[q].valid) continue;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int v = v_tile + 16 * j + 4 * (lane >> 4);
+                    if (v >= p.V) continue;
+                    float c[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) c[i] = z[j][q][i] + acc[j][q][i];
+                    head_epilogue4<MODE, YT>(p, ri[q], v, c, st[q], rs[q]);
+                }
+            }
+        }
+    }
+
+    if (!wave_active) return;
+    // merge the four lanes that share a request (lane, lane^16, lane^32, lane^48)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if constexpr (MODE == HeadMode::Draft) {
+            const bool greedy = ri[q].T == 0.f;
+#pragma unroll
+            for (int mask = 16; mask <= 32; mask <<= 1) {
+                const SampleState o = shfl_xor_state(st[q], mask);
+                merge_into(st[q], o, greedy);
+            }
+        } else {
+#pragma unroll
+            for (int mask = 16; mask <= 32; mask <<= 1)
+                rs[q] = resid_merge(rs[q], resid_shfl_xor(rs[q], mask));
+        }
+        const int row = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + (lane & 15);
+        if (lane < 16 && ri[q].valid) {
+            Partial out;
+            if constexpr (MODE == HeadMode::Draft) {
+                out = to_partial(st[q]);
+            } else {
+                out.g = rs[q].gr;
+                out.idx = rs[q].ir;
+                out.m = rs[q].gp;
+                out.pad = rs[q].ip;
+                out.l = 0.f;
+                out.sb = 0.f;
+            }
+            p.partials[(size_t)row * p.n_slabs + slab] = out;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Vector-ALU kernel: one workgroup per (row, slab); float32 or bfloat16 factors, any rank.
+// ---------------------------------------------------------------------------------------
+
+template <typename FT>
+__device__ __forceinline__ float factor_at(const void *base, size_t idx);
+template <>
+__device__ __forceinline__ float factor_at<float>(const void *base, size_t idx) {
+    return reinterpret_cast<const float *>(base)[idx];
+}
+template <>
+__device__ __forceinline__ float factor_at<uint16_t>(const void *base, size_t idx) {
+    return bf16_to_f32(reinterpret_cast<const uint16_t *>(base)[idx]);
+}
+
+constexpr int kValuThreads = 256;
+constexpr int kMaxValuRank = 1024;
+
+template <HeadMode MODE, typename ZT, typename YT, typename FT>
+__global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p) {
+    __shared__ float urow[kMaxValuRank];
+    __shared__ SampleState red_st[kValuThreads / 64];
+    __shared__ ResidState red_rs[kValuThreads / 64];
+    const int slab = (int)(blockIdx.x % (unsigned)p.n_slabs);
+    const int row = (int)(blockIdx.x / (unsigned)p.n_slabs);
+    const int n_rows = (MODE == HeadMode::Residual) ? *p.n_rows_dev : p.n_rows_max;
+    const RowInfo ri = row_info<MODE>(p, row, n_rows);
+    if (!ri.valid) return;  // uniform per block
+    const void *Ub = p.Uf ? (const void *)p.Uf : (const void *)p.U;
+    const void *Wb = p.Wf ? (const void *)p.Wf : (const void *)p.W;
+    for (int i = threadIdx.x; i < p.r; i += kValuThreads)
+        urow[i] = factor_at<FT>(Ub, (size_t)ri.prev * p.r + i);
+    __syncthreads();
+
+    const int n_tiles = (p.V + kTileV - 1) / kTileV;
+    const int v_begin = (int)((long long)slab * n_tiles / p.n_slabs) * kTileV;
+    int v_end = (int)((long long)(slab + 1) * n_tiles / p.n_slabs) * kTileV;
+    if (v_end > p.V) v_end = p.V;
+
+    SampleState st = sample_state_init();
+    ResidState rs = resid_init();
+    for (int v = v_begin + 4 * threadIdx.x; v < v_end; v += 4 * kValuThreads) {
+        float z[4], c[4];
+        load4<ZT>(p.Z, ri.zrow, p.V, v, z);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float acc = 0.f;
+            const size_t wrow = (size_t)(v + i) * p.r;
+            for (int j = 0; j < p.r; ++j) acc = fmaf(urow[j], factor_at<FT>(Wb, wrow + j), acc);
+            c[i] = z[i] + acc;
+        }
+        head_epilogue4<MODE, YT>(p, ri, v, c, st, rs);
+    }
+    // block reduction
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool greedy = ri.T == 0.f;
+    for (int mask = 1; mask < 64; mask <<= 1) {
+        if constexpr (MODE == HeadMode::Draft) {
+            const SampleState o = shfl_xor_state(st, mask);
+            merge_into(st, o, greedy);
+        } else {
+            rs = resid_merge(rs, resid_shfl_xor(rs, mask));
+        }
+    }
+    if (lane == 0) {
+        red_st[wave] = st;
+        red_rs[wave] = rs;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Partial out;
+        if constexpr (MODE == HeadMode::Draft) {
+            SampleState a = red_st[0];
+            for (int w = 1; w < kValuThreads / 64; ++w)
+                merge_into(a, red_st[w], greedy);
+            out = to_partial(a);
+        } else {
+            ResidState a = red_rs[0];
+            for (int w = 1; w < kValuThreads / 64; ++w) a = resid_merge(a, red_rs[w]);
+            out.g = a.gr;
+            out.idx = a.ir;
+            out.m = a.gp;
+            out.pad = a.ip;
+            out.l = 0.f;
+            out.sb = 0.f;
+        }
+        p.partials[(size_t)row * p.n_slabs + slab] = out;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Draft: prepare (status, validated first tokens) and per-step row reduction
+// ---------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void draft_prepare_kernel(int B, int V, const int32_t *prev_token,
+                                                            int32_t *prev_cur, uint32_t *status) {
+    if (threadIdx.x == 0) *status = 0u;
+    __syncthreads();
+    for (int b = threadIdx.x; b < B; b += blockDim.x)
+        prev_cur[b] = checked_token(prev_token[b], V, status);
+}
+
+__global__ __launch_bounds__(256) void draft_reduce_kernel(int B, int K, int V, int k,
+                                                           const int32_t *draft_len,
+                                                           const float *temperature,
+                                                           const Partial *partials, int n_slabs,
+                                                           int32_t *prev_cur, int32_t *tokens,
+                                                           float *q_tok, float *q_lse,
+                                                           uint32_t *status) {
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (b >= B) return;
+    int kb = draft_len ? draft_len[b] : K;
+    if (kb < 0 || kb > K) {
+        if (lane == 0 && k == 0) atomicOr(status, DSPARK_DEV_BAD_LENGTH);
+        kb = kb < 0 ? 0 : K;
+    }
+    const size_t o = (size_t)b * K + k;
+    if (k >= kb) {
+        if (lane == 0) {
+            tokens[o] = -1;
+            q_tok[o] = 0.f;
+            q_lse[o] = 0.f;
+        }
+        return;
+    }
+    const float T = (lane == 0 && k == 0) ? checked_temperature(temperature[b], status)
+                                          : temperature[b];
+    const bool greedy = !(T > 0.f);
+    SampleState st = sample_state_init();
+    for (int s = lane; s < n_slabs; s += 64) {
+        const SampleState o2 = from_partial(partials[(size_t)b * n_slabs + s]);
+        merge_into(st, o2, greedy);
+    }
+    for (int mask = 1; mask < 64; mask <<= 1) {
+        const SampleState o2 = shfl_xor_state(st, mask);
+        merge_into(st, o2, greedy);
+    }
+    if (lane == 0) {
+        // a row with no finite score (all -inf / NaN logits) has no winner: token 0, flagged,
+        // so that the next step's gather stays inside U
+        int x = st.idx;
+        if (x < 0 || x >= V) {
+            atomicOr(status, DSPARK_DEV_BAD_TOKEN);
+            x = 0;
+        }
+        tokens[o] = x;
+        prev_cur[b] = x;
+        if (greedy) {
+            q_tok[o] = 1.f;
+            q_lse[o] = 0.f;
+        } else {
+            const float lse2 = st.m + fast_log2(st.l);
+            q_tok[o] = fast_exp2(st.sb - lse2);
+            q_lse[o] = lse2 * kLn2;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------
+
+static bool use_mfma(int uw_dtype, int r) {
+    return uw_dtype == DSPARK_BF16 && r % 32 == 0 && r >= 32 && r <= 256;
+}
+
+template <HeadMode MODE, typename ZT, typename YT>
+static hipError_t launch_head_t(const HeadParams &p, int uw_dtype, hipStream_t s) {
+    if (use_mfma(uw_dtype, p.r)) {
+        const int groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
+        const dim3 grid(p.n_slabs * groups), block(kMfmaWaves * 64);
+        switch (p.r) {
+            case 32: markov_mfma_kernel<MODE, ZT, YT, 32><<<grid, block, 0, s>>>(p); break;
+            case 64: markov_mfma_kernel<MODE, ZT, YT, 64><<<grid, block, 0, s>>>(p); break;
+            case 96: markov_mfma_kernel<MODE, ZT, YT, 96><<<grid, block, 0, s>>>(p); break;
+            case 128: markov_mfma_kernel<MODE, ZT, YT, 128><<<grid, block, 0, s>>>(p); break;
+            case 160: markov_mfma_kernel<MODE, ZT, YT, 160><<<grid, block, 0, s>>>(p); break;
+            case 192: markov_mfma_kernel<MODE, ZT, YT, 192><<<grid, block, 0, s>>>(p); break;
+            case 224: markov_mfma_kernel<MODE, ZT, YT, 224><<<grid, block, 0, s>>>(p); break;
+            case 256: markov_mfma_kernel<MODE, ZT, YT, 256><<<grid, block, 0, s>>>(p); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        const dim3 grid((unsigned)p.n_slabs * (unsigned)p.n_rows_max), block(kValuThreads);
+        if (uw_dtype == DSPARK_F32)
+            markov_valu_kernel<MODE, ZT, YT, float><<<grid, block, 0, s>>>(p);
+        else
+            markov_valu_kernel<MODE, ZT, YT, uint16_t><<<grid, block, 0, s>>>(p);
+    }
+    return hipGetLastError();
+}
+
+template <HeadMode MODE>
+static hipError_t launch_head(const HeadParams &p, int z_dtype, int uw_dtype, int y_dtype,
+                              hipStream_t s) {
+    if (z_dtype == DSPARK_BF16) {
+        if (y_dtype == DSPARK_BF16) return launch_head_t<MODE, uint16_t, uint16_t>(p, uw_dtype, s);
+        return launch_head_t<MODE, uint16_t, float>(p, uw_dtype, s);
+    }
+    if (y_dtype == DSPARK_BF16) return launch_head_t<MODE, float, uint16_t>(p, uw_dtype, s);
+    return launch_head_t<MODE, float, float>(p, uw_dtype, s);
+}
+
+static void set_factors(HeadParams &hp, const void *U, const void *W, int uw_dtype) {
+    if (uw_dtype == DSPARK_F32) {
+        hp.Uf = reinterpret_cast<const float *>(U);
+        hp.Wf = reinterpret_cast<const float *>(W);
+        hp.U = nullptr;
+        hp.W = nullptr;
+    } else {
+        hp.U = reinterpret_cast<const uint16_t *>(U);
+        hp.W = reinterpret_cast<const uint16_t *>(W);
+        hp.Uf = nullptr;
+        hp.Wf = nullptr;
+    }
+}
+
+hipError_t launch_draft_prepare(const dspark_draft_args &a, const DraftWs &ws, hipStream_t s) {
+    draft_prepare_kernel<<<1, 256, 0, s>>>(a.B, a.V, a.prev_token, ws.prev_cur, ws.status);
+    return hipGetLastError();
+}
+
+hipError_t launch_draft_step(const DraftStepParams &d, int z_dtype, int uw_dtype, hipStream_t s) {
+    HeadParams hp{};
+    hp.B = d.B;
+    hp.K = d.K;
+    hp.V = d.V;
+    hp.r = d.r;
+    hp.n_rows_max = d.B;
+    hp.n_rows_dev = nullptr;
+    hp.k = d.k;
+    hp.Z = d.Z;
+    set_factors(hp, d.U, d.W, uw_dtype);
+    hp.draft_len = d.draft_len;
+    hp.temperature = d.temperature;
+    hp.req_id = d.req_id;
+    hp.key0 = d.key0;
+    hp.key1 = d.key1;
+    hp.prev_cur = d.prev_cur;
+    hp.partials = d.partials;
+    hp.corrected = d.corrected;
+    hp.status = d.status;
+    hp.n_slabs = d.n_slabs;
+    return launch_head<HeadMode::Draft>(hp, z_dtype, uw_dtype, DSPARK_F32, s);
+}
+
+hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, int k,
+                               hipStream_t s) {
+    const int per_block = 4;  // one wave per request
+    draft_reduce_kernel<<<(a.B + per_block - 1) / per_block, 64 * per_block, 0, s>>>(
+        a.B, a.K, a.V, k, a.draft_len, a.temperature, ws.partials, ws.n_slabs, ws.prev_cur,
+        a.draft_tokens, a.q_tok, a.q_lse, ws.status);
+    return hipGetLastError();
+}
+
+hipError_t launch_verify_residual(const dspark_verify_args &a, const VerifyWs &ws,
+                                  hipStream_t s) {
+    HeadParams hp{};
+    hp.B = a.B;
+    hp.K = a.K;
+    hp.V = a.V;
+    hp.r = a.r;
+    hp.n_rows_max = a.B;
+    hp.n_rows_dev = ws.n_resid;
+    hp.k = 0;
+    hp.Z = a.Z;
+    set_factors(hp, a.U, a.W, a.uw_dtype);
+    hp.draft_len = nullptr;
+    hp.temperature = a.temperature;
+    hp.req_id = a.req_id;
+    hp.key0 = (uint32_t)(a.seed & 0xFFFFFFFFu);
+    hp.key1 = (uint32_t)(a.seed >> 32);
+    hp.resid_rows = ws.resid_rows;
+    hp.prev_token = a.prev_token;
+    hp.draft_tokens = a.draft_tokens;
+    hp.Y = a.Y;
+    hp.rowstats = ws.rowstats;
+    hp.q_lse = a.q_lse;
+    hp.partials = ws.partials;
+    hp.corrected = nullptr;
+    hp.status = ws.status;
+    hp.n_slabs = ws.n_slabs;
+    return launch_head<HeadMode::Residual>(hp, a.z_dtype, a.uw_dtype, a.y_dtype, s);
+}
+
+}  // namespace dspark

@@ -1,0 +1,331 @@
+"""Thin ctypes binding of libdspark.so (C ABI in include/dspark.h).
+
+Argument marshalling only: every step of the round runs in the HIP library.  Tensors are
+PyTorch device tensors (PyTorch provides device memory and streams); the binding checks
+their dtype / shape / contiguity, takes their data pointers and the current HIP stream, and
+raises DSparkError on a non-OK status.  The library must be built (draft_head_verification_amd
+/build.py); importing this module without it raises immediately -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdspark.so")
+
+DSPARK_OK, DSPARK_EINVAL, DSPARK_EDTYPE, DSPARK_EWORKSPACE, DSPARK_EHIP, DSPARK_EDEVICE = \
+    0, -1, -2, -3, -4, -5
+DSPARK_F32, DSPARK_BF16 = 0, 1
+DEV_BAD_TOKEN, DEV_BAD_TEMPERATURE, DEV_BAD_LENGTH, DEV_BAD_PROFILE = 0x1, 0x2, 0x4, 0x8
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, status: int, where: str, bits: int = 0):
+        self.status = status
+        self.bits = bits
+        super().__init__(f"{where}: {status_string(status)} (status {status}, device bits {bits:#x})")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m draft_head_verification_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+_p = C.c_void_p
+_i32 = C.c_int32
+
+
+class DraftArgs(C.Structure):
+    _fields_ = [("B", _i32), ("K", _i32), ("V", _i32), ("r", _i32),
+                ("z_dtype", _i32), ("uw_dtype", _i32),
+                ("Z", _p), ("U", _p), ("W", _p),
+                ("prev_token", _p), ("draft_len", _p), ("temperature", _p), ("req_id", _p),
+                ("seed", C.c_uint64),
+                ("draft_tokens", _p), ("q_tok", _p), ("q_lse", _p), ("corrected", _p),
+                ("trace", _p)]
+
+
+class ScheduleArgs(C.Structure):
+    _fields_ = [("B", _i32), ("K", _i32), ("conf_logits", _p), ("draft_len", _p),
+                ("n_knots", _i32), ("knot_tokens", _p), ("knot_tps", _p), ("enabled", _i32),
+                ("verify_len", _p), ("expected_tokens", _p), ("trace", _p)]
+
+
+class VerifyArgs(C.Structure):
+    _fields_ = [("B", _i32), ("K", _i32), ("V", _i32), ("r", _i32),
+                ("y_dtype", _i32), ("z_dtype", _i32), ("uw_dtype", _i32),
+                ("Y", _p), ("draft_tokens", _p), ("q_tok", _p), ("q_lse", _p),
+                ("Z", _p), ("U", _p), ("W", _p), ("prev_token", _p), ("verify_len", _p),
+                ("temperature", _p), ("req_id", _p), ("seed", C.c_uint64),
+                ("accept_len", _p), ("next_token", _p), ("p_tok", _p), ("trace", _p)]
+
+
+_lib.dspark_draft_workspace_size.restype = C.c_size_t
+_lib.dspark_draft_workspace_size.argtypes = [_i32] * 4
+_lib.dspark_verify_workspace_size.restype = C.c_size_t
+_lib.dspark_verify_workspace_size.argtypes = [_i32] * 4
+_lib.dspark_schedule_workspace_size.restype = C.c_size_t
+_lib.dspark_schedule_workspace_size.argtypes = [_i32] * 2
+_lib.dspark_draft_block.restype = C.c_int
+_lib.dspark_draft_block.argtypes = [C.POINTER(DraftArgs), _p, C.c_size_t, _p]
+_lib.dspark_schedule.restype = C.c_int
+_lib.dspark_schedule.argtypes = [C.POINTER(ScheduleArgs), _p, C.c_size_t, _p]
+_lib.dspark_verify.restype = C.c_int
+_lib.dspark_verify.argtypes = [C.POINTER(VerifyArgs), _p, C.c_size_t, _p]
+_lib.dspark_query_device_status.restype = C.c_int
+_lib.dspark_query_device_status.argtypes = [_p, _p, C.POINTER(C.c_uint32)]
+_lib.dspark_status_string.restype = C.c_char_p
+_lib.dspark_status_string.argtypes = [C.c_int]
+_lib.dspark_version.restype = C.c_char_p
+_lib.dspark_trace_create.restype = _p
+_lib.dspark_trace_create.argtypes = [_i32]
+_lib.dspark_trace_destroy.argtypes = [_p]
+_lib.dspark_trace_reset.argtypes = [_p]
+_lib.dspark_trace_count.restype = _i32
+_lib.dspark_trace_count.argtypes = [_p]
+_lib.dspark_trace_get.restype = C.c_int
+_lib.dspark_trace_get.argtypes = [_p, _i32, C.POINTER(C.c_char_p), C.POINTER(C.c_float)]
+
+
+def status_string(status: int) -> str:
+    return _lib.dspark_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return _lib.dspark_version().decode()
+
+
+# ----------------------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------------------
+
+_DT = {torch.float32: DSPARK_F32, torch.bfloat16: DSPARK_BF16}
+
+
+def _dev(t: torch.Tensor, name: str, dtypes=None, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def _ws(ws: torch.Tensor | None, need: int, device) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+_INT = (torch.int32,)
+_F32 = (torch.float32,)
+_LOGIT = (torch.float32, torch.bfloat16)
+
+
+class Trace:
+    """Per-kernel HIP-event timing of the calls it is passed to (dspark_trace_*)."""
+
+    def __init__(self, capacity: int = 4096):
+        self.handle = _lib.dspark_trace_create(int(capacity))
+        if not self.handle:
+            raise DSparkError(DSPARK_EHIP, "dspark_trace_create")
+
+    def reset(self):
+        _lib.dspark_trace_reset(self.handle)
+
+    def records(self):
+        out = []
+        for i in range(_lib.dspark_trace_count(self.handle)):
+            name, ms = C.c_char_p(), C.c_float()
+            st = _lib.dspark_trace_get(self.handle, i, C.byref(name), C.byref(ms))
+            if st != DSPARK_OK:
+                raise DSparkError(st, "dspark_trace_get")
+            out.append((name.value.decode(), float(ms.value)))
+        return out
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            _lib.dspark_trace_destroy(self.handle)
+            self.handle = None
+
+
+def _trace(trace):
+    return None if trace is None else trace.handle
+
+
+# ----------------------------------------------------------------------------------------
+# the C entry points
+# ----------------------------------------------------------------------------------------
+
+def dspark_draft_workspace_size(B, K, V, r) -> int:
+    return int(_lib.dspark_draft_workspace_size(B, K, V, r))
+
+
+def dspark_verify_workspace_size(B, K, V, r) -> int:
+    return int(_lib.dspark_verify_workspace_size(B, K, V, r))
+
+
+def dspark_schedule_workspace_size(B, K) -> int:
+    return int(_lib.dspark_schedule_workspace_size(B, K))
+
+
+def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok, q_lse,
+                       draft_len=None, req_id=None, corrected=None, workspace=None, stream=None,
+                       trace=None):
+    """Draft one block (see dspark_draft_block in include/dspark.h).  Returns the workspace
+    (reusable; it also carries the device status word)."""
+    B, K, V = Z.shape
+    r = U.shape[1]
+    _dev(Z, "Z", _LOGIT)
+    _dev(U, "U", _LOGIT, (V, r))
+    _dev(W, "W", (U.dtype,), (V, r))
+    _dev(prev_token, "prev_token", _INT, (B,))
+    _dev(temperature, "temperature", _F32, (B,))
+    _dev(draft_tokens, "draft_tokens", _INT, (B, K))
+    _dev(q_tok, "q_tok", _F32, (B, K))
+    _dev(q_lse, "q_lse", _F32, (B, K))
+    if draft_len is not None:
+        _dev(draft_len, "draft_len", _INT, (B,))
+    if req_id is not None:
+        _dev(req_id, "req_id", _INT, (B,))
+    if corrected is not None:
+        _dev(corrected, "corrected", _F32, (B, K, V))
+    need = dspark_draft_workspace_size(B, K, V, r)
+    ws = _ws(workspace, need, Z.device)
+    a = DraftArgs(B, K, V, r, _DT[Z.dtype], _DT[U.dtype], _ptr(Z), _ptr(U), _ptr(W),
+                  _ptr(prev_token), _ptr(draft_len), _ptr(temperature), _ptr(req_id),
+                  int(seed) & (2**64 - 1), _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse),
+                  _ptr(corrected), _trace(trace))
+    st = _lib.dspark_draft_block(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
+    if st != DSPARK_OK:
+        raise DSparkError(st, "dspark_draft_block")
+    return ws
+
+
+def dspark_schedule(conf_logits, verify_len, knot_tokens=None, knot_tps=None, enabled=True,
+                    draft_len=None, expected_tokens=None, workspace=None, stream=None, trace=None):
+    """Per-request verification lengths (see dspark_schedule in include/dspark.h)."""
+    B, K = conf_logits.shape
+    _dev(conf_logits, "conf_logits", _F32)
+    _dev(verify_len, "verify_len", _INT, (B,))
+    n_knots = 0
+    if enabled:
+        _dev(knot_tokens, "knot_tokens", (torch.float64,))
+        _dev(knot_tps, "knot_tps", (torch.float64,), knot_tokens.shape)
+        n_knots = knot_tokens.numel()
+    if draft_len is not None:
+        _dev(draft_len, "draft_len", _INT, (B,))
+    if expected_tokens is not None:
+        _dev(expected_tokens, "expected_tokens", (torch.float64,), (B,))
+    ws = _ws(workspace, dspark_schedule_workspace_size(B, K), conf_logits.device)
+    a = ScheduleArgs(B, K, _ptr(conf_logits), _ptr(draft_len), n_knots,
+                     _ptr(knot_tokens) if enabled else None, _ptr(knot_tps) if enabled else None,
+                     int(bool(enabled)), _ptr(verify_len), _ptr(expected_tokens), _trace(trace))
+    st = _lib.dspark_schedule(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
+    if st != DSPARK_OK:
+        raise DSparkError(st, "dspark_schedule")
+    return ws
+
+
+def dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature,
+                  seed, accept_len, next_token, req_id=None, p_tok=None, workspace=None,
+                  stream=None, trace=None):
+    """Rejection-sampling verification (see dspark_verify in include/dspark.h)."""
+    B, K, V = Z.shape
+    r = U.shape[1]
+    _dev(Y, "Y", _LOGIT, (B, K + 1, V))
+    _dev(draft_tokens, "draft_tokens", _INT, (B, K))
+    _dev(q_tok, "q_tok", _F32, (B, K))
+    _dev(q_lse, "q_lse", _F32, (B, K))
+    _dev(Z, "Z", _LOGIT)
+    _dev(U, "U", _LOGIT, (V, r))
+    _dev(W, "W", (U.dtype,), (V, r))
+    _dev(prev_token, "prev_token", _INT, (B,))
+    _dev(verify_len, "verify_len", _INT, (B,))
+    _dev(temperature, "temperature", _F32, (B,))
+    _dev(accept_len, "accept_len", _INT, (B,))
+    _dev(next_token, "next_token", _INT, (B,))
+    if req_id is not None:
+        _dev(req_id, "req_id", _INT, (B,))
+    if p_tok is not None:
+        _dev(p_tok, "p_tok", _F32, (B, K))
+    ws = _ws(workspace, dspark_verify_workspace_size(B, K, V, r), Z.device)
+    a = VerifyArgs(B, K, V, r, _DT[Y.dtype], _DT[Z.dtype], _DT[U.dtype], _ptr(Y),
+                   _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse), _ptr(Z), _ptr(U), _ptr(W),
+                   _ptr(prev_token), _ptr(verify_len), _ptr(temperature), _ptr(req_id),
+                   int(seed) & (2**64 - 1), _ptr(accept_len), _ptr(next_token), _ptr(p_tok),
+                   _trace(trace))
+    st = _lib.dspark_verify(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
+    if st != DSPARK_OK:
+        raise DSparkError(st, "dspark_verify")
+    return ws
+
+
+def dspark_query_device_status(workspace: torch.Tensor, stream=None) -> int:
+    """Synchronise and return the device status bits of a workspace (0 = clean)."""
+    bits = C.c_uint32(0)
+    st = _lib.dspark_query_device_status(_ptr(workspace), _stream(stream), C.byref(bits))
+    if st not in (DSPARK_OK, DSPARK_EDEVICE):
+        raise DSparkError(st, "dspark_query_device_status")
+    return int(bits.value)
+
+
+# ----------------------------------------------------------------------------------------
+# convenience: allocate outputs, run one call
+# ----------------------------------------------------------------------------------------
+
+def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=None,
+                want_corrected=False, workspace=None, trace=None):
+    B, K, V = Z.shape
+    dev = Z.device
+    out = dict(tokens=torch.empty(B, K, dtype=torch.int32, device=dev),
+               q_tok=torch.empty(B, K, dtype=torch.float32, device=dev),
+               q_lse=torch.empty(B, K, dtype=torch.float32, device=dev),
+               corrected=(torch.empty(B, K, V, dtype=torch.float32, device=dev)
+                          if want_corrected else None))
+    out["workspace"] = dspark_draft_block(Z, U, W, prev_token, temperature, seed, out["tokens"],
+                                          out["q_tok"], out["q_lse"], draft_len=draft_len,
+                                          req_id=req_id, corrected=out["corrected"],
+                                          workspace=workspace, trace=trace)
+    return out
+
+
+def schedule(conf_logits, knot_tokens=None, knot_tps=None, enabled=True, draft_len=None,
+             workspace=None, trace=None):
+    B, K = conf_logits.shape
+    dev = conf_logits.device
+    out = dict(verify_len=torch.empty(B, dtype=torch.int32, device=dev),
+               expected_tokens=torch.empty(B, dtype=torch.float64, device=dev))
+    out["workspace"] = dspark_schedule(conf_logits, out["verify_len"], knot_tokens, knot_tps,
+                                       enabled, draft_len, out["expected_tokens"], workspace,
+                                       trace=trace)
+    return out
+
+
+def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature, seed,
+           req_id=None, want_p=True, workspace=None, trace=None):
+    B, K = draft_tokens.shape
+    dev = Y.device
+    out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+               next_token=torch.empty(B, dtype=torch.int32, device=dev),
+               p_tok=torch.empty(B, K, dtype=torch.float32, device=dev) if want_p else None)
+    out["workspace"] = dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token,
+                                     verify_len, temperature, seed, out["accept_len"],
+                                     out["next_token"], req_id=req_id, p_tok=out["p_tok"],
+                                     workspace=workspace, trace=trace)
+    return out

@@ -1,0 +1,235 @@
+/*
+ * dspark.h -- C ABI of the MI355X (gfx950) DSpark round library, libdspark.so.
+ *
+ * One speculative-decoding round of a DSpark-style drafter is three calls, in the order the
+ * pages state the problem:
+ *
+ *   1. dspark_draft_block  -- the lightweight sequential head on top of the parallel backbone.
+ *      The backbone has already produced base logits for every draft position of the block;
+ *      the head walks the block left to right, adds a prefix-dependent bias taken from the
+ *      previous token only (a rank-r low-rank Markov factorisation, r = 256 by default), and
+ *      samples each position from the corrected distribution.
+ *      (QbitAI "DSpark in 10 concepts", sections "DSpark = Eagle + DFlash" and "Cheaper serial
+ *      module: the Markov head"; 10100.com commentary, section on parallel drafts turning
+ *      "of course" into "of problem".)
+ *   2. dspark_schedule     -- confidence-scheduled verification length: per-position survival
+ *      scores, their running products (probability that the whole prefix survives), and a
+ *      measured engine throughput curve decide how many draft tokens of each request are
+ *      worth verifying this round; all on the GPU, no host round trip.
+ *      (QbitAI, section "Variable-length drafts and hardware-aware scheduling"; 10100.com,
+ *      section "letting the GPU decide how much to verify"; wangjunjian.com tag page,
+ *      translated abstract.)
+ *   3. dspark_verify       -- lossless rejection-sampling verification against the target
+ *      model's logits: accept the longest prefix whose tokens pass the probability-ratio test,
+ *      resample the first rejected position from the normalised positive part of (p - q), or
+ *      draw a bonus token from p when every verified token passes.
+ *      (QbitAI, section "Speculative decoding"; 10100.com, section "speculative decoding is
+ *      block checking", rule of Leviathan et al. arXiv 2211.17192; wangjunjian.com tag page,
+ *      post "Speculative Decoding", steps 3-4.)
+ *
+ * Conventions shared by every call
+ *   - All array pointers are DEVICE pointers, caller-owned, row-major, densely packed.
+ *     The library allocates no device memory and keeps no global state: scratch space comes
+ *     from the caller's workspace (size from the *_workspace_size queries, 256-byte aligned).
+ *     Calls on distinct workspaces may run concurrently.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is asynchronous on
+ *     that stream and never synchronises the host, except dspark_query_device_status.
+ *   - Host-visible argument errors (null pointers, sizes, dtypes, workspace) are returned
+ *     before anything is launched.  A failed launch returns DSPARK_EHIP.  Errors in device
+ *     data (a token id outside [0, V), a negative or NaN temperature, a bad verify length,
+ *     non-increasing profile knots) cannot be seen without a host sync: the kernels record
+ *     them as bits of a status word in the workspace, replace the bad value by a safe one
+ *     (token 0, greedy, clamped length) so that no access leaves its buffer, and
+ *     dspark_query_device_status reports them.
+ *   - Dtypes: DSPARK_F32 (IEEE float32) or DSPARK_BF16 (bfloat16 bit patterns).
+ *   - Vocabulary size V must be a multiple of 8 (vectorised row loads).
+ *
+ * Randomness (all three calls): Philox4x32-10 (Salmon et al., SC'11) keyed by `seed`
+ * (low word, high word), counter = (v >> 2, position, request key, stream), output word v & 3,
+ * uniform u = ((word >> 8) + 0.5) / 2^24 in (0, 1).  Streams: 0 draft sampling, 1 accept test
+ * (v = 0), 2 residual resampling, 3 bonus.  Sampling is Gumbel-max:
+ * x = argmax_v (s_v - log(-log u_v)).  Results therefore depend only on (inputs, seed,
+ * request keys), not on launch geometry.  Every argmax breaks ties towards the lowest index.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSPARK_OK = 0,
+    DSPARK_EINVAL = -1,     /* a size, pointer or flag is invalid                       */
+    DSPARK_EDTYPE = -2,     /* unsupported dtype combination                            */
+    DSPARK_EWORKSPACE = -3, /* workspace missing, misaligned or smaller than required   */
+    DSPARK_EHIP = -4,       /* the HIP runtime reported an error (launch or sync)       */
+    DSPARK_EDEVICE = -5     /* device data was invalid (see dspark_query_device_status) */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* Bits of the device status word. */
+#define DSPARK_DEV_BAD_TOKEN 0x1u       /* a token id outside [0, V) was replaced by 0     */
+#define DSPARK_DEV_BAD_TEMPERATURE 0x2u /* a negative / NaN temperature was taken as 0     */
+#define DSPARK_DEV_BAD_LENGTH 0x4u      /* a draft / verify length was clamped to [0, K]   */
+#define DSPARK_DEV_BAD_PROFILE 0x8u     /* profile knots not increasing / not positive     */
+
+/* Optional per-kernel timing: when an args struct carries a trace handle, the library records
+ * a pair of HIP events around every kernel it launches for that call. */
+typedef struct dspark_trace dspark_trace;
+
+/*
+ * dspark_draft_block -- draft one block with the Markov sequential head.
+ *
+ * For request b and position k = 0 .. K_b - 1 (K_b = draft_len[b], or K):
+ *   prev   = prev_token[b] for k = 0, else x[b][k-1]          (previous token only)
+ *   c[v]   = Z[b][k][v] + sum_i U[prev][i] * W[v][i]          (float32 accumulation)
+ *   T_b = 0: x = argmax_v c[v],  q_tok = 1, q_lse = 0
+ *   T_b > 0: s = c / T_b, q_lse = log sum_v exp(s_v), x = Gumbel-max of s on stream 0 at
+ *            position k, q_tok = exp(s_x - q_lse)
+ * Positions k >= K_b get x = -1, q_tok = 0, q_lse = 0.
+ *
+ * Layouts: Z [B][K][V]; U [V][r] (row t is the left factor of token t); W [V][r] -- row v
+ * holds column v of the r x V right factor (the same layout as an output-projection weight).
+ * U and W share a dtype.  Z may be float32 or bfloat16.  Supported: r in [1, 1024]; bfloat16
+ * factors with r a multiple of 32 and r <= 256 run on the matrix cores, anything else on the
+ * vector ALUs.  K in [1, 64].  B >= 0 (B = 0 launches nothing).
+ * Outputs: draft_tokens [B][K] int32, q_tok [B][K] float32, q_lse [B][K] float32; corrected
+ * [B][K][V] float32 is optional (NULL skips it) and receives c.
+ * req_id [B] (NULL: the request index) keys the random streams of each request.
+ */
+typedef struct {
+    int32_t B, K, V, r;
+    int32_t z_dtype, uw_dtype; /* dspark_dtype */
+    const void *Z;
+    const void *U;
+    const void *W;
+    const int32_t *prev_token;  /* [B]                          */
+    const int32_t *draft_len;   /* [B] in [0, K], or NULL (= K) */
+    const float *temperature;   /* [B] >= 0; 0 = greedy         */
+    const uint32_t *req_id;     /* [B] or NULL                  */
+    uint64_t seed;
+    int32_t *draft_tokens; /* out [B][K]                 */
+    float *q_tok;          /* out [B][K]                 */
+    float *q_lse;          /* out [B][K]                 */
+    float *corrected;      /* optional out [B][K][V]     */
+    dspark_trace *trace;   /* optional                   */
+} dspark_draft_args;
+
+/*
+ * dspark_schedule -- per-request verification length.
+ *
+ * surv[b][k] = 1 / (1 + exp(-conf_logits[b][k])); P[b][k] = prod_{j <= k} surv[b][j]
+ * (float64).  Every item (b, k) with k < K_b is ranked by (P desc, k asc, b asc).  For
+ * n = 0 .. sum_b K_b:  E(n) = B + (sum of the top-n P), N(n) = B + n,
+ * G(n) = E(n) * T(N(n)) / N(n), where T is the throughput profile (tokens/s as a function of
+ * the total tokens in the verify batch) interpolated linearly between knots and clamped
+ * outside them.  n* = the smallest n maximising G; verify_len[b] = the number of request b's
+ * items among the top n* (always a prefix of its draft).  E counts one correction / bonus
+ * token per request, N one target position per verified token plus one per request.
+ * enabled = 0: verify_len = draft_len (or K).
+ * expected_tokens [B] (optional, float64) = 1 + sum_{k < verify_len[b]} P[b][k].
+ * Limits: K in [1, 64]; when enabled, sum_b K_b <= 8192 and n_knots in [1, 64]; knot tokens
+ * strictly increasing and positive, throughputs positive (checked on the device).
+ */
+typedef struct {
+    int32_t B, K;
+    const float *conf_logits;  /* [B][K]            */
+    const int32_t *draft_len;  /* [B] or NULL (= K) */
+    int32_t n_knots;
+    const double *knot_tokens; /* [n_knots]         */
+    const double *knot_tps;    /* [n_knots]         */
+    int32_t enabled;
+    int32_t *verify_len;       /* out [B]           */
+    double *expected_tokens;   /* optional out [B]  */
+    dspark_trace *trace;
+} dspark_schedule_args;
+
+/*
+ * dspark_verify -- lossless rejection-sampling verification.
+ *
+ * For request b with L = verify_len[b] (<= K) and temperature T = temperature[b]:
+ *   for k = 0 .. L-1:
+ *     T = 0: accept iff draft_tokens[b][k] == argmax_v Y[b][k][v];
+ *     T > 0: p = softmax(Y[b][k] / T); u = uniform(stream 1, position k, v = 0);
+ *            accept iff u * q_tok[b][k] < p(x_k)   (u < p/q; p >= q always passes).
+ *   First rejection at k = j: accept_len = j and next_token is
+ *     T = 0: argmax_v Y[b][j][v];
+ *     T > 0: q_j(v) = exp(c_j[v] / T - q_lse[b][j]) with c_j recomputed by the Markov head
+ *            (previous token prev_token[b] for j = 0, else draft_tokens[b][j-1]);
+ *            r = max(0, p - q_j); Gumbel-max of log r over r > 0 on stream 2 at position j;
+ *            if r is identically zero, Gumbel-max of p on stream 2.
+ *   No rejection: accept_len = L and next_token is argmax_v Y[b][L][v] (T = 0) or the
+ *   Gumbel-max of Y[b][L] / T on stream 3 at position L (the bonus token).
+ * Layouts: Y [B][K+1][V] (row K+1 exists for the bonus); draft_tokens, q_tok, q_lse [B][K]
+ * as written by dspark_draft_block; Z, U, W, prev_token, req_id, seed and the dtypes must be
+ * the ones the draft used.  Y may be float32 or bfloat16.
+ * Outputs: accept_len [B], next_token [B]; p_tok [B][K] optional: p(x_k) for each tested
+ * position (1 / 0 for a greedy match / mismatch), 0 for untested positions.
+ */
+typedef struct {
+    int32_t B, K, V, r;
+    int32_t y_dtype, z_dtype, uw_dtype;
+    const void *Y;
+    const int32_t *draft_tokens; /* [B][K] */
+    const float *q_tok;          /* [B][K] */
+    const float *q_lse;          /* [B][K] */
+    const void *Z;
+    const void *U;
+    const void *W;
+    const int32_t *prev_token;   /* [B]    */
+    const int32_t *verify_len;   /* [B]    */
+    const float *temperature;    /* [B]    */
+    const uint32_t *req_id;      /* [B] or NULL */
+    uint64_t seed;
+    int32_t *accept_len;         /* out [B]               */
+    int32_t *next_token;         /* out [B]               */
+    float *p_tok;                /* optional out [B][K]   */
+    dspark_trace *trace;
+} dspark_verify_args;
+
+/* Workspace bytes each call needs for the given sizes (0 on invalid sizes). */
+size_t dspark_draft_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r);
+size_t dspark_schedule_workspace_size(int32_t B, int32_t K);
+size_t dspark_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r);
+
+/* The three calls.  `ws` is a device buffer of at least the queried size, 256-byte aligned;
+ * `stream` is a hipStream_t.  Return DSPARK_OK once everything is enqueued. */
+dspark_status dspark_draft_block(const dspark_draft_args *args, void *ws, size_t ws_bytes,
+                                 void *stream);
+dspark_status dspark_schedule(const dspark_schedule_args *args, void *ws, size_t ws_bytes,
+                              void *stream);
+dspark_status dspark_verify(const dspark_verify_args *args, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Synchronises `stream`, then reads the device status word of workspace `ws` (written by the
+ * last call that used it).  Returns DSPARK_OK, DSPARK_EDEVICE (and the bits in *bits when
+ * bits is not NULL) or DSPARK_EHIP. */
+dspark_status dspark_query_device_status(const void *ws, void *stream, uint32_t *bits);
+
+/* Human-readable name of a status code (static string). */
+const char *dspark_status_string(dspark_status s);
+
+/* Per-kernel timing.  create: room for `capacity` launches (NULL on failure); reset: forget
+ * the recorded launches; count: launches recorded so far; get: synchronises on the i-th
+ * launch's end event and returns its kernel name and duration in milliseconds (DSPARK_EINVAL
+ * for an index out of range). */
+dspark_trace *dspark_trace_create(int32_t capacity);
+void dspark_trace_destroy(dspark_trace *t);
+void dspark_trace_reset(dspark_trace *t);
+int32_t dspark_trace_count(const dspark_trace *t);
+dspark_status dspark_trace_get(dspark_trace *t, int32_t i, const char **kernel_name,
+                               float *milliseconds);
+
+/* Library version string. */
+const char *dspark_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -116,7 +116,8 @@ def _subset(a, rows):
     try:
         import torch
         if isinstance(a, torch.Tensor):
-            return a.detach().cpu()[torch.as_tensor(rows, dtype=torch.long)].contiguous()
+            idx = torch.as_tensor(rows, dtype=torch.long, device=a.device)
+            return a.detach()[idx].cpu().contiguous()
     except ImportError:  # pragma: no cover
         pass
     return np.ascontiguousarray(np.asarray(a)[rows])

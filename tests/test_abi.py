@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every entry point include/dspark.h declares, and rejects
+invalid host-visible arguments before touching the GPU (no compute calls here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+LIB = os.path.join(ROOT, "draft_head_verification_amd", "libdspark.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdspark.so is not built (run __graft_entry__.build())")
+    return C.CDLL(LIB)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"dspark_draft_block", "dspark_schedule", "dspark_verify"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dspark.h but not exported"
+
+
+def test_binding_structs_match_header():
+    """The ctypes structs in the binding list the same fields, in order, as the C structs."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for cname, pyname in (("dspark_draft_args", "DraftArgs"), ("dspark_schedule_args", "ScheduleArgs"),
+                          ("dspark_verify_args", "VerifyArgs")):
+        body = re.search(r"typedef struct \{([^{}]*)\}\s*" + cname + ";", src).group(1)
+        fields = []
+        for decl in body.split(";"):
+            decl = decl.strip()
+            if not decl:
+                continue
+            decl = re.sub(r"^(const\s+)?[a-z_0-9]+\s*", "", decl)
+            for part in decl.split(","):
+                fields.append(part.strip().lstrip("*").strip())
+        pysrc = open(os.path.join(ROOT, "draft_head_verification_amd", "dspark.py")).read()
+        block = re.search(r"class " + pyname + r"\(C\.Structure\):\s*_fields_ = \[(.*?)\]\n\n", pysrc, re.S).group(1)
+        pyfields = re.findall(r'\("(\w+)"', block)
+        assert pyfields == fields, (cname, pyfields, fields)
+
+
+def test_workspace_queries_and_strings(lib):
+    lib.dspark_draft_workspace_size.restype = C.c_size_t
+    lib.dspark_verify_workspace_size.restype = C.c_size_t
+    lib.dspark_schedule_workspace_size.restype = C.c_size_t
+    lib.dspark_status_string.restype = C.c_char_p
+    assert lib.dspark_draft_workspace_size(256, 16, 151936, 256) > 256 * 4
+    assert lib.dspark_verify_workspace_size(256, 16, 151936, 256) > 256 * 17 * 16
+    assert lib.dspark_schedule_workspace_size(512, 16) == 256
+    # invalid sizes give 0
+    assert lib.dspark_draft_workspace_size(4, 0, 1024, 16) == 0
+    assert lib.dspark_draft_workspace_size(4, 4, 1020, 16) == 0  # V % 8 != 0
+    assert lib.dspark_draft_workspace_size(4, 65, 1024, 16) == 0
+    assert lib.dspark_draft_workspace_size(4, 4, 1024, 2048) == 0
+    assert lib.dspark_schedule_workspace_size(9000, 4) == 0
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.dspark_status_string(s)
+    lib.dspark_version.restype = C.c_char_p
+    assert b"gfx950" in lib.dspark_version()
+
+
+def test_host_validation_without_gpu():
+    """Argument errors come back before any HIP call, so they are testable on the CPU."""
+    import torch  # noqa: F401  (the binding module needs torch for its types only)
+    from draft_head_verification_amd import dspark as D
+    lib = D._lib
+    fake = 0x1000  # never dereferenced: validation fails first
+    a = D.DraftArgs(4, 4, 1024, 16, 0, 0, fake, fake, fake, fake, None, fake, None, 1,
+                    fake, fake, fake, None, None)
+    assert lib.dspark_draft_block(None, None, 0, None) == D.DSPARK_EINVAL
+    bad = D.DraftArgs(*[getattr(a, f) for f, _ in a._fields_])
+    bad.K = 0
+    assert lib.dspark_draft_block(C.byref(bad), None, 0, None) == D.DSPARK_EINVAL
+    bad.K, bad.V = 4, 1020
+    assert lib.dspark_draft_block(C.byref(bad), None, 0, None) == D.DSPARK_EINVAL
+    bad.V, bad.z_dtype = 1024, 7
+    assert lib.dspark_draft_block(C.byref(bad), None, 0, None) == D.DSPARK_EDTYPE
+    bad.z_dtype, bad.Z = 0, None
+    assert lib.dspark_draft_block(C.byref(bad), None, 0, None) == D.DSPARK_EINVAL
+    # missing / misaligned / short workspace
+    assert lib.dspark_draft_block(C.byref(a), None, 0, None) == D.DSPARK_EWORKSPACE
+    assert lib.dspark_draft_block(C.byref(a), fake + 8, 1 << 30, None) == D.DSPARK_EWORKSPACE
+    assert lib.dspark_draft_block(C.byref(a), fake, 16, None) == D.DSPARK_EWORKSPACE
+    # B = 0 is a no-op
+    empty = D.DraftArgs(*[getattr(a, f) for f, _ in a._fields_])
+    empty.B = 0
+    assert lib.dspark_draft_block(C.byref(empty), None, 0, None) == D.DSPARK_OK
+
+    s = D.ScheduleArgs(4, 4, fake, None, 0, None, None, 1, fake, None, None)
+    assert lib.dspark_schedule(C.byref(s), fake, 256, None) == D.DSPARK_EINVAL  # no knots
+    s.n_knots, s.knot_tokens, s.knot_tps = 2, fake, fake
+    s.B = 600  # B*K > 8192 with scheduling on
+    s.K = 16
+    assert lib.dspark_schedule(C.byref(s), fake, 256, None) == D.DSPARK_EINVAL
+    s.B, s.K = 4, 4
+    assert lib.dspark_schedule(C.byref(s), fake, 8, None) == D.DSPARK_EWORKSPACE
+
+    v = D.VerifyArgs(4, 4, 1024, 16, 0, 0, 0, fake, fake, fake, fake, fake, fake, fake, fake,
+                     fake, fake, None, 1, fake, fake, None, None)
+    assert lib.dspark_verify(C.byref(v), None, 0, None) == D.DSPARK_EWORKSPACE
+    v.y_dtype = 3
+    assert lib.dspark_verify(C.byref(v), None, 0, None) == D.DSPARK_EDTYPE
+    v.y_dtype, v.Y = 0, None
+    assert lib.dspark_verify(C.byref(v), None, 0, None) == D.DSPARK_EINVAL

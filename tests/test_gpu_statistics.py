@@ -1,0 +1,45 @@
+"""Losslessness through the GPU path: on a tiny vocabulary, over 2^17 request keys, the first
+token a round emits is distributed as the target p_1, and the second (given the first draft
+token was accepted) as p_2 -- the guarantee the pages state for rejection-sampling
+verification (QbitAI "DSpark in 10 concepts", section "Speculative decoding"; 10100.com,
+section on speculative decoding, rule of Leviathan et al.).  Chi-squared against the exact
+softmax computed in float64 on the CPU."""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_gpu_round_output_law_equals_target(T):
+    from draft_head_verification_amd import dspark as D
+    n, V, r, K = 1 << 17, 16, 8, 3
+    g = torch.Generator().manual_seed(21)
+    U = 0.7 * torch.randn(V, r, generator=g)
+    W = 0.7 * torch.randn(V, r, generator=g)
+    zrow = torch.randn(K, V, generator=g)
+    Yrow = 0.8 * torch.randn(K + 1, V, generator=g) + torch.cat([zrow, zrow[-1:]], 0)
+    dev = "cuda"
+    Z = zrow.expand(n, K, V).contiguous().to(dev)
+    Y = Yrow.expand(n, K + 1, V).contiguous().to(dev)
+    U, W = U.to(dev), W.to(dev)
+    prev = torch.full((n,), 2, dtype=torch.int32, device=dev)
+    temp = torch.full((n,), T, device=dev)
+    d = D.draft_block(Z, U, W, prev, temp, 4242)
+    v = D.verify(Y, d["tokens"], d["q_tok"], d["q_lse"], Z, U, W, prev,
+                 torch.full((n,), K, dtype=torch.int32, device=dev), temp, 4242)
+    a = v["accept_len"].cpu().numpy()
+    nt = v["next_token"].cpu().numpy()
+    toks = d["tokens"].cpu().numpy()
+    T32 = float(np.float32(T))
+    p1 = torch.softmax(Yrow[0].double() / T32, 0).numpy()
+    p2 = torch.softmax(Yrow[1].double() / T32, 0).numpy()
+    first = np.where(a >= 1, toks[:, 0], nt)
+    assert stats.chisquare(np.bincount(first, minlength=V), p1 * n).pvalue > 1e-4
+    sel = a >= 1
+    second = np.where(a[sel] >= 2, toks[sel, 1], nt[sel])
+    assert stats.chisquare(np.bincount(second, minlength=V), p2 * sel.sum()).pvalue > 1e-4
+    # the draft alone does not follow p_1, so the test has power
+    assert stats.chisquare(np.bincount(toks[:, 0], minlength=V), p1 * n).pvalue < 1e-6
