@@ -39,7 +39,21 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the benchmark, run a plain device copy of BYTES bytes five "
+                         "times (scales the HBM byte counters of the profiler)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int):
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 5}), flush=True)
 
 
 def build_targets_on_gpu(inp, tokens, corrected, w):
@@ -111,6 +125,9 @@ def cpu_baseline(inp, w, n_threads_hint):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path shards by "
               "request with no exchange, so multi-GPU throughput is N x the one-GPU figure; "
