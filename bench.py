@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--temperature", type=float, default=None,
+                    help="override every request's temperature (0 = greedy)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -140,7 +142,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.WORKLOADS[args.workload]
     dev = "cuda"
-    inp = synth.make_inputs(w, device=dev)
+    inp = synth.make_inputs(w, device=dev, temperature=args.temperature)
     for k in list(inp):
         if isinstance(inp[k], torch.Tensor):
             inp[k] = inp[k].contiguous()
@@ -246,7 +248,7 @@ def main():
         "data": "synthetic (seeded generator; random factors; no checkpoint)",
         "config": {"workload": f"{w.name}: B={B} K={K} V={V} r={r} base/factors "
                                f"{'bf16' if zb == 2 else 'fp32'}, target {'bf16' if yb == 2 else 'fp32'}, "
-                               f"T={','.join(str(t) for t in w.temperature)}, "
+                               f"T={args.temperature if args.temperature is not None else ','.join(str(t) for t in w.temperature)}, "
                                f"schedule {'on' if w.schedule else 'off'}",
                    "B": B, "K": K, "V": V, "r": r, "parallelism": "single GPU"},
         "roofline": roofline,

@@ -48,8 +48,8 @@ bool head_sizes_ok(int32_t B, int32_t K, int32_t V, int32_t r) {
            r <= kMaxRank;
 }
 
-// draft workspace: status | prev_cur[B] | partials[B][n_slabs]
-size_t draft_layout(int32_t B, int32_t V, DraftWs *ws, char *base) {
+// draft workspace: status | prev_cur[B] | partials[B][n_slabs] | bound[K][B]
+size_t draft_layout(int32_t B, int32_t K, int32_t V, DraftWs *ws, char *base) {
     const int ns = num_vslabs(V, B);
     size_t off = 0;
     if (ws) ws->status = reinterpret_cast<uint32_t *>(base + off);
@@ -58,6 +58,8 @@ size_t draft_layout(int32_t B, int32_t V, DraftWs *ws, char *base) {
     off += align256((size_t)B * sizeof(int32_t));
     if (ws) ws->partials = reinterpret_cast<Partial *>(base + off);
     off += align256((size_t)B * ns * sizeof(Partial));
+    if (ws) ws->bound = reinterpret_cast<uint32_t *>(base + off);
+    off += align256((size_t)B * K * sizeof(uint32_t));
     if (ws) ws->n_slabs = ns;
     return off;
 }
@@ -76,6 +78,8 @@ size_t verify_layout(int32_t B, int32_t K, int32_t V, VerifyWs *ws, char *base) 
     off += align256((size_t)B * (K + 1) * sizeof(float4));
     if (ws) ws->partials = reinterpret_cast<Partial *>(base + off);
     off += align256((size_t)B * ns * sizeof(Partial));
+    if (ws) ws->bound = reinterpret_cast<uint32_t *>(base + off);
+    off += align256((size_t)B * 2 * sizeof(uint32_t));
     if (ws) ws->n_slabs = ns;
     return off;
 }
@@ -100,7 +104,7 @@ const char *dspark_status_string(dspark_status s) {
 
 size_t dspark_draft_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r) {
     if (!head_sizes_ok(B, K, V, r)) return 0;
-    return draft_layout(B, V, nullptr, nullptr);
+    return draft_layout(B, K, V, nullptr, nullptr);
 }
 
 size_t dspark_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r) {
@@ -126,7 +130,7 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
         return DSPARK_EWORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     DraftWs w;
-    draft_layout(a->B, a->V, &w, reinterpret_cast<char *>(ws));
+    draft_layout(a->B, a->K, a->V, &w, reinterpret_cast<char *>(ws));
     hipError_t e = traced(a->trace, "draft_prepare", s,
                           [&] { return launch_draft_prepare(*a, w, s); });
     if (e != hipSuccess) return DSPARK_EHIP;
@@ -150,6 +154,7 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
     p.n_slabs = w.n_slabs;
     for (int k = 0; k < a->K; ++k) {
         p.k = k;
+        p.bound = w.bound + (size_t)k * a->B;
         e = traced(a->trace, "markov_head_step", s,
                    [&] { return launch_draft_step(p, a->z_dtype, a->uw_dtype, s); });
         if (e != hipSuccess) return DSPARK_EHIP;

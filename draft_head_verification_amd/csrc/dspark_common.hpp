@@ -107,29 +107,92 @@ __device__ __forceinline__ SampleState sample_state_init() {
 }
 
 __device__ __forceinline__ void greedy_update(SampleState &st, float c, int v) {
-    if (c > st.m) {
-        st.m = c;
-        st.idx = v;
-    }
+    const bool take = c > st.m;
+    st.m = take ? c : st.m;
+    st.idx = take ? v : st.idx;
 }
 
-// Softmax statistics of four consecutive scores (already in log2 units; -inf = masked).
+// Softmax statistics of four consecutive scores (already in log2 units; -inf = masked),
+// branch-free: an all -inf history and group leave l = 0.
 __device__ __forceinline__ void lse_update4(SampleState &st, const float s[4]) {
     const float m4 = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    if (m4 == -INFINITY) return;
     const float mn = fmaxf(st.m, m4);
-    const float scale = fast_exp2(st.m - mn);  // st.m = -inf gives 0
-    st.l = st.l * scale + fast_exp2(s[0] - mn) + fast_exp2(s[1] - mn) + fast_exp2(s[2] - mn) +
-           fast_exp2(s[3] - mn);
+    const float base = (mn == -INFINITY) ? 0.f : mn;
+    st.l = st.l * fast_exp2(st.m - base) + fast_exp2(s[0] - base) + fast_exp2(s[1] - base) +
+           fast_exp2(s[2] - base) + fast_exp2(s[3] - base);
     st.m = mn;
+}
+
+// Order-preserving map of a float to an unsigned key (key 0 is reserved for "no bound"), so
+// that the best score found by any workgroup can be shared with one unsigned atomic max.
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    if (k == 0u) return -INFINITY;
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Current shared bound (read around the L1, which may hold a stale line; a stale value is
+// still a valid, only weaker, bound).
+__device__ __forceinline__ float load_bound(const uint32_t *b) {
+    return key_to_float(__hip_atomic_load(b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Exact pruning of Gumbel-max work.  An element with noise-free score a (log2 units) beats
+// the running best g only if a - log2(E) > g, i.e. E < 2^(a - g); since E = -ln u >= 1 - u,
+// that needs 1 - u < 2^(a - g).  With k = 2^24 - 1 - (word >> 8), 1 - u = (k + 0.5) 2^-24, so
+// only words w >= candidate_threshold(max a, g) can win.  The 0.1% margin covers the rounding
+// of exp2, so every element skipped here would have lost by more than 1e-3 in log2 units: the
+// selected index is identical to evaluating every element.
+__device__ __forceinline__ uint32_t candidate_threshold(float amax, float g) {
+    const float y = fast_exp2(amax - g) * (1.001f * 16777216.0f);
+    if (!(y < 16777215.0f)) return 0u;  // also NaN / inf: everything is a candidate
+    return (0xFFFFFFu - (uint32_t)y) << 8;
+}
+
+// Per-entry form of the same test.  With a = log2 of the entry's weight and g the best
+// perturbed score, the entry can win only if E < exp2(a - g); E >= 1 - u = (d + 1/2) 2^-24
+// with d = 2^24 - 1 - (word >> 8), so d <= x * scale is necessary, where x = exp2(a - ref)
+// is already at hand and scale = exp2(ref - g + 24) (with the same 0.1% margin).  A weak
+// bound (ref - g >= 100, or no bound at all) makes every entry a candidate.
+struct PruneScale {
+    float scale;
+    bool all;
+};
+
+__device__ __forceinline__ PruneScale prune_scale(float ref_minus_g) {
+    PruneScale ps;
+    ps.all = !(ref_minus_g < 100.f);
+    ps.scale = fast_exp2(fminf(ref_minus_g, 100.f) + 24.f) * 1.001f;
+    return ps;
+}
+
+__device__ __forceinline__ bool may_win(const PruneScale &ps, float x, uint32_t word) {
+    return ps.all || (float)(0xFFFFFFu - (word >> 8)) <= x * ps.scale;
 }
 
 __device__ __forceinline__ void gumbel_update(SampleState &st, float s2, uint32_t word, int v) {
     const float g = s2 - fast_log2(exp_from_word(word));
-    if (g > st.g) {
-        st.g = g;
-        st.sb = s2;
-        st.idx = v;
+    const bool take = g > st.g;
+    st.g = take ? g : st.g;
+    st.sb = take ? s2 : st.sb;
+    st.idx = take ? v : st.idx;
+}
+
+// Gumbel-max over four consecutive scores with their Philox words, pruned as above against
+// the larger of the running best and `lb`, a perturbed score some element of the same row
+// has reached (shared between workgroups): an element below it cannot be the row's winner.
+__device__ __forceinline__ void gumbel_update4(SampleState &st, const float s[4], const uint32_t w[4],
+                                               int v, float lb = -INFINITY) {
+    const float amax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    const uint32_t t = candidate_threshold(amax, fmaxf(st.g, lb));
+    if ((w[0] >= t) | (w[1] >= t) | (w[2] >= t) | (w[3] >= t)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (w[i] >= t) gumbel_update(st, s[i], w[i], v + i);
     }
 }
 
@@ -228,7 +291,7 @@ constexpr int kTileV = 64;           // vocabulary rows per W tile (4 MFMA row b
 constexpr int kMfmaWaves = 8;        // waves per matrix-core workgroup
 constexpr int kRowsPerWave = 32;     // requests per wave (two 16-wide MFMA column blocks)
 constexpr int kRowsPerGroup = kMfmaWaves * kRowsPerWave;  // 256 requests per workgroup
-constexpr int kTargetSlabs = 1024;   // aim for this many workgroups per launch
+constexpr int kTargetSlabs = 256;    // aim for this many workgroups per launch (one per CU)
 
 // Number of V-slabs (workgroups along the vocabulary) a launch over n_rows rows uses; a
 // multiple of 8 so that the slab -> XCD mapping is a bijection.
@@ -251,6 +314,7 @@ struct DraftWs {
     uint32_t *status;    // [1] device status bits
     int32_t *prev_cur;   // [B] previous token of the current step
     Partial *partials;   // [B][n_slabs]
+    uint32_t *bound;     // [K][B] shared pruning bounds (ordered keys, 0 = none)
     int n_slabs;
 };
 
@@ -260,6 +324,7 @@ struct VerifyWs {
     int32_t *resid_rows;  // [B] packed (b * 128 + j)
     float4 *rowstats;     // [B][K+1] {m2, l, idx-as-bits, unused}
     Partial *partials;    // [B][n_slabs] residual candidates
+    uint32_t *bound;      // [B][2] shared pruning bounds of the residual / fallback draws
     int n_slabs;
 };
 
@@ -279,6 +344,7 @@ struct DraftStepParams {
     const int32_t *prev_cur;       // [B]
     Partial *partials;             // [B][n_slabs]
     float *corrected;              // [B][K][V] or null
+    uint32_t *bound;               // [B] shared pruning bounds of this step
     uint32_t *status;
     int n_slabs;
 };

@@ -51,6 +51,7 @@ struct HeadParams {
     const float *q_lse;             // residual: [B][K]
     Partial *partials;              // [rows][n_slabs]
     float *corrected;               // draft: optional [B][K][V]
+    uint32_t *bound;                // draft: [B]; residual: [B][2]; null = no sharing
     uint32_t *status;
     int n_slabs;
 };
@@ -149,39 +150,56 @@ __device__ __forceinline__ ResidState resid_shfl_xor(ResidState s, int mask) {
     return r;
 }
 
-// Four consecutive logits of a row starting at v (v % 4 == 0, v + 3 < V when v < V).
+// Four consecutive logits of a row starting at v (v % 4 == 0, v + 3 < V when v < V), kept
+// in their storage format until the epilogue needs them.
 template <typename T>
-__device__ __forceinline__ void load4(const void *base, size_t row, int V, int v, float out[4]);
-
+struct Raw4;
 template <>
-__device__ __forceinline__ void load4<uint16_t>(const void *base, size_t row, int V, int v,
-                                                float out[4]) {
-    const uint2 q = *reinterpret_cast<const uint2 *>(
-        reinterpret_cast<const uint16_t *>(base) + row * (size_t)V + v);
-    out[0] = bf16_lo(q.x);
-    out[1] = bf16_hi(q.x);
-    out[2] = bf16_lo(q.y);
-    out[3] = bf16_hi(q.y);
-}
-
+struct Raw4<uint16_t> {
+    uint2 q;
+    __device__ __forceinline__ void load(const void *base, size_t row, int V, int v) {
+        q = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(base) +
+                                             row * (size_t)V + v);
+    }
+    __device__ __forceinline__ void zero() { q = make_uint2(0u, 0u); }
+    __device__ __forceinline__ void get(float out[4]) const {
+        out[0] = bf16_lo(q.x);
+        out[1] = bf16_hi(q.x);
+        out[2] = bf16_lo(q.y);
+        out[3] = bf16_hi(q.y);
+    }
+};
 template <>
-__device__ __forceinline__ void load4<float>(const void *base, size_t row, int V, int v,
-                                             float out[4]) {
-    const float4 q = *reinterpret_cast<const float4 *>(
-        reinterpret_cast<const float *>(base) + row * (size_t)V + v);
-    out[0] = q.x;
-    out[1] = q.y;
-    out[2] = q.z;
-    out[3] = q.w;
+struct Raw4<float> {
+    float4 q;
+    __device__ __forceinline__ void load(const void *base, size_t row, int V, int v) {
+        q = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) +
+                                              row * (size_t)V + v);
+    }
+    __device__ __forceinline__ void zero() { q = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void get(float out[4]) const {
+        out[0] = q.x;
+        out[1] = q.y;
+        out[2] = q.z;
+        out[3] = q.w;
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ void load4(const void *base, size_t row, int V, int v, float out[4]) {
+    Raw4<T> r;
+    r.load(base, row, V, v);
+    r.get(out);
 }
 
 // Epilogue for four consecutive corrected logits c[0..3] = entries v..v+3 of one row.
+// `live` is false for the vocabulary tail beyond V (no output, no candidate).
 template <HeadMode MODE, typename YT>
 __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInfo &ri, int v,
-                                               const float c[4], SampleState &st,
-                                               ResidState &rs) {
+                                               bool live, const float c[4], SampleState &st,
+                                               ResidState &rs, float lb0, float lb1) {
     if constexpr (MODE == HeadMode::Draft) {
-        if (p.corrected) {
+        if (p.corrected && live) {
             float4 o;
             o.x = c[0];
             o.y = c[1];
@@ -191,40 +209,57 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
         }
         if (ri.T == 0.f) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) greedy_update(st, c[i], v + i);
+            for (int i = 0; i < 4; ++i) greedy_update(st, live ? c[i] : -INFINITY, v + i);
         } else {
             const float inv = kLog2e / ri.T;
             float s[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[i] = c[i] * inv;
+            for (int i = 0; i < 4; ++i) s[i] = live ? c[i] * inv : -INFINITY;
             lse_update4(st, s);
             const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
                                              kStreamDraft, p.key0, p.key1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gumbel_update(st, s[i], ph.w[i], v + i);
+            gumbel_update4(st, s, ph.w, v, lb0);
         }
     } else {
         float y[4];
-        load4<YT>(p.Y, ri.yrow, p.V, v, y);
+        if (live) {
+            load4<YT>(p.Y, ri.yrow, p.V, v, y);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = -INFINITY;
+        }
         const float inv = kLog2e / ri.T;
-        const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
-                                         kStreamResidual, p.key0, p.key1);
+        float lp[4], rv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float lp = y[i] * inv - ri.lse2p;        // log2 p_v
-            const float lq = c[i] * inv - ri.qlse2;        // log2 q_v
-            const float rv = fast_exp2(lp) - fast_exp2(lq);
-            const float le = fast_log2(exp_from_word(ph.w[i]));
-            const float gp = lp - le;
-            if (gp > rs.gp) {
-                rs.gp = gp;
-                rs.ip = v + i;
-            }
-            if (rv > 0.f) {
-                const float gr = fast_log2(rv) - le;
-                if (gr > rs.gr) {
-                    rs.gr = gr;
-                    rs.ir = v + i;
+            lp[i] = y[i] * inv - ri.lse2p;                       // log2 p_v
+            rv[i] = fast_exp2(lp[i]) - fast_exp2(c[i] * inv - ri.qlse2);  // p_v - q_v
+        }
+        const float lpmax = fmaxf(fmaxf(lp[0], lp[1]), fmaxf(lp[2], lp[3]));
+        const float rmax = fmaxf(fmaxf(rv[0], rv[1]), fmaxf(rv[2], rv[3]));
+        const float lrmax = rmax > 0.f ? fast_log2(rmax) : -INFINITY;
+        const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
+                                         kStreamResidual, p.key0, p.key1);
+        // residual candidates (score log2 r) and fallback candidates (score log2 p), each
+        // pruned against its own running best
+        const uint32_t tr =
+            rmax > 0.f ? candidate_threshold(lrmax, fmaxf(rs.gr, lb0)) : 0xFFFFFFFFu;
+        const uint32_t tp = candidate_threshold(lpmax, fmaxf(rs.gp, lb1));
+        const uint32_t t = min(tr, tp);
+        if ((ph.w[0] >= t) | (ph.w[1] >= t) | (ph.w[2] >= t) | (ph.w[3] >= t)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (ph.w[i] < t) continue;
+                const float le = fast_log2(exp_from_word(ph.w[i]));
+                const float gp = lp[i] - le;
+                const bool tp_ = gp > rs.gp;
+                rs.gp = tp_ ? gp : rs.gp;
+                rs.ip = tp_ ? v + i : rs.ip;
+                if (rv[i] > 0.f) {
+                    const float gr = fast_log2(rv[i]) - le;
+                    const bool tr_ = gr > rs.gr;
+                    rs.gr = tr_ ? gr : rs.gr;
+                    rs.ir = tr_ ? v + i : rs.ir;
                 }
             }
         }
@@ -233,18 +268,204 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
 
 // ---------------------------------------------------------------------------------------
 // Matrix-core kernel
+//
+// Work split: workgroup = 8 waves = up to 256 GEMM rows (requests); a slab of 64-row W tiles.
+// MFMA mapping: block j (0..3) of a tile, MFMA row m (= lane & 15) is tile row
+//   trow(j, m) = 16 (m >> 2) + 4 j + (m & 3),
+// so lane l (g = l >> 4) ends up holding tile rows 16 g .. 16 g + 15 of request (l & 15) across
+// the four blocks: 16 contiguous vocabulary entries, i.e. 16-byte base-logit loads and four
+// whole Philox blocks per lane and request.
+// W tiles reach LDS through direct global->LDS loads into a 4-stage ring (3 tiles ahead, no
+// registers); each 16-byte chunk sits at column (col ^ swz(row)) of its row, which makes the
+// A-fragment reads of the 16 lanes of a row group hit 16 different bank groups.
+// The accumulators are double-buffered: the MFMAs of tile t+1 are issued before the VALU
+// epilogue of tile t, so the matrix cores and the vector ALUs overlap within each wave.
 // ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ int tile_row(int j, int m) { return 16 * (m >> 2) + 4 * j + (m & 3); }
+
+template <int CPR>
+__device__ __forceinline__ int w_swizzle(int row) {
+    return ((((row >> 4) & 3) << 2) | (row & 3)) & (CPR - 1);
+}
+
+// 16 consecutive logits of one row (v0 % 16 == 0) held by one lane, in storage format.
+template <typename T>
+struct Raw16;
+template <>
+struct Raw16<uint16_t> {
+    uint4 q[2];
+    __device__ __forceinline__ void load(const void *base, size_t row, int V, int v0) {
+        // every lane issues both loads (a fixed count per wave); chunks past V re-read the
+        // row's last chunk and are masked by the caller
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + row * (size_t)V;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int v = min(v0 + 8 * h, V - 8);
+            q[h] = *reinterpret_cast<const uint4 *>(p + v);
+        }
+    }
+    __device__ __forceinline__ void zero() {
+        q[0] = make_uint4(0u, 0u, 0u, 0u);
+        q[1] = q[0];
+    }
+    __device__ __forceinline__ float get(int e) const {  // e is a compile-time constant
+        const uint4 &u = q[e >> 3];
+        const uint32_t w = ((e >> 1) & 3) == 0 ? u.x : ((e >> 1) & 3) == 1 ? u.y : ((e >> 1) & 3) == 2 ? u.z : u.w;
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+};
+template <>
+struct Raw16<float> {
+    float4 q[4];
+    __device__ __forceinline__ void load(const void *base, size_t row, int V, int v0) {
+        const float *p = reinterpret_cast<const float *>(base) + row * (size_t)V;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int v = min(v0 + 4 * h, V - 4);
+            q[h] = *reinterpret_cast<const float4 *>(p + v);
+        }
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) q[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __device__ __forceinline__ float get(int e) const {
+        const float4 &u = q[e >> 2];
+        return (e & 3) == 0 ? u.x : (e & 3) == 1 ? u.y : (e & 3) == 2 ? u.z : u.w;
+    }
+};
+
+// Sampling epilogue of one lane for one request over its 16 entries v0 .. v0 + 15 of a tile;
+// n_live = how many of them are < V (16 except in the last tile).
+template <HeadMode MODE, typename YT>
+__device__ __forceinline__ void tile_epilogue(const HeadParams &p, const RowInfo &ri, int v0,
+                                              int n_live, const float c[16], SampleState &st,
+                                              ResidState &rs, float lb0, float lb1) {
+    if constexpr (MODE == HeadMode::Draft) {
+        if (p.corrected) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                if (4 * h < n_live)
+                    *reinterpret_cast<float4 *>(p.corrected + ri.zrow * (size_t)p.V + v0 + 4 * h) =
+                        make_float4(c[4 * h], c[4 * h + 1], c[4 * h + 2], c[4 * h + 3]);
+        }
+        if (ri.T == 0.f) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) greedy_update(st, e < n_live ? c[e] : -INFINITY, v0 + e);
+            return;
+        }
+        const float inv = kLog2e / ri.T;
+        float s[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = e < n_live ? c[e] * inv : -INFINITY;
+        // online softmax statistics, one rescale per 16 entries
+        float m16 = s[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) m16 = fmaxf(m16, s[e]);
+        const float mn = fmaxf(st.m, m16);
+        const float base = (mn == -INFINITY) ? 0.f : mn;
+        float ex[16];
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            ex[e] = fast_exp2(s[e] - base);
+            acc += ex[e];
+        }
+        st.l = st.l * fast_exp2(st.m - base) + acc;
+        st.m = mn;
+        // Gumbel-max, pruned per entry against the best perturbed score known for the row
+        // (exp2(s - g) = ex * exp2(base - g), so the test costs one multiply per entry)
+        const PruneScale ps = prune_scale(base - fmaxf(st.g, lb0));
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+            const Philox4 ph = philox4x32_10((uint32_t)(v0 + 4 * b4) >> 2, (uint32_t)ri.pos,
+                                             ri.req, kStreamDraft, p.key0, p.key1);
+            bool cand[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cand[i] = may_win(ps, ex[4 * b4 + i], ph.w[i]);
+            if (cand[0] | cand[1] | cand[2] | cand[3]) {  // rare once a good bound is known
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (cand[i]) gumbel_update(st, s[4 * b4 + i], ph.w[i], v0 + 4 * b4 + i);
+            }
+        }
+    } else {
+        Raw16<YT> yr;
+        yr.load(p.Y, ri.yrow, p.V, v0);
+        const float inv = kLog2e / ri.T;
+        float lp[16], pv[16], rv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            lp[e] = e < n_live ? yr.get(e) * inv - ri.lse2p : -INFINITY;   // log2 p_v
+            pv[e] = fast_exp2(lp[e]);
+            rv[e] = pv[e] - fast_exp2(c[e] * inv - ri.qlse2);                // p_v - q_v
+        }
+        // two races on the same uniforms: the residual max(p - q, 0) and the fallback p;
+        // an entry is evaluated when it may win either (log2 p and log2 r are <= 0 here)
+        const PruneScale pr = prune_scale(-fmaxf(rs.gr, lb0));
+        const PruneScale pp = prune_scale(-fmaxf(rs.gp, lb1));
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+            const Philox4 ph = philox4x32_10((uint32_t)(v0 + 4 * b4) >> 2, (uint32_t)ri.pos,
+                                             ri.req, kStreamResidual, p.key0, p.key1);
+            bool cand[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * b4 + i;
+                cand[i] = (e < n_live) && (may_win(pp, pv[e], ph.w[i]) ||
+                                           (rv[e] > 0.f && may_win(pr, rv[e], ph.w[i])));
+            }
+            if (cand[0] | cand[1] | cand[2] | cand[3]) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * b4 + i;
+                    if (!cand[i]) continue;
+                    const float le = fast_log2(exp_from_word(ph.w[i]));
+                    const float gp = lp[e] - le;
+                    const bool take_p = gp > rs.gp;
+                    rs.gp = take_p ? gp : rs.gp;
+                    rs.ip = take_p ? v0 + e : rs.ip;
+                    if (rv[e] > 0.f) {
+                        const float gr = fast_log2(rv[e]) - le;
+                        const bool take_r = gr > rs.gr;
+                        rs.gr = take_r ? gr : rs.gr;
+                        rs.ir = take_r ? v0 + e : rs.ir;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
+#define DSPARK_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
 template <HeadMode MODE, typename ZT, typename YT, int R>
 __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadParams p) {
-    constexpr int KS = R / 32;               // MFMA k-steps
-    constexpr int LDS_STRIDE = R + 8;        // bf16 elements per LDS row (16-byte pad)
-    constexpr int CHUNKS = kTileV * R / 8;   // 16-byte chunks per W tile
-    constexpr int NT = kMfmaWaves * 64;
-    constexpr int CPT = (CHUNKS + NT - 1) / NT;  // chunks per thread
-    __shared__ __align__(16) uint16_t wt[2][kTileV * LDS_STRIDE];
+    static_assert(R == 64 || R == 128 || R == 256, "matrix-core path: rank 64, 128 or 256");
+    constexpr int KS = R / 32;                     // MFMA k-steps of 32
+    constexpr int CPR = R / 8;                     // 16-byte chunks per W row
+    constexpr int TILE_CH = kTileV * CPR;          // chunks per W tile
+    constexpr int LPW = TILE_CH / 64 / kMfmaWaves; // direct loads per wave per tile
+    constexpr int STAGES = 4;
+    // Vector-memory operations every wave issues per tile, unconditionally (clamped
+    // addresses): LPW global->LDS loads of W(t+3), then per row the base logits (NZ in all)
+    // and the shared bounds (NB in all) of tile t+1.  They retire in issue order, so:
+    //  * W(t) has landed once at most WAIT_W operations are pending: at least
+    //    2 LPW + NZ + NB younger ones exist at the top of iteration t (first tile: W(t0+1),
+    //    W(t0+2), the prologue's base logits and bounds; later ones have more);
+    //  * once at most LPW are pending right after the W(t+3) loads, every load of the
+    //    previous iteration -- the base logits and bounds this epilogue reads -- has landed.
+    constexpr int NZ = (sizeof(ZT) == 2) ? 4 : 8;
+    constexpr int NB = (MODE == HeadMode::Draft) ? 2 : 4;
+    constexpr int WAIT_W = 2 * LPW + NZ + NB;
+    static_assert(WAIT_W <= 63, "vmcnt range");
+    __shared__ __align__(16) uint4 wt[STAGES * TILE_CH];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
     const int n_groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
     const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
     const int group = slot % n_groups;
@@ -256,16 +477,16 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     const int t_begin = (int)((long long)slab * n_tiles / p.n_slabs);
     const int t_end = (int)((long long)(slab + 1) * n_tiles / p.n_slabs);
 
-    // the two 16-request column blocks of this wave; lane & 15 selects the request
     RowInfo ri[2];
     bf16x8 ufrag[2][KS];
     bool any_valid = false;
+    int rowid[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const int row = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + (lane & 15);
-        ri[q] = row_info<MODE>(p, row, n_rows);
+        rowid[q] = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + m;
+        ri[q] = row_info<MODE>(p, rowid[q], n_rows);
         any_valid |= ri[q].valid;
-        const uint16_t *urow = p.U + (size_t)ri[q].prev * R + 8 * (lane >> 4);
+        const uint16_t *urow = p.U + (size_t)ri[q].prev * R + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             uint4 raw = make_uint4(0, 0, 0, 0);
@@ -274,93 +495,135 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         }
     }
     const bool wave_active = __any(any_valid);
-
     SampleState st[2] = {sample_state_init(), sample_state_init()};
     ResidState rs[2] = {resid_init(), resid_init()};
 
-    // W tile t -> registers (rows beyond V read as zero)
-    uint4 wreg[CPT];
-    auto fetch = [&](int t) {
+    // per-lane A-fragment offsets (in chunks) of the four blocks, and the column key
+    int a_off[4];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            wreg[i] = make_uint4(0, 0, 0, 0);
-            if (c < CHUNKS) {
-                const int row = c / (R / 8), col = c % (R / 8);
-                const int v = t * kTileV + row;
-                if (v < p.V)
-                    wreg[i] = *reinterpret_cast<const uint4 *>(p.W + (size_t)v * R + col * 8);
+    for (int j = 0; j < 4; ++j) a_off[j] = tile_row(j, m) * CPR;
+    const int a_key = w_swizzle<CPR>(tile_row(0, m));
+
+    // W tile t -> LDS stage s, 16 bytes per lane, swizzled; tiles past the slab re-read the
+    // slab's last tile (cache-resident) so every wave issues the same number of loads.
+    auto issue_w = [&](int t, int s) {
+        const int tc = t < t_end ? t : t_end - 1;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int cb = wave * LPW + i;
+            const int P = cb * 64 + lane;
+            const int row = P / CPR, pc = P % CPR;
+            const int col = pc ^ w_swizzle<CPR>(row);
+            int v = tc * kTileV + row;
+            v = v < p.V ? v : p.V - 1;
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)(p.W + (size_t)v * R + col * 8),
+                (void __attribute__((address_space(3))) *)(wt + s * TILE_CH + cb * 64), 16, 0, 0);
+        }
+    };
+    // shared bounds of the lane's rows (rows past the batch read the last row; unused)
+    const int brow0 = min(rowid[0], p.n_rows_max - 1), brow1 = min(rowid[1], p.n_rows_max - 1);
+    auto mfma_tile = [&](int s, floatx4 (&acc)[4][2]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) acc[j][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const uint4 *base = wt + s * TILE_CH;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, base[a_off[j] + ((4 * kk + g) ^ a_key)]);
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    acc[j][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ufrag[q][kk], acc[j][q],
+                                                                         0, 0, 0);
             }
         }
     };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            if (c < CHUNKS) {
-                const int row = c / (R / 8), col = c % (R / 8);
-                *reinterpret_cast<uint4 *>(&wt[buf][row * LDS_STRIDE + col * 8]) = wreg[i];
-            }
+    // base logits and shared bound of one row of tile t (invalid rows read row 0 of Z and a
+    // valid bound; those values are never used)
+    auto load_zq = [&](int t, int q, Raw16<ZT> &z) {
+        const int tc = t < t_end ? t : t_end - 1;
+        z.load(p.Z, ri[q].zrow, p.V, tc * kTileV + 16 * g);
+    };
+    auto load_bq = [&](int q, float (&lb)[2]) {
+        const int br = q ? brow1 : brow0;
+        const bool use = ri[q].valid && ri[q].T > 0.f;
+        if constexpr (MODE == HeadMode::Draft) {
+            const float b0 = load_bound(p.bound + br);
+            lb[0] = use ? b0 : -INFINITY;
+            lb[1] = -INFINITY;
+        } else {
+            const float b0 = load_bound(p.bound + 2 * br), b1 = load_bound(p.bound + 2 * br + 1);
+            lb[0] = use ? b0 : -INFINITY;
+            lb[1] = use ? b1 : -INFINITY;
         }
     };
 
-    if (t_begin < t_end) fetch(t_begin);
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        stash(buf);
-        __syncthreads();
-        if (t + 1 < t_end) fetch(t + 1);
-        if (wave_active) {
-            const int v_tile = t * kTileV;
-            // base logits for this tile (issued before the matrix work)
-            float z[4][2][4];
+    if (t_begin < t_end) {
+        const int t0 = t_begin;
+        // prologue: W tiles t0 .. t0+2, base logits and bounds of tile t0 in flight
+        for (int u = 0; u < STAGES - 1; ++u) issue_w(t0 + u, u);
+        Raw16<ZT> z[2];
+        float lb[2][2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int v = v_tile + 16 * j + 4 * (lane >> 4);
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    if (ri[q].valid && v < p.V) {
-                        load4<ZT>(p.Z, ri[q].zrow, p.V, v, z[j][q]);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) z[j][q][i] = 0.f;
-                    }
-                }
-            }
+        for (int q = 0; q < 2; ++q) {
+            load_zq(t0, q, z[q]);
+            load_bq(q, lb[q]);
+        }
+        for (int t = t0; t < t_end; ++t) {
+            // W(t) has landed once at most WAIT_W operations are pending; after the barrier
+            // every wave is done with stage (t - 1) % 4 (untouched when t = t0), which
+            // takes tile t + 3
+            DSPARK_WAIT_VMCNT(WAIT_W);
+            __syncthreads();
+            issue_w(t + 3, (t + 3 - t0) & 3);
             floatx4 acc[4][2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) acc[j][q] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 araw = *reinterpret_cast<const uint4 *>(
-                        &wt[buf][(16 * j + (lane & 15)) * LDS_STRIDE + 32 * kk + 8 * (lane >> 4)]);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, araw);
-#pragma unroll
-                    for (int q = 0; q < 2; ++q)
-                        acc[j][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ufrag[q][kk],
-                                                                             acc[j][q], 0, 0, 0);
-                }
-            }
+            if (wave_active) mfma_tile((t - t0) & 3, acc);
+            // base logits and bounds of this tile (loaded during the previous one) have landed
+            DSPARK_WAIT_VMCNT(LPW);
+            const int v0 = t * kTileV + 16 * g;
+            const int live = min(16, p.V - v0);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                if (!ri[q].valid) continue;
+                if (wave_active && ri[q].valid) {
+                    float c[16];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int v = v_tile + 16 * j + 4 * (lane >> 4);
-                    if (v >= p.V) continue;
-                    float c[4];
+                    for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) c[i] = z[j][q][i] + acc[j][q][i];
-                    head_epilogue4<MODE, YT>(p, ri[q], v, c, st[q], rs[q]);
+                        for (int i = 0; i < 4; ++i) c[4 * j + i] = z[q].get(4 * j + i) + acc[j][q][i];
+                    tile_epilogue<MODE, YT>(p, ri[q], v0, live, c, st[q], rs[q], lb[q][0], lb[q][1]);
                 }
+                // publish this workgroup's best for the row when it beats the shared bound
+                if (wave_active) {
+                    const bool share = ri[q].valid && ri[q].T > 0.f && lane < 16;
+                    if constexpr (MODE == HeadMode::Draft) {
+                        float gg = st[q].g;
+                        gg = fmaxf(gg, __shfl_xor(gg, 16));
+                        gg = fmaxf(gg, __shfl_xor(gg, 32));
+                        if (share && gg > lb[q][0]) atomicMax(p.bound + rowid[q], ordered_key(gg));
+                    } else {
+                        float gr = rs[q].gr, gp = rs[q].gp;
+                        gr = fmaxf(gr, __shfl_xor(gr, 16));
+                        gr = fmaxf(gr, __shfl_xor(gr, 32));
+                        gp = fmaxf(gp, __shfl_xor(gp, 16));
+                        gp = fmaxf(gp, __shfl_xor(gp, 32));
+                        if (share && gr > lb[q][0])
+                            atomicMax(p.bound + 2 * rowid[q], ordered_key(gr));
+                        if (share && gp > lb[q][1])
+                            atomicMax(p.bound + 2 * rowid[q] + 1, ordered_key(gp));
+                    }
+                }
+                // this row's registers are free: fetch its next tile (every wave, every tile)
+                load_zq(t + 1, q, z[q]);
+                load_bq(q, lb[q]);
             }
         }
     }
 
+    // every global->LDS load has landed before the workgroup can exit
+    DSPARK_WAIT_VMCNT(0);
     if (!wave_active) return;
     // merge the four lanes that share a request (lane, lane^16, lane^32, lane^48)
 #pragma unroll
@@ -377,7 +640,6 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             for (int mask = 16; mask <= 32; mask <<= 1)
                 rs[q] = resid_merge(rs[q], resid_shfl_xor(rs[q], mask));
         }
-        const int row = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + (lane & 15);
         if (lane < 16 && ri[q].valid) {
             Partial out;
             if constexpr (MODE == HeadMode::Draft) {
@@ -390,7 +652,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                 out.l = 0.f;
                 out.sb = 0.f;
             }
-            p.partials[(size_t)row * p.n_slabs + slab] = out;
+            p.partials[(size_t)rowid[q] * p.n_slabs + slab] = out;
         }
     }
 }
@@ -446,7 +708,7 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
             for (int j = 0; j < p.r; ++j) acc = fmaf(urow[j], factor_at<FT>(Wb, wrow + j), acc);
             c[i] = z[i] + acc;
         }
-        head_epilogue4<MODE, YT>(p, ri, v, c, st, rs);
+        head_epilogue4<MODE, YT>(p, ri, v, true, c, st, rs, -INFINITY, -INFINITY);
     }
     // block reduction
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -489,12 +751,15 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
 // Draft: prepare (status, validated first tokens) and per-step row reduction
 // ---------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void draft_prepare_kernel(int B, int V, const int32_t *prev_token,
-                                                            int32_t *prev_cur, uint32_t *status) {
+__global__ __launch_bounds__(256) void draft_prepare_kernel(int B, int K, int V,
+                                                            const int32_t *prev_token,
+                                                            int32_t *prev_cur, uint32_t *bound,
+                                                            uint32_t *status) {
     if (threadIdx.x == 0) *status = 0u;
     __syncthreads();
     for (int b = threadIdx.x; b < B; b += blockDim.x)
         prev_cur[b] = checked_token(prev_token[b], V, status);
+    for (int i = threadIdx.x; i < B * K; i += blockDim.x) bound[i] = 0u;
 }
 
 __global__ __launch_bounds__(256) void draft_reduce_kernel(int B, int K, int V, int k,
@@ -559,7 +824,7 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(int B, int K, int V, 
 // ---------------------------------------------------------------------------------------
 
 static bool use_mfma(int uw_dtype, int r) {
-    return uw_dtype == DSPARK_BF16 && r % 32 == 0 && r >= 32 && r <= 256;
+    return uw_dtype == DSPARK_BF16 && (r == 64 || r == 128 || r == 256);
 }
 
 template <HeadMode MODE, typename ZT, typename YT>
@@ -568,13 +833,8 @@ static hipError_t launch_head_t(const HeadParams &p, int uw_dtype, hipStream_t s
         const int groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
         const dim3 grid(p.n_slabs * groups), block(kMfmaWaves * 64);
         switch (p.r) {
-            case 32: markov_mfma_kernel<MODE, ZT, YT, 32><<<grid, block, 0, s>>>(p); break;
             case 64: markov_mfma_kernel<MODE, ZT, YT, 64><<<grid, block, 0, s>>>(p); break;
-            case 96: markov_mfma_kernel<MODE, ZT, YT, 96><<<grid, block, 0, s>>>(p); break;
             case 128: markov_mfma_kernel<MODE, ZT, YT, 128><<<grid, block, 0, s>>>(p); break;
-            case 160: markov_mfma_kernel<MODE, ZT, YT, 160><<<grid, block, 0, s>>>(p); break;
-            case 192: markov_mfma_kernel<MODE, ZT, YT, 192><<<grid, block, 0, s>>>(p); break;
-            case 224: markov_mfma_kernel<MODE, ZT, YT, 224><<<grid, block, 0, s>>>(p); break;
             case 256: markov_mfma_kernel<MODE, ZT, YT, 256><<<grid, block, 0, s>>>(p); break;
             default: return hipErrorInvalidValue;
         }
@@ -614,7 +874,8 @@ static void set_factors(HeadParams &hp, const void *U, const void *W, int uw_dty
 }
 
 hipError_t launch_draft_prepare(const dspark_draft_args &a, const DraftWs &ws, hipStream_t s) {
-    draft_prepare_kernel<<<1, 256, 0, s>>>(a.B, a.V, a.prev_token, ws.prev_cur, ws.status);
+    draft_prepare_kernel<<<1, 256, 0, s>>>(a.B, a.K, a.V, a.prev_token, ws.prev_cur, ws.bound,
+                                           ws.status);
     return hipGetLastError();
 }
 
@@ -637,6 +898,7 @@ hipError_t launch_draft_step(const DraftStepParams &d, int z_dtype, int uw_dtype
     hp.prev_cur = d.prev_cur;
     hp.partials = d.partials;
     hp.corrected = d.corrected;
+    hp.bound = d.bound;
     hp.status = d.status;
     hp.n_slabs = d.n_slabs;
     return launch_head<HeadMode::Draft>(hp, z_dtype, uw_dtype, DSPARK_F32, s);
@@ -676,6 +938,7 @@ hipError_t launch_verify_residual(const dspark_verify_args &a, const VerifyWs &w
     hp.q_lse = a.q_lse;
     hp.partials = ws.partials;
     hp.corrected = nullptr;
+    hp.bound = ws.bound;
     hp.status = ws.status;
     hp.n_slabs = ws.n_slabs;
     return launch_head<HeadMode::Residual>(hp, a.z_dtype, a.uw_dtype, a.y_dtype, s);

@@ -24,11 +24,13 @@ namespace dspark {
 
 constexpr int kRowThreads = 512;
 
-__global__ __launch_bounds__(64) void verify_prepare_kernel(uint32_t *status, int32_t *n_resid) {
+__global__ __launch_bounds__(256) void verify_prepare_kernel(int B, uint32_t *status,
+                                                             int32_t *n_resid, uint32_t *bound) {
     if (threadIdx.x == 0) {
         *status = 0u;
         *n_resid = 0;
     }
+    for (int i = threadIdx.x; i < 2 * B; i += blockDim.x) bound[i] = 0u;
 }
 
 __device__ __forceinline__ int clamp_len(int L, int K, uint32_t *status, bool report) {
@@ -105,8 +107,7 @@ __global__ __launch_bounds__(kRowThreads) void verify_rowstats_kernel(
                 if (bonus) {
                     const Philox4 ph = philox4x32_10((uint32_t)(v + 4 * h) >> 2, (uint32_t)k, req,
                                                      kStreamBonus, key0, key1);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) gumbel_update(st, s[i], ph.w[i], v + 4 * h + i);
+                    gumbel_update4(st, s, ph.w, v + 4 * h);
                 }
             }
         }
@@ -240,8 +241,7 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
 // ---------------------------------------------------------------------------------------
 
 hipError_t launch_verify_prepare(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s) {
-    (void)a;
-    verify_prepare_kernel<<<1, 64, 0, s>>>(ws.status, ws.n_resid);
+    verify_prepare_kernel<<<1, 256, 0, s>>>(a.B, ws.status, ws.n_resid, ws.bound);
     return hipGetLastError();
 }
 
