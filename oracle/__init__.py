@@ -53,6 +53,11 @@ def lib() -> C.CDLL:
         L.oracle_gumbel.restype = C.c_double
         L.oracle_gumbel.argtypes = [u64, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32]
         L.oracle_uniform_batch.argtypes = [i32, u64, p, p, p, C.c_uint32, p]
+        L.oracle_block_uniform.restype = C.c_double
+        L.oracle_block_uniform.argtypes = [u64, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32]
+        L.oracle_two_level_sample.restype = i32
+        L.oracle_two_level_sample.argtypes = [i32, p, u64, C.c_uint32, C.c_uint32, C.c_uint32,
+                                              C.c_uint32, p]
         L.oracle_corrected_row.argtypes = [i32, i32, i32, p, i32, p, p, i32, p]
         L.oracle_draft_block.restype = i32
         L.oracle_draft_block.argtypes = [i32, i32, i32, i32, i32, p, i32, p, p, p, p, p, p, u64,
@@ -147,6 +152,25 @@ def uniform(seed, req, pos, v, stream):
     lib().oracle_uniform_batch(len(req), C.c_uint64(seed), _ptr(req), _ptr(pos), _ptr(v),
                                stream, _ptr(out))
     return out.reshape(shape)
+
+
+def block_uniform(seed, req, pos, beta, stream):
+    """Uniform of 16-token block beta of the two-level sampler (scalar arguments)."""
+    return lib().oracle_block_uniform(C.c_uint64(seed), req, pos, beta, stream)
+
+
+def two_level_sample(log_w, seed, req, pos, race_stream, within_stream):
+    """Two-level Gumbel-max draw from log-weights log_w [n] -> (token, margin)."""
+    a = _np(log_w, np.float64)
+    gap = np.zeros(1, np.float64)
+    x = lib().oracle_two_level_sample(len(a), _ptr(a), C.c_uint64(seed), req, pos, race_stream,
+                                      within_stream, _ptr(gap))
+    return int(x), float(gap[0])
+
+
+# stream ids of the random draws (race / within-block pairs of the two-level sampler)
+STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESIDUAL, STREAM_BONUS = 0, 1, 2, 3
+STREAM_DRAFT_WITHIN, STREAM_RESIDUAL_WITHIN, STREAM_BONUS_WITHIN = 4, 5, 6
 
 
 # ----------------------------------------------------------------------------------------

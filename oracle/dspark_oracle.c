@@ -40,12 +40,20 @@
  *  - Random numbers: Philox4x32 with 10 rounds (Salmon et al., SC'11), key = (seed low word,
  *    seed high word), counter = (v >> 2, position, request key, stream), output word v & 3,
  *    uniform = ((word >> 8) + 0.5) * 2^-24, which lies strictly inside (0, 1).
- *    Streams: 0 draft sampling, 1 accept test (v = 0), 2 residual resampling, 3 bonus.
- *  - Gumbel-max sampling: x = argmax_v (s_v + G_v), G_v = -log(-log u_v).
+ *    Streams: 0 / 4 draft sampling (block race / within the block), 1 accept test (v = 0),
+ *    2 / 5 residual resampling, 3 / 6 bonus.
+ *  - Sampling a token from weights w_v = exp(a_v) (the pages fix only the law, not how the
+ *    draw is made): a two-level Gumbel-max.  The vocabulary is cut into blocks of 16
+ *    consecutive ids (the last one may be shorter); block beta gets the log-weight
+ *    A_beta = log sum_{v in beta} w_v and the race score A_beta + G_beta, where G_beta is the
+ *    Gumbel draw of block beta on the race stream (block uniforms: see oracle_block_uniform);
+ *    the best block wins, and inside it the token with the best a_v + G_v, G_v the Gumbel draw
+ *    of token v on the within stream.  The block race picks beta with probability
+ *    W_beta / sum W and the second step v with probability w_v / W_beta, so the token has
+ *    probability w_v / sum w, the law of one Gumbel-max over all tokens.
  *  - Accept test: u * q(x) < p(x)  (equivalent to u < p/q for q > 0; p >= q always accepts).
- *  - Residual: r_v = max(0, p_v - q_v); the correction is argmax over r_v > 0 of
- *    (log r_v + G_v) on the residual stream; if every r_v is 0 the correction is drawn from
- *    p with the same stream.
+ *  - Residual: r_v = max(0, p_v - q_v); the correction is the two-level draw from the
+ *    weights r (residual streams); if every r_v is 0 it is the same draw from p.
  *  - Schedule: survival s = 1/(1+exp(-C)); P = running product over positions; rank all
  *    (request, position) items by (P desc, position asc, request asc); for n = 0..sum K_b
  *    E(n) = B + sum of the top-n P, N(n) = B + n, G(n) = E(n) * T(N(n)) / N(n) with T the
@@ -69,6 +77,12 @@
 #define ORACLE_STREAM_ACCEPT 1u
 #define ORACLE_STREAM_RESIDUAL 2u
 #define ORACLE_STREAM_BONUS 3u
+#define ORACLE_STREAM_DRAFT_WITHIN 4u
+#define ORACLE_STREAM_RESIDUAL_WITHIN 5u
+#define ORACLE_STREAM_BONUS_WITHIN 6u
+
+/* tokens per block of the two-level sampler */
+#define ORACLE_SAMPLE_BLOCK 16
 
 /* ------------------------------------------------------------------------------------ */
 /* element access                                                                         */
@@ -147,6 +161,64 @@ double oracle_gumbel(uint64_t seed, uint32_t req, uint32_t pos, uint32_t v, uint
     return -log(-log(u));
 }
 
+/* Uniform of block beta of the two-level sampler.  Writing beta = 16 a + 4 b + c
+ * (b, c in 0..3), block beta takes word b of the Philox block at counter (4 a + c, position,
+ * request key, stream): a one-to-one map from block ids to (counter, word) pairs, under which
+ * four blocks that are 16 apart share one Philox block. */
+double oracle_block_uniform(uint64_t seed, uint32_t req, uint32_t pos, uint32_t beta,
+                            uint32_t stream)
+{
+    uint32_t a = beta >> 4, b = (beta >> 2) & 3u, c = beta & 3u;
+    uint32_t ctr[4] = {4u * a + c, pos, req, stream};
+    uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    return ((double)(out[b] >> 8) + 0.5) * (1.0 / 16777216.0);
+}
+
+static int argmax_double(const double *a, int n, double *gap);
+
+/*
+ * Two-level Gumbel-max draw from log-weights a[0..n) (-inf = weight 0; at least one finite).
+ * Returns the token; *gap (optional) receives the smaller of the two decisions' margins over
+ * their runners-up (block race, then within the block), so that tests can recognise near-ties.
+ */
+int oracle_two_level_sample(int n, const double *a, uint64_t seed, uint32_t req, uint32_t pos,
+                            uint32_t race_stream, uint32_t within_stream, double *gap)
+{
+    int n_blocks = (n + ORACLE_SAMPLE_BLOCK - 1) / ORACLE_SAMPLE_BLOCK;
+    double *race = (double *)malloc(sizeof(double) * (size_t)(n_blocks > 0 ? n_blocks : 1));
+    for (int beta = 0; beta < n_blocks; ++beta) {
+        int lo = beta * ORACLE_SAMPLE_BLOCK;
+        int hi = lo + ORACLE_SAMPLE_BLOCK < n ? lo + ORACLE_SAMPLE_BLOCK : n;
+        double m = -INFINITY;
+        for (int v = lo; v < hi; ++v)
+            if (a[v] > m)
+                m = a[v];
+        if (m == -INFINITY) {
+            race[beta] = -INFINITY;
+            continue;
+        }
+        double acc = 0.0;
+        for (int v = lo; v < hi; ++v)
+            acc += exp(a[v] - m);
+        double u = oracle_block_uniform(seed, req, pos, (uint32_t)beta, race_stream);
+        race[beta] = m + log(acc) - log(-log(u));
+    }
+    double g_race, g_within;
+    int best = argmax_double(race, n_blocks, &g_race);
+    free(race);
+    int lo = best * ORACLE_SAMPLE_BLOCK;
+    int len = (lo + ORACLE_SAMPLE_BLOCK < n ? ORACLE_SAMPLE_BLOCK : n - lo);
+    double inner[ORACLE_SAMPLE_BLOCK];
+    for (int i = 0; i < len; ++i)
+        inner[i] = a[lo + i] + oracle_gumbel(seed, req, pos, (uint32_t)(lo + i), within_stream);
+    int x = lo + argmax_double(inner, len, &g_within);
+    if (gap)
+        *gap = g_race < g_within ? g_race : g_within;
+    return x;
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Markov sequential head                                                                 */
 /* ------------------------------------------------------------------------------------ */
@@ -205,13 +277,14 @@ static double log_sum_exp(const double *s, int n)
  *   prev = t0_b for k = 0, else x_{b,k-1};
  *   c = corrected row (above);
  *   T = 0: x = argmax c, q_tok = 1, q_lse = 0;
- *   T > 0: s = c / T, lse = log sum exp s, x = argmax (s_v + G_v) with the draft stream,
- *          q_tok = exp(s_x - lse), q_lse = lse.
+ *   T > 0: s = c / T, lse = log sum exp s, x = two-level Gumbel-max draw from s (draft
+ *          streams), q_tok = exp(s_x - lse), q_lse = lse.
  * Positions k >= K_b get x = -1, q_tok = 0, q_lse = 0.
  * Arrays are full-size ([B][K] / [B][K][V]); only the listed requests are written.
  * corrected (optional, [B][K][V]) receives the float corrected logits.
  * gap (optional, [B][K]) receives the winning score's margin over the runner-up
- * (c for greedy, s + G for sampling) so that near-ties can be recognised by the tests.
+ * (c for greedy; the smaller margin of the sampler's two decisions) so that near-ties can be
+ * recognised by the tests.
  * Returns 0, or -1 when a token index is out of range.
  */
 int oracle_draft_block(int B, int K, int V, int r, int z_dtype, const void *Z, int uw_dtype,
@@ -263,12 +336,8 @@ int oracle_draft_block(int B, int K, int V, int r, int z_dtype, const void *Z, i
                 for (int v = 0; v < V; ++v)
                     s[v] = (double)c[v] / T;
                 double lse = log_sum_exp(s, V);
-                double *pert = (double *)malloc(sizeof(double) * (size_t)V);
-                for (int v = 0; v < V; ++v)
-                    pert[v] = s[v] + oracle_gumbel(seed, req, (uint32_t)k, (uint32_t)v,
-                                                   ORACLE_STREAM_DRAFT);
-                x = argmax_double(pert, V, &g);
-                free(pert);
+                x = oracle_two_level_sample(V, s, seed, req, (uint32_t)k, ORACLE_STREAM_DRAFT,
+                                            ORACLE_STREAM_DRAFT_WITHIN, &g);
                 q_tok[bk] = exp(s[x] - lse);
                 q_lse[bk] = lse;
             }
@@ -420,10 +489,10 @@ int oracle_schedule(int B, int K, const float *conf_logits, const int32_t *draft
  *       T = 0: argmax Y[b][j];
  *       T > 0: q_j(v) = exp(c_{j,v} / T - q_lse[b][j]) with c_j the corrected row of position j
  *              (previous token t0 for j = 0, else x_{j-1}); r = max(0, p - q_j);
- *              argmax over r_v > 0 of log r_v + G_v (residual stream, position j);
- *              if r is identically zero, argmax of log p_v + G_v (same stream).
- *   If all L pass: accept_len = L and the bonus token is argmax Y[b][L] (T = 0) or
- *   argmax of Y[b][L]/T + G_v with the bonus stream at position L.
+ *              two-level Gumbel-max draw from log r (residual streams, position j);
+ *              if r is identically zero, the same draw from log p.
+ *   If all L pass: accept_len = L and the bonus token is argmax Y[b][L] (T = 0) or the
+ *   two-level draw from Y[b][L]/T with the bonus streams at position L.
  * Outputs: accept_len[b], next_token[b]; p_tok (optional, [B][K]) = p(x_k) for the tested
  * positions (1 for a greedy match, 0 for a greedy mismatch); diag (optional, [B][2]) =
  * {|u - p/q| of the deciding test (inf for greedy / none), margin of the sampled correction
@@ -503,17 +572,17 @@ int oracle_verify(int B, int K, int V, int r, int y_dtype, const void *Y,
                         double rv = p[v] - qv;
                         if (rv > 0.0) {
                             any = 1;
-                            score[v] = log(rv) + oracle_gumbel(seed, req, (uint32_t)k, (uint32_t)v,
-                                                               ORACLE_STREAM_RESIDUAL);
+                            score[v] = log(rv);
                         } else {
                             score[v] = -INFINITY;
                         }
                     }
                     if (!any)
                         for (int v = 0; v < V; ++v)
-                            score[v] = log(p[v]) + oracle_gumbel(seed, req, (uint32_t)k,
-                                                                 (uint32_t)v, ORACLE_STREAM_RESIDUAL);
-                    token = argmax_double(score, V, &sample_margin);
+                            score[v] = log(p[v]);
+                    token = oracle_two_level_sample(V, score, seed, req, (uint32_t)k,
+                                                    ORACLE_STREAM_RESIDUAL,
+                                                    ORACLE_STREAM_RESIDUAL_WITHIN, &sample_margin);
                 }
             }
             if (!accept) {
@@ -529,9 +598,10 @@ int oracle_verify(int B, int K, int V, int r, int y_dtype, const void *Y,
                 token = argmax_double(y, V, NULL);
             } else {
                 for (int v = 0; v < V; ++v)
-                    score[v] = y[v] / T + oracle_gumbel(seed, req, (uint32_t)L, (uint32_t)v,
-                                                        ORACLE_STREAM_BONUS);
-                token = argmax_double(score, V, &sample_margin);
+                    score[v] = y[v] / T;
+                token = oracle_two_level_sample(V, score, seed, req, (uint32_t)L,
+                                                ORACLE_STREAM_BONUS, ORACLE_STREAM_BONUS_WITHIN,
+                                                &sample_margin);
             }
         }
         accept_len[b] = a;

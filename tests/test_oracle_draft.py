@@ -1,7 +1,7 @@
 """Pins for the oracle's draft block (Markov sequential head + fused softmax / sampling).
 
 Each test checks the oracle against something fixed outside it: a library routine run in
-float64 (torch.matmul, torch.argmax, torch.logsumexp), the softmax law of Gumbel-max sampling
+float64 (torch.matmul, torch.argmax, torch.logsumexp), the softmax law of the sampler
 (chi-squared), or the pages' qualitative "of course" / "of problem" example.
 """
 import json
@@ -84,7 +84,7 @@ def _tiny_block(n_req, V, r, K, seed=0, strong=1.0):
 def test_gumbel_max_sampling_follows_softmax(T):
     """Across 200k request keys, position 1 is distributed as softmax(c_1 / T) and position 2,
     given x_1 = a, as softmax(c_2(a) / T) -- the chain feeds the sampled token back."""
-    n, V, r, K = 200_000, 16, 4, 2
+    n, V, r, K = 200_000, 40, 4, 2  # three sampler blocks, the last one 8 tokens long
     Z, U, W = _tiny_block(n, V, r, K, seed=4, strong=0.8)
     prev = torch.full((n,), 3, dtype=torch.int32)
     temp = torch.full((n,), T)

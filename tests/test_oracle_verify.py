@@ -57,7 +57,7 @@ def _emitted(d, v, i):
 
 @pytest.mark.parametrize("T", [1.0, 0.7])
 def test_output_distribution_equals_target(T):
-    n, V, r, K = 200_000, 16, 4, 3
+    n, V, r, K = 200_000, 40, 4, 3  # three sampler blocks, the last one 8 tokens long
     Z, U, W, Y, prev, temp = _setup(n, V, r, K, T, seed=11)
     d, v = _run(Z, U, W, Y, prev, temp, L=K)
     T32 = float(np.float32(T))
@@ -70,6 +70,12 @@ def test_output_distribution_equals_target(T):
     sel = t2 >= 0
     assert sel.mean() > 0.2
     assert stats.chisquare(np.bincount(t2[sel], minlength=V), p2 * sel.sum()).pvalue > 1e-4
+    # bonus draws (every draft accepted) follow the target of the extra row
+    full = v["accept_len"] == K
+    assert full.sum() > 2000
+    pb = torch.softmax(Y[0, K].double() / T32, 0).numpy()
+    assert stats.chisquare(np.bincount(v["next_token"][full], minlength=V),
+                           pb * full.sum()).pvalue > 1e-4
     # the draft law alone differs from the target here, so the test has power
     q1 = np.bincount(d["tokens"][:, 0], minlength=V)
     assert stats.chisquare(q1, p1 * n).pvalue < 1e-6
@@ -158,3 +164,18 @@ def test_zero_target_probability_rejects_immediately():
                       Z, U, W, prev, torch.full((n,), K, dtype=torch.int32), temp, 9)
     assert np.all(v["accept_len"] == 0)
     assert np.all(v["next_token"] != d["tokens"][:, 0])
+
+
+def test_bonus_draw_uses_extra_row_position_and_bonus_streams():
+    """The bonus token is the two-level draw from Y[L] / T at position L on the bonus streams
+    (a convention of where its random numbers come from: the law alone cannot tell)."""
+    n, V, r, K = 64, 40, 4, 3
+    Z, U, W, Y, prev, temp = _setup(n, V, r, K, 1.0, seed=21, zero_head=True)
+    Y = torch.cat([Z, Z[:, -1:]], 1).contiguous()  # q = p on the drafted rows: always accepted
+    for L in (0, 2, 3):
+        d, v = _run(Z, U, W, Y, prev, temp, L=L, seed=99)
+        assert np.all(v["accept_len"] == L)
+        for b in range(n):
+            want, _ = oracle.two_level_sample(Y[b, L].double().numpy(), 99, b, L,
+                                              oracle.STREAM_BONUS, oracle.STREAM_BONUS_WITHIN)
+            assert v["next_token"][b] == want
