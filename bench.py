@@ -75,14 +75,17 @@ def build_targets_on_gpu(inp, tokens, corrected, w):
     return Y
 
 
-def algorithmic_bytes(name, w, inp, vlen_host, n_resid, zb, ub, yb):
-    """Bytes the method must move per launch (reads of base logits, factors and target rows,
-    plus the outputs that leave the kernel); see the design notes for the accounting."""
+def algorithmic_bytes(name, w, inp, acc_host, n_resid, zb, ub, yb):
+    """Bytes the method must move per step, per kernel (reads of base logits, factors and
+    target rows).  The draft step runs K times, each reading the base logits of one position
+    and all of W.  The verifier needs the target rows up to the deciding one: a + 1 rows of a
+    request whose accepted length is a (the rejected row, or the bonus row when all are
+    accepted)."""
     B, K, V, r = w.B, w.K, w.V, w.r
     if name == "markov_head_step":
-        return B * V * zb + V * r * ub + B * r * ub
-    if name == "verify_rowstats":
-        return int(sum((int(L) + 1) for L in vlen_host)) * V * yb
+        return K * (B * V * zb + V * r * ub + B * r * ub)
+    if name == "verify_rows":
+        return int(sum((int(a) + 1) for a in acc_host)) * V * yb
     if name == "verify_residual":
         return n_resid * V * (zb + yb) + (V * r * ub if n_resid else 0) + n_resid * r * ub
     return None
@@ -212,17 +215,19 @@ def main():
         s = per.setdefault(name, [0, 0.0])
         s[0] += 1
         s[1] += ms
-    vlen_host = vlen.cpu().numpy()
+    acc_host = acc.cpu().numpy()
     n_resid = int(torch.from_numpy(ws_v[256:260].cpu().numpy().copy()).view(torch.int32)[0])
     kernels = []
     for name, (cnt, tot) in sorted(per.items(), key=lambda kv: -kv[1][1]):
         avg_us = tot / cnt * 1e3
-        nbytes = algorithmic_bytes(name, w, inp, vlen_host, n_resid, zb, ub, yb)
-        kernels.append({"kernel": name, "launches_per_step": cnt / args.steps,
+        nbytes = algorithmic_bytes(name, w, inp, acc_host, n_resid, zb, ub, yb)
+        lps = cnt / args.steps
+        per_launch = nbytes / lps if nbytes else None
+        kernels.append({"kernel": name, "launches_per_step": lps,
                         "avg_us": round(avg_us, 2), "share": round(tot / max(1e-9, sum(v[1] for v in per.values())), 4),
-                        "algorithmic_bytes": nbytes,
-                        "achieved_GBs": (round(nbytes / (avg_us * 1e-6) / 1e9, 1) if nbytes else None)})
-    dom = next(k for k in kernels if k["algorithmic_bytes"])
+                        "algorithmic_bytes_per_launch": (int(per_launch) if per_launch else per_launch),
+                        "achieved_GBs": (round(per_launch / (avg_us * 1e-6) / 1e9, 1) if per_launch else None)})
+    dom = next(k for k in kernels if k["algorithmic_bytes_per_launch"])
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
@@ -235,7 +240,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["achieved_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": traffic}
-    step_bytes = sum((k["algorithmic_bytes"] or 0) * k["launches_per_step"] for k in kernels)
+    step_bytes = sum((k["algorithmic_bytes_per_launch"] or 0) * k["launches_per_step"] for k in kernels)
 
     cpu = None
     if not args.no_cpu_baseline:

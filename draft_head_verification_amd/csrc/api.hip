@@ -48,8 +48,9 @@ bool head_sizes_ok(int32_t B, int32_t K, int32_t V, int32_t r) {
            r <= kMaxRank;
 }
 
-// draft workspace: status | prev_cur[B] | partials[B][n_slabs] | bound[K][B]
+// draft workspace: status | prev_cur[B] | partials[B][n_slabs]
 size_t draft_layout(int32_t B, int32_t K, int32_t V, DraftWs *ws, char *base) {
+    (void)K;
     const int ns = num_vslabs(V, B);
     size_t off = 0;
     if (ws) ws->status = reinterpret_cast<uint32_t *>(base + off);
@@ -58,29 +59,35 @@ size_t draft_layout(int32_t B, int32_t K, int32_t V, DraftWs *ws, char *base) {
     off += align256((size_t)B * sizeof(int32_t));
     if (ws) ws->partials = reinterpret_cast<Partial *>(base + off);
     off += align256((size_t)B * ns * sizeof(Partial));
-    if (ws) ws->bound = reinterpret_cast<uint32_t *>(base + off);
-    off += align256((size_t)B * K * sizeof(uint32_t));
     if (ws) ws->n_slabs = ns;
     return off;
 }
 
-// verify workspace: status | n_resid | resid_rows[B] | rowstats[B][K+1] | partials[B][n_slabs]
+// verify workspace: status | n_resid | first_reject[B] | resid_rows[B] | rowstats[B][K+1] |
+// row_partials[B][K+1][n_row_slabs] | partials[B][n_slabs]
 size_t verify_layout(int32_t B, int32_t K, int32_t V, VerifyWs *ws, char *base) {
     const int ns = num_vslabs(V, B);
+    const int nrs = num_row_slabs(V, B);
+    const size_t rows = (size_t)B * (K + 1);
     size_t off = 0;
     if (ws) ws->status = reinterpret_cast<uint32_t *>(base + off);
     off += 256;
     if (ws) ws->n_resid = reinterpret_cast<int32_t *>(base + off);
     off += 256;
+    if (ws) ws->first_reject = reinterpret_cast<int32_t *>(base + off);
+    off += align256((size_t)B * sizeof(int32_t));
     if (ws) ws->resid_rows = reinterpret_cast<int32_t *>(base + off);
     off += align256((size_t)B * sizeof(int32_t));
     if (ws) ws->rowstats = reinterpret_cast<float4 *>(base + off);
-    off += align256((size_t)B * (K + 1) * sizeof(float4));
+    off += align256(rows * sizeof(float4));
+    if (ws) ws->row_partials = reinterpret_cast<Partial *>(base + off);
+    off += align256(rows * nrs * sizeof(Partial));
     if (ws) ws->partials = reinterpret_cast<Partial *>(base + off);
     off += align256((size_t)B * ns * sizeof(Partial));
-    if (ws) ws->bound = reinterpret_cast<uint32_t *>(base + off);
-    off += align256((size_t)B * 2 * sizeof(uint32_t));
-    if (ws) ws->n_slabs = ns;
+    if (ws) {
+        ws->n_slabs = ns;
+        ws->n_row_slabs = nrs;
+    }
     return off;
 }
 
@@ -154,7 +161,6 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
     p.n_slabs = w.n_slabs;
     for (int k = 0; k < a->K; ++k) {
         p.k = k;
-        p.bound = w.bound + (size_t)k * a->B;
         e = traced(a->trace, "markov_head_step", s,
                    [&] { return launch_draft_step(p, a->z_dtype, a->uw_dtype, s); });
         if (e != hipSuccess) return DSPARK_EHIP;
@@ -200,8 +206,12 @@ dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_byt
     hipError_t e;
     e = traced(a->trace, "verify_prepare", s, [&] { return launch_verify_prepare(*a, w, s); });
     if (e != hipSuccess) return DSPARK_EHIP;
-    e = traced(a->trace, "verify_rowstats", s, [&] { return launch_verify_rowstats(*a, w, s); });
-    if (e != hipSuccess) return DSPARK_EHIP;
+    int bounds[kMaxChunks + 1];
+    const int n_chunks = verify_chunks(a->K, bounds);
+    for (int c = 0; c < n_chunks; ++c) {
+        e = traced(a->trace, "verify_rows", s, [&] { return launch_verify_rows(*a, w, c, s); });
+        if (e != hipSuccess) return DSPARK_EHIP;
+    }
     e = traced(a->trace, "verify_finish", s, [&] { return launch_verify_finish(*a, w, s); });
     if (e != hipSuccess) return DSPARK_EHIP;
     e = traced(a->trace, "verify_residual", s, [&] { return launch_verify_residual(*a, w, s); });

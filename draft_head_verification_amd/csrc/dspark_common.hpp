@@ -13,7 +13,11 @@ namespace dspark {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr uint32_t kStreamDraft = 0, kStreamAccept = 1, kStreamResidual = 2, kStreamBonus = 3;
+// Philox stream ids: the block race and the within-block draw of each sampled token, and
+// the accept test.
+constexpr uint32_t kStreamDraft = 0, kStreamAccept = 1, kStreamResidual = 2, kStreamBonus = 3,
+                   kStreamDraftWithin = 4, kStreamResidualWithin = 5, kStreamBonusWithin = 6;
+constexpr int kSampleBlock = 16;  // tokens per block of the two-level sampler
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -63,7 +67,7 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
 }
 
 // Uniform u = ((word >> 8) + 0.5) / 2^24 as float.  Exact for u < 1/2; above that the float
-// rounds to the 2^-24 grid (the accept test tolerates it; the sampler uses exp_from_word).
+// rounds to the 2^-24 grid (the accept test tolerates it; the samplers use exp_from_word).
 __device__ __forceinline__ float uniform_from_word(uint32_t word) {
     return fmaf((float)(word >> 8), 0x1p-24f, 0x1p-25f);
 }
@@ -81,18 +85,49 @@ __device__ __forceinline__ float exp_from_word(uint32_t word) {
     return d < 0x1p-8f ? series : direct;
 }
 
+// Gumbel draw of a word in log2 units: -log2(E) = log2(e) * (-ln E).
+__device__ __forceinline__ float gumbel2_from_word(uint32_t word) {
+    return -fast_log2(exp_from_word(word));
+}
+
+// Two-level sampler, block uniforms: block beta = 16 a + 4 b + c (b, c in 0..3) takes word b
+// of the Philox block at counter (4 a + c, position, request key, stream).  Four blocks 16
+// apart share one Philox block, so a lane that visits blocks beta, beta + 16, ... of one
+// lane-group position needs one Philox call per four of them.
+__device__ __forceinline__ uint32_t race_counter(uint32_t beta) {
+    return ((beta >> 4) << 2) | (beta & 3u);
+}
+
+__device__ __forceinline__ uint32_t pick_word(const Philox4 &ph, uint32_t i) {
+    return i == 0 ? ph.w[0] : (i == 1 ? ph.w[1] : (i == 2 ? ph.w[2] : ph.w[3]));
+}
+
+__device__ __forceinline__ uint32_t race_word(uint32_t beta, uint32_t pos, uint32_t req,
+                                              uint32_t stream, uint32_t k0, uint32_t k1) {
+    const Philox4 ph = philox4x32_10(race_counter(beta), pos, req, stream, k0, k1);
+    return pick_word(ph, (beta >> 2) & 3u);
+}
+
+// Word of token v for the within-block draw (and every per-token draw): word v & 3 of the
+// Philox block at counter (v >> 2, position, request key, stream).
+__device__ __forceinline__ uint32_t token_word(uint32_t v, uint32_t pos, uint32_t req,
+                                               uint32_t stream, uint32_t k0, uint32_t k1) {
+    const Philox4 ph = philox4x32_10(v >> 2, pos, req, stream, k0, k1);
+    return pick_word(ph, v & 3u);
+}
+
 // ---------------------------------------------------------------------------------------
-// Online softmax statistics + Gumbel-max / argmax candidate, in log2 units.
-//   stochastic: s2 = c * log2(e) / T; m = max s2; l = sum exp2(s2 - m);
-//               g = best s2 - log2(E) (the Gumbel-perturbed score scaled by log2 e, minus a
-//               constant), sb = s2 at the best, idx = its index.
-//   greedy:     m = max c, idx = its index (l, g, sb unused).
+// Online softmax statistics + block-race / argmax candidate, in log2 units.
+//   sampled: s2 = c * log2(e) / T; m = max s2; l = sum exp2(s2 - m);
+//            g = best race score A2 - log2(E) of a 16-token block (A2 = log2 of the block's
+//            total weight), idx = first token of that block.
+//   greedy:  m = max c, idx = its index (l, g unused).
 // Elements are visited in increasing index inside a lane (strict > keeps the lowest index);
 // merges across lanes / blocks break exact ties towards the lower index explicitly.
 // ---------------------------------------------------------------------------------------
 
 struct SampleState {
-    float m, l, g, sb;
+    float m, l, g;
     int idx;
 };
 
@@ -101,7 +136,6 @@ __device__ __forceinline__ SampleState sample_state_init() {
     s.m = -INFINITY;
     s.l = 0.f;
     s.g = -INFINITY;
-    s.sb = -INFINITY;
     s.idx = 0x7FFFFFFF;
     return s;
 }
@@ -123,77 +157,14 @@ __device__ __forceinline__ void lse_update4(SampleState &st, const float s[4]) {
     st.m = mn;
 }
 
-// Order-preserving map of a float to an unsigned key (key 0 is reserved for "no bound"), so
-// that the best score found by any workgroup can be shared with one unsigned atomic max.
-__device__ __forceinline__ uint32_t ordered_key(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-    if (k == 0u) return -INFINITY;
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// Current shared bound (read around the L1, which may hold a stale line; a stale value is
-// still a valid, only weaker, bound).
-__device__ __forceinline__ float load_bound(const uint32_t *b) {
-    return key_to_float(__hip_atomic_load(b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-
-// Exact pruning of Gumbel-max work.  An element with noise-free score a (log2 units) beats
-// the running best g only if a - log2(E) > g, i.e. E < 2^(a - g); since E = -ln u >= 1 - u,
-// that needs 1 - u < 2^(a - g).  With k = 2^24 - 1 - (word >> 8), 1 - u = (k + 0.5) 2^-24, so
-// only words w >= candidate_threshold(max a, g) can win.  The 0.1% margin covers the rounding
-// of exp2, so every element skipped here would have lost by more than 1e-3 in log2 units: the
-// selected index is identical to evaluating every element.
-__device__ __forceinline__ uint32_t candidate_threshold(float amax, float g) {
-    const float y = fast_exp2(amax - g) * (1.001f * 16777216.0f);
-    if (!(y < 16777215.0f)) return 0u;  // also NaN / inf: everything is a candidate
-    return (0xFFFFFFu - (uint32_t)y) << 8;
-}
-
-// Per-entry form of the same test.  With a = log2 of the entry's weight and g the best
-// perturbed score, the entry can win only if E < exp2(a - g); E >= 1 - u = (d + 1/2) 2^-24
-// with d = 2^24 - 1 - (word >> 8), so d <= x * scale is necessary, where x = exp2(a - ref)
-// is already at hand and scale = exp2(ref - g + 24) (with the same 0.1% margin).  A weak
-// bound (ref - g >= 100, or no bound at all) makes every entry a candidate.
-struct PruneScale {
-    float scale;
-    bool all;
-};
-
-__device__ __forceinline__ PruneScale prune_scale(float ref_minus_g) {
-    PruneScale ps;
-    ps.all = !(ref_minus_g < 100.f);
-    ps.scale = fast_exp2(fminf(ref_minus_g, 100.f) + 24.f) * 1.001f;
-    return ps;
-}
-
-__device__ __forceinline__ bool may_win(const PruneScale &ps, float x, uint32_t word) {
-    return ps.all || (float)(0xFFFFFFu - (word >> 8)) <= x * ps.scale;
-}
-
-__device__ __forceinline__ void gumbel_update(SampleState &st, float s2, uint32_t word, int v) {
-    const float g = s2 - fast_log2(exp_from_word(word));
-    const bool take = g > st.g;
-    st.g = take ? g : st.g;
-    st.sb = take ? s2 : st.sb;
-    st.idx = take ? v : st.idx;
-}
-
-// Gumbel-max over four consecutive scores with their Philox words, pruned as above against
-// the larger of the running best and `lb`, a perturbed score some element of the same row
-// has reached (shared between workgroups): an element below it cannot be the row's winner.
-__device__ __forceinline__ void gumbel_update4(SampleState &st, const float s[4], const uint32_t w[4],
-                                               int v, float lb = -INFINITY) {
-    const float amax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    const uint32_t t = candidate_threshold(amax, fmaxf(st.g, lb));
-    if ((w[0] >= t) | (w[1] >= t) | (w[2] >= t) | (w[3] >= t)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (w[i] >= t) gumbel_update(st, s[i], w[i], v + i);
-    }
+// One block of the race: `ref` + log2(sum) is the block's log2 weight (sum = 0: weight 0,
+// never drawn), `word` its race uniform, v0 its first token.
+__device__ __forceinline__ void race_update(float &g, int &idx, float ref, float sum,
+                                            uint32_t word, int v0) {
+    const float sc = sum > 0.f ? ref + fast_log2(sum) + gumbel2_from_word(word) : -INFINITY;
+    const bool take = sc > g;
+    g = take ? sc : g;
+    idx = take ? v0 : idx;
 }
 
 __device__ __forceinline__ SampleState merge_stochastic(SampleState a, SampleState b) {
@@ -203,7 +174,6 @@ __device__ __forceinline__ SampleState merge_stochastic(SampleState a, SampleSta
     const bool take_b = (b.g > a.g) || (b.g == a.g && b.idx < a.idx);
     if (take_b) {
         a.g = b.g;
-        a.sb = b.sb;
         a.idx = b.idx;
     }
     a.m = mn;
@@ -233,16 +203,16 @@ __device__ __forceinline__ SampleState shfl_xor_state(SampleState s, int mask) {
     r.m = __shfl_xor(s.m, mask);
     r.l = __shfl_xor(s.l, mask);
     r.g = __shfl_xor(s.g, mask);
-    r.sb = __shfl_xor(s.sb, mask);
     r.idx = __shfl_xor(s.idx, mask);
     return r;
 }
 
-// Partial record written per (request row, V-slab): 6 words, 8-byte aligned.
-struct __align__(8) Partial {
-    float m, l, g, sb;
+// Partial record written per (request row, V-slab): 16 bytes.  Draft rows: the sample state.
+// Residual rows: m = best p-race score, l = its block (int bits), g = best r-race score,
+// idx = its block.
+struct __align__(16) Partial {
+    float m, l, g;
     int idx;
-    int pad;
 };
 
 __device__ __forceinline__ Partial to_partial(const SampleState &s) {
@@ -250,9 +220,7 @@ __device__ __forceinline__ Partial to_partial(const SampleState &s) {
     p.m = s.m;
     p.l = s.l;
     p.g = s.g;
-    p.sb = s.sb;
     p.idx = s.idx;
-    p.pad = 0;
     return p;
 }
 
@@ -261,9 +229,147 @@ __device__ __forceinline__ SampleState from_partial(const Partial &p) {
     s.m = p.m;
     s.l = p.l;
     s.g = p.g;
-    s.sb = p.sb;
     s.idx = p.idx;
     return s;
+}
+
+// ---------------------------------------------------------------------------------------
+// Logit loads
+// ---------------------------------------------------------------------------------------
+
+// 16 consecutive logits of one row (v0 % 16 == 0) held by one lane, in storage format.
+template <typename T>
+struct Raw16;
+template <>
+struct Raw16<uint16_t> {
+    uint4 q[2];
+    __device__ __forceinline__ void load(const void *base, size_t row, int V, int v0) {
+        // every lane issues both loads (a fixed count per wave); chunks past V re-read the
+        // row's last chunk and are masked by the caller
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + row * (size_t)V;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int v = min(v0 + 8 * h, V - 8);
+            q[h] = *reinterpret_cast<const uint4 *>(p + v);
+        }
+    }
+    __device__ __forceinline__ void zero() {
+        q[0] = make_uint4(0u, 0u, 0u, 0u);
+        q[1] = q[0];
+    }
+    __device__ __forceinline__ float get(int e) const {  // e is a compile-time constant
+        const uint4 &u = q[e >> 3];
+        const uint32_t w = ((e >> 1) & 3) == 0 ? u.x : ((e >> 1) & 3) == 1 ? u.y : ((e >> 1) & 3) == 2 ? u.z : u.w;
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+};
+template <>
+struct Raw16<float> {
+    float4 q[4];
+    __device__ __forceinline__ void load(const void *base, size_t row, int V, int v0) {
+        const float *p = reinterpret_cast<const float *>(base) + row * (size_t)V;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int v = min(v0 + 4 * h, V - 4);
+            q[h] = *reinterpret_cast<const float4 *>(p + v);
+        }
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) q[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __device__ __forceinline__ float get(int e) const {
+        const float4 &u = q[e >> 2];
+        return (e & 3) == 0 ? u.x : (e & 3) == 1 ? u.y : (e & 3) == 2 ? u.z : u.w;
+    }
+};
+
+// ---------------------------------------------------------------------------------------
+// Within-block step of the two-level sampler (one wave, all 64 lanes must call)
+// ---------------------------------------------------------------------------------------
+
+__device__ __forceinline__ float load_value(const void *base, int dtype, size_t idx) {
+    return dtype == DSPARK_BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(base)[idx])
+                                : reinterpret_cast<const float *>(base)[idx];
+}
+
+// Corrected logit c_v = Z[zrow][v] + sum_i U[prev][i] W[v][i] of token v = v0 + (lane & 15),
+// accumulated in float; quarter h = lane >> 4 of the wave takes one quarter of the rank.  When
+// the quarter is a whole number of 16-byte chunks its loads are issued together as vectors.
+// Lanes whose token is past V read token V - 1; the caller masks them.
+template <typename FT, int N>
+__device__ __forceinline__ float dot_chunks(const FT *u, const FT *w, int n_chunks) {
+    float acc = 0.f;
+    for (int c = 0; c < n_chunks; c += 4) {
+        uint4 ru[4], rw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int cc = c + j < n_chunks ? c + j : n_chunks - 1;
+            ru[j] = *reinterpret_cast<const uint4 *>(u + cc * N);
+            rw[j] = *reinterpret_cast<const uint4 *>(w + cc * N);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (c + j >= n_chunks) break;
+            const uint32_t *a = reinterpret_cast<const uint32_t *>(&ru[j]);
+            const uint32_t *b = reinterpret_cast<const uint32_t *>(&rw[j]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (N == 8) {  // bf16 pairs
+                    acc = fmaf(bf16_lo(a[q]), bf16_lo(b[q]), acc);
+                    acc = fmaf(bf16_hi(a[q]), bf16_hi(b[q]), acc);
+                } else {
+                    acc = fmaf(__uint_as_float(a[q]), __uint_as_float(b[q]), acc);
+                }
+            }
+        }
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float wave_corrected16(const void *Z, int z_dtype, size_t zrow,
+                                                  const void *U, const void *W, int uw_dtype,
+                                                  int r, int V, int prev, int v0) {
+    const int lane = threadIdx.x & 63, h = lane >> 4;
+    const int v = min(v0 + (lane & 15), V - 1);
+    const float z = load_value(Z, z_dtype, zrow * (size_t)V + v);
+    float acc = 0.f;
+    const int per = uw_dtype == DSPARK_BF16 ? 8 : 4;  // elements per 16-byte chunk
+    const bool aligned = ((reinterpret_cast<uintptr_t>(U) | reinterpret_cast<uintptr_t>(W)) & 15u) == 0;
+    if (aligned && r % (4 * per) == 0) {
+        const int q = r / 4, n_chunks = q / per;
+        if (uw_dtype == DSPARK_BF16)
+            acc = dot_chunks<uint16_t, 8>(reinterpret_cast<const uint16_t *>(U) + (size_t)prev * r + h * q,
+                                          reinterpret_cast<const uint16_t *>(W) + (size_t)v * r + h * q,
+                                          n_chunks);
+        else
+            acc = dot_chunks<float, 4>(reinterpret_cast<const float *>(U) + (size_t)prev * r + h * q,
+                                       reinterpret_cast<const float *>(W) + (size_t)v * r + h * q,
+                                       n_chunks);
+    } else {
+        for (int i = h; i < r; i += 4)
+            acc = fmaf(load_value(U, uw_dtype, (size_t)prev * r + i),
+                       load_value(W, uw_dtype, (size_t)v * r + i), acc);
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    return z + acc;
+}
+
+// Best (score, token) over the 16 lanes of each quarter of the wave, ties to the lower
+// token; `aux` travels with the winner.
+__device__ __forceinline__ void wave_argmax16(float &score, int &token, float &aux) {
+#pragma unroll
+    for (int mask = 1; mask < 16; mask <<= 1) {
+        const float os = __shfl_xor(score, mask), oa = __shfl_xor(aux, mask);
+        const int ot = __shfl_xor(token, mask);
+        const bool take = os > score || (os == score && ot < token);
+        if (take) {
+            score = os;
+            token = ot;
+            aux = oa;
+        }
+    }
 }
 
 // Temperature handling shared by every kernel: negative / NaN -> greedy and flagged.
@@ -314,18 +420,29 @@ struct DraftWs {
     uint32_t *status;    // [1] device status bits
     int32_t *prev_cur;   // [B] previous token of the current step
     Partial *partials;   // [B][n_slabs]
-    uint32_t *bound;     // [K][B] shared pruning bounds (ordered keys, 0 = none)
     int n_slabs;
 };
 
+// Verification splits every target row over n_row_slabs workgroups (slabs of whole 16-token
+// blocks, about two per thread and sweep), so that a chunk of rows keeps the CUs streaming
+// even when few requests are still being verified.
+constexpr int kRowThreads = 256;
+inline int num_row_slabs(int V, int B) {
+    (void)B;
+    const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
+    const int s = (n_blk + 2 * kRowThreads - 1) / (2 * kRowThreads);
+    return s < 1 ? 1 : s;
+}
+
 struct VerifyWs {
-    uint32_t *status;     // [1]
-    int32_t *n_resid;     // [1] number of rows needing a residual draw
-    int32_t *resid_rows;  // [B] packed (b * 128 + j)
-    float4 *rowstats;     // [B][K+1] {m2, l, idx-as-bits, unused}
-    Partial *partials;    // [B][n_slabs] residual candidates
-    uint32_t *bound;      // [B][2] shared pruning bounds of the residual / fallback draws
-    int n_slabs;
+    uint32_t *status;      // [1]
+    int32_t *n_resid;      // [1] number of rows needing a residual draw
+    int32_t *first_reject; // [B] first rejected position (K + 1: none so far)
+    int32_t *resid_rows;   // [B] packed (b * 128 + j)
+    float4 *rowstats;      // [B][K+1] {m2, l, idx-as-bits, g}
+    Partial *row_partials; // [B][K+1][n_row_slabs]
+    Partial *partials;     // [B][n_slabs] residual candidates
+    int n_slabs, n_row_slabs;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -344,7 +461,6 @@ struct DraftStepParams {
     const int32_t *prev_cur;       // [B]
     Partial *partials;             // [B][n_slabs]
     float *corrected;              // [B][K][V] or null
-    uint32_t *bound;               // [B] shared pruning bounds of this step
     uint32_t *status;
     int n_slabs;
 };
@@ -357,7 +473,12 @@ hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, in
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, hipStream_t s);
 
 hipError_t launch_verify_prepare(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s);
-hipError_t launch_verify_rowstats(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s);
+// Target rows are verified in chunks (one launch each); verify_chunks fills the chunk edges
+// for K and returns their count.
+constexpr int kMaxChunks = 8;
+int verify_chunks(int K, int bounds[kMaxChunks + 1]);
+hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
+                              hipStream_t s);
 hipError_t launch_verify_finish(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s);
 hipError_t launch_verify_residual(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s);
 hipError_t launch_verify_residual_reduce(const dspark_verify_args &a, const VerifyWs &ws,

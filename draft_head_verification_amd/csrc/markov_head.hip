@@ -9,19 +9,24 @@
 // section on parallel drafts and the rank-256 transition correction).  Steps run left to right
 // because position k needs the token sampled at k-1 (QbitAI, section "DSpark = Eagle + DFlash").
 //
-// Matrix-core path (bf16 factors, r % 32 == 0, r <= 256):
+// Sampled rows use the two-level Gumbel-max draw: a race between 16-token blocks weighted by
+// their total softmax weight (one uniform per block), then a Gumbel-max inside the winning
+// block.  The head kernels run the race; the reduction kernels recompute the 16 corrected
+// logits of the winning block and draw the token inside it.
+//
+// Matrix-core path (bf16 factors, r = 64, 128 or 256):
 //   GEMM view: rows = vocabulary (M), columns = requests (N), reduction = r (K).
 //   A workgroup of 8 waves owns up to 256 requests (32 per wave, two 16-wide column blocks)
 //   and a contiguous slab of the vocabulary.  Each wave keeps its requests' gathered U rows
 //   in registers as MFMA B fragments for the whole slab.  The slab streams through LDS in
-//   tiles of 64 vocabulary rows of W (double-buffered, one barrier per tile); every wave reads
-//   its A fragments from the shared tile, so W leaves HBM once per 256 requests.
-//   v_mfma_f32_16x16x32_bf16 leaves each lane 4 consecutive vocabulary entries of one
-//   request, which is exactly one Philox4x32 block: the Gumbel noise costs one Philox call
-//   per 4 outputs with no data exchange.
-//   Workgroups are laid out so that the (up to 2) request groups sharing a vocabulary slab
-//   are dispatched to the same XCD and meet the slab's W tiles in that XCD's L2.
-// Vector-ALU path (any other factor dtype / rank): one workgroup per (request, slab).
+//   tiles of 64 vocabulary rows of W (direct global->LDS loads, four stages, one barrier per
+//   tile); every wave reads its A fragments from the shared tile, so W leaves HBM once per
+//   256 requests.  The fragment layout leaves each lane 16 consecutive vocabulary entries of
+//   a request per tile: exactly one sampler block, so the block sums need no data exchange.
+//   Workgroups are laid out so that the request groups sharing a vocabulary slab are
+//   dispatched to the same XCD and meet the slab's W tiles in that XCD's L2.
+// Vector-ALU path (any other factor dtype / rank): one workgroup per (request, slab); four
+// neighbouring lanes hold one sampler block.
 #include "dspark_common.hpp"
 
 namespace dspark {
@@ -51,7 +56,6 @@ struct HeadParams {
     const float *q_lse;             // residual: [B][K]
     Partial *partials;              // [rows][n_slabs]
     float *corrected;               // draft: optional [B][K][V]
-    uint32_t *bound;                // draft: [B]; residual: [B][2]; null = no sharing
     uint32_t *status;
     int n_slabs;
 };
@@ -112,9 +116,9 @@ __device__ __forceinline__ RowInfo row_info(const HeadParams &p, int row, int n_
     return ri;
 }
 
-// Residual candidates: best score over r = p - q > 0 and, as the fallback when the residual
-// is identically zero, best score over p.  Packed into a Partial as
-// {g: best r-score, idx: its index, m: best p-score, pad: its index}.
+// Residual race: best block over the weights r = max(p - q, 0) and, as the fallback when the
+// residual is identically zero, best block over p.  Packed into a Partial as
+// {g: best r-score, idx: its block, m: best p-score, l: its block (int bits)}.
 struct ResidState {
     float gr, gp;
     int ir, ip;
@@ -192,12 +196,15 @@ __device__ __forceinline__ void load4(const void *base, size_t row, int V, int v
     r.get(out);
 }
 
-// Epilogue for four consecutive corrected logits c[0..3] = entries v..v+3 of one row.
-// `live` is false for the vocabulary tail beyond V (no output, no candidate).
+// Epilogue for four consecutive corrected logits c[0..3] = entries v..v+3 of one row, v a
+// multiple of 4; lanes 4j..4j+3 of the workgroup hold one 16-token sampler block and every
+// lane must call this (the block sums are exchanged between them).  `live` is false past
+// the slab end (no output, weight 0).
 template <HeadMode MODE, typename YT>
 __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInfo &ri, int v,
                                                bool live, const float c[4], SampleState &st,
-                                               ResidState &rs, float lb0, float lb1) {
+                                               ResidState &rs) {
+    const bool lead = (threadIdx.x & 3) == 0;  // holds the block's first token
     if constexpr (MODE == HeadMode::Draft) {
         if (p.corrected && live) {
             float4 o;
@@ -207,18 +214,28 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
             o.w = c[3];
             *reinterpret_cast<float4 *>(p.corrected + ri.zrow * (size_t)p.V + v) = o;
         }
-        if (ri.T == 0.f) {
+        if (ri.T == 0.f) {  // uniform: one row per workgroup
 #pragma unroll
             for (int i = 0; i < 4; ++i) greedy_update(st, live ? c[i] : -INFINITY, v + i);
-        } else {
-            const float inv = kLog2e / ri.T;
-            float s[4];
+            return;
+        }
+        const float inv = kLog2e / ri.T;
+        float s[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[i] = live ? c[i] * inv : -INFINITY;
-            lse_update4(st, s);
-            const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
-                                             kStreamDraft, p.key0, p.key1);
-            gumbel_update4(st, s, ph.w, v, lb0);
+        for (int i = 0; i < 4; ++i) s[i] = live ? c[i] * inv : -INFINITY;
+        lse_update4(st, s);
+        float M = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        M = fmaxf(M, __shfl_xor(M, 1));
+        M = fmaxf(M, __shfl_xor(M, 2));
+        const float ref = (M == -INFINITY) ? 0.f : M;
+        float a = fast_exp2(s[0] - ref) + fast_exp2(s[1] - ref) + fast_exp2(s[2] - ref) +
+                  fast_exp2(s[3] - ref);
+        a += __shfl_xor(a, 1);
+        a += __shfl_xor(a, 2);
+        if (lead) {
+            const uint32_t w = race_word((uint32_t)v >> 4, (uint32_t)ri.pos, ri.req,
+                                         kStreamDraft, p.key0, p.key1);
+            race_update(st.g, st.idx, ref, a, w, v);
         }
     } else {
         float y[4];
@@ -229,39 +246,23 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
             for (int i = 0; i < 4; ++i) y[i] = -INFINITY;
         }
         const float inv = kLog2e / ri.T;
-        float lp[4], rv[4];
+        float R = 0.f, P = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            lp[i] = y[i] * inv - ri.lse2p;                       // log2 p_v
-            rv[i] = fast_exp2(lp[i]) - fast_exp2(c[i] * inv - ri.qlse2);  // p_v - q_v
+            const float pv = fast_exp2(y[i] * inv - ri.lse2p);
+            const float rv = pv - fast_exp2(c[i] * inv - ri.qlse2);
+            R += live ? fmaxf(rv, 0.f) : 0.f;
+            P += pv;
         }
-        const float lpmax = fmaxf(fmaxf(lp[0], lp[1]), fmaxf(lp[2], lp[3]));
-        const float rmax = fmaxf(fmaxf(rv[0], rv[1]), fmaxf(rv[2], rv[3]));
-        const float lrmax = rmax > 0.f ? fast_log2(rmax) : -INFINITY;
-        const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
+        R += __shfl_xor(R, 1);
+        R += __shfl_xor(R, 2);
+        P += __shfl_xor(P, 1);
+        P += __shfl_xor(P, 2);
+        if (lead) {
+            const uint32_t w = race_word((uint32_t)v >> 4, (uint32_t)ri.pos, ri.req,
                                          kStreamResidual, p.key0, p.key1);
-        // residual candidates (score log2 r) and fallback candidates (score log2 p), each
-        // pruned against its own running best
-        const uint32_t tr =
-            rmax > 0.f ? candidate_threshold(lrmax, fmaxf(rs.gr, lb0)) : 0xFFFFFFFFu;
-        const uint32_t tp = candidate_threshold(lpmax, fmaxf(rs.gp, lb1));
-        const uint32_t t = min(tr, tp);
-        if ((ph.w[0] >= t) | (ph.w[1] >= t) | (ph.w[2] >= t) | (ph.w[3] >= t)) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (ph.w[i] < t) continue;
-                const float le = fast_log2(exp_from_word(ph.w[i]));
-                const float gp = lp[i] - le;
-                const bool tp_ = gp > rs.gp;
-                rs.gp = tp_ ? gp : rs.gp;
-                rs.ip = tp_ ? v + i : rs.ip;
-                if (rv[i] > 0.f) {
-                    const float gr = fast_log2(rv[i]) - le;
-                    const bool tr_ = gr > rs.gr;
-                    rs.gr = tr_ ? gr : rs.gr;
-                    rs.ir = tr_ ? v + i : rs.ir;
-                }
-            }
+            race_update(rs.gr, rs.ir, 0.f, R, w, v);
+            race_update(rs.gp, rs.ip, 0.f, P, w, v);
         }
     }
 }
@@ -273,13 +274,11 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
 // MFMA mapping: block j (0..3) of a tile, MFMA row m (= lane & 15) is tile row
 //   trow(j, m) = 16 (m >> 2) + 4 j + (m & 3),
 // so lane l (g = l >> 4) ends up holding tile rows 16 g .. 16 g + 15 of request (l & 15) across
-// the four blocks: 16 contiguous vocabulary entries, i.e. 16-byte base-logit loads and four
-// whole Philox blocks per lane and request.
+// the four blocks: 16 contiguous vocabulary entries, i.e. one sampler block, 16-byte
+// base-logit loads, and one race uniform per lane and request (block 4 t + g of tile t).
 // W tiles reach LDS through direct global->LDS loads into a 4-stage ring (3 tiles ahead, no
 // registers); each 16-byte chunk sits at column (col ^ swz(row)) of its row, which makes the
 // A-fragment reads of the 16 lanes of a row group hit 16 different bank groups.
-// The accumulators are double-buffered: the MFMAs of tile t+1 are issued before the VALU
-// epilogue of tile t, so the matrix cores and the vector ALUs overlap within each wave.
 // ---------------------------------------------------------------------------------------
 
 __device__ __forceinline__ int tile_row(int j, int m) { return 16 * (m >> 2) + 4 * j + (m & 3); }
@@ -289,59 +288,13 @@ __device__ __forceinline__ int w_swizzle(int row) {
     return ((((row >> 4) & 3) << 2) | (row & 3)) & (CPR - 1);
 }
 
-// 16 consecutive logits of one row (v0 % 16 == 0) held by one lane, in storage format.
-template <typename T>
-struct Raw16;
-template <>
-struct Raw16<uint16_t> {
-    uint4 q[2];
-    __device__ __forceinline__ void load(const void *base, size_t row, int V, int v0) {
-        // every lane issues both loads (a fixed count per wave); chunks past V re-read the
-        // row's last chunk and are masked by the caller
-        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + row * (size_t)V;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int v = min(v0 + 8 * h, V - 8);
-            q[h] = *reinterpret_cast<const uint4 *>(p + v);
-        }
-    }
-    __device__ __forceinline__ void zero() {
-        q[0] = make_uint4(0u, 0u, 0u, 0u);
-        q[1] = q[0];
-    }
-    __device__ __forceinline__ float get(int e) const {  // e is a compile-time constant
-        const uint4 &u = q[e >> 3];
-        const uint32_t w = ((e >> 1) & 3) == 0 ? u.x : ((e >> 1) & 3) == 1 ? u.y : ((e >> 1) & 3) == 2 ? u.z : u.w;
-        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
-    }
-};
-template <>
-struct Raw16<float> {
-    float4 q[4];
-    __device__ __forceinline__ void load(const void *base, size_t row, int V, int v0) {
-        const float *p = reinterpret_cast<const float *>(base) + row * (size_t)V;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int v = min(v0 + 4 * h, V - 4);
-            q[h] = *reinterpret_cast<const float4 *>(p + v);
-        }
-    }
-    __device__ __forceinline__ void zero() {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) q[h] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __device__ __forceinline__ float get(int e) const {
-        const float4 &u = q[e >> 2];
-        return (e & 3) == 0 ? u.x : (e & 3) == 1 ? u.y : (e & 3) == 2 ? u.z : u.w;
-    }
-};
-
-// Sampling epilogue of one lane for one request over its 16 entries v0 .. v0 + 15 of a tile;
-// n_live = how many of them are < V (16 except in the last tile).
+// Epilogue of one lane for one request over its 16 entries v0 .. v0 + 15 of a tile (one
+// sampler block; n_live = how many of them are < V).  `word` is the block's race uniform and
+// `yr` its 16 target logits (residual mode).
 template <HeadMode MODE, typename YT>
 __device__ __forceinline__ void tile_epilogue(const HeadParams &p, const RowInfo &ri, int v0,
-                                              int n_live, const float c[16], SampleState &st,
-                                              ResidState &rs, float lb0, float lb1) {
+                                              int n_live, const float c[16], const Raw16<YT> &yr,
+                                              uint32_t word, SampleState &st, ResidState &rs) {
     if constexpr (MODE == HeadMode::Draft) {
         if (p.corrected) {
 #pragma unroll
@@ -359,82 +312,32 @@ __device__ __forceinline__ void tile_epilogue(const HeadParams &p, const RowInfo
         float s[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = e < n_live ? c[e] * inv : -INFINITY;
-        // online softmax statistics, one rescale per 16 entries
+        // online softmax statistics with one rescale per block; the same sum, taken against
+        // the running maximum, is the block's weight for the race
         float m16 = s[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) m16 = fmaxf(m16, s[e]);
         const float mn = fmaxf(st.m, m16);
         const float base = (mn == -INFINITY) ? 0.f : mn;
-        float ex[16];
         float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            ex[e] = fast_exp2(s[e] - base);
-            acc += ex[e];
-        }
+        for (int e = 0; e < 16; ++e) acc += fast_exp2(s[e] - base);
         st.l = st.l * fast_exp2(st.m - base) + acc;
         st.m = mn;
-        // Gumbel-max, pruned per entry against the best perturbed score known for the row
-        // (exp2(s - g) = ex * exp2(base - g), so the test costs one multiply per entry)
-        const PruneScale ps = prune_scale(base - fmaxf(st.g, lb0));
-#pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4) {
-            const Philox4 ph = philox4x32_10((uint32_t)(v0 + 4 * b4) >> 2, (uint32_t)ri.pos,
-                                             ri.req, kStreamDraft, p.key0, p.key1);
-            bool cand[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cand[i] = may_win(ps, ex[4 * b4 + i], ph.w[i]);
-            if (cand[0] | cand[1] | cand[2] | cand[3]) {  // rare once a good bound is known
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (cand[i]) gumbel_update(st, s[4 * b4 + i], ph.w[i], v0 + 4 * b4 + i);
-            }
-        }
+        race_update(st.g, st.idx, base, acc, word, v0);
     } else {
-        Raw16<YT> yr;
-        yr.load(p.Y, ri.yrow, p.V, v0);
         const float inv = kLog2e / ri.T;
-        float lp[16], pv[16], rv[16];
+        float R = 0.f, P = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            lp[e] = e < n_live ? yr.get(e) * inv - ri.lse2p : -INFINITY;   // log2 p_v
-            pv[e] = fast_exp2(lp[e]);
-            rv[e] = pv[e] - fast_exp2(c[e] * inv - ri.qlse2);                // p_v - q_v
+            const bool in = e < n_live;
+            const float pv = in ? fast_exp2(yr.get(e) * inv - ri.lse2p) : 0.f;  // p_v
+            const float rv = pv - fast_exp2(c[e] * inv - ri.qlse2);             // p_v - q_v
+            R += in ? fmaxf(rv, 0.f) : 0.f;
+            P += pv;
         }
-        // two races on the same uniforms: the residual max(p - q, 0) and the fallback p;
-        // an entry is evaluated when it may win either (log2 p and log2 r are <= 0 here)
-        const PruneScale pr = prune_scale(-fmaxf(rs.gr, lb0));
-        const PruneScale pp = prune_scale(-fmaxf(rs.gp, lb1));
-#pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4) {
-            const Philox4 ph = philox4x32_10((uint32_t)(v0 + 4 * b4) >> 2, (uint32_t)ri.pos,
-                                             ri.req, kStreamResidual, p.key0, p.key1);
-            bool cand[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = 4 * b4 + i;
-                cand[i] = (e < n_live) && (may_win(pp, pv[e], ph.w[i]) ||
-                                           (rv[e] > 0.f && may_win(pr, rv[e], ph.w[i])));
-            }
-            if (cand[0] | cand[1] | cand[2] | cand[3]) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = 4 * b4 + i;
-                    if (!cand[i]) continue;
-                    const float le = fast_log2(exp_from_word(ph.w[i]));
-                    const float gp = lp[e] - le;
-                    const bool take_p = gp > rs.gp;
-                    rs.gp = take_p ? gp : rs.gp;
-                    rs.ip = take_p ? v0 + e : rs.ip;
-                    if (rv[e] > 0.f) {
-                        const float gr = fast_log2(rv[e]) - le;
-                        const bool take_r = gr > rs.gr;
-                        rs.gr = take_r ? gr : rs.gr;
-                        rs.ir = take_r ? v0 + e : rs.ir;
-                    }
-                }
-            }
-        }
+        race_update(rs.gr, rs.ir, 0.f, R, word, v0);
+        race_update(rs.gp, rs.ip, 0.f, P, word, v0);
     }
 }
 
@@ -450,17 +353,19 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     constexpr int TILE_CH = kTileV * CPR;          // chunks per W tile
     constexpr int LPW = TILE_CH / 64 / kMfmaWaves; // direct loads per wave per tile
     constexpr int STAGES = 4;
+    constexpr bool kResid = MODE == HeadMode::Residual;
     // Vector-memory operations every wave issues per tile, unconditionally (clamped
     // addresses): LPW global->LDS loads of W(t+3), then per row the base logits (NZ in all)
-    // and the shared bounds (NB in all) of tile t+1.  They retire in issue order, so:
+    // and, in residual mode, the target logits (NY in all) of tile t+1.  They retire in issue
+    // order, so:
     //  * W(t) has landed once at most WAIT_W operations are pending: at least
-    //    2 LPW + NZ + NB younger ones exist at the top of iteration t (first tile: W(t0+1),
-    //    W(t0+2), the prologue's base logits and bounds; later ones have more);
+    //    2 LPW + NZ + NY younger ones exist at the top of iteration t (first tile: W(t0+1),
+    //    W(t0+2) and the prologue's logits; later ones have more);
     //  * once at most LPW are pending right after the W(t+3) loads, every load of the
-    //    previous iteration -- the base logits and bounds this epilogue reads -- has landed.
-    constexpr int NZ = (sizeof(ZT) == 2) ? 4 : 8;
-    constexpr int NB = (MODE == HeadMode::Draft) ? 2 : 4;
-    constexpr int WAIT_W = 2 * LPW + NZ + NB;
+    //    previous iteration -- the logits this epilogue reads -- has landed.
+    constexpr int NZ = 2 * (int)(sizeof(ZT) * 16 / 16);
+    constexpr int NY = kResid ? 2 * (int)(sizeof(YT) * 16 / 16) : 0;
+    constexpr int WAIT_W = 2 * LPW + NZ + NY;
     static_assert(WAIT_W <= 63, "vmcnt range");
     __shared__ __align__(16) uint4 wt[STAGES * TILE_CH];
 
@@ -470,39 +375,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
     const int group = slot % n_groups;
     const int slab = (slot / n_groups) * 8 + xcd;
-    const int n_rows = (MODE == HeadMode::Residual) ? *p.n_rows_dev : p.n_rows_max;
+    const int n_rows = kResid ? *p.n_rows_dev : p.n_rows_max;
     if (group * kRowsPerGroup >= n_rows || slab >= p.n_slabs) return;  // uniform exit
 
     const int n_tiles = (p.V + kTileV - 1) / kTileV;
     const int t_begin = (int)((long long)slab * n_tiles / p.n_slabs);
     const int t_end = (int)((long long)(slab + 1) * n_tiles / p.n_slabs);
-
-    RowInfo ri[2];
-    bf16x8 ufrag[2][KS];
-    bool any_valid = false;
-    int rowid[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        rowid[q] = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + m;
-        ri[q] = row_info<MODE>(p, rowid[q], n_rows);
-        any_valid |= ri[q].valid;
-        const uint16_t *urow = p.U + (size_t)ri[q].prev * R + 8 * g;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            uint4 raw = make_uint4(0, 0, 0, 0);
-            if (ri[q].valid) raw = *reinterpret_cast<const uint4 *>(urow + 32 * kk);
-            ufrag[q][kk] = __builtin_bit_cast(bf16x8, raw);
-        }
-    }
-    const bool wave_active = __any(any_valid);
-    SampleState st[2] = {sample_state_init(), sample_state_init()};
-    ResidState rs[2] = {resid_init(), resid_init()};
-
-    // per-lane A-fragment offsets (in chunks) of the four blocks, and the column key
-    int a_off[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a_off[j] = tile_row(j, m) * CPR;
-    const int a_key = w_swizzle<CPR>(tile_row(0, m));
 
     // W tile t -> LDS stage s, 16 bytes per lane, swizzled; tiles past the slab re-read the
     // slab's last tile (cache-resident) so every wave issues the same number of loads.
@@ -521,8 +399,41 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                 (void __attribute__((address_space(3))) *)(wt + s * TILE_CH + cb * 64), 16, 0, 0);
         }
     };
-    // shared bounds of the lane's rows (rows past the batch read the last row; unused)
-    const int brow0 = min(rowid[0], p.n_rows_max - 1), brow1 = min(rowid[1], p.n_rows_max - 1);
+    // W tiles t0 .. t0+2 go out first: they depend on nothing
+    const bool have_tiles = t_begin < t_end;
+    if (have_tiles)
+        for (int u = 0; u < STAGES - 1; ++u) issue_w(t_begin + u, u);
+
+    RowInfo ri[2];
+    bf16x8 ufrag[2][KS];
+    bool any_valid = false, any_sampled = false;
+    int rowid[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        rowid[q] = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + m;
+        ri[q] = row_info<MODE>(p, rowid[q], n_rows);
+        any_valid |= ri[q].valid;
+        any_sampled |= ri[q].valid && ri[q].T > 0.f;
+    }
+    // gathered U rows (rows past the batch read token 0's row; their results are dropped)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const uint16_t *urow = p.U + (size_t)ri[q].prev * R + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            ufrag[q][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(urow + 32 * kk));
+    }
+    const bool wave_active = __any(any_valid);
+    const bool wave_sampled = __any(any_sampled);
+    SampleState st[2] = {sample_state_init(), sample_state_init()};
+    ResidState rs[2] = {resid_init(), resid_init()};
+
+    // per-lane A-fragment offsets (in chunks) of the four blocks, and the column key
+    int a_off[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a_off[j] = tile_row(j, m) * CPR;
+    const int a_key = w_swizzle<CPR>(tile_row(0, m));
+
     auto mfma_tile = [&](int s, floatx4 (&acc)[4][2]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -541,37 +452,25 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             }
         }
     };
-    // base logits and shared bound of one row of tile t (invalid rows read row 0 of Z and a
-    // valid bound; those values are never used)
-    auto load_zq = [&](int t, int q, Raw16<ZT> &z) {
+    // base (and target) logits of one row of tile t; invalid rows read row 0 (never used)
+    auto load_row = [&](int t, int q, Raw16<ZT> &z, Raw16<YT> &y) {
         const int tc = t < t_end ? t : t_end - 1;
         z.load(p.Z, ri[q].zrow, p.V, tc * kTileV + 16 * g);
-    };
-    auto load_bq = [&](int q, float (&lb)[2]) {
-        const int br = q ? brow1 : brow0;
-        const bool use = ri[q].valid && ri[q].T > 0.f;
-        if constexpr (MODE == HeadMode::Draft) {
-            const float b0 = load_bound(p.bound + br);
-            lb[0] = use ? b0 : -INFINITY;
-            lb[1] = -INFINITY;
-        } else {
-            const float b0 = load_bound(p.bound + 2 * br), b1 = load_bound(p.bound + 2 * br + 1);
-            lb[0] = use ? b0 : -INFINITY;
-            lb[1] = use ? b1 : -INFINITY;
-        }
+        if constexpr (kResid) y.load(p.Y, ri[q].yrow, p.V, tc * kTileV + 16 * g);
     };
 
-    if (t_begin < t_end) {
+    if (have_tiles) {
         const int t0 = t_begin;
-        // prologue: W tiles t0 .. t0+2, base logits and bounds of tile t0 in flight
-        for (int u = 0; u < STAGES - 1; ++u) issue_w(t0 + u, u);
         Raw16<ZT> z[2];
-        float lb[2][2];
+        Raw16<YT> y[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            load_zq(t0, q, z[q]);
-            load_bq(q, lb[q]);
-        }
+        for (int q = 0; q < 2; ++q) load_row(t0, q, z[q], y[q]);
+        // the gathered U fragments (and W(t0..t0+2)) have landed once only the logits of
+        // tile t0 are pending; settling this here keeps the per-tile loop free of waits on
+        // registers loaded before it
+        DSPARK_WAIT_VMCNT(NZ + NY);
+        uint32_t rw[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+        const uint32_t stream = kResid ? kStreamResidual : kStreamDraft;
         for (int t = t0; t < t_end; ++t) {
             // W(t) has landed once at most WAIT_W operations are pending; after the barrier
             // every wave is done with stage (t - 1) % 4 (untouched when t = t0), which
@@ -579,12 +478,24 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             DSPARK_WAIT_VMCNT(WAIT_W);
             __syncthreads();
             issue_w(t + 3, (t + 3 - t0) & 3);
+            // race uniforms of blocks 4t + g for four tiles at a time (one Philox call per row)
+            if (wave_sampled && (t == t0 || (t & 3) == 0)) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const Philox4 ph = philox4x32_10(race_counter((uint32_t)(4 * t + g)),
+                                                     (uint32_t)ri[q].pos, ri[q].req, stream,
+                                                     p.key0, p.key1);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) rw[q][i] = ph.w[i];
+                }
+            }
             floatx4 acc[4][2];
             if (wave_active) mfma_tile((t - t0) & 3, acc);
-            // base logits and bounds of this tile (loaded during the previous one) have landed
+            // the logits of this tile (loaded during the previous one) have landed
             DSPARK_WAIT_VMCNT(LPW);
             const int v0 = t * kTileV + 16 * g;
             const int live = min(16, p.V - v0);
+            const uint32_t wsel = (uint32_t)t & 3u;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 if (wave_active && ri[q].valid) {
@@ -593,31 +504,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) c[4 * j + i] = z[q].get(4 * j + i) + acc[j][q][i];
-                    tile_epilogue<MODE, YT>(p, ri[q], v0, live, c, st[q], rs[q], lb[q][0], lb[q][1]);
-                }
-                // publish this workgroup's best for the row when it beats the shared bound
-                if (wave_active) {
-                    const bool share = ri[q].valid && ri[q].T > 0.f && lane < 16;
-                    if constexpr (MODE == HeadMode::Draft) {
-                        float gg = st[q].g;
-                        gg = fmaxf(gg, __shfl_xor(gg, 16));
-                        gg = fmaxf(gg, __shfl_xor(gg, 32));
-                        if (share && gg > lb[q][0]) atomicMax(p.bound + rowid[q], ordered_key(gg));
-                    } else {
-                        float gr = rs[q].gr, gp = rs[q].gp;
-                        gr = fmaxf(gr, __shfl_xor(gr, 16));
-                        gr = fmaxf(gr, __shfl_xor(gr, 32));
-                        gp = fmaxf(gp, __shfl_xor(gp, 16));
-                        gp = fmaxf(gp, __shfl_xor(gp, 32));
-                        if (share && gr > lb[q][0])
-                            atomicMax(p.bound + 2 * rowid[q], ordered_key(gr));
-                        if (share && gp > lb[q][1])
-                            atomicMax(p.bound + 2 * rowid[q] + 1, ordered_key(gp));
-                    }
+                    const uint32_t word = wsel == 0 ? rw[q][0]
+                                          : (wsel == 1 ? rw[q][1] : (wsel == 2 ? rw[q][2] : rw[q][3]));
+                    tile_epilogue<MODE, YT>(p, ri[q], v0, live, c, y[q], word, st[q], rs[q]);
                 }
                 // this row's registers are free: fetch its next tile (every wave, every tile)
-                load_zq(t + 1, q, z[q]);
-                load_bq(q, lb[q]);
+                load_row(t + 1, q, z[q], y[q]);
             }
         }
     }
@@ -648,9 +540,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                 out.g = rs[q].gr;
                 out.idx = rs[q].ir;
                 out.m = rs[q].gp;
-                out.pad = rs[q].ip;
-                out.l = 0.f;
-                out.sb = 0.f;
+                out.l = __int_as_float(rs[q].ip);
             }
             p.partials[(size_t)rowid[q] * p.n_slabs + slab] = out;
         }
@@ -698,17 +588,23 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
 
     SampleState st = sample_state_init();
     ResidState rs = resid_init();
-    for (int v = v_begin + 4 * threadIdx.x; v < v_end; v += 4 * kValuThreads) {
-        float z[4], c[4];
-        load4<ZT>(p.Z, ri.zrow, p.V, v, z);
+    // every lane runs every iteration: the epilogue exchanges block sums between lanes
+    for (int vb = v_begin; vb < v_end; vb += 4 * kValuThreads) {
+        const int v = vb + 4 * threadIdx.x;
+        const bool live = v < v_end;
+        float c[4] = {0.f, 0.f, 0.f, 0.f};
+        if (live) {
+            float z[4];
+            load4<ZT>(p.Z, ri.zrow, p.V, v, z);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float acc = 0.f;
-            const size_t wrow = (size_t)(v + i) * p.r;
-            for (int j = 0; j < p.r; ++j) acc = fmaf(urow[j], factor_at<FT>(Wb, wrow + j), acc);
-            c[i] = z[i] + acc;
+            for (int i = 0; i < 4; ++i) {
+                float acc = 0.f;
+                const size_t wrow = (size_t)(v + i) * p.r;
+                for (int j = 0; j < p.r; ++j) acc = fmaf(urow[j], factor_at<FT>(Wb, wrow + j), acc);
+                c[i] = z[i] + acc;
+            }
         }
-        head_epilogue4<MODE, YT>(p, ri, v, true, c, st, rs, -INFINITY, -INFINITY);
+        head_epilogue4<MODE, YT>(p, ri, v, live, c, st, rs);
     }
     // block reduction
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -739,9 +635,7 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
             out.g = a.gr;
             out.idx = a.ir;
             out.m = a.gp;
-            out.pad = a.ip;
-            out.l = 0.f;
-            out.sb = 0.f;
+            out.l = __int_as_float(a.ip);
         }
         p.partials[(size_t)row * p.n_slabs + slab] = out;
     }
@@ -751,27 +645,25 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
 // Draft: prepare (status, validated first tokens) and per-step row reduction
 // ---------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void draft_prepare_kernel(int B, int K, int V,
+__global__ __launch_bounds__(256) void draft_prepare_kernel(int B, int V,
                                                             const int32_t *prev_token,
-                                                            int32_t *prev_cur, uint32_t *bound,
-                                                            uint32_t *status) {
+                                                            int32_t *prev_cur, uint32_t *status) {
     if (threadIdx.x == 0) *status = 0u;
     __syncthreads();
     for (int b = threadIdx.x; b < B; b += blockDim.x)
         prev_cur[b] = checked_token(prev_token[b], V, status);
-    for (int i = threadIdx.x; i < B * K; i += blockDim.x) bound[i] = 0u;
 }
 
-__global__ __launch_bounds__(256) void draft_reduce_kernel(int B, int K, int V, int k,
-                                                           const int32_t *draft_len,
-                                                           const float *temperature,
-                                                           const Partial *partials, int n_slabs,
-                                                           int32_t *prev_cur, int32_t *tokens,
-                                                           float *q_tok, float *q_lse,
-                                                           uint32_t *status) {
+// One wave per request: merge the slabs' partials of position k, then (sampled rows) draw the
+// token inside the winning 16-token block from its recomputed corrected logits.
+__global__ __launch_bounds__(256) void draft_reduce_kernel(
+    int B, int K, int V, int r, int k, int z_dtype, int uw_dtype, const void *Z, const void *U,
+    const void *W, const int32_t *draft_len, const float *temperature, const uint32_t *req_id,
+    uint32_t key0, uint32_t key1, const Partial *partials, int n_slabs, int32_t *prev_cur,
+    int32_t *tokens, float *q_tok, float *q_lse, uint32_t *status) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (b >= B) return;
+    if (b >= B) return;  // uniform per wave
     int kb = draft_len ? draft_len[b] : K;
     if (kb < 0 || kb > K) {
         if (lane == 0 && k == 0) atomicOr(status, DSPARK_DEV_BAD_LENGTH);
@@ -789,6 +681,7 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(int B, int K, int V, 
     const float T = (lane == 0 && k == 0) ? checked_temperature(temperature[b], status)
                                           : temperature[b];
     const bool greedy = !(T > 0.f);
+    const int prev = prev_cur[b];  // issued together with the partials below
     SampleState st = sample_state_init();
     for (int s = lane; s < n_slabs; s += 64) {
         const SampleState o2 = from_partial(partials[(size_t)b * n_slabs + s]);
@@ -798,24 +691,45 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(int B, int K, int V, 
         const SampleState o2 = shfl_xor_state(st, mask);
         merge_into(st, o2, greedy);
     }
+    // a row with no finite score (all -inf / NaN logits) has no winner: token 0, flagged,
+    // so that the next step's gather stays inside U
+    int x;
+    float qt = 1.f, ql = 0.f;
+    if (greedy) {
+        x = st.idx;
+        if (x < 0 || x >= V) x = -1;
+    } else {
+        const int v0 = st.idx;
+        if (v0 < 0 || v0 >= V || (v0 % kSampleBlock) != 0) {
+            x = -1;
+        } else {
+            const int e = lane & 15;
+            const bool in = v0 + e < V;
+            const float c = wave_corrected16(Z, z_dtype, o, U, W, uw_dtype, r, V, prev, v0);
+            const float s2 = c * (kLog2e / T);
+            const uint32_t req = req_id ? req_id[b] : (uint32_t)b;
+            const uint32_t w = token_word((uint32_t)(v0 + e), (uint32_t)k, req, kStreamDraftWithin,
+                                         key0, key1);
+            const float sc = in ? s2 + gumbel2_from_word(w) : -INFINITY;
+            int best = v0 + e;
+            float bsc = sc, bs2 = s2;
+            wave_argmax16(bsc, best, bs2);
+            x = (bsc > -INFINITY) ? best : -1;
+            const float lse2 = st.m + fast_log2(st.l);
+            qt = fast_exp2(bs2 - lse2);
+            ql = lse2 * kLn2;
+        }
+    }
     if (lane == 0) {
-        // a row with no finite score (all -inf / NaN logits) has no winner: token 0, flagged,
-        // so that the next step's gather stays inside U
-        int x = st.idx;
-        if (x < 0 || x >= V) {
+        if (x < 0) {
             atomicOr(status, DSPARK_DEV_BAD_TOKEN);
             x = 0;
+            qt = 0.f;
         }
         tokens[o] = x;
         prev_cur[b] = x;
-        if (greedy) {
-            q_tok[o] = 1.f;
-            q_lse[o] = 0.f;
-        } else {
-            const float lse2 = st.m + fast_log2(st.l);
-            q_tok[o] = fast_exp2(st.sb - lse2);
-            q_lse[o] = lse2 * kLn2;
-        }
+        q_tok[o] = qt;
+        q_lse[o] = ql;
     }
 }
 
@@ -874,8 +788,7 @@ static void set_factors(HeadParams &hp, const void *U, const void *W, int uw_dty
 }
 
 hipError_t launch_draft_prepare(const dspark_draft_args &a, const DraftWs &ws, hipStream_t s) {
-    draft_prepare_kernel<<<1, 256, 0, s>>>(a.B, a.K, a.V, a.prev_token, ws.prev_cur, ws.bound,
-                                           ws.status);
+    draft_prepare_kernel<<<1, 256, 0, s>>>(a.B, a.V, a.prev_token, ws.prev_cur, ws.status);
     return hipGetLastError();
 }
 
@@ -898,7 +811,6 @@ hipError_t launch_draft_step(const DraftStepParams &d, int z_dtype, int uw_dtype
     hp.prev_cur = d.prev_cur;
     hp.partials = d.partials;
     hp.corrected = d.corrected;
-    hp.bound = d.bound;
     hp.status = d.status;
     hp.n_slabs = d.n_slabs;
     return launch_head<HeadMode::Draft>(hp, z_dtype, uw_dtype, DSPARK_F32, s);
@@ -908,8 +820,9 @@ hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, in
                                hipStream_t s) {
     const int per_block = 4;  // one wave per request
     draft_reduce_kernel<<<(a.B + per_block - 1) / per_block, 64 * per_block, 0, s>>>(
-        a.B, a.K, a.V, k, a.draft_len, a.temperature, ws.partials, ws.n_slabs, ws.prev_cur,
-        a.draft_tokens, a.q_tok, a.q_lse, ws.status);
+        a.B, a.K, a.V, a.r, k, a.z_dtype, a.uw_dtype, a.Z, a.U, a.W, a.draft_len, a.temperature,
+        a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu), (uint32_t)(a.seed >> 32), ws.partials,
+        ws.n_slabs, ws.prev_cur, a.draft_tokens, a.q_tok, a.q_lse, ws.status);
     return hipGetLastError();
 }
 
@@ -938,7 +851,6 @@ hipError_t launch_verify_residual(const dspark_verify_args &a, const VerifyWs &w
     hp.q_lse = a.q_lse;
     hp.partials = ws.partials;
     hp.corrected = nullptr;
-    hp.bound = ws.bound;
     hp.status = ws.status;
     hp.n_slabs = ws.n_slabs;
     return launch_head<HeadMode::Residual>(hp, a.z_dtype, a.uw_dtype, a.y_dtype, s);

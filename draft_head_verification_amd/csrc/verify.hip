@@ -9,28 +9,37 @@
 // tag page, post "Speculative Decoding", steps 3-4).
 //
 // Kernels, in launch order:
-//   verify_prepare   clear the status word and the residual-row counter (1 workgroup)
-//   verify_rowstats  one workgroup per target row k <= L_b: streams Y once; softmax max /
-//                    sum-exp of Y/T (log2 units), argmax for greedy rows, and for the bonus
-//                    row of a sampled request the Gumbel-max bonus candidate
-//   verify_finish    one thread per request: the accept scan, then the greedy correction /
-//                    bonus, or enqueue the first rejected row for a residual draw
+//   verify_prepare   clear the status word, the residual-row counter and the per-request
+//                    first rejection
+//   verify_rows      one launch per chunk of target rows ([0,2), [2,5), [5,9), [9,17), ...):
+//                    a workgroup per (request, row of the chunk, vocabulary slab).  It first
+//                    merges the previous chunk's slab statistics of its request and replays
+//                    that chunk's accept decisions (every workgroup of the request reaches the
+//                    same result; one of them writes it), then, if the request is still being
+//                    verified at its row, streams its slab of Y[b][k] once: softmax max /
+//                    sum-exp of Y/T in log2 units, the argmax for greedy rows, and the bonus
+//                    row's block race.  Rows after the first rejection are never needed, so
+//                    only the chunks up to it are read; the kernel boundaries order the data
+//                    between chunks.
+//   verify_finish    one wave per request: decides the last chunk, then the accepted length,
+//                    the greedy correction / the bonus draw inside its winning block, or
+//                    enqueues the first rejected row for a residual draw
 //   (markov_head.hip) the residual rows: recompute q_j with the Markov head on the matrix
-//                    cores and take the Gumbel-max of max(0, p - q_j)
-//   verify_residual_reduce  merge the residual candidates of each row -> next_token
+//                    cores and run the block race of max(0, p - q_j)
+//   verify_residual_reduce  merge the race, draw the token inside the winning block
 #include "dspark_common.hpp"
 
 namespace dspark {
 
-constexpr int kRowThreads = 512;
-
-__global__ __launch_bounds__(256) void verify_prepare_kernel(int B, uint32_t *status,
-                                                             int32_t *n_resid, uint32_t *bound) {
-    if (threadIdx.x == 0) {
+__global__ __launch_bounds__(256) void verify_prepare_kernel(int B, int K, uint32_t *status,
+                                                             int32_t *n_resid,
+                                                             int32_t *first_reject) {
+    const int i0 = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
+    if (i0 == 0) {
         *status = 0u;
         *n_resid = 0;
     }
-    for (int i = threadIdx.x; i < 2 * B; i += blockDim.x) bound[i] = 0u;
+    for (int i = i0; i < B; i += stride) first_reject[i] = K + 1;
 }
 
 __device__ __forceinline__ int clamp_len(int L, int K, uint32_t *status, bool report) {
@@ -39,97 +48,6 @@ __device__ __forceinline__ int clamp_len(int L, int K, uint32_t *status, bool re
         return L < 0 ? 0 : K;
     }
     return L;
-}
-
-// Eight consecutive logits starting at v (v % 8 == 0).
-template <typename YT>
-__device__ __forceinline__ void load8(const void *Y, size_t row, int V, int v, float y[8]);
-
-template <>
-__device__ __forceinline__ void load8<float>(const void *Y, size_t row, int V, int v, float y[8]) {
-    const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(Y) +
-                                                       row * (size_t)V + v);
-    const float4 a = p[0], b = p[1];
-    y[0] = a.x;
-    y[1] = a.y;
-    y[2] = a.z;
-    y[3] = a.w;
-    y[4] = b.x;
-    y[5] = b.y;
-    y[6] = b.z;
-    y[7] = b.w;
-}
-
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const void *Y, size_t row, int V, int v,
-                                                float y[8]) {
-    const uint4 q = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(Y) +
-                                                     row * (size_t)V + v);
-    y[0] = bf16_lo(q.x);
-    y[1] = bf16_hi(q.x);
-    y[2] = bf16_lo(q.y);
-    y[3] = bf16_hi(q.y);
-    y[4] = bf16_lo(q.z);
-    y[5] = bf16_hi(q.z);
-    y[6] = bf16_lo(q.w);
-    y[7] = bf16_hi(q.w);
-}
-
-template <typename YT>
-__global__ __launch_bounds__(kRowThreads) void verify_rowstats_kernel(
-    int B, int K, int V, const void *Y, const int32_t *verify_len, const float *temperature,
-    const uint32_t *req_id, uint32_t key0, uint32_t key1, float4 *rowstats, uint32_t *status) {
-    __shared__ SampleState red[kRowThreads / 64];
-    const int row = blockIdx.x;
-    const int b = row / (K + 1), k = row % (K + 1);
-    const int L = clamp_len(verify_len[b], K, status, threadIdx.x == 0 && k == 0);
-    if (k > L) return;
-    const float T = temperature[b];
-    const bool greedy = !(T > 0.f);
-    const bool bonus = !greedy && k == L;
-    const float inv = greedy ? 1.f : kLog2e / T;
-    const uint32_t req = req_id ? req_id[b] : (uint32_t)b;
-
-    SampleState st = sample_state_init();
-    for (int v = 8 * threadIdx.x; v < V; v += 8 * kRowThreads) {
-        float y[8];
-        load8<YT>(Y, (size_t)row, V, v, y);
-        if (greedy) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) greedy_update(st, y[i], v + i);
-        } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float s[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[i] = y[4 * h + i] * inv;
-                lse_update4(st, s);
-                if (bonus) {
-                    const Philox4 ph = philox4x32_10((uint32_t)(v + 4 * h) >> 2, (uint32_t)k, req,
-                                                     kStreamBonus, key0, key1);
-                    gumbel_update4(st, s, ph.w, v + 4 * h);
-                }
-            }
-        }
-    }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int mask = 1; mask < 64; mask <<= 1) {
-        const SampleState o = shfl_xor_state(st, mask);
-        merge_into(st, o, greedy);
-    }
-    if (lane == 0) red[wave] = st;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        SampleState a = red[0];
-        for (int w = 1; w < kRowThreads / 64; ++w)
-            merge_into(a, red[w], greedy);
-        float4 out;
-        out.x = a.m;
-        out.y = a.l;
-        out.z = __int_as_float(a.idx);
-        out.w = 0.f;
-        rowstats[row] = out;
-    }
 }
 
 template <typename YT>
@@ -143,53 +61,264 @@ __device__ __forceinline__ float load1<uint16_t>(const void *Y, size_t idx) {
     return bf16_to_f32(reinterpret_cast<const uint16_t *>(Y)[idx]);
 }
 
+// Per-request constants of the verifier.
+struct ReqInfo {
+    int L;
+    float T, inv;
+    bool greedy;
+    uint32_t req;
+};
+
+__device__ __forceinline__ ReqInfo req_info(int b, int K, const int32_t *verify_len,
+                                            const float *temperature, const uint32_t *req_id) {
+    ReqInfo r;
+    int L = verify_len[b];
+    r.L = L < 0 ? 0 : (L > K ? K : L);  // out-of-range lengths are flagged by the finish
+    r.T = temperature[b];                // NaN / negative: greedy here, flagged by the finish
+    r.greedy = !(r.T > 0.f);
+    r.inv = r.greedy ? 1.f : kLog2e / r.T;
+    r.req = req_id ? req_id[b] : (uint32_t)b;
+    return r;
+}
+
+// One wave: merge the slab statistics of rows [k0, k1) of request b (rows past L are not
+// verified) and take their accept decisions in order.  Returns the first rejected row, or -1.
+// The writer records row statistics, p(x_k) and the rejection; every caller computes the same.
+// *last receives the statistics of the last row merged (the rejected row, or row L).
+// Everything a decision reads is fetched up front (lane j holds row k0 + j's draft token,
+// target logit and q; the slab partials of eight rows at a time), so a chunk costs a couple of
+// memory round trips rather than a few per row.
+template <typename YT>
+__device__ int decide_rows(int b, int k0, int k1, const ReqInfo &ri, int K, int V, int S,
+                           const void *Y, const int32_t *draft_tokens, const float *q_tok,
+                           const Partial *row_partials, uint32_t key0, uint32_t key1,
+                           bool writer, float4 *rowstats, float *p_tok, int32_t *first_reject,
+                           uint32_t *status, float4 *last = nullptr) {
+    const int lane = threadIdx.x & 63;
+    const int n = min(k1, ri.L + 1) - k0;  // rows to merge (at most 64)
+    if (n <= 0) return -1;
+    const size_t rbase = (size_t)b * (K + 1);
+    int x = 0;
+    float yx = 0.f, q = 0.f;
+    if (lane < n && k0 + lane < ri.L) {
+        const int k = k0 + lane;
+        x = draft_tokens[(size_t)b * K + k];
+        if (x < 0 || x >= V) {
+            if (writer) atomicOr(status, DSPARK_DEV_BAD_TOKEN);
+            x = 0;
+        }
+        if (!ri.greedy) {
+            q = q_tok[(size_t)b * K + k];
+            yx = load1<YT>(Y, (rbase + k) * (size_t)V + x);
+        }
+    }
+    const Partial none = to_partial(sample_state_init());
+    constexpr int G = 8;
+    for (int g0 = 0; g0 < n; g0 += G) {
+        Partial pr[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            pr[j] = (g0 + j < n && lane < S) ? row_partials[(rbase + k0 + g0 + j) * S + lane] : none;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (g0 + j >= n) break;  // uniform
+            const int k = k0 + g0 + j;
+            const size_t row = rbase + k;
+            SampleState a = from_partial(pr[j]);
+            for (int s = lane + 64; s < S; s += 64)
+                merge_into(a, from_partial(row_partials[row * S + s]), ri.greedy);
+            for (int mask = 1; mask < 64; mask <<= 1) {
+                const SampleState o = shfl_xor_state(a, mask);
+                merge_into(a, o, ri.greedy);
+            }
+            const float4 stats = make_float4(a.m, a.l, __int_as_float(a.idx), a.g);
+            if (writer && lane == 0) rowstats[row] = stats;
+            if (last) *last = stats;
+            if (k == ri.L) return -1;  // the bonus row: nothing to test
+            const int xk = __shfl(x, g0 + j);
+            bool accept;
+            float p;
+            if (ri.greedy) {
+                accept = xk == a.idx;
+                p = accept ? 1.f : 0.f;
+            } else {
+                const float lse2 = a.m + fast_log2(a.l);
+                p = fast_exp2(__shfl(yx, g0 + j) * ri.inv - lse2);
+                const Philox4 ph = philox4x32_10(0u, (uint32_t)k, ri.req, kStreamAccept, key0, key1);
+                accept = uniform_from_word(ph.w[0]) * __shfl(q, g0 + j) < p;
+            }
+            if (writer && lane == 0) {
+                if (p_tok) p_tok[(size_t)b * K + k] = p;
+                if (!accept)
+                    __hip_atomic_store(first_reject + b, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (!accept) return k;
+        }
+    }
+    return -1;
+}
+
+// Statistics of one vocabulary slab of one target row (whole workgroup); two sampler blocks
+// per thread and iteration are in flight.
+template <typename YT>
+__device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V, int blk_lo,
+                                               int blk_hi, const ReqInfo &ri, bool bonus, int k,
+                                               uint32_t key0, uint32_t key1, SampleState &st) {
+    for (int blk = blk_lo + (int)threadIdx.x; blk < blk_hi; blk += 2 * kRowThreads) {
+        const int blk2 = blk + kRowThreads;
+        const bool two = blk2 < blk_hi;
+        Raw16<YT> y[2];
+        y[0].load(Y, row, V, blk * kSampleBlock);
+        y[1].load(Y, row, V, (two ? blk2 : blk) * kSampleBlock);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (h == 1 && !two) break;
+            const int bb = h ? blk2 : blk;
+            const int v0 = bb * kSampleBlock;
+            const int n_live = min(kSampleBlock, V - v0);
+            if (ri.greedy) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    greedy_update(st, e < n_live ? y[h].get(e) : -INFINITY, v0 + e);
+            } else {
+                float s[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s[e] = e < n_live ? y[h].get(e) * ri.inv : -INFINITY;
+                float m16 = s[0];
+#pragma unroll
+                for (int e = 1; e < 16; ++e) m16 = fmaxf(m16, s[e]);
+                const float mn = fmaxf(st.m, m16);
+                const float base = (mn == -INFINITY) ? 0.f : mn;
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc += fast_exp2(s[e] - base);
+                st.l = st.l * fast_exp2(st.m - base) + acc;
+                st.m = mn;
+                if (bonus) {
+                    const uint32_t w = race_word((uint32_t)bb, (uint32_t)k, ri.req, kStreamBonus,
+                                                 key0, key1);
+                    race_update(st.g, st.idx, base, acc, w, v0);
+                }
+            }
+        }
+    }
+}
+
+// Chunk [k_lo, k_hi) of the target rows; the previous chunk is [p_lo, k_lo) (empty for the
+// first).  Grid: B * (k_hi - k_lo) * S workgroups, (request, row in chunk, slab).
+template <typename YT>
+__global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
+    int B, int K, int V, const void *Y, const int32_t *draft_tokens, const float *q_tok,
+    const int32_t *verify_len, const float *temperature, const uint32_t *req_id, uint32_t key0,
+    uint32_t key1, int S, int p_lo, int k_lo, int k_hi, Partial *row_partials,
+    int32_t *first_reject, float4 *rowstats, float *p_tok, uint32_t *status) {
+    __shared__ SampleState red[kRowThreads / 64];
+    __shared__ int s_go;
+    const int R = k_hi - k_lo;
+    const int b = blockIdx.x / (R * S), rem = blockIdx.x % (R * S);
+    const int kr = rem / S, slab = rem % S;
+    const int k = k_lo + kr;
+    const ReqInfo ri = req_info(b, K, verify_len, temperature, req_id);
+    // rejections of earlier chunks were recorded by earlier launches
+    const int fr = __hip_atomic_load(first_reject + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (fr < p_lo || ri.L < p_lo) return;  // uniform: the request stopped before this chunk
+    if (threadIdx.x < 64) {
+        int rej = -1;
+        if (p_lo < k_lo)
+            rej = decide_rows<YT>(b, p_lo, k_lo, ri, K, V, S, Y, draft_tokens, q_tok,
+                                  row_partials, key0, key1, kr == 0 && slab == 0, rowstats,
+                                  p_tok, first_reject, status);
+        if (threadIdx.x == 0) s_go = rej < 0 && k <= ri.L;
+    }
+    __syncthreads();
+    if (!s_go) return;
+
+    const size_t row = (size_t)b * (K + 1) + k;
+    const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
+    const int blk_lo = (int)((long long)slab * n_blk / S);
+    const int blk_hi = (int)((long long)(slab + 1) * n_blk / S);
+    SampleState st = sample_state_init();
+    row_slab_stats<YT>(Y, row, V, blk_lo, blk_hi, ri, !ri.greedy && k == ri.L, k, key0, key1, st);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int mask = 1; mask < 64; mask <<= 1) {
+        const SampleState o = shfl_xor_state(st, mask);
+        merge_into(st, o, ri.greedy);
+    }
+    if (lane == 0) red[wave] = st;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        SampleState a = red[0];
+        for (int w = 1; w < kRowThreads / 64; ++w) merge_into(a, red[w], ri.greedy);
+        row_partials[row * S + slab] = to_partial(a);
+    }
+}
+
+// One wave per request.  [c_lo, c_hi) is the last chunk of rows, which no later launch has
+// decided.
 template <typename YT>
 __global__ __launch_bounds__(256) void verify_finish_kernel(
     int B, int K, int V, const void *Y, const int32_t *draft_tokens, const float *q_tok,
     const int32_t *verify_len, const float *temperature, const uint32_t *req_id, uint32_t key0,
-    uint32_t key1, const float4 *rowstats, int32_t *accept_len, int32_t *next_token,
+    uint32_t key1, int S, int c_lo, int c_hi, const Partial *row_partials,
+    int32_t *first_reject, float4 *rowstats, int32_t *accept_len, int32_t *next_token,
     float *p_tok, int32_t *n_resid, int32_t *resid_rows, uint32_t *status) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= B) return;
-    const int L = clamp_len(verify_len[b], K, status, false);
-    const float T = checked_temperature(temperature[b], status);
-    const bool greedy = !(T > 0.f);
-    const float inv = greedy ? 1.f : kLog2e / T;
-    const uint32_t req = req_id ? req_id[b] : (uint32_t)b;
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (b >= B) return;  // uniform per wave
+    if (lane == 0) {
+        clamp_len(verify_len[b], K, status, true);
+        checked_temperature(temperature[b], status);
+    }
+    const ReqInfo ri = req_info(b, K, verify_len, temperature, req_id);
     const size_t rbase = (size_t)b * (K + 1);
-    int a = L;
-    bool rejected = false;
-    for (int k = 0; k < L; ++k) {
-        const int x = checked_token(draft_tokens[(size_t)b * K + k], V, status);
-        const float4 rs = rowstats[rbase + k];
-        bool accept;
-        float p;
-        if (greedy) {
-            accept = (x == __float_as_int(rs.z));
-            p = accept ? 1.f : 0.f;
-        } else {
-            const float lse2 = rs.x + fast_log2(rs.y);
-            p = fast_exp2(load1<YT>(Y, (rbase + k) * (size_t)V + x) * inv - lse2);
-            const Philox4 ph = philox4x32_10(0u, (uint32_t)k, req, kStreamAccept, key0, key1);
-            const float u = uniform_from_word(ph.w[0]);
-            accept = u * q_tok[(size_t)b * K + k] < p;
+    int fr = first_reject[b];
+    bool here = false;  // the deciding row is in the last chunk, merged by this wave
+    float4 rs = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (fr >= c_lo && ri.L >= c_lo) {
+        const int rej = decide_rows<YT>(b, c_lo, c_hi, ri, K, V, S, Y, draft_tokens, q_tok,
+                                        row_partials, key0, key1, true, rowstats, p_tok,
+                                        first_reject, status, &rs);
+        if (rej >= 0) fr = rej;
+        here = true;
+    }
+    // every position before the first rejection was decided
+    const bool rejected = fr < ri.L;
+    const int a = rejected ? fr : ri.L;
+    if (lane == 0) {
+        if (p_tok)  // positions after the deciding one were not tested
+            for (int k = a + (rejected ? 1 : 0); k < K; ++k) p_tok[(size_t)b * K + k] = 0.f;
+        accept_len[b] = a;
+    }
+    if (rejected && !ri.greedy) {
+        if (lane == 0) {
+            const int slot = atomicAdd(n_resid, 1);
+            resid_rows[slot] = b * 128 + a;
+            next_token[b] = -1;  // written by the residual reduction
         }
-        if (p_tok) p_tok[(size_t)b * K + k] = p;
-        if (!accept) {
-            a = k;
-            rejected = true;
-            break;
+        return;
+    }
+    // row a's statistics: merged just now, or written by an earlier launch
+    if (!here) rs = rowstats[rbase + a];
+    int t = __float_as_int(rs.z);
+    if (!ri.greedy) {
+        // bonus: the token inside the winning block of row L
+        const int v0 = t;
+        t = -1;
+        if (v0 >= 0 && v0 < V && v0 % kSampleBlock == 0) {
+            const int e = lane & 15;
+            const int v = min(v0 + e, V - 1);
+            const uint32_t w = token_word((uint32_t)(v0 + e), (uint32_t)ri.L, ri.req,
+                                          kStreamBonusWithin, key0, key1);
+            float sc = v0 + e < V ? load1<YT>(Y, (rbase + ri.L) * (size_t)V + v) * ri.inv +
+                                        gumbel2_from_word(w)
+                                  : -INFINITY;
+            int tok = v0 + e;
+            float aux = 0.f;
+            wave_argmax16(sc, tok, aux);
+            if (sc > -INFINITY) t = tok;
         }
     }
-    if (p_tok)
-        for (int k = a + (rejected ? 1 : 0); k < K; ++k) p_tok[(size_t)b * K + k] = 0.f;
-    accept_len[b] = a;
-    if (rejected && !greedy) {
-        const int slot = atomicAdd(n_resid, 1);
-        resid_rows[slot] = b * 128 + a;
-        next_token[b] = -1;  // written by the residual reduction
-    } else {
-        int t = __float_as_int(rowstats[rbase + a].z);
+    if (lane == 0) {
         if (t < 0 || t >= V) {  // no finite logit in the row
             atomicOr(status, DSPARK_DEV_BAD_TOKEN);
             t = 0;
@@ -198,23 +327,30 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
     }
 }
 
+// One wave per residual row: merge the block races, then draw inside the winning block from
+// the recomputed weights r_v = max(p_v - q_v, 0) (or p_v when the residual is zero).
 __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
-    int B, int V, const int32_t *n_resid, const int32_t *resid_rows, const Partial *partials,
-    int n_slabs, int32_t *next_token) {
+    int B, int K, int V, int r, int y_dtype, int z_dtype, int uw_dtype, const void *Y,
+    const void *Z, const void *U, const void *W, const int32_t *prev_token,
+    const int32_t *draft_tokens, const float *q_lse, const float *temperature,
+    const uint32_t *req_id, uint32_t key0, uint32_t key1, const float4 *rowstats,
+    const int32_t *n_resid, const int32_t *resid_rows, const Partial *partials, int n_slabs,
+    int32_t *next_token, uint32_t *status) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (row >= *n_resid) return;
+    if (row >= *n_resid) return;  // uniform per wave
     float gr = -INFINITY, gp = -INFINITY;
     int ir = 0x7FFFFFFF, ip = 0x7FFFFFFF;
     for (int s = lane; s < n_slabs; s += 64) {
         const Partial q = partials[(size_t)row * n_slabs + s];
+        const int qip = __float_as_int(q.l);
         if (q.g > gr || (q.g == gr && q.idx < ir)) {
             gr = q.g;
             ir = q.idx;
         }
-        if (q.m > gp || (q.m == gp && q.pad < ip)) {
+        if (q.m > gp || (q.m == gp && qip < ip)) {
             gp = q.m;
-            ip = q.pad;
+            ip = qip;
         }
     }
     for (int mask = 1; mask < 64; mask <<= 1) {
@@ -229,10 +365,49 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
             ip = oip;
         }
     }
+    const int packed = resid_rows[row];
+    const int b = packed >> 7, j = packed & 127;
+    const bool use_r = gr > -INFINITY;
+    const int v0 = use_r ? ir : ip;
+    int t = -1;
+    if (v0 >= 0 && v0 < V && v0 % kSampleBlock == 0) {
+        const float T = temperature[b];  // > 0: greedy rows never need a residual
+        const float inv = kLog2e / T;
+        const uint32_t req = req_id ? req_id[b] : (uint32_t)b;
+        int prev = (j == 0) ? prev_token[b] : draft_tokens[(size_t)b * K + j - 1];
+        if (prev < 0 || prev >= V) prev = 0;  // flagged by the rows / finish kernels
+        const size_t zrow = (size_t)b * K + j, yrow = (size_t)b * (K + 1) + j;
+        const float4 rs = rowstats[yrow];
+        const float lse2p = rs.x + fast_log2(rs.y);
+        const float qlse2 = q_lse[zrow] * kLog2e;
+        const float c = wave_corrected16(Z, z_dtype, zrow, U, W, uw_dtype, r, V, prev, v0);
+        const int e = lane & 15;
+        const int v = min(v0 + e, V - 1);
+        const bool in = v0 + e < V;
+        const float pv = fast_exp2(load_value(Y, y_dtype, yrow * (size_t)V + v) * inv - lse2p);
+        const float rv = pv - fast_exp2(c * inv - qlse2);
+        const float g = gumbel2_from_word(token_word((uint32_t)(v0 + e), (uint32_t)j, req,
+                                                     kStreamResidualWithin, key0, key1));
+        const float lw_r = (in && rv > 0.f) ? fast_log2(rv) : -INFINITY;
+        const float lw_p = (in && pv > 0.f) ? fast_log2(pv) : -INFINITY;
+        float sc = (use_r ? lw_r : lw_p) + g;
+        int tok = v0 + e;
+        float aux = 0.f;
+        wave_argmax16(sc, tok, aux);
+        if (!(sc > -INFINITY) && use_r) {
+            // the recomputed residual of the chosen block rounded to zero: draw from p there
+            sc = lw_p + g;
+            tok = v0 + e;
+            wave_argmax16(sc, tok, aux);
+        }
+        if (sc > -INFINITY) t = tok;
+    }
     if (lane == 0) {
-        const int b = resid_rows[row] >> 7;
-        const int t = (gr > -INFINITY) ? ir : ip;
-        next_token[b] = (t >= 0 && t < V) ? t : 0;
+        if (t < 0 || t >= V) {
+            atomicOr(status, DSPARK_DEV_BAD_TOKEN);
+            t = 0;
+        }
+        next_token[b] = t;
     }
 }
 
@@ -241,37 +416,66 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
 // ---------------------------------------------------------------------------------------
 
 hipError_t launch_verify_prepare(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s) {
-    verify_prepare_kernel<<<1, 256, 0, s>>>(a.B, ws.status, ws.n_resid, ws.bound);
+    const int blocks = (a.B + 255) / 256 < 1024 ? (a.B + 255) / 256 : 1024;
+    verify_prepare_kernel<<<blocks < 1 ? 1 : blocks, 256, 0, s>>>(a.B, a.K, ws.status,
+                                                                   ws.n_resid, ws.first_reject);
     return hipGetLastError();
 }
 
-hipError_t launch_verify_rowstats(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s) {
+int verify_chunks(int K, int bounds[kMaxChunks + 1]) {
+    // rows 0 .. K (K + 1 target rows) in chunks of 2, 3, 4, 8, 16, ... rows
+    static const int edges[] = {0, 2, 5, 9, 17, 33, 65};
+    int n = 0;
+    bounds[0] = 0;
+    for (int i = 1; i < (int)(sizeof(edges) / sizeof(edges[0])); ++i) {
+        const int e = edges[i] < K + 1 ? edges[i] : K + 1;
+        if (e > bounds[n]) bounds[++n] = e;
+        if (e == K + 1) break;
+    }
+    return n;
+}
+
+hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
+                              hipStream_t s) {
+    int bounds[kMaxChunks + 1];
+    const int n = verify_chunks(a.K, bounds);
+    if (chunk < 0 || chunk >= n) return hipErrorInvalidValue;
+    const int p_lo = chunk > 0 ? bounds[chunk - 1] : 0;
+    const int k_lo = bounds[chunk], k_hi = bounds[chunk + 1];
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
-    const dim3 grid((unsigned)a.B * (unsigned)(a.K + 1)), block(kRowThreads);
+    const long long n_wg = (long long)a.B * (k_hi - k_lo) * ws.n_row_slabs;
+    if (n_wg > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)n_wg), block(kRowThreads);
     if (a.y_dtype == DSPARK_BF16)
-        verify_rowstats_kernel<uint16_t><<<grid, block, 0, s>>>(
-            a.B, a.K, a.V, a.Y, a.verify_len, a.temperature, a.req_id, k0, k1, ws.rowstats,
-            ws.status);
+        verify_rows_kernel<uint16_t><<<grid, block, 0, s>>>(
+            a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
+            k0, k1, ws.n_row_slabs, p_lo, k_lo, k_hi, ws.row_partials, ws.first_reject,
+            ws.rowstats, a.p_tok, ws.status);
     else
-        verify_rowstats_kernel<float><<<grid, block, 0, s>>>(a.B, a.K, a.V, a.Y, a.verify_len,
-                                                             a.temperature, a.req_id, k0, k1,
-                                                             ws.rowstats, ws.status);
+        verify_rows_kernel<float><<<grid, block, 0, s>>>(
+            a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
+            k0, k1, ws.n_row_slabs, p_lo, k_lo, k_hi, ws.row_partials, ws.first_reject,
+            ws.rowstats, a.p_tok, ws.status);
     return hipGetLastError();
 }
 
 hipError_t launch_verify_finish(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s) {
+    int bounds[kMaxChunks + 1];
+    const int n = verify_chunks(a.K, bounds);
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
-    const dim3 grid((a.B + 255) / 256), block(256);
+    const int per_block = 4;  // one wave per request
+    const dim3 grid((a.B + per_block - 1) / per_block), block(64 * per_block);
+    const int c_lo = bounds[n - 1], c_hi = bounds[n];
     if (a.y_dtype == DSPARK_BF16)
         verify_finish_kernel<uint16_t><<<grid, block, 0, s>>>(
             a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
-            k0, k1, ws.rowstats, a.accept_len, a.next_token, a.p_tok, ws.n_resid, ws.resid_rows,
-            ws.status);
+            k0, k1, ws.n_row_slabs, c_lo, c_hi, ws.row_partials, ws.first_reject, ws.rowstats,
+            a.accept_len, a.next_token, a.p_tok, ws.n_resid, ws.resid_rows, ws.status);
     else
         verify_finish_kernel<float><<<grid, block, 0, s>>>(
             a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
-            k0, k1, ws.rowstats, a.accept_len, a.next_token, a.p_tok, ws.n_resid, ws.resid_rows,
-            ws.status);
+            k0, k1, ws.n_row_slabs, c_lo, c_hi, ws.row_partials, ws.first_reject, ws.rowstats,
+            a.accept_len, a.next_token, a.p_tok, ws.n_resid, ws.resid_rows, ws.status);
     return hipGetLastError();
 }
 
@@ -279,7 +483,10 @@ hipError_t launch_verify_residual_reduce(const dspark_verify_args &a, const Veri
                                          hipStream_t s) {
     const int per_block = 4;
     verify_residual_reduce_kernel<<<(a.B + per_block - 1) / per_block, 64 * per_block, 0, s>>>(
-        a.B, a.V, ws.n_resid, ws.resid_rows, ws.partials, ws.n_slabs, a.next_token);
+        a.B, a.K, a.V, a.r, a.y_dtype, a.z_dtype, a.uw_dtype, a.Y, a.Z, a.U, a.W, a.prev_token,
+        a.draft_tokens, a.q_lse, a.temperature, a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu),
+        (uint32_t)(a.seed >> 32), ws.rowstats, ws.n_resid, ws.resid_rows, ws.partials,
+        ws.n_slabs, a.next_token, ws.status);
     return hipGetLastError();
 }
 

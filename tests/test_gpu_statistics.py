@@ -1,4 +1,5 @@
-"""Losslessness through the GPU path: on a tiny vocabulary, over 2^17 request keys, the first
+"""Losslessness through the GPU path: on a small vocabulary (three sampler blocks, the last
+one short), over 2^17 request keys, the first
 token a round emits is distributed as the target p_1, and the second (given the first draft
 token was accepted) as p_2 -- the guarantee the pages state for rejection-sampling
 verification (QbitAI "DSpark in 10 concepts", section "Speculative decoding"; 10100.com,
@@ -15,7 +16,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("T", [1.0, 0.7])
 def test_gpu_round_output_law_equals_target(T):
     from draft_head_verification_amd import dspark as D
-    n, V, r, K = 1 << 17, 16, 8, 3
+    n, V, r, K = 1 << 17, 40, 8, 3
     g = torch.Generator().manual_seed(21)
     U = 0.7 * torch.randn(V, r, generator=g)
     W = 0.7 * torch.randn(V, r, generator=g)
@@ -41,5 +42,9 @@ def test_gpu_round_output_law_equals_target(T):
     sel = a >= 1
     second = np.where(a[sel] >= 2, toks[sel, 1], nt[sel])
     assert stats.chisquare(np.bincount(second, minlength=V), p2 * sel.sum()).pvalue > 1e-4
+    # bonus tokens (every draft accepted) follow the target of the extra row
+    full = a == K
+    pb = torch.softmax(Yrow[K].double() / T32, 0).numpy()
+    assert stats.chisquare(np.bincount(nt[full], minlength=V), pb * full.sum()).pvalue > 1e-4
     # the draft alone does not follow p_1, so the test has power
     assert stats.chisquare(np.bincount(toks[:, 0], minlength=V), p1 * n).pvalue < 1e-6
