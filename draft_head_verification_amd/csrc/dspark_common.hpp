@@ -161,7 +161,8 @@ __device__ __forceinline__ void lse_update4(SampleState &st, const float s[4]) {
 // never drawn), `word` its race uniform, v0 its first token.
 __device__ __forceinline__ void race_update(float &g, int &idx, float ref, float sum,
                                             uint32_t word, int v0) {
-    const float sc = sum > 0.f ? ref + fast_log2(sum) + gumbel2_from_word(word) : -INFINITY;
+    // log2(0) = -inf: a block of weight 0 scores -inf and is never taken (branch-free)
+    const float sc = ref + fast_log2(sum) + gumbel2_from_word(word);
     const bool take = sc > g;
     g = take ? sc : g;
     idx = take ? v0 : idx;
@@ -253,6 +254,11 @@ struct Raw16<uint16_t> {
             q[h] = *reinterpret_cast<const uint4 *>(p + v);
         }
     }
+    // entries 8h .. 8h + 7 only (one 16-byte load)
+    __device__ __forceinline__ void load_half(const void *base, size_t row, int V, int v0, int h) {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + row * (size_t)V;
+        q[h] = *reinterpret_cast<const uint4 *>(p + min(v0 + 8 * h, V - 8));
+    }
     __device__ __forceinline__ void zero() {
         q[0] = make_uint4(0u, 0u, 0u, 0u);
         q[1] = q[0];
@@ -273,6 +279,12 @@ struct Raw16<float> {
             const int v = min(v0 + 4 * h, V - 4);
             q[h] = *reinterpret_cast<const float4 *>(p + v);
         }
+    }
+    // entries 8h .. 8h + 7 only (two 16-byte loads)
+    __device__ __forceinline__ void load_half(const void *base, size_t row, int V, int v0, int h) {
+        const float *p = reinterpret_cast<const float *>(base) + row * (size_t)V;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) q[2 * h + k] = *reinterpret_cast<const float4 *>(p + min(v0 + 8 * h + 4 * k, V - 4));
     }
     __device__ __forceinline__ void zero() {
 #pragma unroll

@@ -27,6 +27,8 @@
 //   dispatched to the same XCD and meet the slab's W tiles in that XCD's L2.
 // Vector-ALU path (any other factor dtype / rank): one workgroup per (request, slab); four
 // neighbouring lanes hold one sampler block.
+#include <type_traits>
+
 #include "dspark_common.hpp"
 
 namespace dspark {
@@ -288,62 +290,96 @@ __device__ __forceinline__ int w_swizzle(int row) {
     return ((((row >> 4) & 3) << 2) | (row & 3)) & (CPR - 1);
 }
 
-// Epilogue of one lane for one request over its 16 entries v0 .. v0 + 15 of a tile (one
-// sampler block; n_live = how many of them are < V).  `word` is the block's race uniform and
-// `yr` its 16 target logits (residual mode).
-template <HeadMode MODE, typename YT>
-__device__ __forceinline__ void tile_epilogue(const HeadParams &p, const RowInfo &ri, int v0,
-                                              int n_live, const float c[16], const Raw16<YT> &yr,
-                                              uint32_t word, SampleState &st, ResidState &rs) {
-    if constexpr (MODE == HeadMode::Draft) {
-        if (p.corrected) {
+// Epilogues of one lane for one request, one half at a time: half h holds entries
+// v0 + 8h .. v0 + 8h + 7 of the lane's 16-entry sampler block (n_live = how many of its
+// entries are < V).  All are branch-free, so that the compiler can interleave them with the
+// matrix-core instructions of the other half.
+//   kEpiGreedy   every request of the wave is greedy: running max / argmax of c
+//   kEpiSampled  every request is sampled: online softmax statistics, and the block race
+//                once both halves of a block are in (the block's weight is its sum taken
+//                against the running maximum)
+//   kEpiMixed    both, with the greedy max / argmax kept in (gm, gi)
+//   kEpiResid    residual mode: block race over max(p - q, 0) and over p
+enum { kEpiGreedy = 0, kEpiSampled = 1, kEpiMixed = 2, kEpiResid = 3 };
+
+// The low half's contribution to a block's race weight, carried to the high half.
+struct BlockPart {
+    float ref, sum;  // sampled: sum of exp2(s - ref); residual: ref = sum of p, sum = sum of r
+};
+
+__device__ __forceinline__ void epi_greedy8(const float c[8], int v, int n_live, float &m,
+                                            int &idx) {
 #pragma unroll
-            for (int h = 0; h < 4; ++h)
-                if (4 * h < n_live)
-                    *reinterpret_cast<float4 *>(p.corrected + ri.zrow * (size_t)p.V + v0 + 4 * h) =
-                        make_float4(c[4 * h], c[4 * h + 1], c[4 * h + 2], c[4 * h + 3]);
-        }
-        if (ri.T == 0.f) {
+    for (int e = 0; e < 8; ++e) {
+        const float x = e < n_live ? c[e] : -INFINITY;
+        const bool take = x > m;
+        m = take ? x : m;
+        idx = take ? v + e : idx;
+    }
+}
+
+template <int H>
+__device__ __forceinline__ void epi_sampled8(const float c[8], int v0, int n_live, float inv,
+                                             uint32_t word, SampleState &st, BlockPart &bp) {
+    float s[8];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) greedy_update(st, e < n_live ? c[e] : -INFINITY, v0 + e);
-            return;
-        }
-        const float inv = kLog2e / ri.T;
-        float s[16];
+    for (int e = 0; e < 8; ++e) s[e] = e < n_live ? c[e] * inv : -INFINITY;
+    float m8 = s[0];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = e < n_live ? c[e] * inv : -INFINITY;
-        // online softmax statistics with one rescale per block; the same sum, taken against
-        // the running maximum, is the block's weight for the race
-        float m16 = s[0];
+    for (int e = 1; e < 8; ++e) m8 = fmaxf(m8, s[e]);
+    const float mn = fmaxf(st.m, m8);
+    const float base = (mn == -INFINITY) ? 0.f : mn;
+    float acc = 0.f;
 #pragma unroll
-        for (int e = 1; e < 16; ++e) m16 = fmaxf(m16, s[e]);
-        const float mn = fmaxf(st.m, m16);
-        const float base = (mn == -INFINITY) ? 0.f : mn;
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc += fast_exp2(s[e] - base);
-        st.l = st.l * fast_exp2(st.m - base) + acc;
-        st.m = mn;
-        race_update(st.g, st.idx, base, acc, word, v0);
+    for (int e = 0; e < 8; ++e) acc += fast_exp2(s[e] - base);
+    st.l = st.l * fast_exp2(st.m - base) + acc;
+    st.m = mn;
+    if constexpr (H == 0) {
+        bp.ref = base;
+        bp.sum = acc;
     } else {
-        const float inv = kLog2e / ri.T;
-        float R = 0.f, P = 0.f;
+        // the low half's sum was taken against a maximum <= base (0 when it had no weight)
+        const float sum = (bp.sum > 0.f ? bp.sum * fast_exp2(bp.ref - base) : 0.f) + acc;
+        race_update(st.g, st.idx, base, sum, word, v0);
+    }
+}
+
+template <int H, typename YT>
+__device__ __forceinline__ void epi_resid8(const float c[8], const Raw16<YT> &yr, int v0,
+                                           int n_live, const RowInfo &ri, uint32_t word,
+                                           ResidState &rs, BlockPart &bp) {
+    const float inv = kLog2e / ri.T;
+    float R = 0.f, P = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const bool in = e < n_live;
-            const float pv = in ? fast_exp2(yr.get(e) * inv - ri.lse2p) : 0.f;  // p_v
-            const float rv = pv - fast_exp2(c[e] * inv - ri.qlse2);             // p_v - q_v
-            R += in ? fmaxf(rv, 0.f) : 0.f;
-            P += pv;
-        }
-        race_update(rs.gr, rs.ir, 0.f, R, word, v0);
-        race_update(rs.gp, rs.ip, 0.f, P, word, v0);
+    for (int e = 0; e < 8; ++e) {
+        const bool in = e < n_live;
+        const float pv = in ? fast_exp2(yr.get(8 * H + e) * inv - ri.lse2p) : 0.f;  // p_v
+        const float rv = pv - fast_exp2(c[e] * inv - ri.qlse2);                     // p_v - q_v
+        R += in ? fmaxf(rv, 0.f) : 0.f;
+        P += pv;
+    }
+    if constexpr (H == 0) {
+        bp.ref = P;
+        bp.sum = R;
+    } else {
+        race_update(rs.gr, rs.ir, 0.f, bp.sum + R, word, v0);
+        race_update(rs.gp, rs.ip, 0.f, bp.ref + P, word, v0);
     }
 }
 
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
 #define DSPARK_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// Workgroup barrier of the tile pipeline.  The only LDS writes are the global->LDS loads,
+// each retired by its own wave's explicit vmcnt wait before that wave reaches the barrier, so
+// the barrier needs no wait on global memory.  It does retire this wave's LDS reads: the
+// compiler may sink the matrix-core instructions that consume them below the barrier, and a
+// stage must not be refilled while a read of it is still in flight.  The "memory" clobber
+// keeps every memory access on its side.
+__device__ __forceinline__ void tile_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <HeadMode MODE, typename ZT, typename YT, int R>
 __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadParams p) {
@@ -354,19 +390,24 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     constexpr int LPW = TILE_CH / 64 / kMfmaWaves; // direct loads per wave per tile
     constexpr int STAGES = 4;
     constexpr bool kResid = MODE == HeadMode::Residual;
-    // Vector-memory operations every wave issues per tile, unconditionally (clamped
-    // addresses): LPW global->LDS loads of W(t+3), then per row the base logits (NZ in all)
-    // and, in residual mode, the target logits (NY in all) of tile t+1.  They retire in issue
-    // order, so:
-    //  * W(t) has landed once at most WAIT_W operations are pending: at least
-    //    2 LPW + NZ + NY younger ones exist at the top of iteration t (first tile: W(t0+1),
-    //    W(t0+2) and the prologue's logits; later ones have more);
-    //  * once at most LPW are pending right after the W(t+3) loads, every load of the
-    //    previous iteration -- the logits this epilogue reads -- has landed.
-    constexpr int NZ = 2 * (int)(sizeof(ZT) * 16 / 16);
-    constexpr int NY = kResid ? 2 * (int)(sizeof(YT) * 16 / 16) : 0;
-    constexpr int WAIT_W = 2 * LPW + NZ + NY;
-    static_assert(WAIT_W <= 63, "vmcnt range");
+    // Software pipeline over half tiles.  Phase A of tile t: W(t+3) goes out to LDS, then the
+    // matrix-core work of the low half of tile t (blocks j = 0, 1) runs together with the
+    // epilogue of the high half of tile t - 1.  Phase B: the high logit registers take the
+    // high half of tile t, then the high half's matrix-core work runs with the low half's
+    // epilogue, and the low logit registers take tile t + 1.  Every wave issues every load,
+    // unconditionally (clamped addresses), and loads retire in issue order, so:
+    //  * in phase A, once at most NL + LPW operations are pending after W(t+3) (the low
+    //    logits of tile t, W(t+3)), the high logits of tile t - 1 have landed, and with them
+    //    W(t+2);
+    //  * in phase B, once at most LPW + NH are pending (W(t+3), the high logits of tile t),
+    //    the low logits of tile t have landed.
+    // W(t) was thus forced two phases before phase A of tile t in every wave; the barrier
+    // there makes all of it visible and retires every read of stage (t-1) % 4 (last used in
+    // phase B of tile t - 1), which W(t+3) overwrites.
+    constexpr int NH = 2 * ((int)sizeof(ZT) / 2) + (kResid ? 2 * ((int)sizeof(YT) / 2) : 0);
+    constexpr int NL = NH;
+    constexpr int WAIT_A = NL + LPW, WAIT_B = LPW + NH;
+    static_assert(WAIT_A <= 63 && WAIT_B <= 63, "vmcnt range");
     __shared__ __align__(16) uint4 wt[STAGES * TILE_CH];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -381,6 +422,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     const int n_tiles = (p.V + kTileV - 1) / kTileV;
     const int t_begin = (int)((long long)slab * n_tiles / p.n_slabs);
     const int t_end = (int)((long long)(slab + 1) * n_tiles / p.n_slabs);
+    // an empty slab (more slabs than tiles) still writes its (empty) partials
+    const bool have_tiles = t_begin < t_end;
+    const int t0 = t_begin;
 
     // W tile t -> LDS stage s, 16 bytes per lane, swizzled; tiles past the slab re-read the
     // slab's last tile (cache-resident) so every wave issues the same number of loads.
@@ -400,13 +444,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         }
     };
     // W tiles t0 .. t0+2 go out first: they depend on nothing
-    const bool have_tiles = t_begin < t_end;
     if (have_tiles)
-        for (int u = 0; u < STAGES - 1; ++u) issue_w(t_begin + u, u);
+        for (int u = 0; u < STAGES - 1; ++u) issue_w(t0 + u, u);
 
     RowInfo ri[2];
     bf16x8 ufrag[2][KS];
-    bool any_valid = false, any_sampled = false;
+    bool any_valid = false, any_sampled = false, any_greedy = false;
     int rowid[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -414,6 +457,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         ri[q] = row_info<MODE>(p, rowid[q], n_rows);
         any_valid |= ri[q].valid;
         any_sampled |= ri[q].valid && ri[q].T > 0.f;
+        any_greedy |= ri[q].valid && !(ri[q].T > 0.f);
     }
     // gathered U rows (rows past the batch read token 0's row; their results are dropped)
 #pragma unroll
@@ -425,8 +469,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     }
     const bool wave_active = __any(any_valid);
     const bool wave_sampled = __any(any_sampled);
+    const bool wave_greedy = __any(any_greedy);
     SampleState st[2] = {sample_state_init(), sample_state_init()};
     ResidState rs[2] = {resid_init(), resid_init()};
+    float gm[2] = {-INFINITY, -INFINITY};  // greedy rows of a mixed wave
+    int gi[2] = {0x7FFFFFFF, 0x7FFFFFFF};
+    BlockPart bp[2] = {{0.f, 0.f}, {0.f, 0.f}};
 
     // per-lane A-fragment offsets (in chunks) of the four blocks, and the column key
     int a_off[4];
@@ -434,83 +482,178 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     for (int j = 0; j < 4; ++j) a_off[j] = tile_row(j, m) * CPR;
     const int a_key = w_swizzle<CPR>(tile_row(0, m));
 
-    auto mfma_tile = [&](int s, floatx4 (&acc)[4][2]) {
+    // matrix-core work of half h (blocks j = 2h, 2h + 1) of the tile in stage s
+    auto mfma_half = [&](int s, int h, floatx4 (&acc)[2][2]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) acc[j][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < 2; ++q) acc[jj][q] = floatx4{0.f, 0.f, 0.f, 0.f};
         const uint4 *base = wt + s * TILE_CH;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * h + jj;
                 const bf16x8 a = __builtin_bit_cast(bf16x8, base[a_off[j] + ((4 * kk + g) ^ a_key)]);
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
-                    acc[j][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ufrag[q][kk], acc[j][q],
-                                                                         0, 0, 0);
+                    acc[jj][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ufrag[q][kk], acc[jj][q],
+                                                                          0, 0, 0);
             }
         }
     };
-    // base (and target) logits of one row of tile t; invalid rows read row 0 (never used)
-    auto load_row = [&](int t, int q, Raw16<ZT> &z, Raw16<YT> &y) {
+    // logits (base, and target in residual mode) of half h of tile t; invalid rows read row 0
+    Raw16<ZT> z[2];
+    Raw16<YT> y[2];
+    auto load_half = [&](int t, int h) {
         const int tc = t < t_end ? t : t_end - 1;
-        z.load(p.Z, ri[q].zrow, p.V, tc * kTileV + 16 * g);
-        if constexpr (kResid) y.load(p.Y, ri[q].yrow, p.V, tc * kTileV + 16 * g);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            z[q].load_half(p.Z, ri[q].zrow, p.V, tc * kTileV + 16 * g, h);
+            if constexpr (kResid) y[q].load_half(p.Y, ri[q].yrow, p.V, tc * kTileV + 16 * g, h);
+        }
     };
 
-    if (have_tiles) {
-        const int t0 = t_begin;
-        Raw16<ZT> z[2];
-        Raw16<YT> y[2];
+    // race uniforms of blocks 4t + g for four tiles at a time (one Philox call per row)
+    uint32_t rw[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    const uint32_t stream = kResid ? kStreamResidual : kStreamDraft;
+    auto race_words = [&](int t) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) load_row(t0, q, z[q], y[q]);
-        // the gathered U fragments (and W(t0..t0+2)) have landed once only the logits of
-        // tile t0 are pending; settling this here keeps the per-tile loop free of waits on
-        // registers loaded before it
-        DSPARK_WAIT_VMCNT(NZ + NY);
-        uint32_t rw[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-        const uint32_t stream = kResid ? kStreamResidual : kStreamDraft;
-        for (int t = t0; t < t_end; ++t) {
-            // W(t) has landed once at most WAIT_W operations are pending; after the barrier
-            // every wave is done with stage (t - 1) % 4 (untouched when t = t0), which
-            // takes tile t + 3
-            DSPARK_WAIT_VMCNT(WAIT_W);
-            __syncthreads();
-            issue_w(t + 3, (t + 3 - t0) & 3);
-            // race uniforms of blocks 4t + g for four tiles at a time (one Philox call per row)
-            if (wave_sampled && (t == t0 || (t & 3) == 0)) {
+        for (int q = 0; q < 2; ++q) {
+            const Philox4 ph = philox4x32_10(race_counter((uint32_t)(4 * t + g)),
+                                             (uint32_t)ri[q].pos, ri[q].req, stream, p.key0,
+                                             p.key1);
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const Philox4 ph = philox4x32_10(race_counter((uint32_t)(4 * t + g)),
-                                                     (uint32_t)ri[q].pos, ri[q].req, stream,
-                                                     p.key0, p.key1);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) rw[q][i] = ph.w[i];
-                }
-            }
-            floatx4 acc[4][2];
-            if (wave_active) mfma_tile((t - t0) & 3, acc);
-            // the logits of this tile (loaded during the previous one) have landed
-            DSPARK_WAIT_VMCNT(LPW);
+            for (int i = 0; i < 4; ++i) rw[q][i] = ph.w[i];
+        }
+    };
+    // word t & 3 of the row's four, selected with masks (no branches inside the pipeline)
+    auto word_of = [&](int q, int t) {
+        const uint32_t i = (uint32_t)t & 3u;
+        const uint32_t m0 = 0u - (uint32_t)(i == 0), m1 = 0u - (uint32_t)(i == 1);
+        const uint32_t m2 = 0u - (uint32_t)(i == 2), m3 = 0u - (uint32_t)(i == 3);
+        return (rw[q][0] & m0) | (rw[q][1] & m1) | (rw[q][2] & m2) | (rw[q][3] & m3);
+    };
+
+    floatx4 acc_lo[2][2], acc_hi[2][2];
+    auto run = [&](auto epi_tag, auto store_tag) {
+        constexpr int EPI = decltype(epi_tag)::value;
+        constexpr bool STORE = decltype(store_tag)::value;
+        constexpr bool WORDS = EPI != kEpiGreedy;
+        // epilogue of half H of tile t from acc, with the race words w[q] of that tile
+        auto epilogue = [&](auto half_tag, int t, const floatx4 (&acc)[2][2], const uint32_t (&w)[2]) {
+            constexpr int H = decltype(half_tag)::value;
             const int v0 = t * kTileV + 16 * g;
-            const int live = min(16, p.V - v0);
-            const uint32_t wsel = (uint32_t)t & 3u;
+            const int live = min(8, p.V - v0 - 8 * H);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                if (wave_active && ri[q].valid) {
-                    float c[16];
+                float c[8];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) c[4 * j + i] = z[q].get(4 * j + i) + acc[j][q][i];
-                    const uint32_t word = wsel == 0 ? rw[q][0]
-                                          : (wsel == 1 ? rw[q][1] : (wsel == 2 ? rw[q][2] : rw[q][3]));
-                    tile_epilogue<MODE, YT>(p, ri[q], v0, live, c, y[q], word, st[q], rs[q]);
+                    for (int i = 0; i < 4; ++i) c[4 * jj + i] = z[q].get(8 * H + 4 * jj + i) + acc[jj][q][i];
+                if constexpr (STORE) {
+                    if (ri[q].valid) {
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh)
+                            if (4 * hh < live)
+                                *reinterpret_cast<float4 *>(p.corrected + ri[q].zrow * (size_t)p.V + v0 + 8 * H + 4 * hh) =
+                                    make_float4(c[4 * hh], c[4 * hh + 1], c[4 * hh + 2], c[4 * hh + 3]);
+                    }
                 }
-                // this row's registers are free: fetch its next tile (every wave, every tile)
-                load_row(t + 1, q, z[q], y[q]);
+                if constexpr (EPI == kEpiGreedy) {
+                    epi_greedy8(c, v0 + 8 * H, live, st[q].m, st[q].idx);
+                } else if constexpr (EPI == kEpiSampled) {
+                    epi_sampled8<H>(c, v0, live, kLog2e / ri[q].T, w[q], st[q], bp[q]);
+                } else if constexpr (EPI == kEpiMixed) {
+                    const bool samp = ri[q].T > 0.f;
+                    epi_sampled8<H>(c, v0, live, samp ? kLog2e / ri[q].T : 1.f, w[q], st[q], bp[q]);
+                    epi_greedy8(c, v0 + 8 * H, live, gm[q], gi[q]);
+                } else {
+                    epi_resid8<H, YT>(c, y[q], v0, live, ri[q], w[q], rs[q], bp[q]);
+                }
             }
+        };
+        using H0 = std::integral_constant<int, 0>;
+        using H1 = std::integral_constant<int, 1>;
+        const uint32_t nw[2] = {0u, 0u};
+
+        if constexpr (WORDS) race_words(t0);
+        // tile t0: phase A without an epilogue
+        tile_barrier();
+        issue_w(t0 + 3, 3);
+        mfma_half(0, 0, acc_lo);
+        // phase B of tile t0
+        load_half(t0, 1);
+        DSPARK_WAIT_VMCNT(WAIT_B);
+        mfma_half(0, 1, acc_hi);
+        {
+            uint32_t w[2] = {0u, 0u};
+            if constexpr (WORDS) {
+                w[0] = word_of(0, t0);
+                w[1] = word_of(1, t0);
+            }
+            epilogue(H0{}, t0, acc_lo, w);
+        }
+        load_half(t0 + 1, 0);
+        for (int t = t0 + 1; t < t_end; ++t) {
+            const int stg = (t - t0) & 3;
+            uint32_t wp[2] = {0u, 0u}, wc[2] = {0u, 0u};  // race words of tiles t - 1 and t
+            if constexpr (WORDS) {
+                wp[0] = word_of(0, t - 1);
+                wp[1] = word_of(1, t - 1);
+            }
+            // phase A
+            tile_barrier();
+            issue_w(t + 3, (t + 3 - t0) & 3);
+            if constexpr (WORDS) {
+                if ((t & 3) == 0) race_words(t);
+                wc[0] = word_of(0, t);
+                wc[1] = word_of(1, t);
+            }
+            DSPARK_WAIT_VMCNT(WAIT_A);
+            mfma_half(stg, 0, acc_lo);
+            epilogue(H1{}, t - 1, acc_hi, wp);
+            // phase B (the high logit registers are free again)
+            load_half(t, 1);
+            DSPARK_WAIT_VMCNT(WAIT_B);
+            mfma_half(stg, 1, acc_hi);
+            epilogue(H0{}, t, acc_lo, wc);
+            load_half(t + 1, 0);
+        }
+        // the high half of the last tile
+        uint32_t w[2] = {0u, 0u};
+        if constexpr (WORDS) {
+            w[0] = word_of(0, t_end - 1);
+            w[1] = word_of(1, t_end - 1);
+        }
+        (void)nw;
+        DSPARK_WAIT_VMCNT(0);
+        epilogue(H1{}, t_end - 1, acc_hi, w);
+    };
+
+    using I0 = std::integral_constant<int, kEpiGreedy>;
+    using I1 = std::integral_constant<int, kEpiSampled>;
+    using I2 = std::integral_constant<int, kEpiMixed>;
+    using I3 = std::integral_constant<int, kEpiResid>;
+    using B0 = std::integral_constant<bool, false>;
+    using B1 = std::integral_constant<bool, true>;
+    if (have_tiles) {  // uniform
+        // the low logits of tile t0; then the gathered U fragments (and W(t0..t0+2)) have
+        // landed once only those are pending, which keeps the loop free of waits on registers
+        // loaded before it
+        load_half(t0, 0);
+        DSPARK_WAIT_VMCNT(NL);
+        if constexpr (kResid) {
+            run(I3{}, B0{});
+        } else if (p.corrected) {
+            run(I2{}, B1{});
+        } else if (!wave_sampled) {
+            run(I0{}, B0{});
+        } else if (!wave_greedy) {
+            run(I1{}, B0{});
+        } else {
+            run(I2{}, B0{});
         }
     }
 
@@ -521,7 +664,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         if constexpr (MODE == HeadMode::Draft) {
-            const bool greedy = ri[q].T == 0.f;
+            const bool greedy = !(ri[q].T > 0.f);
+            if (greedy && (wave_sampled || p.corrected)) {  // the mixed epilogue kept it aside
+                st[q].m = gm[q];
+                st[q].idx = gi[q];
+            }
 #pragma unroll
             for (int mask = 16; mask <= 32; mask <<= 1) {
                 const SampleState o = shfl_xor_state(st[q], mask);
