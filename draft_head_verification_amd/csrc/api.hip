@@ -63,8 +63,9 @@ size_t draft_layout(int32_t B, int32_t K, int32_t V, DraftWs *ws, char *base) {
     return off;
 }
 
-// verify workspace: status | n_resid | first_reject[B] | resid_rows[B] | rowstats[B][K+1] |
-// row_partials[B][K+1][n_row_slabs] | partials[B][n_slabs]
+// verify workspace: status | n_resid | n_alive[kMaxChunks] | alive[kMaxChunks][B] |
+// first_reject[B] | resid_rows[B] | rowstats[B][K+1] | row_partials[B][K+1][n_row_slabs] |
+// partials[B][n_slabs]
 size_t verify_layout(int32_t B, int32_t K, int32_t V, VerifyWs *ws, char *base) {
     const int ns = num_vslabs(V, B);
     const int nrs = num_row_slabs(V, B);
@@ -74,6 +75,10 @@ size_t verify_layout(int32_t B, int32_t K, int32_t V, VerifyWs *ws, char *base) 
     off += 256;
     if (ws) ws->n_resid = reinterpret_cast<int32_t *>(base + off);
     off += 256;
+    if (ws) ws->n_alive = reinterpret_cast<int32_t *>(base + off);
+    off += 256;
+    if (ws) ws->alive = reinterpret_cast<int32_t *>(base + off);
+    off += align256((size_t)kMaxChunks * B * sizeof(int32_t));
     if (ws) ws->first_reject = reinterpret_cast<int32_t *>(base + off);
     off += align256((size_t)B * sizeof(int32_t));
     if (ws) ws->resid_rows = reinterpret_cast<int32_t *>(base + off);
@@ -211,6 +216,11 @@ dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_byt
     for (int c = 0; c < n_chunks; ++c) {
         e = traced(a->trace, "verify_rows", s, [&] { return launch_verify_rows(*a, w, c, s); });
         if (e != hipSuccess) return DSPARK_EHIP;
+        if (c + 1 < n_chunks) {
+            e = traced(a->trace, "verify_decide", s,
+                       [&] { return launch_verify_decide(*a, w, c, s); });
+            if (e != hipSuccess) return DSPARK_EHIP;
+        }
     }
     e = traced(a->trace, "verify_finish", s, [&] { return launch_verify_finish(*a, w, s); });
     if (e != hipSuccess) return DSPARK_EHIP;

@@ -439,6 +439,8 @@ struct DraftWs {
 // blocks, about two per thread and sweep), so that a chunk of rows keeps the CUs streaming
 // even when few requests are still being verified.
 constexpr int kRowThreads = 256;
+constexpr int kRowGrid = 2048;   // workgroups of a row-statistics launch (8 per CU)
+constexpr int kMaxChunks = 8;    // chunks of target rows (K + 1 <= 65 rows)
 inline int num_row_slabs(int V, int B) {
     (void)B;
     const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
@@ -449,6 +451,8 @@ inline int num_row_slabs(int V, int B) {
 struct VerifyWs {
     uint32_t *status;      // [1]
     int32_t *n_resid;      // [1] number of rows needing a residual draw
+    int32_t *n_alive;      // [kMaxChunks] requests listed for each chunk
+    int32_t *alive;        // [kMaxChunks][B] the listed requests (chunk 0: all, unlisted)
     int32_t *first_reject; // [B] first rejected position (K + 1: none so far)
     int32_t *resid_rows;   // [B] packed (b * 128 + j)
     float4 *rowstats;      // [B][K+1] {m2, l, idx-as-bits, g}
@@ -485,12 +489,13 @@ hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, in
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, hipStream_t s);
 
 hipError_t launch_verify_prepare(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s);
-// Target rows are verified in chunks (one launch each); verify_chunks fills the chunk edges
-// for K and returns their count.
-constexpr int kMaxChunks = 8;
+// Target rows are verified in chunks (one launch each, and a decide launch after every chunk
+// but the last); verify_chunks fills the chunk edges for K and returns their count.
 int verify_chunks(int K, int bounds[kMaxChunks + 1]);
 hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
                               hipStream_t s);
+hipError_t launch_verify_decide(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
+                                hipStream_t s);
 hipError_t launch_verify_finish(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s);
 hipError_t launch_verify_residual(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s);
 hipError_t launch_verify_residual_reduce(const dspark_verify_args &a, const VerifyWs &ws,

@@ -9,18 +9,18 @@
 // tag page, post "Speculative Decoding", steps 3-4).
 //
 // Kernels, in launch order:
-//   verify_prepare   clear the status word, the residual-row counter and the per-request
-//                    first rejection
-//   verify_rows      one launch per chunk of target rows ([0,2), [2,5), [5,9), [9,17), ...):
-//                    a workgroup per (request, row of the chunk, vocabulary slab).  It first
-//                    merges the previous chunk's slab statistics of its request and replays
-//                    that chunk's accept decisions (every workgroup of the request reaches the
-//                    same result; one of them writes it), then, if the request is still being
-//                    verified at its row, streams its slab of Y[b][k] once: softmax max /
-//                    sum-exp of Y/T in log2 units, the argmax for greedy rows, and the bonus
-//                    row's block race.  Rows after the first rejection are never needed, so
-//                    only the chunks up to it are read; the kernel boundaries order the data
-//                    between chunks.
+//   verify_prepare   clear the status word, the residual-row counter, the per-chunk request
+//                    counts and the per-request first rejection
+//   verify_rows      one launch per chunk of target rows ([0,2), [2,5), [5,9), [9,17), ...),
+//                    over the requests still being verified there: a fixed grid takes the
+//                    (request, row of the chunk, vocabulary slab) items in turn and streams
+//                    each slab of Y[b][k] once: softmax max / sum-exp of Y/T in log2 units,
+//                    the argmax for greedy rows, and the bonus row's block race.  Rows after
+//                    the first rejection are never needed, so only the chunks up to it are
+//                    read; the kernel boundaries order the data between chunks.
+//   verify_decide    after every chunk but the last, one wave per listed request: merges the
+//                    chunk's slab statistics, takes its accept decisions and lists the
+//                    request for the next chunk if it is still being verified
 //   verify_finish    one wave per request: decides the last chunk, then the accepted length,
 //                    the greedy correction / the bonus draw inside its winning block, or
 //                    enqueues the first rejected row for a residual draw
@@ -33,12 +33,14 @@ namespace dspark {
 
 __global__ __launch_bounds__(256) void verify_prepare_kernel(int B, int K, uint32_t *status,
                                                              int32_t *n_resid,
-                                                             int32_t *first_reject) {
+                                                             int32_t *first_reject,
+                                                             int32_t *n_alive) {
     const int i0 = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
     if (i0 == 0) {
         *status = 0u;
         *n_resid = 0;
     }
+    if (i0 < kMaxChunks) n_alive[i0] = 0;
     for (int i = i0; i < B; i += stride) first_reject[i] = K + 1;
 }
 
@@ -204,53 +206,68 @@ __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V,
     }
 }
 
-// Chunk [k_lo, k_hi) of the target rows; the previous chunk is [p_lo, k_lo) (empty for the
-// first).  Grid: B * (k_hi - k_lo) * S workgroups, (request, row in chunk, slab).
+// Chunk [k_lo, k_hi) of the target rows for the requests still being verified: all B for the
+// first chunk, else the n_alive listed in alive.  Items (request, row in chunk, slab) are
+// spread over a fixed grid; each workgroup takes every gridDim.x-th.
 template <typename YT>
 __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
+    int B, int K, int V, const void *Y, const int32_t *verify_len, const float *temperature,
+    const uint32_t *req_id, uint32_t key0, uint32_t key1, int S, int k_lo, int k_hi,
+    const int32_t *n_alive, const int32_t *alive, Partial *row_partials) {
+    __shared__ SampleState red[kRowThreads / 64];
+    const int R = k_hi - k_lo;
+    const int n_req = alive ? *n_alive : B;
+    const long long n_items = (long long)n_req * R * S;
+    const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {  // uniform
+        const int ai = (int)(item / (R * S)), rem = (int)(item % (R * S));
+        const int kr = rem / S, slab = rem % S;
+        const int b = alive ? alive[ai] : ai;
+        const int k = k_lo + kr;
+        const ReqInfo ri = req_info(b, K, verify_len, temperature, req_id);
+        if (k > ri.L) continue;  // uniform: past this request's rows
+        const size_t row = (size_t)b * (K + 1) + k;
+        const int blk_lo = (int)((long long)slab * n_blk / S);
+        const int blk_hi = (int)((long long)(slab + 1) * n_blk / S);
+        SampleState st = sample_state_init();
+        row_slab_stats<YT>(Y, row, V, blk_lo, blk_hi, ri, !ri.greedy && k == ri.L, k, key0, key1,
+                           st);
+        for (int mask = 1; mask < 64; mask <<= 1) {
+            const SampleState o = shfl_xor_state(st, mask);
+            merge_into(st, o, ri.greedy);
+        }
+        if (lane == 0) red[wave] = st;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            SampleState a = red[0];
+            for (int w = 1; w < kRowThreads / 64; ++w) merge_into(a, red[w], ri.greedy);
+            row_partials[row * S + slab] = to_partial(a);
+        }
+        __syncthreads();  // red is reused by the next item
+    }
+}
+
+// One wave per request of chunk [k_lo, k_hi) (all B for the first chunk, else the listed
+// ones): merge the chunk's slab statistics, take its accept decisions, and list the request
+// for the next chunk when it is still being verified there.
+template <typename YT>
+__global__ __launch_bounds__(256) void verify_decide_kernel(
     int B, int K, int V, const void *Y, const int32_t *draft_tokens, const float *q_tok,
     const int32_t *verify_len, const float *temperature, const uint32_t *req_id, uint32_t key0,
-    uint32_t key1, int S, int p_lo, int k_lo, int k_hi, Partial *row_partials,
-    int32_t *first_reject, float4 *rowstats, float *p_tok, uint32_t *status) {
-    __shared__ SampleState red[kRowThreads / 64];
-    __shared__ int s_go;
-    const int R = k_hi - k_lo;
-    const int b = blockIdx.x / (R * S), rem = blockIdx.x % (R * S);
-    const int kr = rem / S, slab = rem % S;
-    const int k = k_lo + kr;
+    uint32_t key1, int S, int k_lo, int k_hi, const int32_t *n_alive, const int32_t *alive,
+    const Partial *row_partials, int32_t *first_reject, float4 *rowstats, float *p_tok,
+    int32_t *n_next, int32_t *next, uint32_t *status) {
+    const int lane = threadIdx.x & 63;
+    const int ai = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    const int n_req = alive ? *n_alive : B;
+    if (ai >= n_req) return;  // uniform per wave
+    const int b = alive ? alive[ai] : ai;
     const ReqInfo ri = req_info(b, K, verify_len, temperature, req_id);
-    // rejections of earlier chunks were recorded by earlier launches
-    const int fr = __hip_atomic_load(first_reject + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (fr < p_lo || ri.L < p_lo) return;  // uniform: the request stopped before this chunk
-    if (threadIdx.x < 64) {
-        int rej = -1;
-        if (p_lo < k_lo)
-            rej = decide_rows<YT>(b, p_lo, k_lo, ri, K, V, S, Y, draft_tokens, q_tok,
-                                  row_partials, key0, key1, kr == 0 && slab == 0, rowstats,
-                                  p_tok, first_reject, status);
-        if (threadIdx.x == 0) s_go = rej < 0 && k <= ri.L;
-    }
-    __syncthreads();
-    if (!s_go) return;
-
-    const size_t row = (size_t)b * (K + 1) + k;
-    const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
-    const int blk_lo = (int)((long long)slab * n_blk / S);
-    const int blk_hi = (int)((long long)(slab + 1) * n_blk / S);
-    SampleState st = sample_state_init();
-    row_slab_stats<YT>(Y, row, V, blk_lo, blk_hi, ri, !ri.greedy && k == ri.L, k, key0, key1, st);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int mask = 1; mask < 64; mask <<= 1) {
-        const SampleState o = shfl_xor_state(st, mask);
-        merge_into(st, o, ri.greedy);
-    }
-    if (lane == 0) red[wave] = st;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        SampleState a = red[0];
-        for (int w = 1; w < kRowThreads / 64; ++w) merge_into(a, red[w], ri.greedy);
-        row_partials[row * S + slab] = to_partial(a);
-    }
+    const int rej = decide_rows<YT>(b, k_lo, k_hi, ri, K, V, S, Y, draft_tokens, q_tok,
+                                    row_partials, key0, key1, true, rowstats, p_tok, first_reject,
+                                    status);
+    if (lane == 0 && rej < 0 && ri.L >= k_hi) next[atomicAdd(n_next, 1)] = b;
 }
 
 // One wave per request.  [c_lo, c_hi) is the last chunk of rows, which no later launch has
@@ -417,8 +434,8 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
 
 hipError_t launch_verify_prepare(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s) {
     const int blocks = (a.B + 255) / 256 < 1024 ? (a.B + 255) / 256 : 1024;
-    verify_prepare_kernel<<<blocks < 1 ? 1 : blocks, 256, 0, s>>>(a.B, a.K, ws.status,
-                                                                   ws.n_resid, ws.first_reject);
+    verify_prepare_kernel<<<blocks < 1 ? 1 : blocks, 256, 0, s>>>(
+        a.B, a.K, ws.status, ws.n_resid, ws.first_reject, ws.n_alive);
     return hipGetLastError();
 }
 
@@ -435,27 +452,56 @@ int verify_chunks(int K, int bounds[kMaxChunks + 1]) {
     return n;
 }
 
+// requests listed for chunk c (chunk 0: all of them, no list)
+static const int32_t *alive_list(const VerifyWs &ws, int c, int B) {
+    return c == 0 ? nullptr : ws.alive + (size_t)c * B;
+}
+
 hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
                               hipStream_t s) {
     int bounds[kMaxChunks + 1];
     const int n = verify_chunks(a.K, bounds);
     if (chunk < 0 || chunk >= n) return hipErrorInvalidValue;
-    const int p_lo = chunk > 0 ? bounds[chunk - 1] : 0;
     const int k_lo = bounds[chunk], k_hi = bounds[chunk + 1];
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
-    const long long n_wg = (long long)a.B * (k_hi - k_lo) * ws.n_row_slabs;
-    if (n_wg > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)n_wg), block(kRowThreads);
+    const long long max_items = (long long)a.B * (k_hi - k_lo) * ws.n_row_slabs;
+    const int grid = (int)(max_items < kRowGrid ? max_items : kRowGrid);
+    const int32_t *list = alive_list(ws, chunk, a.B);
+    const int32_t *cnt = ws.n_alive + chunk;
     if (a.y_dtype == DSPARK_BF16)
-        verify_rows_kernel<uint16_t><<<grid, block, 0, s>>>(
-            a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
-            k0, k1, ws.n_row_slabs, p_lo, k_lo, k_hi, ws.row_partials, ws.first_reject,
-            ws.rowstats, a.p_tok, ws.status);
+        verify_rows_kernel<uint16_t><<<grid, kRowThreads, 0, s>>>(
+            a.B, a.K, a.V, a.Y, a.verify_len, a.temperature, a.req_id, k0, k1, ws.n_row_slabs,
+            k_lo, k_hi, cnt, list, ws.row_partials);
     else
-        verify_rows_kernel<float><<<grid, block, 0, s>>>(
+        verify_rows_kernel<float><<<grid, kRowThreads, 0, s>>>(
+            a.B, a.K, a.V, a.Y, a.verify_len, a.temperature, a.req_id, k0, k1, ws.n_row_slabs,
+            k_lo, k_hi, cnt, list, ws.row_partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_verify_decide(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
+                                hipStream_t s) {
+    int bounds[kMaxChunks + 1];
+    const int n = verify_chunks(a.K, bounds);
+    if (chunk < 0 || chunk + 1 >= n) return hipErrorInvalidValue;  // not the last chunk
+    const int k_lo = bounds[chunk], k_hi = bounds[chunk + 1];
+    const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
+    const int per_block = 4;  // one wave per request
+    const dim3 grid((a.B + per_block - 1) / per_block), block(64 * per_block);
+    const int32_t *list = alive_list(ws, chunk, a.B);
+    const int32_t *cnt = ws.n_alive + chunk;
+    int32_t *next = ws.alive + (size_t)(chunk + 1) * a.B;
+    int32_t *n_next = ws.n_alive + chunk + 1;
+    if (a.y_dtype == DSPARK_BF16)
+        verify_decide_kernel<uint16_t><<<grid, block, 0, s>>>(
             a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
-            k0, k1, ws.n_row_slabs, p_lo, k_lo, k_hi, ws.row_partials, ws.first_reject,
-            ws.rowstats, a.p_tok, ws.status);
+            k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials, ws.first_reject,
+            ws.rowstats, a.p_tok, n_next, next, ws.status);
+    else
+        verify_decide_kernel<float><<<grid, block, 0, s>>>(
+            a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
+            k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials, ws.first_reject,
+            ws.rowstats, a.p_tok, n_next, next, ws.status);
     return hipGetLastError();
 }
 
