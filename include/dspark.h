@@ -45,11 +45,20 @@
  *   - Vocabulary size V must be a multiple of 8 (vectorised row loads).
  *
  * Randomness (all three calls): Philox4x32-10 (Salmon et al., SC'11) keyed by `seed`
- * (low word, high word), counter = (v >> 2, position, request key, stream), output word v & 3,
- * uniform u = ((word >> 8) + 0.5) / 2^24 in (0, 1).  Streams: 0 draft sampling, 1 accept test
- * (v = 0), 2 residual resampling, 3 bonus.  Sampling is Gumbel-max:
- * x = argmax_v (s_v - log(-log u_v)).  Results therefore depend only on (inputs, seed,
- * request keys), not on launch geometry.  Every argmax breaks ties towards the lowest index.
+ * (low word, high word); a draw takes one output word w and u = ((w >> 8) + 0.5) / 2^24 in
+ * (0, 1), G = -log(-log u) a standard Gumbel draw.  Token v's draw on stream s at position k
+ * uses word v & 3 of the block at counter (v >> 2, k, request key, s).
+ *
+ * Sampling a token from weights w_v = exp(a_v) (the pages fix only the law, the draw is this
+ * library's): a two-level Gumbel-max.  The vocabulary is cut into blocks of 16 consecutive
+ * ids (the last one may be shorter); block beta has the log-weight A = log sum_{v in beta} w_v
+ * and the race score A + G_beta, where G_beta comes from word b of the Philox block at
+ * counter (4 a + c, k, request key, race stream) for beta = 16 a + 4 b + c (b, c in 0..3).
+ * The best block wins; inside it the token with the best a_v + G_v (token draws on the
+ * within stream) is drawn.  Token v then has probability w_v / sum w.  Streams (race /
+ * within): 0 / 4 draft, 2 / 5 residual, 3 / 6 bonus; 1 is the accept test (v = 0).
+ * Results therefore depend only on (inputs, seed, request keys), not on launch geometry.
+ * Every argmax, and the race, breaks exact ties towards the lowest index.
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -89,14 +98,14 @@ typedef struct dspark_trace dspark_trace;
  *   prev   = prev_token[b] for k = 0, else x[b][k-1]          (previous token only)
  *   c[v]   = Z[b][k][v] + sum_i U[prev][i] * W[v][i]          (float32 accumulation)
  *   T_b = 0: x = argmax_v c[v],  q_tok = 1, q_lse = 0
- *   T_b > 0: s = c / T_b, q_lse = log sum_v exp(s_v), x = Gumbel-max of s on stream 0 at
- *            position k, q_tok = exp(s_x - q_lse)
+ *   T_b > 0: s = c / T_b, q_lse = log sum_v exp(s_v), x = two-level draw from s on the
+ *            draft streams at position k, q_tok = exp(s_x - q_lse)
  * Positions k >= K_b get x = -1, q_tok = 0, q_lse = 0.
  *
  * Layouts: Z [B][K][V]; U [V][r] (row t is the left factor of token t); W [V][r] -- row v
  * holds column v of the r x V right factor (the same layout as an output-projection weight).
  * U and W share a dtype.  Z may be float32 or bfloat16.  Supported: r in [1, 1024]; bfloat16
- * factors with r a multiple of 32 and r <= 256 run on the matrix cores, anything else on the
+ * factors with r = 64, 128 or 256 run on the matrix cores, anything else on the
  * vector ALUs.  K in [1, 64].  B >= 0 (B = 0 launches nothing).
  * Outputs: draft_tokens [B][K] int32, q_tok [B][K] float32, q_lse [B][K] float32; corrected
  * [B][K][V] float32 is optional (NULL skips it) and receives c.
@@ -161,10 +170,10 @@ typedef struct {
  *     T = 0: argmax_v Y[b][j][v];
  *     T > 0: q_j(v) = exp(c_j[v] / T - q_lse[b][j]) with c_j recomputed by the Markov head
  *            (previous token prev_token[b] for j = 0, else draft_tokens[b][j-1]);
- *            r = max(0, p - q_j); Gumbel-max of log r over r > 0 on stream 2 at position j;
- *            if r is identically zero, Gumbel-max of p on stream 2.
+ *            r = max(0, p - q_j); the two-level draw from the weights r on the residual
+ *            streams at position j; if r is identically zero, the same draw from p.
  *   No rejection: accept_len = L and next_token is argmax_v Y[b][L][v] (T = 0) or the
- *   Gumbel-max of Y[b][L] / T on stream 3 at position L (the bonus token).
+ *   two-level draw from Y[b][L] / T on the bonus streams at position L (the bonus token).
  * Layouts: Y [B][K+1][V] (row K+1 exists for the bonus); draft_tokens, q_tok, q_lse [B][K]
  * as written by dspark_draft_block; Z, U, W, prev_token, req_id, seed and the dtypes must be
  * the ones the draft used.  Y may be float32 or bfloat16.
