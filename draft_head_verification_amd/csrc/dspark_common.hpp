@@ -435,16 +435,17 @@ struct DraftWs {
     int n_slabs;
 };
 
-// Verification splits every target row over n_row_slabs workgroups (slabs of whole 16-token
-// blocks, about two per thread and sweep), so that a chunk of rows keeps the CUs streaming
-// even when few requests are still being verified.
+// Verification splits every target row over n_row_slabs items (slabs of whole 16-token
+// blocks, at most kRowBlocks per thread), so that a chunk of rows keeps the CUs streaming even
+// when few requests are still being verified.
 constexpr int kRowThreads = 256;
-constexpr int kRowGrid = 2048;   // workgroups of a row-statistics launch (8 per CU)
+constexpr int kRowBlocks = 4;    // sampler blocks per thread and sweep, loads issued together
+constexpr int kRowGrid = 1024;   // workgroups of a row-statistics launch (4 per CU)
 constexpr int kMaxChunks = 8;    // chunks of target rows (K + 1 <= 65 rows)
 inline int num_row_slabs(int V, int B) {
     (void)B;
     const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
-    const int s = (n_blk + 2 * kRowThreads - 1) / (2 * kRowThreads);
+    const int s = (n_blk + kRowBlocks * kRowThreads - 1) / (kRowBlocks * kRowThreads);
     return s < 1 ? 1 : s;
 }
 

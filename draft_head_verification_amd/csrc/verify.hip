@@ -160,22 +160,23 @@ __device__ int decide_rows(int b, int k0, int k1, const ReqInfo &ri, int K, int 
     return -1;
 }
 
-// Statistics of one vocabulary slab of one target row (whole workgroup); two sampler blocks
-// per thread and iteration are in flight.
+// Statistics of one vocabulary slab of one target row (whole workgroup).  Each thread takes
+// kRowBlocks sampler blocks per sweep and issues all their loads before using any.
 template <typename YT>
 __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V, int blk_lo,
                                                int blk_hi, const ReqInfo &ri, bool bonus, int k,
                                                uint32_t key0, uint32_t key1, SampleState &st) {
-    for (int blk = blk_lo + (int)threadIdx.x; blk < blk_hi; blk += 2 * kRowThreads) {
-        const int blk2 = blk + kRowThreads;
-        const bool two = blk2 < blk_hi;
-        Raw16<YT> y[2];
-        y[0].load(Y, row, V, blk * kSampleBlock);
-        y[1].load(Y, row, V, (two ? blk2 : blk) * kSampleBlock);
+    for (int blk = blk_lo + (int)threadIdx.x; blk < blk_hi; blk += kRowBlocks * kRowThreads) {
+        Raw16<YT> y[kRowBlocks];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (h == 1 && !two) break;
-            const int bb = h ? blk2 : blk;
+        for (int h = 0; h < kRowBlocks; ++h) {
+            const int bb = blk + h * kRowThreads;
+            y[h].load(Y, row, V, (bb < blk_hi ? bb : blk) * kSampleBlock);
+        }
+#pragma unroll
+        for (int h = 0; h < kRowBlocks; ++h) {
+            const int bb = blk + h * kRowThreads;
+            if (bb >= blk_hi) break;
             const int v0 = bb * kSampleBlock;
             const int n_live = min(kSampleBlock, V - v0);
             if (ri.greedy) {
