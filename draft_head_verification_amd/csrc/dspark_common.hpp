@@ -259,6 +259,11 @@ struct Raw16<uint16_t> {
         const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + row * (size_t)V;
         q[h] = *reinterpret_cast<const uint4 *>(p + min(v0 + 8 * h, V - 8));
     }
+    // the same when entries v0 + 8h .. + 7 are known to lie inside the row
+    __device__ __forceinline__ void load_half_nc(const void *base, size_t row, int V, int v0, int h) {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + row * (size_t)V;
+        q[h] = *reinterpret_cast<const uint4 *>(p + v0 + 8 * h);
+    }
     __device__ __forceinline__ void zero() {
         q[0] = make_uint4(0u, 0u, 0u, 0u);
         q[1] = q[0];
@@ -285,6 +290,11 @@ struct Raw16<float> {
         const float *p = reinterpret_cast<const float *>(base) + row * (size_t)V;
 #pragma unroll
         for (int k = 0; k < 2; ++k) q[2 * h + k] = *reinterpret_cast<const float4 *>(p + min(v0 + 8 * h + 4 * k, V - 4));
+    }
+    __device__ __forceinline__ void load_half_nc(const void *base, size_t row, int V, int v0, int h) {
+        const float *p = reinterpret_cast<const float *>(base) + row * (size_t)V;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) q[2 * h + k] = *reinterpret_cast<const float4 *>(p + v0 + 8 * h + 4 * k);
     }
     __device__ __forceinline__ void zero() {
 #pragma unroll

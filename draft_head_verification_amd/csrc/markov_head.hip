@@ -307,31 +307,35 @@ struct BlockPart {
     float ref, sum;  // sampled: sum of exp2(s - ref); residual: ref = sum of p, sum = sum of r
 };
 
+// MASK: the half may run past V (only in a slab holding a partial last tile); entries
+// e >= n_live then have no weight.  Without it every entry is live and no test is emitted.
+template <bool MASK>
 __device__ __forceinline__ void epi_greedy8(const float c[8], int v, int n_live, float &m,
                                             int &idx) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float x = e < n_live ? c[e] : -INFINITY;
+        const float x = (!MASK || e < n_live) ? c[e] : -INFINITY;
         const bool take = x > m;
         m = take ? x : m;
         idx = take ? v + e : idx;
     }
 }
 
-template <int H>
+// The block maximum is taken on c and scaled once (exact: rounding is monotonic and inv > 0),
+// and each weight is exp2(c * inv - base) with one fused multiply-add.
+template <int H, bool MASK>
 __device__ __forceinline__ void epi_sampled8(const float c[8], int v0, int n_live, float inv,
                                              uint32_t word, SampleState &st, BlockPart &bp) {
-    float s[8];
+    float cm[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = e < n_live ? c[e] * inv : -INFINITY;
-    float m8 = s[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) m8 = fmaxf(m8, s[e]);
-    const float mn = fmaxf(st.m, m8);
+    for (int e = 0; e < 8; ++e) cm[e] = (!MASK || e < n_live) ? c[e] : -INFINITY;
+    float m8 = fmaxf(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])),
+                     fmaxf(fmaxf(cm[4], cm[5]), fmaxf(cm[6], cm[7])));
+    const float mn = fmaxf(st.m, m8 * inv);
     const float base = (mn == -INFINITY) ? 0.f : mn;
     float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += fast_exp2(s[e] - base);
+    for (int e = 0; e < 8; ++e) acc += fast_exp2(fmaf(cm[e], inv, -base));
     st.l = st.l * fast_exp2(st.m - base) + acc;
     st.m = mn;
     if constexpr (H == 0) {
@@ -344,7 +348,7 @@ __device__ __forceinline__ void epi_sampled8(const float c[8], int v0, int n_liv
     }
 }
 
-template <int H, typename YT>
+template <int H, typename YT, bool MASK>
 __device__ __forceinline__ void epi_resid8(const float c[8], const Raw16<YT> &yr, int v0,
                                            int n_live, const RowInfo &ri, uint32_t word,
                                            ResidState &rs, BlockPart &bp) {
@@ -352,9 +356,9 @@ __device__ __forceinline__ void epi_resid8(const float c[8], const Raw16<YT> &yr
     float R = 0.f, P = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const bool in = e < n_live;
-        const float pv = in ? fast_exp2(yr.get(8 * H + e) * inv - ri.lse2p) : 0.f;  // p_v
-        const float rv = pv - fast_exp2(c[e] * inv - ri.qlse2);                     // p_v - q_v
+        const bool in = !MASK || e < n_live;
+        const float pv = in ? fast_exp2(fmaf(yr.get(8 * H + e), inv, -ri.lse2p)) : 0.f;  // p_v
+        const float rv = pv - fast_exp2(fmaf(c[e], inv, -ri.qlse2));                   // p - q
         R += in ? fmaxf(rv, 0.f) : 0.f;
         P += pv;
     }
@@ -410,7 +414,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     static_assert(WAIT_A <= 63 && WAIT_B <= 63, "vmcnt range");
     __shared__ __align__(16) uint4 wt[STAGES * TILE_CH];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
     const int m = lane & 15, g = lane >> 4;
     const int n_groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
     const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
@@ -427,25 +432,39 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     const int t0 = t_begin;
 
     // W tile t -> LDS stage s, 16 bytes per lane, swizzled; tiles past the slab re-read the
-    // slab's last tile (cache-resident) so every wave issues the same number of loads.
-    auto issue_w = [&](int t, int s) {
+    // slab's last tile (cache-resident) so every wave issues the same number of loads.  The
+    // lane's element offsets inside a tile are fixed; CLAMP (only for a partial last tile of
+    // the vocabulary) keeps the rows past V on row V - 1.
+    int w_row[LPW], w_off[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int P = (wave * LPW + i) * 64 + lane;
+        const int row = P / CPR, pc = P % CPR;
+        w_row[i] = row;
+        w_off[i] = row * R + (pc ^ w_swizzle<CPR>(row)) * 8;
+    }
+    auto issue_w = [&](int t, int s, auto clamp_tag) {
+        constexpr bool CL = decltype(clamp_tag)::value;
         const int tc = t < t_end ? t : t_end - 1;
+        const uint16_t *tile = p.W + (size_t)tc * kTileV * R;
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            const int cb = wave * LPW + i;
-            const int P = cb * 64 + lane;
-            const int row = P / CPR, pc = P % CPR;
-            const int col = pc ^ w_swizzle<CPR>(row);
-            int v = tc * kTileV + row;
-            v = v < p.V ? v : p.V - 1;
+            const uint16_t *src = tile + w_off[i];
+            if constexpr (CL) {
+                const int over = tc * kTileV + w_row[i] - (p.V - 1);  // rows past V - 1
+                if (over > 0) src -= (size_t)over * R;
+            }
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1))) *)(p.W + (size_t)v * R + col * 8),
-                (void __attribute__((address_space(3))) *)(wt + s * TILE_CH + cb * 64), 16, 0, 0);
+                (const void __attribute__((address_space(1))) *)src,
+                (void __attribute__((address_space(3))) *)(wt + s * TILE_CH + (wave * LPW + i) * 64),
+                16, 0, 0);
         }
     };
+    using B0 = std::integral_constant<bool, false>;
+    using B1 = std::integral_constant<bool, true>;
     // W tiles t0 .. t0+2 go out first: they depend on nothing
     if (have_tiles)
-        for (int u = 0; u < STAGES - 1; ++u) issue_w(t0 + u, u);
+        for (int u = 0; u < STAGES - 1; ++u) issue_w(t0 + u, u, B1{});
 
     RowInfo ri[2];
     bf16x8 ufrag[2][KS];
@@ -505,12 +524,19 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     // logits (base, and target in residual mode) of half h of tile t; invalid rows read row 0
     Raw16<ZT> z[2];
     Raw16<YT> y[2];
-    auto load_half = [&](int t, int h) {
+    // (CLAMP: the tile may be the vocabulary's partial last one)
+    auto load_half = [&](int t, int h, auto clamp_tag) {
+        constexpr bool CL = decltype(clamp_tag)::value;
         const int tc = t < t_end ? t : t_end - 1;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            z[q].load_half(p.Z, ri[q].zrow, p.V, tc * kTileV + 16 * g, h);
-            if constexpr (kResid) y[q].load_half(p.Y, ri[q].yrow, p.V, tc * kTileV + 16 * g, h);
+            if constexpr (CL) {
+                z[q].load_half(p.Z, ri[q].zrow, p.V, tc * kTileV + 16 * g, h);
+                if constexpr (kResid) y[q].load_half(p.Y, ri[q].yrow, p.V, tc * kTileV + 16 * g, h);
+            } else {
+                z[q].load_half_nc(p.Z, ri[q].zrow, p.V, tc * kTileV + 16 * g, h);
+                if constexpr (kResid) y[q].load_half_nc(p.Y, ri[q].yrow, p.V, tc * kTileV + 16 * g, h);
+            }
         }
     };
 
@@ -536,15 +562,16 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     };
 
     floatx4 acc_lo[2][2], acc_hi[2][2];
-    auto run = [&](auto epi_tag, auto store_tag) {
+    auto run = [&](auto epi_tag, auto store_tag, auto mask_tag) {
         constexpr int EPI = decltype(epi_tag)::value;
         constexpr bool STORE = decltype(store_tag)::value;
+        constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool WORDS = EPI != kEpiGreedy;
         // epilogue of half H of tile t from acc, with the race words w[q] of that tile
         auto epilogue = [&](auto half_tag, int t, const floatx4 (&acc)[2][2], const uint32_t (&w)[2]) {
             constexpr int H = decltype(half_tag)::value;
             const int v0 = t * kTileV + 16 * g;
-            const int live = min(8, p.V - v0 - 8 * H);
+            const int live = MASK ? min(8, p.V - v0 - 8 * H) : 8;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 float c[8];
@@ -562,15 +589,15 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                     }
                 }
                 if constexpr (EPI == kEpiGreedy) {
-                    epi_greedy8(c, v0 + 8 * H, live, st[q].m, st[q].idx);
+                    epi_greedy8<MASK>(c, v0 + 8 * H, live, st[q].m, st[q].idx);
                 } else if constexpr (EPI == kEpiSampled) {
-                    epi_sampled8<H>(c, v0, live, kLog2e / ri[q].T, w[q], st[q], bp[q]);
+                    epi_sampled8<H, MASK>(c, v0, live, kLog2e / ri[q].T, w[q], st[q], bp[q]);
                 } else if constexpr (EPI == kEpiMixed) {
                     const bool samp = ri[q].T > 0.f;
-                    epi_sampled8<H>(c, v0, live, samp ? kLog2e / ri[q].T : 1.f, w[q], st[q], bp[q]);
-                    epi_greedy8(c, v0 + 8 * H, live, gm[q], gi[q]);
+                    epi_sampled8<H, MASK>(c, v0, live, samp ? kLog2e / ri[q].T : 1.f, w[q], st[q], bp[q]);
+                    epi_greedy8<MASK>(c, v0 + 8 * H, live, gm[q], gi[q]);
                 } else {
-                    epi_resid8<H, YT>(c, y[q], v0, live, ri[q], w[q], rs[q], bp[q]);
+                    epi_resid8<H, YT, MASK>(c, y[q], v0, live, ri[q], w[q], rs[q], bp[q]);
                 }
             }
         };
@@ -581,10 +608,10 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         if constexpr (WORDS) race_words(t0);
         // tile t0: phase A without an epilogue
         tile_barrier();
-        issue_w(t0 + 3, 3);
+        issue_w(t0 + 3, 3, mask_tag);
         mfma_half(0, 0, acc_lo);
         // phase B of tile t0
-        load_half(t0, 1);
+        load_half(t0, 1, mask_tag);
         DSPARK_WAIT_VMCNT(WAIT_B);
         mfma_half(0, 1, acc_hi);
         {
@@ -595,7 +622,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             }
             epilogue(H0{}, t0, acc_lo, w);
         }
-        load_half(t0 + 1, 0);
+        load_half(t0 + 1, 0, mask_tag);
         for (int t = t0 + 1; t < t_end; ++t) {
             const int stg = (t - t0) & 3;
             uint32_t wp[2] = {0u, 0u}, wc[2] = {0u, 0u};  // race words of tiles t - 1 and t
@@ -605,7 +632,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             }
             // phase A
             tile_barrier();
-            issue_w(t + 3, (t + 3 - t0) & 3);
+            issue_w(t + 3, (t + 3 - t0) & 3, mask_tag);
             if constexpr (WORDS) {
                 if ((t & 3) == 0) race_words(t);
                 wc[0] = word_of(0, t);
@@ -615,11 +642,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             mfma_half(stg, 0, acc_lo);
             epilogue(H1{}, t - 1, acc_hi, wp);
             // phase B (the high logit registers are free again)
-            load_half(t, 1);
+            load_half(t, 1, mask_tag);
             DSPARK_WAIT_VMCNT(WAIT_B);
             mfma_half(stg, 1, acc_hi);
             epilogue(H0{}, t, acc_lo, wc);
-            load_half(t + 1, 0);
+            load_half(t + 1, 0, mask_tag);
         }
         // the high half of the last tile
         uint32_t w[2] = {0u, 0u};
@@ -636,24 +663,29 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     using I1 = std::integral_constant<int, kEpiSampled>;
     using I2 = std::integral_constant<int, kEpiMixed>;
     using I3 = std::integral_constant<int, kEpiResid>;
-    using B0 = std::integral_constant<bool, false>;
-    using B1 = std::integral_constant<bool, true>;
     if (have_tiles) {  // uniform
         // the low logits of tile t0; then the gathered U fragments (and W(t0..t0+2)) have
         // landed once only those are pending, which keeps the loop free of waits on registers
         // loaded before it
-        load_half(t0, 0);
+        load_half(t0, 0, B1{});
         DSPARK_WAIT_VMCNT(NL);
+        // only the slab holding a partial last tile needs the masked (and clamped) variant;
+        // writing the corrected logits out is rare and always takes it
+        const bool partial = t_end == n_tiles && p.V % kTileV != 0;
         if constexpr (kResid) {
-            run(I3{}, B0{});
+            if (partial) run(I3{}, B0{}, B1{});
+            else run(I3{}, B0{}, B0{});
         } else if (p.corrected) {
-            run(I2{}, B1{});
+            run(I2{}, B1{}, B1{});
         } else if (!wave_sampled) {
-            run(I0{}, B0{});
+            if (partial) run(I0{}, B0{}, B1{});
+            else run(I0{}, B0{}, B0{});
         } else if (!wave_greedy) {
-            run(I1{}, B0{});
+            if (partial) run(I1{}, B0{}, B1{});
+            else run(I1{}, B0{}, B0{});
         } else {
-            run(I2{}, B0{});
+            if (partial) run(I2{}, B0{}, B1{});
+            else run(I2{}, B0{}, B0{});
         }
     }
 
