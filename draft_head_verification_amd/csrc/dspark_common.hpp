@@ -321,17 +321,19 @@ __device__ __forceinline__ float load_value(const void *base, int dtype, size_t 
 // Lanes whose token is past V read token V - 1; the caller masks them.
 template <typename FT, int N>
 __device__ __forceinline__ float dot_chunks(const FT *u, const FT *w, int n_chunks) {
+    // eight chunks per round: a rank-256 bfloat16 quarter is one round of loads
+    constexpr int kRound = 8;
     float acc = 0.f;
-    for (int c = 0; c < n_chunks; c += 4) {
-        uint4 ru[4], rw[4];
+    for (int c = 0; c < n_chunks; c += kRound) {
+        uint4 ru[kRound], rw[kRound];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kRound; ++j) {
             const int cc = c + j < n_chunks ? c + j : n_chunks - 1;
             ru[j] = *reinterpret_cast<const uint4 *>(u + cc * N);
             rw[j] = *reinterpret_cast<const uint4 *>(w + cc * N);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kRound; ++j) {
             if (c + j >= n_chunks) break;
             const uint32_t *a = reinterpret_cast<const uint32_t *>(&ru[j]);
             const uint32_t *b = reinterpret_cast<const uint32_t *>(&rw[j]);

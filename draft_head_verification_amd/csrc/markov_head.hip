@@ -72,49 +72,77 @@ struct RowInfo {
     float qlse2, lse2p;  // residual mode
 };
 
+// A drafting row's metadata in two steps, so that its loads can go out before other work and
+// be consumed after it.  Absent optional arrays are read at a valid stand-in address and the
+// value replaced afterwards, which keeps every load unconditional.
+struct DraftRowRaw {
+    int kb, prev;
+    float T;
+    uint32_t req;
+};
+__device__ __forceinline__ DraftRowRaw draft_row_load(const HeadParams &p, int row) {
+    const int b = min(row, p.n_rows_max - 1);
+    const int32_t *dl = p.draft_len ? p.draft_len : p.prev_cur;
+    const uint32_t *rq = p.req_id ? p.req_id : reinterpret_cast<const uint32_t *>(p.prev_cur);
+    DraftRowRaw raw;
+    raw.kb = dl[b];
+    raw.prev = p.prev_cur[b];  // validated by the prepare / reduce kernels
+    raw.T = p.temperature[b];
+    raw.req = rq[b];
+    return raw;
+}
+__device__ __forceinline__ RowInfo draft_row_resolve(const HeadParams &p, int row, int n_rows,
+                                                     const DraftRowRaw &raw) {
+    RowInfo ri;
+    const int b = min(row, p.n_rows_max - 1);
+    const int kb_raw = p.draft_len ? raw.kb : p.K;
+    const int kb = kb_raw < 0 ? 0 : (kb_raw > p.K ? p.K : kb_raw);
+    ri.valid = row < n_rows && p.k < kb;
+    ri.b = b;
+    ri.pos = p.k;
+    ri.prev = ri.valid ? raw.prev : 0;
+    ri.zrow = ri.valid ? (size_t)b * p.K + p.k : 0;
+    ri.yrow = 0;
+    ri.T = (ri.valid && raw.T >= 0.f) ? raw.T : 0.f;
+    ri.req = p.req_id ? raw.req : (uint32_t)b;
+    ri.qlse2 = 0.f;
+    ri.lse2p = 0.f;
+    return ri;
+}
+
+// Branch-free: every load is issued at an in-bounds (clamped) index whether or not the row is
+// live, and dead rows are masked with selects afterwards, so that independent loads go out
+// together rather than each behind a branch that an earlier load decides.
 template <HeadMode MODE>
 __device__ __forceinline__ RowInfo row_info(const HeadParams &p, int row, int n_rows) {
     RowInfo ri;
-    ri.valid = false;
-    ri.b = 0;
-    ri.pos = 0;
-    ri.prev = 0;
-    ri.zrow = 0;
-    ri.yrow = 0;
-    ri.T = 0.f;
-    ri.req = 0;
+    const bool in = row < n_rows;
+    const int rc = min(row, p.n_rows_max - 1);
     ri.qlse2 = 0.f;
     ri.lse2p = 0.f;
-    if (row >= n_rows) return ri;
     if constexpr (MODE == HeadMode::Draft) {
-        const int b = row;
-        int kb = p.draft_len ? p.draft_len[b] : p.K;
-        kb = kb < 0 ? 0 : (kb > p.K ? p.K : kb);
-        if (p.k >= kb) return ri;
-        ri.valid = true;
-        ri.b = b;
-        ri.pos = p.k;
-        ri.prev = p.prev_cur[b];  // validated by the prepare / reduce kernels
-        ri.zrow = (size_t)b * p.K + p.k;
-        ri.T = p.temperature[b];
-        if (!(ri.T >= 0.f)) ri.T = 0.f;
+        return draft_row_resolve(p, row, n_rows, draft_row_load(p, row));
     } else {
-        const int packed = p.resid_rows[row];
+        const int raw = p.resid_rows[rc];
+        const int packed = in ? raw : 0;
         const int b = packed >> 7, j = packed & 127;
-        ri.valid = true;
+        ri.valid = in;
         ri.b = b;
         ri.pos = j;
-        int prev = (j == 0) ? p.prev_token[b] : p.draft_tokens[(size_t)b * p.K + j - 1];
-        if (prev < 0 || prev >= p.V) prev = 0;  // flagged by the verifier's finish kernel
-        ri.prev = prev;
+        const int pt = p.prev_token[b];
+        const int dt = p.draft_tokens[(size_t)b * p.K + (j > 0 ? j - 1 : 0)];
         ri.zrow = (size_t)b * p.K + j;
         ri.yrow = (size_t)b * (p.K + 1) + j;
         ri.T = p.temperature[b];  // > 0: greedy rows never need a residual
         const float4 rs = p.rowstats[ri.yrow];
+        const float ql = p.q_lse[ri.zrow];
+        ri.req = p.req_id ? p.req_id[b] : (uint32_t)b;
+        int prev = j == 0 ? pt : dt;
+        prev = (prev < 0 || prev >= p.V) ? 0 : prev;  // flagged by the verifier's finish kernel
+        ri.prev = prev;
         ri.lse2p = rs.x + fast_log2(rs.y);
-        ri.qlse2 = p.q_lse[ri.zrow] * kLog2e;
+        ri.qlse2 = ql * kLog2e;
     }
-    ri.req = p.req_id ? p.req_id[ri.b] : (uint32_t)ri.b;
     return ri;
 }
 
@@ -399,7 +427,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     // epilogue of the high half of tile t - 1.  Phase B: the high logit registers take the
     // high half of tile t, then the high half's matrix-core work runs with the low half's
     // epilogue, and the low logit registers take tile t + 1.  Every wave issues every load,
-    // unconditionally (clamped addresses), and loads retire in issue order, so:
+    // unconditionally (clamped addresses: a W tile past the slab re-reads the slab's last,
+    // cache-resident tile into a stage that is never read), and loads retire in issue order,
+    // so:
     //  * in phase A, once at most NL + LPW operations are pending after W(t+3) (the low
     //    logits of tile t, W(t+3)), the high logits of tile t - 1 have landed, and with them
     //    W(t+2);
@@ -411,7 +441,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     constexpr int NH = 2 * ((int)sizeof(ZT) / 2) + (kResid ? 2 * ((int)sizeof(YT) / 2) : 0);
     constexpr int NL = NH;
     constexpr int WAIT_A = NL + LPW, WAIT_B = LPW + NH;
-    static_assert(WAIT_A <= 63 && WAIT_B <= 63, "vmcnt range");
+    static_assert(WAIT_A <= 63 && WAIT_B <= 63 && NL + 2 * LPW <= 63, "vmcnt range");
     __shared__ __align__(16) uint4 wt[STAGES * TILE_CH];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -445,7 +475,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     }
     auto issue_w = [&](int t, int s, auto clamp_tag) {
         constexpr bool CL = decltype(clamp_tag)::value;
-        const int tc = t < t_end ? t : t_end - 1;
+        const int tc = max(t < t_end ? t : t_end - 1, 0);
         const uint16_t *tile = p.W + (size_t)tc * kTileV * R;
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
@@ -462,18 +492,36 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     };
     using B0 = std::integral_constant<bool, false>;
     using B1 = std::integral_constant<bool, true>;
-    // W tiles t0 .. t0+2 go out first: they depend on nothing
-    if (have_tiles)
-        for (int u = 0; u < STAGES - 1; ++u) issue_w(t0 + u, u, B1{});
 
+    // Prologue.  The first matrix-core step needs W(t0) and the gathered U rows, and the U
+    // gather needs the previous tokens.  Loads retire in issue order, so the short dependent
+    // chain goes first: a drafting step's row metadata (no load of it waits on another), then
+    // W(t0) while it is in flight, then the U gather and the low logits of t0, and only then
+    // W(t0+1), W(t0+2), which the first step need not wait for.  (A residual row's metadata
+    // is itself a two-load chain; its W(t0) goes out before it.)
     RowInfo ri[2];
     bf16x8 ufrag[2][KS];
     bool any_valid = false, any_sampled = false, any_greedy = false;
     int rowid[2];
+    // (an empty slab issues the same loads, of a valid tile, and never reads them)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) rowid[q] = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + m;
+    DraftRowRaw raw[2];
+    if constexpr (!kResid) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) raw[q] = draft_row_load(p, rowid[q]);
+    }
+    issue_w(t0, 0, B1{});
+    // the metadata has landed once only W(t0) is pending; the explicit count keeps the compiler
+    // from waiting for W(t0) as well
+    if constexpr (!kResid) {
+        DSPARK_WAIT_VMCNT(LPW);
+        __builtin_amdgcn_sched_barrier(0);  // no use of the metadata is scheduled above it
+    }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        rowid[q] = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + m;
-        ri[q] = row_info<MODE>(p, rowid[q], n_rows);
+        if constexpr (kResid) ri[q] = row_info<MODE>(p, rowid[q], n_rows);
+        else ri[q] = draft_row_resolve(p, rowid[q], n_rows, raw[q]);
         any_valid |= ri[q].valid;
         any_sampled |= ri[q].valid && ri[q].T > 0.f;
         any_greedy |= ri[q].valid && !(ri[q].T > 0.f);
@@ -527,7 +575,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     // (CLAMP: the tile may be the vocabulary's partial last one)
     auto load_half = [&](int t, int h, auto clamp_tag) {
         constexpr bool CL = decltype(clamp_tag)::value;
-        const int tc = t < t_end ? t : t_end - 1;
+        const int tc = max(t < t_end ? t : t_end - 1, 0);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             if constexpr (CL) {
@@ -663,12 +711,13 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     using I1 = std::integral_constant<int, kEpiSampled>;
     using I2 = std::integral_constant<int, kEpiMixed>;
     using I3 = std::integral_constant<int, kEpiResid>;
+    // the low logits of t0, then W(t0+1), W(t0+2); the U fragments and W(t0) have landed once
+    // only those are pending (phase B of t0 waits for the rest)
+    load_half(t0, 0, B1{});
+    issue_w(t0 + 1, 1, B1{});
+    issue_w(t0 + 2, 2, B1{});
+    DSPARK_WAIT_VMCNT(NL + 2 * LPW);
     if (have_tiles) {  // uniform
-        // the low logits of tile t0; then the gathered U fragments (and W(t0..t0+2)) have
-        // landed once only those are pending, which keeps the loop free of waits on registers
-        // loaded before it
-        load_half(t0, 0, B1{});
-        DSPARK_WAIT_VMCNT(NL);
         // only the slab holding a partial last tile needs the masked (and clamped) variant;
         // writing the corrected logits out is rare and always takes it
         const bool partial = t_end == n_tiles && p.V % kTileV != 0;
@@ -843,7 +892,21 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (b >= B) return;  // uniform per wave
-    int kb = draft_len ? draft_len[b] : K;
+    // Every load that depends on no other goes out first (absent optional arrays are read at a
+    // valid stand-in address and replaced), the slab partials four per lane at a time.
+    const int32_t *dl = draft_len ? draft_len : prev_cur;
+    const uint32_t *rq = req_id ? req_id : reinterpret_cast<const uint32_t *>(prev_cur);
+    const int kb_ld = dl[b];
+    const float T_ld = temperature[b];
+    const int prev = prev_cur[b];
+    const uint32_t req_ld = rq[b];
+    constexpr int kPer = 4;
+    Partial pp[kPer];
+    const Partial *prow = partials + (size_t)b * n_slabs;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) pp[i] = prow[min(lane + 64 * i, n_slabs - 1)];
+
+    int kb = draft_len ? kb_ld : K;
     if (kb < 0 || kb > K) {
         if (lane == 0 && k == 0) atomicOr(status, DSPARK_DEV_BAD_LENGTH);
         kb = kb < 0 ? 0 : K;
@@ -857,13 +920,14 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
         }
         return;
     }
-    const float T = (lane == 0 && k == 0) ? checked_temperature(temperature[b], status)
-                                          : temperature[b];
+    const float T = (lane == 0 && k == 0) ? checked_temperature(T_ld, status) : T_ld;
     const bool greedy = !(T > 0.f);
-    const int prev = prev_cur[b];  // issued together with the partials below
     SampleState st = sample_state_init();
-    for (int s = lane; s < n_slabs; s += 64) {
-        const SampleState o2 = from_partial(partials[(size_t)b * n_slabs + s]);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (lane + 64 * i < n_slabs) merge_into(st, from_partial(pp[i]), greedy);
+    for (int s = lane + 64 * kPer; s < n_slabs; s += 64) {
+        const SampleState o2 = from_partial(prow[s]);
         merge_into(st, o2, greedy);
     }
     for (int mask = 1; mask < 64; mask <<= 1) {
@@ -886,7 +950,7 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
             const bool in = v0 + e < V;
             const float c = wave_corrected16(Z, z_dtype, o, U, W, uw_dtype, r, V, prev, v0);
             const float s2 = c * (kLog2e / T);
-            const uint32_t req = req_id ? req_id[b] : (uint32_t)b;
+            const uint32_t req = req_id ? req_ld : (uint32_t)b;
             const uint32_t w = token_word((uint32_t)(v0 + e), (uint32_t)k, req, kStreamDraftWithin,
                                          key0, key1);
             const float sc = in ? s2 + gumbel2_from_word(w) : -INFINITY;
