@@ -77,8 +77,8 @@ size_t verify_layout(int32_t B, int32_t K, int32_t V, VerifyWs *ws, char *base) 
     off += 256;
     if (ws) ws->n_alive = reinterpret_cast<int32_t *>(base + off);
     off += 256;
-    if (ws) ws->alive = reinterpret_cast<int32_t *>(base + off);
-    off += align256((size_t)kMaxChunks * B * sizeof(int32_t));
+    if (ws) ws->alive = reinterpret_cast<int4 *>(base + off);
+    off += align256((size_t)kMaxChunks * B * sizeof(int4));
     if (ws) ws->first_reject = reinterpret_cast<int32_t *>(base + off);
     off += align256((size_t)B * sizeof(int32_t));
     if (ws) ws->resid_rows = reinterpret_cast<int32_t *>(base + off);

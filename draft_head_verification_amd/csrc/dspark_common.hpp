@@ -447,25 +447,28 @@ struct DraftWs {
     int n_slabs;
 };
 
-// Verification splits every target row over n_row_slabs items (slabs of whole 16-token
-// blocks, at most kRowBlocks per thread), so that a chunk of rows keeps the CUs streaming even
-// when few requests are still being verified.
+// Verification spreads the 16-token blocks of a chunk's target rows evenly over the
+// workgroups of a launch (each takes a contiguous range of at least kRowSweep blocks of the
+// flattened rows), so a chunk keeps every CU streaming to its end whatever the number of
+// requests still being verified.  A row is then covered by at most ceil(n_blk / kRowSweep) + 1
+// workgroups; each leaves one partial in the row's slot (its index mod n_row_slabs), and the
+// workgroup that starts the row fills the slots nobody uses with empty partials.
 constexpr int kRowThreads = 256;
 constexpr int kRowBlocks = 4;    // sampler blocks per thread and sweep, loads issued together
+constexpr int kRowSweep = kRowBlocks * kRowThreads;
 constexpr int kRowGrid = 1024;   // workgroups of a row-statistics launch (4 per CU)
 constexpr int kMaxChunks = 8;    // chunks of target rows (K + 1 <= 65 rows)
 inline int num_row_slabs(int V, int B) {
     (void)B;
     const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
-    const int s = (n_blk + kRowBlocks * kRowThreads - 1) / (kRowBlocks * kRowThreads);
-    return s < 1 ? 1 : s;
+    return (n_blk + kRowSweep - 1) / kRowSweep + 1;
 }
 
 struct VerifyWs {
     uint32_t *status;      // [1]
     int32_t *n_resid;      // [1] number of rows needing a residual draw
     int32_t *n_alive;      // [kMaxChunks] requests listed for each chunk
-    int32_t *alive;        // [kMaxChunks][B] the listed requests (chunk 0: all, unlisted)
+    int4 *alive;           // [kMaxChunks][B] records {b, L, T bits, req} of the listed requests
     int32_t *first_reject; // [B] first rejected position (K + 1: none so far)
     int32_t *resid_rows;   // [B] packed (b * 128 + j)
     float4 *rowstats;      // [B][K+1] {m2, l, idx-as-bits, g}

@@ -442,6 +442,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     constexpr int NL = NH;
     constexpr int WAIT_A = NL + LPW, WAIT_B = LPW + NH;
     static_assert(WAIT_A <= 63 && WAIT_B <= 63 && NL + 2 * LPW <= 63, "vmcnt range");
+    // Cache policy of the W tile loads.  The residual pass streams target logits as well, and
+    // W read there as non-temporal leaves the level-2 cache to the logit rows, whose two halves
+    // are read one phase apart (measured: fewer refetches, shorter launch).  A drafting step
+    // keeps the default policy: there W is re-read every step and gains from staying cached.
+    static constexpr int kWPolicy = kResid ? 2 /* nt */ : 0;
     __shared__ __align__(16) uint4 wt[STAGES * TILE_CH];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             __builtin_amdgcn_global_load_lds(
                 (const void __attribute__((address_space(1))) *)src,
                 (void __attribute__((address_space(3))) *)(wt + s * TILE_CH + (wave * LPW + i) * 64),
-                16, 0, 0);
+                16, 0, kWPolicy);
         }
     };
     using B0 = std::integral_constant<bool, false>;

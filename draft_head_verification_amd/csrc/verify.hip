@@ -31,17 +31,30 @@
 
 namespace dspark {
 
-__global__ __launch_bounds__(256) void verify_prepare_kernel(int B, int K, uint32_t *status,
-                                                             int32_t *n_resid,
-                                                             int32_t *first_reject,
-                                                             int32_t *n_alive) {
+// A listed request: {b, L clamped to [0, K], T as bits, RNG request key}, one 16-byte load.
+__device__ __forceinline__ int4 make_req_rec(int b, int K, const int32_t *verify_len,
+                                             const float *temperature, const uint32_t *req_id) {
+    const int L = verify_len[b];
+    const float T = temperature[b];
+    const uint32_t req = req_id ? req_id[b] : (uint32_t)b;
+    // out-of-range lengths and NaN / negative temperatures are flagged by the finish kernel;
+    // here they act as the nearest bound and as greedy
+    return make_int4(b, L < 0 ? 0 : (L > K ? K : L), __float_as_int(T), (int)req);
+}
+
+__global__ __launch_bounds__(256) void verify_prepare_kernel(
+    int B, int K, const int32_t *verify_len, const float *temperature, const uint32_t *req_id,
+    uint32_t *status, int32_t *n_resid, int32_t *first_reject, int32_t *n_alive, int4 *list0) {
     const int i0 = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
     if (i0 == 0) {
         *status = 0u;
         *n_resid = 0;
     }
-    if (i0 < kMaxChunks) n_alive[i0] = 0;
-    for (int i = i0; i < B; i += stride) first_reject[i] = K + 1;
+    if (i0 < kMaxChunks) n_alive[i0] = i0 == 0 ? B : 0;  // chunk 0 lists every request
+    for (int i = i0; i < B; i += stride) {
+        first_reject[i] = K + 1;
+        list0[i] = make_req_rec(i, K, verify_len, temperature, req_id);
+    }
 }
 
 __device__ __forceinline__ int clamp_len(int L, int K, uint32_t *status, bool report) {
@@ -71,16 +84,19 @@ struct ReqInfo {
     uint32_t req;
 };
 
-__device__ __forceinline__ ReqInfo req_info(int b, int K, const int32_t *verify_len,
-                                            const float *temperature, const uint32_t *req_id) {
+__device__ __forceinline__ ReqInfo req_info(int4 rec) {
     ReqInfo r;
-    int L = verify_len[b];
-    r.L = L < 0 ? 0 : (L > K ? K : L);  // out-of-range lengths are flagged by the finish
-    r.T = temperature[b];                // NaN / negative: greedy here, flagged by the finish
+    r.L = rec.y;
+    r.T = __int_as_float(rec.z);
     r.greedy = !(r.T > 0.f);
     r.inv = r.greedy ? 1.f : kLog2e / r.T;
-    r.req = req_id ? req_id[b] : (uint32_t)b;
+    r.req = (uint32_t)rec.w;
     return r;
+}
+
+__device__ __forceinline__ ReqInfo req_info(int b, int K, const int32_t *verify_len,
+                                            const float *temperature, const uint32_t *req_id) {
+    return req_info(make_req_rec(b, K, verify_len, temperature, req_id));
 }
 
 // One wave: merge the slab statistics of rows [k0, k1) of request b (rows past L are not
@@ -207,45 +223,66 @@ __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V,
     }
 }
 
-// Chunk [k_lo, k_hi) of the target rows for the requests still being verified: all B for the
-// first chunk, else the n_alive listed in alive.  Items (request, row in chunk, slab) are
-// spread over a fixed grid; each workgroup takes every gridDim.x-th.
+// Workgroups of a row-statistics launch that share T blocks: at most the launched grid, and
+// at least kRowSweep blocks each.
+__device__ __forceinline__ long long row_groups(long long T, int grid) {
+    long long G = T / kRowSweep;
+    return G < 1 ? 1 : (G > grid ? grid : G);
+}
+
+// Chunk [k_lo, k_hi) of the target rows for the n_alive requests listed for it.  The chunk's
+// rows, flattened into one sequence of 16-token blocks (row i = list entry i / R, row k_lo +
+// i % R), are cut into G equal contiguous ranges, one per workgroup; each row segment of a
+// range leaves one partial in slot (workgroup % S) of its row.
 template <typename YT>
 __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
-    int B, int K, int V, const void *Y, const int32_t *verify_len, const float *temperature,
-    const uint32_t *req_id, uint32_t key0, uint32_t key1, int S, int k_lo, int k_hi,
-    const int32_t *n_alive, const int32_t *alive, Partial *row_partials) {
+    int K, int V, const void *Y, uint32_t key0, uint32_t key1, int S, int k_lo, int k_hi,
+    const int32_t *n_alive, const int4 *alive, Partial *row_partials) {
     __shared__ SampleState red[kRowThreads / 64];
     const int R = k_hi - k_lo;
-    const int n_req = alive ? *n_alive : B;
-    const long long n_items = (long long)n_req * R * S;
     const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
+    const long long T = (long long)*n_alive * R * n_blk;
+    if (T == 0) return;
+    const long long G = row_groups(T, gridDim.x);
+    const long long w = blockIdx.x;
+    if (w >= G) return;  // uniform
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {  // uniform
-        const int ai = (int)(item / (R * S)), rem = (int)(item % (R * S));
-        const int kr = rem / S, slab = rem % S;
-        const int b = alive ? alive[ai] : ai;
-        const int k = k_lo + kr;
-        const ReqInfo ri = req_info(b, K, verify_len, temperature, req_id);
-        if (k > ri.L) continue;  // uniform: past this request's rows
-        const size_t row = (size_t)b * (K + 1) + k;
-        const int blk_lo = (int)((long long)slab * n_blk / S);
-        const int blk_hi = (int)((long long)(slab + 1) * n_blk / S);
-        SampleState st = sample_state_init();
-        row_slab_stats<YT>(Y, row, V, blk_lo, blk_hi, ri, !ri.greedy && k == ri.L, k, key0, key1,
-                           st);
-        for (int mask = 1; mask < 64; mask <<= 1) {
-            const SampleState o = shfl_xor_state(st, mask);
-            merge_into(st, o, ri.greedy);
+    const long long g1 = (w + 1) * T / G;
+    for (long long gb = w * T / G; gb < g1;) {  // uniform: one row segment per pass
+        const long long ri = gb / n_blk, row_begin = ri * n_blk;
+        const long long seg_end = g1 < row_begin + n_blk ? g1 : row_begin + n_blk;
+        const int4 rec = alive[ri / R];
+        const int k = k_lo + (int)(ri % R);
+        const ReqInfo info = req_info(rec);
+        if (k <= info.L) {  // rows past L are not verified
+            const size_t row = (size_t)rec.x * (K + 1) + k;
+            SampleState st = sample_state_init();
+            row_slab_stats<YT>(Y, row, V, (int)(gb - row_begin), (int)(seg_end - row_begin), info,
+                               !info.greedy && k == info.L, k, key0, key1, st);
+            for (int mask = 1; mask < 64; mask <<= 1) {
+                const SampleState o = shfl_xor_state(st, mask);
+                merge_into(st, o, info.greedy);
+            }
+            if (lane == 0) red[wave] = st;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                SampleState a = red[0];
+                for (int i = 1; i < kRowThreads / 64; ++i) merge_into(a, red[i], info.greedy);
+                row_partials[row * S + (int)(w % S)] = to_partial(a);
+            }
+            if (gb == row_begin) {
+                // this workgroup starts the row: the row's workgroups are w .. w_last, and the
+                // slots none of them takes get empty partials
+                const long long w_last = ((row_begin + n_blk) * G - 1) / T;
+                const Partial none = to_partial(sample_state_init());
+                for (int sl = threadIdx.x; sl < S; sl += kRowThreads) {
+                    const long long first = w + (((long long)sl - w % S) + S) % S;
+                    if (first > w_last) row_partials[row * S + sl] = none;
+                }
+            }
+            __syncthreads();  // red is reused by the next segment
         }
-        if (lane == 0) red[wave] = st;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            SampleState a = red[0];
-            for (int w = 1; w < kRowThreads / 64; ++w) merge_into(a, red[w], ri.greedy);
-            row_partials[row * S + slab] = to_partial(a);
-        }
-        __syncthreads();  // red is reused by the next item
+        gb = seg_end;
     }
 }
 
@@ -254,21 +291,21 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
 // for the next chunk when it is still being verified there.
 template <typename YT>
 __global__ __launch_bounds__(256) void verify_decide_kernel(
-    int B, int K, int V, const void *Y, const int32_t *draft_tokens, const float *q_tok,
-    const int32_t *verify_len, const float *temperature, const uint32_t *req_id, uint32_t key0,
-    uint32_t key1, int S, int k_lo, int k_hi, const int32_t *n_alive, const int32_t *alive,
+    int K, int V, const void *Y, const int32_t *draft_tokens, const float *q_tok, uint32_t key0,
+    uint32_t key1, int S, int k_lo, int k_hi, const int32_t *n_alive, const int4 *alive,
     const Partial *row_partials, int32_t *first_reject, float4 *rowstats, float *p_tok,
-    int32_t *n_next, int32_t *next, uint32_t *status) {
+    int32_t *n_next, int4 *next, uint32_t *status) {
     const int lane = threadIdx.x & 63;
     const int ai = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    const int n_req = alive ? *n_alive : B;
+    const int n_req = *n_alive;
     if (ai >= n_req) return;  // uniform per wave
-    const int b = alive ? alive[ai] : ai;
-    const ReqInfo ri = req_info(b, K, verify_len, temperature, req_id);
+    const int4 rec = alive[ai];
+    const int b = rec.x;
+    const ReqInfo ri = req_info(rec);
     const int rej = decide_rows<YT>(b, k_lo, k_hi, ri, K, V, S, Y, draft_tokens, q_tok,
                                     row_partials, key0, key1, true, rowstats, p_tok, first_reject,
                                     status);
-    if (lane == 0 && rej < 0 && ri.L >= k_hi) next[atomicAdd(n_next, 1)] = b;
+    if (lane == 0 && rej < 0 && ri.L >= k_hi) next[atomicAdd(n_next, 1)] = rec;
 }
 
 // One wave per request.  [c_lo, c_hi) is the last chunk of rows, which no later launch has
@@ -436,7 +473,8 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
 hipError_t launch_verify_prepare(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s) {
     const int blocks = (a.B + 255) / 256 < 1024 ? (a.B + 255) / 256 : 1024;
     verify_prepare_kernel<<<blocks < 1 ? 1 : blocks, 256, 0, s>>>(
-        a.B, a.K, ws.status, ws.n_resid, ws.first_reject, ws.n_alive);
+        a.B, a.K, a.verify_len, a.temperature, a.req_id, ws.status, ws.n_resid,
+        ws.first_reject, ws.n_alive, ws.alive);
     return hipGetLastError();
 }
 
@@ -453,10 +491,8 @@ int verify_chunks(int K, int bounds[kMaxChunks + 1]) {
     return n;
 }
 
-// requests listed for chunk c (chunk 0: all of them, no list)
-static const int32_t *alive_list(const VerifyWs &ws, int c, int B) {
-    return c == 0 ? nullptr : ws.alive + (size_t)c * B;
-}
+// records of the requests listed for chunk c (chunk 0: all of them)
+static int4 *alive_list(const VerifyWs &ws, int c, int B) { return ws.alive + (size_t)c * B; }
 
 hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
                               hipStream_t s) {
@@ -465,18 +501,19 @@ hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, i
     if (chunk < 0 || chunk >= n) return hipErrorInvalidValue;
     const int k_lo = bounds[chunk], k_hi = bounds[chunk + 1];
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
-    const long long max_items = (long long)a.B * (k_hi - k_lo) * ws.n_row_slabs;
-    const int grid = (int)(max_items < kRowGrid ? max_items : kRowGrid);
-    const int32_t *list = alive_list(ws, chunk, a.B);
+    // enough workgroups for every request of the chunk; the kernel uses fewer when fewer are
+    // listed
+    const long long n_blk = (a.V + kSampleBlock - 1) / kSampleBlock;
+    long long grid = (long long)a.B * (k_hi - k_lo) * n_blk / kRowSweep;
+    grid = grid < 1 ? 1 : (grid > kRowGrid ? kRowGrid : grid);
+    const int4 *list = alive_list(ws, chunk, a.B);
     const int32_t *cnt = ws.n_alive + chunk;
     if (a.y_dtype == DSPARK_BF16)
-        verify_rows_kernel<uint16_t><<<grid, kRowThreads, 0, s>>>(
-            a.B, a.K, a.V, a.Y, a.verify_len, a.temperature, a.req_id, k0, k1, ws.n_row_slabs,
-            k_lo, k_hi, cnt, list, ws.row_partials);
+        verify_rows_kernel<uint16_t><<<(unsigned)grid, kRowThreads, 0, s>>>(
+            a.K, a.V, a.Y, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials);
     else
-        verify_rows_kernel<float><<<grid, kRowThreads, 0, s>>>(
-            a.B, a.K, a.V, a.Y, a.verify_len, a.temperature, a.req_id, k0, k1, ws.n_row_slabs,
-            k_lo, k_hi, cnt, list, ws.row_partials);
+        verify_rows_kernel<float><<<(unsigned)grid, kRowThreads, 0, s>>>(
+            a.K, a.V, a.Y, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials);
     return hipGetLastError();
 }
 
@@ -489,20 +526,20 @@ hipError_t launch_verify_decide(const dspark_verify_args &a, const VerifyWs &ws,
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
     const int per_block = 4;  // one wave per request
     const dim3 grid((a.B + per_block - 1) / per_block), block(64 * per_block);
-    const int32_t *list = alive_list(ws, chunk, a.B);
+    const int4 *list = alive_list(ws, chunk, a.B);
     const int32_t *cnt = ws.n_alive + chunk;
-    int32_t *next = ws.alive + (size_t)(chunk + 1) * a.B;
+    int4 *next = alive_list(ws, chunk + 1, a.B);
     int32_t *n_next = ws.n_alive + chunk + 1;
     if (a.y_dtype == DSPARK_BF16)
         verify_decide_kernel<uint16_t><<<grid, block, 0, s>>>(
-            a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
-            k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials, ws.first_reject,
-            ws.rowstats, a.p_tok, n_next, next, ws.status);
+            a.K, a.V, a.Y, a.draft_tokens, a.q_tok, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt,
+            list, ws.row_partials, ws.first_reject, ws.rowstats, a.p_tok, n_next, next,
+            ws.status);
     else
         verify_decide_kernel<float><<<grid, block, 0, s>>>(
-            a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
-            k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials, ws.first_reject,
-            ws.rowstats, a.p_tok, n_next, next, ws.status);
+            a.K, a.V, a.Y, a.draft_tokens, a.q_tok, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt,
+            list, ws.row_partials, ws.first_reject, ws.rowstats, a.p_tok, n_next, next,
+            ws.status);
     return hipGetLastError();
 }
 
