@@ -65,7 +65,11 @@ def lib() -> C.CDLL:
         L.oracle_profile.restype = C.c_double
         L.oracle_profile.argtypes = [i32, p, p, C.c_double]
         L.oracle_schedule.restype = i32
-        L.oracle_schedule.argtypes = [i32, i32, p, p, i32, p, p, i32, p, p, p]
+        L.oracle_schedule.argtypes = [i32, i32, p, p, i32, p, p, i32, p, p, p, p]
+        L.oracle_calibrate_step.restype = i32
+        L.oracle_calibrate_step.argtypes = [i32, i32, p, p, p, C.c_double, C.c_double, p]
+        L.oracle_ece.restype = C.c_double
+        L.oracle_ece.argtypes = [i32, p, p, i32]
         L.oracle_verify.restype = i32
         L.oracle_verify.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, i32, p, i32, p, p, p, p,
                                     p, p, u64, p, i32, p, p, p, p]
@@ -235,8 +239,9 @@ def profile(knot_tokens, knot_tps, N):
     return lib().oracle_profile(len(kt), _ptr(kt), _ptr(kp), float(N))
 
 
-def schedule(conf_logits, knot_tokens, knot_tps, enabled=True, draft_len=None):
-    """Per-request verification lengths (see oracle_schedule in dspark_oracle.c).
+def schedule(conf_logits, knot_tokens, knot_tps, enabled=True, draft_len=None, inv_temp=None):
+    """Per-request verification lengths (see oracle_schedule in dspark_oracle.c); inv_temp
+    [K] float64 are the per-position inverse temperatures of the confidence logits.
 
     Returns dict(verify_len [B] int32, expected_tokens [B] float64, n_star, margin)."""
     c = _np(conf_logits, np.float32)
@@ -244,14 +249,39 @@ def schedule(conf_logits, knot_tokens, knot_tps, enabled=True, draft_len=None):
     dlen = None if draft_len is None else _np(draft_len, np.int32)
     kt = _np(knot_tokens, np.float64)
     kp = _np(knot_tps, np.float64)
+    th = None if inv_temp is None else _np(inv_temp, np.float64)
     vl = np.empty(B, np.int32)
     et = np.empty(B, np.float64)
     diag = np.empty(2, np.float64)
     st = lib().oracle_schedule(B, K, _ptr(c), _ptr(dlen), len(kt), _ptr(kt), _ptr(kp),
-                               int(bool(enabled)), _ptr(vl), _ptr(et), _ptr(diag))
+                               int(bool(enabled)), _ptr(th), _ptr(vl), _ptr(et), _ptr(diag))
     if st != 0:
         raise ValueError("oracle_schedule: invalid argument")
     return dict(verify_len=vl, expected_tokens=et, n_star=int(diag[0]), margin=float(diag[1]))
+
+
+def calibrate_step(conf_logits, verify_len, accept_len, inv_temp, step=1.0, ridge=1e-3):
+    """One online calibration step (see oracle_calibrate_step in dspark_oracle.c).
+
+    Returns the updated inverse temperatures [K] float64 (the input is not modified)."""
+    c = _np(conf_logits, np.float32)
+    B, K = c.shape
+    vl = _np(verify_len, np.int32)
+    al = _np(accept_len, np.int32)
+    th = np.array(_np(inv_temp, np.float64), dtype=np.float64, copy=True)
+    st = lib().oracle_calibrate_step(B, K, _ptr(c), _ptr(vl), _ptr(al), float(step), float(ridge),
+                                     _ptr(th))
+    if st != 0:
+        raise ValueError("oracle_calibrate_step: invalid argument")
+    return th
+
+
+def ece(s, y, n_bins=10):
+    """Expected calibration error (see oracle_ece in dspark_oracle.c)."""
+    s = np.ascontiguousarray(np.asarray(s, dtype=np.float64).ravel())
+    y = np.ascontiguousarray(np.asarray(y, dtype=np.float64).ravel())
+    assert s.shape == y.shape
+    return float(lib().oracle_ece(len(s), _ptr(s), _ptr(y), int(n_bins)))
 
 
 def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature, seed,
