@@ -194,6 +194,26 @@ dspark_status dspark_schedule(const dspark_schedule_args *a, void *ws, size_t ws
     return e == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
 
+size_t dspark_calibrate_workspace_size(int32_t B, int32_t K) {
+    if (B < 0 || K < 1 || K > kMaxK) return 0;
+    return 256;
+}
+
+dspark_status dspark_calibrate(const dspark_calibrate_args *a, void *ws, size_t ws_bytes,
+                               void *stream) {
+    if (!a) return DSPARK_EINVAL;
+    if (a->B < 0 || a->K < 1 || a->K > kMaxK) return DSPARK_EINVAL;
+    if (!(a->step > 0.0 && a->step <= 1.0) || !(a->ridge > 0.0)) return DSPARK_EINVAL;
+    if (a->B == 0) return DSPARK_OK;
+    if (!a->conf_logits || !a->verify_len || !a->accept_len || !a->inv_temp) return DSPARK_EINVAL;
+    if (!check_ws(ws, ws_bytes, dspark_calibrate_workspace_size(a->B, a->K)))
+        return DSPARK_EWORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint32_t *status = reinterpret_cast<uint32_t *>(ws);
+    hipError_t e = traced(a->trace, "calibrate", s, [&] { return launch_calibrate(*a, status, s); });
+    return e == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+}
+
 dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_bytes, void *stream) {
     if (!a) return DSPARK_EINVAL;
     if (!head_sizes_ok(a->B, a->K, a->V, a->r) || a->B >= (1 << 24)) return DSPARK_EINVAL;

@@ -503,6 +503,7 @@ hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, in
                                hipStream_t s);
 
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, hipStream_t s);
+hipError_t launch_calibrate(const dspark_calibrate_args &a, uint32_t *status, hipStream_t s);
 
 hipError_t launch_verify_prepare(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s);
 // Target rows are verified in chunks (one launch each, and a decide launch after every chunk

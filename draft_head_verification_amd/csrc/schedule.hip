@@ -25,7 +25,10 @@ constexpr int kSchedThreads = 1024;
 constexpr int kSchedMaxItems = 8192;
 constexpr int kSchedMaxKnots = 64;
 
-__device__ __forceinline__ double survival(float c) { return 1.0 / (1.0 + exp(-(double)c)); }
+// calibrated survival of confidence logit c at inverse temperature theta (float64)
+__device__ __forceinline__ double survival(float c, double theta) {
+    return 1.0 / (1.0 + exp(-theta * (double)c));
+}
 
 __device__ __forceinline__ double profile_at(const double *kt, const double *kp, int n, double N) {
     if (N <= kt[0]) return kp[0];
@@ -50,8 +53,8 @@ __device__ __forceinline__ bool sched_before(unsigned long long ka, int ia, unsi
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
     int B, int K, const float *conf, const int32_t *draft_len, int n_knots,
-    const double *knot_tokens, const double *knot_tps, int enabled, int32_t *verify_len,
-    double *expected_tokens, uint32_t *status) {
+    const double *knot_tokens, const double *knot_tps, int enabled, const double *inv_temp,
+    int32_t *verify_len, double *expected_tokens, uint32_t *status) {
     __shared__ unsigned long long key[kSchedMaxItems];  // float64 bits of P (P >= 0)
     __shared__ int ids[kSchedMaxItems];                 // k * B + b; sentinel 0x7FFFFFFF
     __shared__ int len[kSchedMaxItems];                 // per-request length being built
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
             const int kb = len[b];
             double run_p = 1.0;
             for (int k = 0; k < K; ++k) {
-                run_p = run_p * survival(conf[(size_t)b * K + k]);
+                run_p = run_p * survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0);
                 const bool real = k < kb;
                 key[b * K + k] = real ? (unsigned long long)__double_as_longlong(run_p) : 0ull;
                 ids[b * K + k] = real ? k * B + b : 0x7FFFFFFF;
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
         if (expected_tokens) {
             double run_p = 1.0, e = 1.0;
             for (int k = 0; k < L; ++k) {
-                run_p = run_p * survival(conf[(size_t)b * K + k]);
+                run_p = run_p * survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0);
                 e += run_p;
             }
             expected_tokens[b] = e;
@@ -213,7 +216,64 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, hipStream_t s) {
     schedule_kernel<<<1, kSchedThreads, 0, s>>>(a.B, a.K, a.conf_logits, a.draft_len, a.n_knots,
                                                  a.knot_tokens, a.knot_tps, a.enabled,
-                                                 a.verify_len, a.expected_tokens, status);
+                                                 a.conf_inv_temp, a.verify_len,
+                                                 a.expected_tokens, status);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Online calibration of the confidence logits (see dspark_calibrate in include/dspark.h):
+// one workgroup per draft position; each thread sums the log-loss derivatives of its share of
+// the requests that tested the position (float64), a fixed-order LDS tree adds them up, and
+// thread 0 takes the damped Newton step.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kCalThreads = 256;
+
+__global__ __launch_bounds__(kCalThreads) void calibrate_kernel(
+    int B, int K, const float *conf, const int32_t *verify_len, const int32_t *accept_len,
+    double *inv_temp, double step, double ridge, uint32_t *status) {
+    __shared__ double s1[kCalThreads], s2[kCalThreads];
+    const int k = blockIdx.x, tid = threadIdx.x;
+    if (k == 0 && tid == 0) *status = 0u;  // only workgroup 0 reports, after this clear
+    __syncthreads();
+    const double theta = inv_temp[k];
+    double d1 = 0.0, d2 = 0.0;
+    for (int b = tid; b < B; b += kCalThreads) {
+        int L = verify_len[b], a = accept_len[b];
+        const bool bad = L < 0 || L > K || a < 0 || a > (L < 0 ? 0 : (L > K ? K : L));
+        if (bad && k == 0) atomicOr(status, DSPARK_DEV_BAD_LENGTH);
+        L = L < 0 ? 0 : (L > K ? K : L);
+        a = a < 0 ? 0 : (a > L ? L : a);
+        if (k < L && k <= a) {  // position k was tested for request b
+            const double y = k < a ? 1.0 : 0.0;
+            const double c = (double)conf[(size_t)b * K + k];
+            const double sg = 1.0 / (1.0 + exp(-theta * c));
+            d1 += (sg - y) * c;
+            d2 += sg * (1.0 - sg) * c * c;
+        }
+    }
+    s1[tid] = d1;
+    s2[tid] = d2;
+    __syncthreads();
+    for (int w = kCalThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) {
+            s1[tid] += s1[tid + w];
+            s2[tid] += s2[tid + w];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        double t = theta - step * s1[0] / (s2[0] + ridge);
+        t = t < 1.0 / 64.0 ? 1.0 / 64.0 : (t > 64.0 ? 64.0 : t);
+        inv_temp[k] = t;
+    }
+}
+
+hipError_t launch_calibrate(const dspark_calibrate_args &a, uint32_t *status, hipStream_t s) {
+    calibrate_kernel<<<a.K, kCalThreads, 0, s>>>(a.B, a.K, a.conf_logits, a.verify_len,
+                                                a.accept_len, a.inv_temp, a.step, a.ridge,
+                                                status);
     return hipGetLastError();
 }
 

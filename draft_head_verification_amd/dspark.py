@@ -50,7 +50,13 @@ class DraftArgs(C.Structure):
 class ScheduleArgs(C.Structure):
     _fields_ = [("B", _i32), ("K", _i32), ("conf_logits", _p), ("draft_len", _p),
                 ("n_knots", _i32), ("knot_tokens", _p), ("knot_tps", _p), ("enabled", _i32),
-                ("verify_len", _p), ("expected_tokens", _p), ("trace", _p)]
+                ("verify_len", _p), ("expected_tokens", _p), ("conf_inv_temp", _p), ("trace", _p)]
+
+
+class CalibrateArgs(C.Structure):
+    _fields_ = [("B", _i32), ("K", _i32), ("conf_logits", _p), ("verify_len", _p),
+                ("accept_len", _p), ("inv_temp", _p), ("step", C.c_double), ("ridge", C.c_double),
+                ("trace", _p)]
 
 
 class VerifyArgs(C.Structure):
@@ -68,6 +74,10 @@ _lib.dspark_verify_workspace_size.restype = C.c_size_t
 _lib.dspark_verify_workspace_size.argtypes = [_i32] * 4
 _lib.dspark_schedule_workspace_size.restype = C.c_size_t
 _lib.dspark_schedule_workspace_size.argtypes = [_i32] * 2
+_lib.dspark_calibrate_workspace_size.restype = C.c_size_t
+_lib.dspark_calibrate_workspace_size.argtypes = [_i32] * 2
+_lib.dspark_calibrate.restype = C.c_int
+_lib.dspark_calibrate.argtypes = [C.POINTER(CalibrateArgs), _p, C.c_size_t, _p]
 _lib.dspark_draft_block.restype = C.c_int
 _lib.dspark_draft_block.argtypes = [C.POINTER(DraftArgs), _p, C.c_size_t, _p]
 _lib.dspark_schedule.restype = C.c_int
@@ -218,11 +228,14 @@ def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_t
 
 
 def dspark_schedule(conf_logits, verify_len, knot_tokens=None, knot_tps=None, enabled=True,
-                    draft_len=None, expected_tokens=None, workspace=None, stream=None, trace=None):
+                    draft_len=None, expected_tokens=None, workspace=None, stream=None, trace=None,
+                    inv_temp=None):
     """Per-request verification lengths (see dspark_schedule in include/dspark.h)."""
     B, K = conf_logits.shape
     _dev(conf_logits, "conf_logits", _F32)
     _dev(verify_len, "verify_len", _INT, (B,))
+    if inv_temp is not None:
+        _dev(inv_temp, "inv_temp", (torch.float64,), (K,))
     n_knots = 0
     if enabled:
         _dev(knot_tokens, "knot_tokens", (torch.float64,))
@@ -235,10 +248,33 @@ def dspark_schedule(conf_logits, verify_len, knot_tokens=None, knot_tps=None, en
     ws = _ws(workspace, dspark_schedule_workspace_size(B, K), conf_logits.device)
     a = ScheduleArgs(B, K, _ptr(conf_logits), _ptr(draft_len), n_knots,
                      _ptr(knot_tokens) if enabled else None, _ptr(knot_tps) if enabled else None,
-                     int(bool(enabled)), _ptr(verify_len), _ptr(expected_tokens), _trace(trace))
+                     int(bool(enabled)), _ptr(verify_len), _ptr(expected_tokens), _ptr(inv_temp),
+                     _trace(trace))
     st = _lib.dspark_schedule(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_schedule")
+    return ws
+
+
+def dspark_calibrate_workspace_size(B, K) -> int:
+    return int(_lib.dspark_calibrate_workspace_size(B, K))
+
+
+def dspark_calibrate(conf_logits, verify_len, accept_len, inv_temp, step=1.0, ridge=1e-3,
+                     workspace=None, stream=None, trace=None):
+    """One online calibration step (see dspark_calibrate in include/dspark.h); inv_temp [K]
+    float64 is updated in place.  Returns the workspace (it carries the status word)."""
+    B, K = conf_logits.shape
+    _dev(conf_logits, "conf_logits", _F32)
+    _dev(verify_len, "verify_len", _INT, (B,))
+    _dev(accept_len, "accept_len", _INT, (B,))
+    _dev(inv_temp, "inv_temp", (torch.float64,), (K,))
+    ws = _ws(workspace, dspark_calibrate_workspace_size(B, K), conf_logits.device)
+    a = CalibrateArgs(B, K, _ptr(conf_logits), _ptr(verify_len), _ptr(accept_len), _ptr(inv_temp),
+                      float(step), float(ridge), _trace(trace))
+    st = _lib.dspark_calibrate(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
+    if st != DSPARK_OK:
+        raise DSparkError(st, "dspark_calibrate")
     return ws
 
 
@@ -306,15 +342,23 @@ def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=N
 
 
 def schedule(conf_logits, knot_tokens=None, knot_tps=None, enabled=True, draft_len=None,
-             workspace=None, trace=None):
+             workspace=None, trace=None, inv_temp=None):
     B, K = conf_logits.shape
     dev = conf_logits.device
     out = dict(verify_len=torch.empty(B, dtype=torch.int32, device=dev),
                expected_tokens=torch.empty(B, dtype=torch.float64, device=dev))
     out["workspace"] = dspark_schedule(conf_logits, out["verify_len"], knot_tokens, knot_tps,
                                        enabled, draft_len, out["expected_tokens"], workspace,
-                                       trace=trace)
+                                       trace=trace, inv_temp=inv_temp)
     return out
+
+
+def calibrate(conf_logits, verify_len, accept_len, inv_temp, step=1.0, ridge=1e-3,
+              workspace=None, trace=None):
+    """One online calibration step; inv_temp (device float64 [K]) is updated in place."""
+    ws = dspark_calibrate(conf_logits, verify_len, accept_len, inv_temp, step, ridge, workspace,
+                          trace=trace)
+    return dict(inv_temp=inv_temp, workspace=ws)
 
 
 def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature, seed,

@@ -132,8 +132,9 @@ typedef struct {
 /*
  * dspark_schedule -- per-request verification length.
  *
- * surv[b][k] = 1 / (1 + exp(-conf_logits[b][k])); P[b][k] = prod_{j <= k} surv[b][j]
- * (float64).  Every item (b, k) with k < K_b is ranked by (P desc, k asc, b asc).  For
+ * surv[b][k] = 1 / (1 + exp(-theta[k] * conf_logits[b][k])); P[b][k] = prod_{j <= k} surv[b][j]
+ * (float64), theta = conf_inv_temp (per-position inverse temperatures, e.g. kept by
+ * dspark_calibrate), or 1 when NULL.  Every item (b, k) with k < K_b is ranked by (P desc, k asc, b asc).  For
  * n = 0 .. sum_b K_b:  E(n) = B + (sum of the top-n P), N(n) = B + n,
  * G(n) = E(n) * T(N(n)) / N(n), where T is the throughput profile (tokens/s as a function of
  * the total tokens in the verify batch) interpolated linearly between knots and clamped
@@ -155,8 +156,43 @@ typedef struct {
     int32_t enabled;
     int32_t *verify_len;       /* out [B]           */
     double *expected_tokens;   /* optional out [B]  */
+    const double *conf_inv_temp; /* [K] or NULL (= 1) */
     dspark_trace *trace;
 } dspark_schedule_args;
+
+/*
+ * dspark_calibrate -- online calibration of the confidence logits, one step per verified
+ * round (QbitAI "DSpark in 10 concepts", section "Online drafter calibration": raw survival
+ * scores are over-confident, sequential temperature scaling brings the expected calibration
+ * error from 3-8% to about 1%, and the thresholds follow the acceptance the running drafter
+ * actually achieves; 10100.com commentary, section "letting the GPU decide how much to
+ * verify").  The pages give no formula; the reading implemented:
+ *
+ *   position k has an inverse temperature theta[k] > 0, calibrated survival
+ *   sigmoid(theta[k] * C[b][k]);  a round labels the positions it tested: position k of
+ *   request b is tested iff k < verify_len[b] and k <= accept_len[b], with label 1 (accepted)
+ *   for k < accept_len[b] and 0 for k = accept_len[b] -- each position is fitted on the
+ *   requests whose earlier positions all passed;  then, per position, one damped Newton step
+ *   on the round's log-loss  l(theta) = sum log(1 + exp(theta C)) - y theta C:
+ *     theta[k] <- clamp(theta[k] - step * l'(theta[k]) / (l''(theta[k]) + ridge), 1/64, 64)
+ *   with l' = sum (sigmoid(theta C) - y) C and l'' = sum sigmoid(theta C)(1 - sigmoid(theta C)) C^2
+ *   (float64; a position with no tested request keeps its theta).
+ *
+ * conf_logits, verify_len, accept_len: the round's schedule input and verify outputs (device).
+ * inv_temp [K] (device, float64): read and updated in place; start from 1.
+ * Lengths outside [0, K] and accepted lengths outside [0, verify_len] are clamped and flagged
+ * (DSPARK_DEV_BAD_LENGTH).  step in (0, 1], ridge > 0 (host-validated: DSPARK_EINVAL).
+ * Limits: K in [1, 64].  Workspace: dspark_calibrate_workspace_size (the status word).
+ */
+typedef struct {
+    int32_t B, K;
+    const float *conf_logits;  /* [B][K]                         */
+    const int32_t *verify_len; /* [B]                            */
+    const int32_t *accept_len; /* [B]                            */
+    double *inv_temp;          /* [K], updated in place          */
+    double step, ridge;
+    dspark_trace *trace;
+} dspark_calibrate_args;
 
 /*
  * dspark_verify -- lossless rejection-sampling verification.
@@ -205,6 +241,7 @@ typedef struct {
 size_t dspark_draft_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r);
 size_t dspark_schedule_workspace_size(int32_t B, int32_t K);
 size_t dspark_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r);
+size_t dspark_calibrate_workspace_size(int32_t B, int32_t K);
 
 /* The three calls.  `ws` is a device buffer of at least the queried size, 256-byte aligned;
  * `stream` is a hipStream_t.  Return DSPARK_OK once everything is enqueued. */
@@ -214,6 +251,8 @@ dspark_status dspark_schedule(const dspark_schedule_args *args, void *ws, size_t
                               void *stream);
 dspark_status dspark_verify(const dspark_verify_args *args, void *ws, size_t ws_bytes,
                             void *stream);
+dspark_status dspark_calibrate(const dspark_calibrate_args *args, void *ws, size_t ws_bytes,
+                               void *stream);
 
 /* Synchronises `stream`, then reads the device status word of workspace `ws` (written by the
  * last call that used it).  Returns DSPARK_OK, DSPARK_EDEVICE (and the bits in *bits when

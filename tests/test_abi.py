@@ -35,7 +35,8 @@ def test_binding_structs_match_header():
     """The ctypes structs in the binding list the same fields, in order, as the C structs."""
     src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     for cname, pyname in (("dspark_draft_args", "DraftArgs"), ("dspark_schedule_args", "ScheduleArgs"),
-                          ("dspark_verify_args", "VerifyArgs")):
+                          ("dspark_verify_args", "VerifyArgs"),
+                          ("dspark_calibrate_args", "CalibrateArgs")):
         body = re.search(r"typedef struct \{([^{}]*)\}\s*" + cname + ";", src).group(1)
         fields = []
         for decl in body.split(";"):
@@ -98,7 +99,7 @@ def test_host_validation_without_gpu():
     empty.B = 0
     assert lib.dspark_draft_block(C.byref(empty), None, 0, None) == D.DSPARK_OK
 
-    s = D.ScheduleArgs(4, 4, fake, None, 0, None, None, 1, fake, None, None)
+    s = D.ScheduleArgs(4, 4, fake, None, 0, None, None, 1, fake, None, None, None)
     assert lib.dspark_schedule(C.byref(s), fake, 256, None) == D.DSPARK_EINVAL  # no knots
     s.n_knots, s.knot_tokens, s.knot_tps = 2, fake, fake
     s.B = 600  # B*K > 8192 with scheduling on
@@ -114,3 +115,16 @@ def test_host_validation_without_gpu():
     assert lib.dspark_verify(C.byref(v), None, 0, None) == D.DSPARK_EDTYPE
     v.y_dtype, v.Y = 0, None
     assert lib.dspark_verify(C.byref(v), None, 0, None) == D.DSPARK_EINVAL
+
+    c = D.CalibrateArgs(4, 4, fake, fake, fake, fake, 1.0, 1e-3, None)
+    assert lib.dspark_calibrate(None, None, 0, None) == D.DSPARK_EINVAL
+    for field, value in (("K", 0), ("K", 65), ("step", 0.0), ("step", 1.5), ("ridge", 0.0),
+                         ("inv_temp", None)):
+        bad = D.CalibrateArgs(*[getattr(c, f) for f, _ in c._fields_])
+        setattr(bad, field, value)
+        assert lib.dspark_calibrate(C.byref(bad), fake, 256, None) == D.DSPARK_EINVAL, field
+    assert lib.dspark_calibrate(C.byref(c), fake, 8, None) == D.DSPARK_EWORKSPACE
+    empty = D.CalibrateArgs(*[getattr(c, f) for f, _ in c._fields_])
+    empty.B = 0
+    assert lib.dspark_calibrate(C.byref(empty), None, 0, None) == D.DSPARK_OK
+    assert D.dspark_calibrate_workspace_size(8, 16) == 256 and D.dspark_calibrate_workspace_size(8, 0) == 0
