@@ -318,6 +318,20 @@ __device__ __forceinline__ int w_swizzle(int row) {
     return ((((row >> 4) & 3) << 2) | (row & 3)) & (CPR - 1);
 }
 
+// The residual pass maps tile rows so that each half of a tile is one contiguous half of the
+// vocabulary range: lane group g holds entries 32h + 8g .. +7 in half h (blocks j = 2h, 2h+1).
+// The target-logit rows it streams are float32, 128 bytes per half: each half is then one
+// cache line, requested once, instead of both halves touching both lines one phase apart.
+// A 16-token block is split between lane groups 2b' and 2b'+1 (lanes l and l ^ 16).
+__device__ __forceinline__ int tile_row_resid(int j, int m) {
+    return 32 * (j >> 1) + 8 * (m >> 2) + 4 * (j & 1) + (m & 3);
+}
+
+template <int CPR>
+__device__ __forceinline__ int w_swizzle_resid(int row) {
+    return ((((row >> 3) & 3) << 2) | (row & 3)) & (CPR - 1);
+}
+
 // Epilogues of one lane for one request, one half at a time: half h holds entries
 // v0 + 8h .. v0 + 8h + 7 of the lane's 16-entry sampler block (n_live = how many of its
 // entries are < V).  All are branch-free, so that the compiler can interleave them with the
@@ -376,10 +390,13 @@ __device__ __forceinline__ void epi_sampled8(const float c[8], int v0, int n_liv
     }
 }
 
-template <int H, typename YT, bool MASK>
-__device__ __forceinline__ void epi_resid8(const float c[8], const Raw16<YT> &yr, int v0,
-                                           int n_live, const RowInfo &ri, uint32_t word,
-                                           ResidState &rs, BlockPart &bp) {
+// Residual epilogue with the residual tile-row map: the lane's 8 entries are half of the
+// 16-token block that starts at vb; the block's sums are completed with the partner lane
+// (lane ^ 16), and both lanes run the same race (a duplicate candidate merges away).
+template <typename YT, bool MASK, int H>
+__device__ __forceinline__ void epi_resid_pair(const float c[8], const Raw16<YT> &yr, int vb,
+                                               int n_live, const RowInfo &ri, uint32_t word,
+                                               ResidState &rs) {
     const float inv = kLog2e / ri.T;
     float R = 0.f, P = 0.f;
 #pragma unroll
@@ -390,13 +407,10 @@ __device__ __forceinline__ void epi_resid8(const float c[8], const Raw16<YT> &yr
         R += in ? fmaxf(rv, 0.f) : 0.f;
         P += pv;
     }
-    if constexpr (H == 0) {
-        bp.ref = P;
-        bp.sum = R;
-    } else {
-        race_update(rs.gr, rs.ir, 0.f, bp.sum + R, word, v0);
-        race_update(rs.gp, rs.ip, 0.f, bp.ref + P, word, v0);
-    }
+    R += __shfl_xor(R, 16);
+    P += __shfl_xor(P, 16);
+    race_update(rs.gr, rs.ir, 0.f, R, word, vb);
+    race_update(rs.gp, rs.ip, 0.f, P, word, vb);
 }
 
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
@@ -476,7 +490,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         const int P = (wave * LPW + i) * 64 + lane;
         const int row = P / CPR, pc = P % CPR;
         w_row[i] = row;
-        w_off[i] = row * R + (pc ^ w_swizzle<CPR>(row)) * 8;
+        const int key = kResid ? w_swizzle_resid<CPR>(row) : w_swizzle<CPR>(row);
+        w_off[i] = row * R + (pc ^ key) * 8;
     }
     auto issue_w = [&](int t, int s, auto clamp_tag) {
         constexpr bool CL = decltype(clamp_tag)::value;
@@ -551,8 +566,10 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     // per-lane A-fragment offsets (in chunks) of the four blocks, and the column key
     int a_off[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a_off[j] = tile_row(j, m) * CPR;
-    const int a_key = w_swizzle<CPR>(tile_row(0, m));
+    for (int j = 0; j < 4; ++j) a_off[j] = (kResid ? tile_row_resid(j, m) : tile_row(j, m)) * CPR;
+    // (the same for every j under either map)
+    const int a_key = kResid ? w_swizzle_resid<CPR>(tile_row_resid(0, m))
+                             : w_swizzle<CPR>(tile_row(0, m));
 
     // matrix-core work of half h (blocks j = 2h, 2h + 1) of the tile in stage s
     auto mfma_half = [&](int s, int h, floatx4 (&acc)[2][2]) {
@@ -581,37 +598,47 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     auto load_half = [&](int t, int h, auto clamp_tag) {
         constexpr bool CL = decltype(clamp_tag)::value;
         const int tc = max(t < t_end ? t : t_end - 1, 0);
+        // half h's 8 entries start at lane_v + 8h (the loaders add 8h)
+        const int lane_v = kResid ? tc * kTileV + 8 * g + 24 * h : tc * kTileV + 16 * g;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             if constexpr (CL) {
-                z[q].load_half(p.Z, ri[q].zrow, p.V, tc * kTileV + 16 * g, h);
-                if constexpr (kResid) y[q].load_half(p.Y, ri[q].yrow, p.V, tc * kTileV + 16 * g, h);
+                z[q].load_half(p.Z, ri[q].zrow, p.V, lane_v, h);
+                if constexpr (kResid) y[q].load_half(p.Y, ri[q].yrow, p.V, lane_v, h);
             } else {
-                z[q].load_half_nc(p.Z, ri[q].zrow, p.V, tc * kTileV + 16 * g, h);
-                if constexpr (kResid) y[q].load_half_nc(p.Y, ri[q].yrow, p.V, tc * kTileV + 16 * g, h);
+                z[q].load_half_nc(p.Z, ri[q].zrow, p.V, lane_v, h);
+                if constexpr (kResid) y[q].load_half_nc(p.Y, ri[q].yrow, p.V, lane_v, h);
             }
         }
     };
 
-    // race uniforms of blocks 4t + g for four tiles at a time (one Philox call per row)
-    uint32_t rw[2][4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    // Race uniforms for four tiles at a time (block beta = 16a + 4b + c takes word b of the
+    // Philox call at counter 4a + c): the lane's block of tile t is 4t + g (drafting map: one
+    // call per row), or 4t + 2h + (g >> 1) in half h (residual map: one call per row and half).
+    constexpr int NH_WORDS = kResid ? 2 : 1;
+    uint32_t rw[2][2][4] = {};
     const uint32_t stream = kResid ? kStreamResidual : kStreamDraft;
     auto race_words = [&](int t) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const Philox4 ph = philox4x32_10(race_counter((uint32_t)(4 * t + g)),
-                                             (uint32_t)ri[q].pos, ri[q].req, stream, p.key0,
-                                             p.key1);
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rw[q][i] = ph.w[i];
-        }
+            for (int hh = 0; hh < NH_WORDS; ++hh) {
+                const uint32_t c = kResid ? (uint32_t)(2 * hh + (g >> 1)) : (uint32_t)g;
+                const Philox4 ph = philox4x32_10(((uint32_t)(t >> 2) << 2) | c,
+                                                 (uint32_t)ri[q].pos, ri[q].req, stream, p.key0,
+                                                 p.key1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rw[q][hh][i] = ph.w[i];
+            }
     };
-    // word t & 3 of the row's four, selected with masks (no branches inside the pipeline)
-    auto word_of = [&](int q, int t) {
+    // word t & 3 of half h's four (drafting: h ignored), selected with masks (no branches
+    // inside the pipeline)
+    auto word_of = [&](int q, int t, int h) {
+        const int hh = kResid ? h : 0;
         const uint32_t i = (uint32_t)t & 3u;
         const uint32_t m0 = 0u - (uint32_t)(i == 0), m1 = 0u - (uint32_t)(i == 1);
         const uint32_t m2 = 0u - (uint32_t)(i == 2), m3 = 0u - (uint32_t)(i == 3);
-        return (rw[q][0] & m0) | (rw[q][1] & m1) | (rw[q][2] & m2) | (rw[q][3] & m3);
+        return (rw[q][hh][0] & m0) | (rw[q][hh][1] & m1) | (rw[q][hh][2] & m2) | (rw[q][hh][3] & m3);
     };
 
     floatx4 acc_lo[2][2], acc_hi[2][2];
@@ -623,8 +650,10 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         // epilogue of half H of tile t from acc, with the race words w[q] of that tile
         auto epilogue = [&](auto half_tag, int t, const floatx4 (&acc)[2][2], const uint32_t (&w)[2]) {
             constexpr int H = decltype(half_tag)::value;
-            const int v0 = t * kTileV + 16 * g;
-            const int live = MASK ? min(8, p.V - v0 - 8 * H) : 8;
+            const int v0 = t * kTileV + 16 * g;  // drafting map: the lane's block
+            // residual map: the lane's 8 entries and the start of their block
+            const int v8 = t * kTileV + 32 * H + 8 * g, vb = t * kTileV + 32 * H + 16 * (g >> 1);
+            const int live = MASK ? min(8, p.V - (kResid ? v8 : v0 + 8 * H)) : 8;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 float c[8];
@@ -650,7 +679,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                     epi_sampled8<H, MASK>(c, v0, live, samp ? kLog2e / ri[q].T : 1.f, w[q], st[q], bp[q]);
                     epi_greedy8<MASK>(c, v0 + 8 * H, live, gm[q], gi[q]);
                 } else {
-                    epi_resid8<H, YT, MASK>(c, y[q], v0, live, ri[q], w[q], rs[q], bp[q]);
+                    epi_resid_pair<YT, MASK, H>(c, y[q], vb, live, ri[q], w[q], rs[q]);
                 }
             }
         };
@@ -670,8 +699,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         {
             uint32_t w[2] = {0u, 0u};
             if constexpr (WORDS) {
-                w[0] = word_of(0, t0);
-                w[1] = word_of(1, t0);
+                w[0] = word_of(0, t0, 0);
+                w[1] = word_of(1, t0, 0);
             }
             epilogue(H0{}, t0, acc_lo, w);
         }
@@ -680,16 +709,16 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             const int stg = (t - t0) & 3;
             uint32_t wp[2] = {0u, 0u}, wc[2] = {0u, 0u};  // race words of tiles t - 1 and t
             if constexpr (WORDS) {
-                wp[0] = word_of(0, t - 1);
-                wp[1] = word_of(1, t - 1);
+                wp[0] = word_of(0, t - 1, 1);
+                wp[1] = word_of(1, t - 1, 1);
             }
             // phase A
             tile_barrier();
             issue_w(t + 3, (t + 3 - t0) & 3, mask_tag);
             if constexpr (WORDS) {
                 if ((t & 3) == 0) race_words(t);
-                wc[0] = word_of(0, t);
-                wc[1] = word_of(1, t);
+                wc[0] = word_of(0, t, 0);
+                wc[1] = word_of(1, t, 0);
             }
             DSPARK_WAIT_VMCNT(WAIT_A);
             mfma_half(stg, 0, acc_lo);
@@ -704,8 +733,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         // the high half of the last tile
         uint32_t w[2] = {0u, 0u};
         if constexpr (WORDS) {
-            w[0] = word_of(0, t_end - 1);
-            w[1] = word_of(1, t_end - 1);
+            w[0] = word_of(0, t_end - 1, 1);
+            w[1] = word_of(1, t_end - 1, 1);
         }
         (void)nw;
         DSPARK_WAIT_VMCNT(0);
