@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
 // One wave per residual row: merge the block races, then draw inside the winning block from
 // the recomputed weights r_v = max(p_v - q_v, 0) (or p_v when the residual is zero).
 __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
-    int B, int K, int V, int r, int y_dtype, int z_dtype, int uw_dtype, const void *Y,
+    int K, int V, int r, int y_dtype, int z_dtype, int uw_dtype, const void *Y,
     const void *Z, const void *U, const void *W, const int32_t *prev_token,
     const int32_t *draft_tokens, const float *q_lse, const float *temperature,
     const uint32_t *req_id, uint32_t key0, uint32_t key1, const float4 *rowstats,
@@ -394,10 +394,27 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (row >= *n_resid) return;  // uniform per wave
+    // the row's record and its slab partials (four per lane) go out together
+    const int packed = resid_rows[row];
+    constexpr int kPer = 4;
+    const Partial *prow = partials + (size_t)row * n_slabs;
+    Partial pp[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) pp[i] = prow[min(lane + 64 * i, n_slabs - 1)];
+    // the request's values: loads that need only the record, issued before the merge needs
+    // the partials (absent optional arrays are read at a stand-in address and replaced)
+    const int b = packed >> 7, j = packed & 127;
+    const size_t zrow = (size_t)b * K + j, yrow = (size_t)b * (K + 1) + j;
+    const uint32_t *rq = req_id ? req_id : reinterpret_cast<const uint32_t *>(prev_token);
+    const float T = temperature[b];  // > 0: greedy rows never need a residual
+    const uint32_t req_ld = rq[b];
+    const int pt = prev_token[b];
+    const int dt = draft_tokens[(size_t)b * K + (j > 0 ? j - 1 : 0)];
+    const float4 rs = rowstats[yrow];
+    const float ql = q_lse[zrow];
     float gr = -INFINITY, gp = -INFINITY;
     int ir = 0x7FFFFFFF, ip = 0x7FFFFFFF;
-    for (int s = lane; s < n_slabs; s += 64) {
-        const Partial q = partials[(size_t)row * n_slabs + s];
+    auto take = [&](const Partial &q) {
         const int qip = __float_as_int(q.l);
         if (q.g > gr || (q.g == gr && q.idx < ir)) {
             gr = q.g;
@@ -407,7 +424,11 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
             gp = q.m;
             ip = qip;
         }
-    }
+    };
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (lane + 64 * i < n_slabs) take(pp[i]);
+    for (int s = lane + 64 * kPer; s < n_slabs; s += 64) take(prow[s]);
     for (int mask = 1; mask < 64; mask <<= 1) {
         const float ogr = __shfl_xor(gr, mask), ogp = __shfl_xor(gp, mask);
         const int oir = __shfl_xor(ir, mask), oip = __shfl_xor(ip, mask);
@@ -420,21 +441,16 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
             ip = oip;
         }
     }
-    const int packed = resid_rows[row];
-    const int b = packed >> 7, j = packed & 127;
     const bool use_r = gr > -INFINITY;
     const int v0 = use_r ? ir : ip;
     int t = -1;
     if (v0 >= 0 && v0 < V && v0 % kSampleBlock == 0) {
-        const float T = temperature[b];  // > 0: greedy rows never need a residual
         const float inv = kLog2e / T;
-        const uint32_t req = req_id ? req_id[b] : (uint32_t)b;
-        int prev = (j == 0) ? prev_token[b] : draft_tokens[(size_t)b * K + j - 1];
+        const uint32_t req = req_id ? req_ld : (uint32_t)b;
+        int prev = (j == 0) ? pt : dt;
         if (prev < 0 || prev >= V) prev = 0;  // flagged by the rows / finish kernels
-        const size_t zrow = (size_t)b * K + j, yrow = (size_t)b * (K + 1) + j;
-        const float4 rs = rowstats[yrow];
         const float lse2p = rs.x + fast_log2(rs.y);
-        const float qlse2 = q_lse[zrow] * kLog2e;
+        const float qlse2 = ql * kLog2e;
         const float c = wave_corrected16(Z, z_dtype, zrow, U, W, uw_dtype, r, V, prev, v0);
         const int e = lane & 15;
         const int v = min(v0 + e, V - 1);
@@ -567,7 +583,7 @@ hipError_t launch_verify_residual_reduce(const dspark_verify_args &a, const Veri
                                          hipStream_t s) {
     const int per_block = 4;
     verify_residual_reduce_kernel<<<(a.B + per_block - 1) / per_block, 64 * per_block, 0, s>>>(
-        a.B, a.K, a.V, a.r, a.y_dtype, a.z_dtype, a.uw_dtype, a.Y, a.Z, a.U, a.W, a.prev_token,
+        a.K, a.V, a.r, a.y_dtype, a.z_dtype, a.uw_dtype, a.Y, a.Z, a.U, a.W, a.prev_token,
         a.draft_tokens, a.q_lse, a.temperature, a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu),
         (uint32_t)(a.seed >> 32), ws.rowstats, ws.n_resid, ws.resid_rows, ws.partials,
         ws.n_slabs, a.next_token, ws.status);
