@@ -48,8 +48,8 @@ bool head_sizes_ok(int32_t B, int32_t K, int32_t V, int32_t r) {
            r <= kMaxRank;
 }
 
-// draft workspace: status | prev_cur[B] | partials[B][n_slabs]
-size_t draft_layout(int32_t B, int32_t K, int32_t V, DraftWs *ws, char *base) {
+// draft workspace: status | prev_cur[B] | a_rows[B][r] (bf16) | partials[B][n_slabs]
+size_t draft_layout(int32_t B, int32_t K, int32_t V, int32_t r, DraftWs *ws, char *base) {
     (void)K;
     const int ns = num_vslabs(V, B);
     size_t off = 0;
@@ -57,6 +57,8 @@ size_t draft_layout(int32_t B, int32_t K, int32_t V, DraftWs *ws, char *base) {
     off += 256;
     if (ws) ws->prev_cur = reinterpret_cast<int32_t *>(base + off);
     off += align256((size_t)B * sizeof(int32_t));
+    if (ws) ws->a_rows = reinterpret_cast<uint16_t *>(base + off);
+    off += align256((size_t)B * r * sizeof(uint16_t));
     if (ws) ws->partials = reinterpret_cast<Partial *>(base + off);
     off += align256((size_t)B * ns * sizeof(Partial));
     if (ws) ws->n_slabs = ns;
@@ -116,7 +118,7 @@ const char *dspark_status_string(dspark_status s) {
 
 size_t dspark_draft_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r) {
     if (!head_sizes_ok(B, K, V, r)) return 0;
-    return draft_layout(B, K, V, nullptr, nullptr);
+    return draft_layout(B, K, V, r, nullptr, nullptr);
 }
 
 size_t dspark_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r) {
@@ -142,7 +144,8 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
         return DSPARK_EWORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     DraftWs w;
-    draft_layout(a->B, a->K, a->V, &w, reinterpret_cast<char *>(ws));
+    draft_layout(a->B, a->K, a->V, a->r, &w, reinterpret_cast<char *>(ws));
+    if (!draft_gathers_rows(*a)) w.a_rows = nullptr;
     hipError_t e = traced(a->trace, "draft_prepare", s,
                           [&] { return launch_draft_prepare(*a, w, s); });
     if (e != hipSuccess) return DSPARK_EHIP;
@@ -160,6 +163,7 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
     p.key0 = (uint32_t)(a->seed & 0xFFFFFFFFu);
     p.key1 = (uint32_t)(a->seed >> 32);
     p.prev_cur = w.prev_cur;
+    p.a_rows = w.a_rows;
     p.partials = w.partials;
     p.corrected = a->corrected;
     p.status = w.status;

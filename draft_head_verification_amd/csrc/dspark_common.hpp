@@ -443,6 +443,7 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct DraftWs {
     uint32_t *status;    // [1] device status bits
     int32_t *prev_cur;   // [B] previous token of the current step
+    uint16_t *a_rows;    // [B][r] bf16: U row of that token (matrix-core path), or null
     Partial *partials;   // [B][n_slabs]
     int n_slabs;
 };
@@ -491,12 +492,16 @@ struct DraftStepParams {
     const uint32_t *req_id;        // [B] or null
     uint32_t key0, key1;
     const int32_t *prev_cur;       // [B]
+    const uint16_t *a_rows;        // [B][r] gathered U rows (matrix-core path)
     Partial *partials;             // [B][n_slabs]
     float *corrected;              // [B][K][V] or null
     uint32_t *status;
     int n_slabs;
 };
 
+// Whether the drafting steps run on the matrix cores, which take each request's U row from a
+// gathered copy that the prepare and reduce kernels keep up to date.
+bool draft_gathers_rows(const dspark_draft_args &a);
 hipError_t launch_draft_prepare(const dspark_draft_args &a, const DraftWs &ws, hipStream_t s);
 hipError_t launch_draft_step(const DraftStepParams &p, int z_dtype, int uw_dtype, hipStream_t s);
 hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, int k,

@@ -27,6 +27,7 @@
 //   dispatched to the same XCD and meet the slab's W tiles in that XCD's L2.
 // Vector-ALU path (any other factor dtype / rank): one workgroup per (request, slab); four
 // neighbouring lanes hold one sampler block.
+#include <algorithm>
 #include <type_traits>
 
 #include "dspark_common.hpp"
@@ -50,6 +51,7 @@ struct HeadParams {
     const uint32_t *req_id;         // [B] or null
     uint32_t key0, key1;
     const int32_t *prev_cur;        // draft: [B]
+    const uint16_t *A;              // draft, matrix-core path: [B][r] U rows of prev_cur
     const int32_t *resid_rows;      // residual: packed rows
     const int32_t *prev_token;      // residual: [B]
     const int32_t *draft_tokens;    // residual: [B][K]
@@ -513,50 +515,48 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     using B0 = std::integral_constant<bool, false>;
     using B1 = std::integral_constant<bool, true>;
 
-    // Prologue.  The first matrix-core step needs W(t0) and the gathered U rows, and the U
-    // gather needs the previous tokens.  Loads retire in issue order, so the short dependent
-    // chain goes first: a drafting step's row metadata (no load of it waits on another), then
-    // W(t0) while it is in flight, then the U gather and the low logits of t0, and only then
-    // W(t0+1), W(t0+2), which the first step need not wait for.  (A residual row's metadata
-    // is itself a two-load chain; its W(t0) goes out before it.)
+    // Prologue.  The first matrix-core step needs W(t0) and the U rows of the previous tokens.
+    // A drafting step reads those rows from the copy the previous reduction gathered, and its
+    // logit rows follow from the row index alone, so nothing it loads waits on another load:
+    // row metadata, U rows, W(t0), the low logits of t0 and W(t0+1), W(t0+2) all go out
+    // together, and one explicit count waits for all but the last three.  A residual row's
+    // metadata is a two-load chain, then its U gather; its W(t0) goes out first.
     RowInfo ri[2];
     bf16x8 ufrag[2][KS];
-    bool any_valid = false, any_sampled = false, any_greedy = false;
     int rowid[2];
+    size_t zr[2] = {0, 0}, yr[2] = {0, 0};  // logit rows of the tile loads
     // (an empty slab issues the same loads, of a valid tile, and never reads them)
 #pragma unroll
     for (int q = 0; q < 2; ++q) rowid[q] = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + m;
+    auto load_u = [&](int q, const uint16_t *urow) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            ufrag[q][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(urow + 32 * kk));
+    };
     DraftRowRaw raw[2];
     if constexpr (!kResid) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) raw[q] = draft_row_load(p, rowid[q]);
-    }
-    issue_w(t0, 0, B1{});
-    // the metadata has landed once only W(t0) is pending; the explicit count keeps the compiler
-    // from waiting for W(t0) as well
-    if constexpr (!kResid) {
-        DSPARK_WAIT_VMCNT(LPW);
-        __builtin_amdgcn_sched_barrier(0);  // no use of the metadata is scheduled above it
-    }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        if constexpr (kResid) ri[q] = row_info<MODE>(p, rowid[q], n_rows);
-        else ri[q] = draft_row_resolve(p, rowid[q], n_rows, raw[q]);
-        any_valid |= ri[q].valid;
-        any_sampled |= ri[q].valid && ri[q].T > 0.f;
-        any_greedy |= ri[q].valid && !(ri[q].T > 0.f);
-    }
-    // gathered U rows (rows past the batch read token 0's row; their results are dropped)
+        for (int q = 0; q < 2; ++q) {
+            // rows past the batch (or past their draft) read a valid row; results are dropped
+            const int b = min(rowid[q], p.n_rows_max - 1);
+            zr[q] = (size_t)b * p.K + p.k;
+            load_u(q, p.A + (size_t)b * R + 8 * g);
+        }
+        issue_w(t0, 0, B1{});
+    } else {
+        issue_w(t0, 0, B1{});
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const uint16_t *urow = p.U + (size_t)ri[q].prev * R + 8 * g;
+        for (int q = 0; q < 2; ++q) {
+            ri[q] = row_info<MODE>(p, rowid[q], n_rows);
+            zr[q] = ri[q].zrow;
+            yr[q] = ri[q].yrow;
+        }
+        // (rows past the batch read token 0's row; their results are dropped)
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            ufrag[q][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(urow + 32 * kk));
+        for (int q = 0; q < 2; ++q) load_u(q, p.U + (size_t)ri[q].prev * R + 8 * g);
     }
-    const bool wave_active = __any(any_valid);
-    const bool wave_sampled = __any(any_sampled);
-    const bool wave_greedy = __any(any_greedy);
     SampleState st[2] = {sample_state_init(), sample_state_init()};
     ResidState rs[2] = {resid_init(), resid_init()};
     float gm[2] = {-INFINITY, -INFINITY};  // greedy rows of a mixed wave
@@ -603,11 +603,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             if constexpr (CL) {
-                z[q].load_half(p.Z, ri[q].zrow, p.V, lane_v, h);
-                if constexpr (kResid) y[q].load_half(p.Y, ri[q].yrow, p.V, lane_v, h);
+                z[q].load_half(p.Z, zr[q], p.V, lane_v, h);
+                if constexpr (kResid) y[q].load_half(p.Y, yr[q], p.V, lane_v, h);
             } else {
-                z[q].load_half_nc(p.Z, ri[q].zrow, p.V, lane_v, h);
-                if constexpr (kResid) y[q].load_half_nc(p.Y, ri[q].yrow, p.V, lane_v, h);
+                z[q].load_half_nc(p.Z, zr[q], p.V, lane_v, h);
+                if constexpr (kResid) y[q].load_half_nc(p.Y, yr[q], p.V, lane_v, h);
             }
         }
     };
@@ -745,12 +745,35 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     using I1 = std::integral_constant<int, kEpiSampled>;
     using I2 = std::integral_constant<int, kEpiMixed>;
     using I3 = std::integral_constant<int, kEpiResid>;
-    // the low logits of t0, then W(t0+1), W(t0+2); the U fragments and W(t0) have landed once
-    // only those are pending (phase B of t0 waits for the rest)
+    // the low logits of t0, then W(t0+1), W(t0+2); the metadata, the U fragments and W(t0)
+    // have landed once only those are pending (phase B of t0 waits for the rest)
     load_half(t0, 0, B1{});
     issue_w(t0 + 1, 1, B1{});
     issue_w(t0 + 2, 2, B1{});
     DSPARK_WAIT_VMCNT(NL + 2 * LPW);
+    if constexpr (!kResid) {
+        // Every use of the metadata is made to depend on a clock read that stays after the
+        // wait (both have side effects), so none is moved above it, where the compiler would
+        // wait for every outstanding load.  The clock never reads all ones.
+        const bool never = __builtin_amdgcn_s_memtime() == ~0ull;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            raw[q].kb = never ? 0 : raw[q].kb;
+            raw[q].T = never ? 0.f : raw[q].T;
+            raw[q].req = never ? 0u : raw[q].req;
+        }
+    }
+    bool any_valid = false, any_sampled = false, any_greedy = false;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if constexpr (!kResid) ri[q] = draft_row_resolve(p, rowid[q], n_rows, raw[q]);
+        any_valid |= ri[q].valid;
+        any_sampled |= ri[q].valid && ri[q].T > 0.f;
+        any_greedy |= ri[q].valid && !(ri[q].T > 0.f);
+    }
+    const bool wave_active = __any(any_valid);
+    const bool wave_sampled = __any(any_sampled);
+    const bool wave_greedy = __any(any_greedy);
     if (have_tiles) {  // uniform
         // only the slab holding a partial last tile needs the masked (and clamped) variant;
         // writing the corrected logits out is rare and always takes it
@@ -907,22 +930,40 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
 // Draft: prepare (status, validated first tokens) and per-step row reduction
 // ---------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void draft_prepare_kernel(int B, int V,
+// The first position's previous tokens (workgroup 0, which also clears the status word) and,
+// on the matrix-core path (a_rows set), their U rows gathered into a_rows, one 16-byte chunk
+// per thread over the whole grid.
+__global__ __launch_bounds__(256) void draft_prepare_kernel(int B, int V, int r,
                                                             const int32_t *prev_token,
-                                                            int32_t *prev_cur, uint32_t *status) {
-    if (threadIdx.x == 0) *status = 0u;
-    __syncthreads();
-    for (int b = threadIdx.x; b < B; b += blockDim.x)
-        prev_cur[b] = checked_token(prev_token[b], V, status);
+                                                            const uint16_t *U, int32_t *prev_cur,
+                                                            uint16_t *a_rows, uint32_t *status) {
+    if (blockIdx.x == 0) {
+        if (threadIdx.x == 0) *status = 0u;
+        __syncthreads();
+        for (int b = threadIdx.x; b < B; b += blockDim.x)
+            prev_cur[b] = checked_token(prev_token[b], V, status);
+    }
+    if (a_rows) {
+        const int cpr = r / 8;  // 16-byte chunks per row
+        const int i = blockIdx.x * blockDim.x + threadIdx.x;
+        if (i < B * cpr) {
+            const int b = i / cpr, c = i - b * cpr;
+            const int t = prev_token[b];
+            const int tc = (t < 0 || t >= V) ? 0 : t;  // as checked_token (flagged there)
+            *reinterpret_cast<uint4 *>(a_rows + (size_t)b * r + 8 * c) =
+                *reinterpret_cast<const uint4 *>(U + (size_t)tc * r + 8 * c);
+        }
+    }
 }
 
 // One wave per request: merge the slabs' partials of position k, then (sampled rows) draw the
-// token inside the winning 16-token block from its recomputed corrected logits.
+// token inside the winning 16-token block from its recomputed corrected logits.  On the
+// matrix-core path (a_rows set) it also copies the drawn token's U row for the next position.
 __global__ __launch_bounds__(256) void draft_reduce_kernel(
     int B, int K, int V, int r, int k, int z_dtype, int uw_dtype, const void *Z, const void *U,
     const void *W, const int32_t *draft_len, const float *temperature, const uint32_t *req_id,
     uint32_t key0, uint32_t key1, const Partial *partials, int n_slabs, int32_t *prev_cur,
-    int32_t *tokens, float *q_tok, float *q_lse, uint32_t *status) {
+    uint16_t *a_rows, int32_t *tokens, float *q_tok, float *q_lse, uint32_t *status) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (b >= B) return;  // uniform per wave
@@ -1008,6 +1049,14 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
         q_tok[o] = qt;
         q_lse[o] = ql;
     }
+    // the next position's U row (x is the same in every lane; a flagged row takes token 0's)
+    if (a_rows && k + 1 < kb) {
+        const int xs = x < 0 ? 0 : x;
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(U) + (size_t)xs * r;
+        for (int c = lane; c < r / 8; c += 64)
+            *reinterpret_cast<uint4 *>(a_rows + (size_t)b * r + 8 * c) =
+                *reinterpret_cast<const uint4 *>(src + 8 * c);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1064,8 +1113,14 @@ static void set_factors(HeadParams &hp, const void *U, const void *W, int uw_dty
     }
 }
 
+bool draft_gathers_rows(const dspark_draft_args &a) { return use_mfma(a.uw_dtype, a.r); }
+
 hipError_t launch_draft_prepare(const dspark_draft_args &a, const DraftWs &ws, hipStream_t s) {
-    draft_prepare_kernel<<<1, 256, 0, s>>>(a.B, a.V, a.prev_token, ws.prev_cur, ws.status);
+    const int chunks = ws.a_rows ? a.B * (a.r / 8) : 0;
+    const int grid = std::max(1, (chunks + 255) / 256);
+    draft_prepare_kernel<<<grid, 256, 0, s>>>(a.B, a.V, a.r, a.prev_token,
+                                            reinterpret_cast<const uint16_t *>(a.U), ws.prev_cur,
+                                            ws.a_rows, ws.status);
     return hipGetLastError();
 }
 
@@ -1086,6 +1141,7 @@ hipError_t launch_draft_step(const DraftStepParams &d, int z_dtype, int uw_dtype
     hp.key0 = d.key0;
     hp.key1 = d.key1;
     hp.prev_cur = d.prev_cur;
+    hp.A = d.a_rows;
     hp.partials = d.partials;
     hp.corrected = d.corrected;
     hp.status = d.status;
@@ -1095,11 +1151,11 @@ hipError_t launch_draft_step(const DraftStepParams &d, int z_dtype, int uw_dtype
 
 hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, int k,
                                hipStream_t s) {
-    const int per_block = 4;  // one wave per request
+    const int per_block = 1;  // one wave per request and workgroup: spread over the CUs
     draft_reduce_kernel<<<(a.B + per_block - 1) / per_block, 64 * per_block, 0, s>>>(
         a.B, a.K, a.V, a.r, k, a.z_dtype, a.uw_dtype, a.Z, a.U, a.W, a.draft_len, a.temperature,
         a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu), (uint32_t)(a.seed >> 32), ws.partials,
-        ws.n_slabs, ws.prev_cur, a.draft_tokens, a.q_tok, a.q_lse, ws.status);
+        ws.n_slabs, ws.prev_cur, ws.a_rows, a.draft_tokens, a.q_tok, a.q_lse, ws.status);
     return hipGetLastError();
 }
 

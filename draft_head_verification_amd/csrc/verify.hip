@@ -540,7 +540,7 @@ hipError_t launch_verify_decide(const dspark_verify_args &a, const VerifyWs &ws,
     if (chunk < 0 || chunk + 1 >= n) return hipErrorInvalidValue;  // not the last chunk
     const int k_lo = bounds[chunk], k_hi = bounds[chunk + 1];
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
-    const int per_block = 4;  // one wave per request
+    const int per_block = 1;  // one wave per request and workgroup: spread over the CUs
     const dim3 grid((a.B + per_block - 1) / per_block), block(64 * per_block);
     const int4 *list = alive_list(ws, chunk, a.B);
     const int32_t *cnt = ws.n_alive + chunk;
@@ -563,7 +563,7 @@ hipError_t launch_verify_finish(const dspark_verify_args &a, const VerifyWs &ws,
     int bounds[kMaxChunks + 1];
     const int n = verify_chunks(a.K, bounds);
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
-    const int per_block = 4;  // one wave per request
+    const int per_block = 1;  // one wave per request and workgroup: spread over the CUs
     const dim3 grid((a.B + per_block - 1) / per_block), block(64 * per_block);
     const int c_lo = bounds[n - 1], c_hi = bounds[n];
     if (a.y_dtype == DSPARK_BF16)
@@ -581,7 +581,7 @@ hipError_t launch_verify_finish(const dspark_verify_args &a, const VerifyWs &ws,
 
 hipError_t launch_verify_residual_reduce(const dspark_verify_args &a, const VerifyWs &ws,
                                          hipStream_t s) {
-    const int per_block = 4;
+    const int per_block = 1;  // one wave per request and workgroup
     verify_residual_reduce_kernel<<<(a.B + per_block - 1) / per_block, 64 * per_block, 0, s>>>(
         a.K, a.V, a.r, a.y_dtype, a.z_dtype, a.uw_dtype, a.Y, a.Z, a.U, a.W, a.prev_token,
         a.draft_tokens, a.q_lse, a.temperature, a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu),
