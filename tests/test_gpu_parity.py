@@ -3,7 +3,9 @@
 Sizes keep the recipe of each workload but shrink the vocabulary to a few thousand entries,
 which still spans many 64-row W tiles and leaves a ragged last tile (V = 2392 = 37*64 + 24).
 The rank stays 256 (bf16 factors -> matrix-core path) except in the float32 "tiny" workload
-(rank 16 -> vector path).  Tolerances and near-tie rules: tests/parity.py.
+(rank 16 -> vector path) and three cases that change it: ranks 64 and 128 (the other
+matrix-core instantiations) and 96 (bf16 factors on the vector path).  Tolerances and
+near-tie rules: tests/parity.py.
 """
 import numpy as np
 import pytest
@@ -26,12 +28,16 @@ CASES = [
     ("concurrent", {"V": 1208}, None, False),
     ("ragged", {"V": 2392}, None, False),
     ("headline", {"V": 2392}, None, False),
+    ("moderate", {"V": 2392, "r": 64}, None, True),
+    ("ragged", {"V": 1208, "r": 128}, None, True),
+    ("single", {"V": 1208, "r": 96}, None, True),
 ]
 
 
 def _ids(c):
     name, kw, T, strong = c
-    return f"{name}-V{kw.get('V', 'full')}-T{T}-{'strong' if strong else 'std'}" + (f"-K{kw['K']}" if "K" in kw else "")
+    return (f"{name}-V{kw.get('V', 'full')}-T{T}-{'strong' if strong else 'std'}"
+            + (f"-K{kw['K']}" if "K" in kw else "") + (f"-r{kw['r']}" if "r" in kw else ""))
 
 
 def run_round(w, T, strong, tally, tag, draft_len_override=None):
