@@ -163,3 +163,16 @@ def make_inputs(w: Workload, device="cpu", temperature=None, strong_bias=False) 
 def target_logits(corrected_ext: torch.Tensor, noise: torch.Tensor, dtype: torch.dtype):
     """Target logits of the workload: corrected draft logits [B,K+1,V] plus the drawn noise."""
     return (corrected_ext.float() + noise.to(corrected_ext.device)).to(dtype)
+
+
+def make_gru(r: int, seed: int, device="cpu") -> tuple:
+    """Seeded weights of a recurrent head's GRU cell: Wi, Wh [3r, r] and bi, bh [3r], float32,
+    uniform in (-1/sqrt(r), 1/sqrt(r)) (the usual initialisation of a GRU of width r)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    a = 1.0 / float(r) ** 0.5
+
+    def u(*shape):
+        return (2.0 * torch.rand(*shape, generator=gen, device=device) - 1.0) * a
+
+    return u(3 * r, r), u(3 * r, r), u(3 * r), u(3 * r)

@@ -73,6 +73,16 @@ def lib() -> C.CDLL:
         L.oracle_verify.restype = i32
         L.oracle_verify.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, i32, p, i32, p, p, p, p,
                                     p, p, u64, p, i32, p, p, p, p]
+        L.oracle_gru_cell.argtypes = [i32, p, p, p, p, p, p, p]
+        L.oracle_float_to_bf16.restype = C.c_uint16
+        L.oracle_float_to_bf16.argtypes = [C.c_float]
+        L.oracle_corrected_row_operand.argtypes = [i32, i32, i32, p, p, i32, p, p]
+        L.oracle_draft_block_head.restype = i32
+        L.oracle_draft_block_head.argtypes = [i32, i32, i32, i32, i32, p, i32, p, p, p, p, p, p,
+                                              p, p, p, p, u64, p, i32, p, p, p, p, p, p]
+        L.oracle_verify_head.restype = i32
+        L.oracle_verify_head.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, i32, p, i32, p,
+                                         p, p, p, p, p, p, u64, p, i32, p, p, p, p]
         L.oracle_num_threads.restype = i32
         _lib = L
     return _lib
@@ -194,15 +204,43 @@ def corrected_row(z_row, U, W, prev):
     return out
 
 
+def _gru_arrays(gru, r):
+    wi, wh, bi, bh = (_np(x, np.float32) for x in gru)
+    assert wi.shape == (3 * r, r) and wh.shape == (3 * r, r), "GRU weights are [3r, r]"
+    assert bi.shape == (3 * r,) and bh.shape == (3 * r,), "GRU biases are [3r]"
+    return wi, wh, bi, bh
+
+
+def gru_cell(e, h, gru):
+    """One GRU update (oracle_gru_cell): e, h [r] -> h' [r], float64."""
+    e = _np(e, np.float64)
+    h = _np(h, np.float64)
+    r = e.shape[0]
+    wi, wh, bi, bh = _gru_arrays(gru, r)
+    out = np.empty(r, np.float64)
+    lib().oracle_gru_cell(r, _ptr(wi), _ptr(wh), _ptr(bi), _ptr(bh), _ptr(e), _ptr(h), _ptr(out))
+    return out
+
+
+def float_to_bf16(x):
+    """bfloat16 bit patterns (uint16) of float32 values, nearest with ties to even."""
+    x = _np(x, np.float32).ravel()
+    f = lib().oracle_float_to_bf16
+    return np.array([f(float(v)) for v in x], dtype=np.uint16)
+
+
 def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=None, rows=None,
-                want_corrected=False):
-    """Draft tokens for a block (see oracle_draft_block in dspark_oracle.c).
+                want_corrected=False, gru=None):
+    """Draft tokens for a block (see oracle_draft_block_head in dspark_oracle.c).
 
     Z [B,K,V] (float32 or bfloat16), U [V,r], W [V,r] (row v = column v of the r x V factor),
     prev_token [B], temperature [B], draft_len [B] or None (= K), req_id [B] or None (= b).
+    gru: None (Markov head) or (Wi [3r,r], Wh [3r,r], bi [3r], bh [3r]) float32 for the
+    recurrent head.
     rows: optional list of requests to compute; the result arrays then have len(rows) rows.
-    Returns a dict with tokens [n,K] int32, q_tok / q_lse [n,K] float64, gap [n,K] float64
-    and, when asked, corrected [n,K,V] float32.
+    Returns a dict with tokens [n,K] int32, q_tok / q_lse [n,K] float64, gap [n,K] float64,
+    when asked corrected [n,K,V] float32, and with the recurrent head state [n,K,r] uint16
+    (the bfloat16 operand of each drafted position; zero elsewhere).
     """
     B = int(Z.shape[0])
     rows = np.arange(B) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -224,13 +262,17 @@ def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=N
     q_lse = np.empty((n, K), np.float64)
     gap = np.empty((n, K), np.float64)
     corrected = np.empty((n, K, V), np.float32) if want_corrected else None
-    st = lib().oracle_draft_block(n, K, V, r, zdt, _ptr(z), udt, _ptr(u), _ptr(w), _ptr(prev),
-                                  _ptr(dlen), _ptr(temp), _ptr(req), C.c_uint64(seed),
-                                  _ptr(sub_rows), n, _ptr(tokens), _ptr(q_tok), _ptr(q_lse),
-                                  _ptr(corrected), _ptr(gap))
+    g = (None,) * 4 if gru is None else _gru_arrays(gru, r)
+    state = None if gru is None else np.zeros((n, K, r), np.uint16)
+    st = lib().oracle_draft_block_head(n, K, V, r, zdt, _ptr(z), udt, _ptr(u), _ptr(w),
+                                       *(_ptr(x) for x in g), _ptr(prev), _ptr(dlen), _ptr(temp),
+                                       _ptr(req), C.c_uint64(seed), _ptr(sub_rows), n,
+                                       _ptr(tokens), _ptr(q_tok), _ptr(q_lse), _ptr(corrected),
+                                       _ptr(gap), _ptr(state))
     if st != 0:
         raise ValueError("oracle_draft_block: token index out of range")
-    return dict(tokens=tokens, q_tok=q_tok, q_lse=q_lse, gap=gap, corrected=corrected)
+    return dict(tokens=tokens, q_tok=q_tok, q_lse=q_lse, gap=gap, corrected=corrected,
+                state=state)
 
 
 def profile(knot_tokens, knot_tps, N):
@@ -285,11 +327,13 @@ def ece(s, y, n_bins=10):
 
 
 def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature, seed,
-           req_id=None, rows=None):
-    """Rejection-sampling verification (see oracle_verify in dspark_oracle.c).
+           req_id=None, rows=None, head_state=None):
+    """Rejection-sampling verification (see oracle_verify_head in dspark_oracle.c).
 
     Y [B,K+1,V] (float32 or bfloat16); draft_tokens [B,K]; q_tok, q_lse [B,K] (taken as
-    float32, the precision the draft hands over); Z, U, W, prev_token as for draft_block.
+    float32, the precision the draft hands over); Z, U, W, prev_token as for draft_block;
+    head_state [B,K,r] (uint16 bfloat16 bits, or a bfloat16 tensor) from a recurrent-head
+    draft, or None for the Markov head.
     Returns dict(accept_len [n], next_token [n], p_tok [n,K], accept_margin [n],
     sample_margin [n]) for the listed rows (all by default)."""
     B = int(Y.shape[0])
@@ -317,10 +361,14 @@ def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, tempe
     nxt = np.empty(n, np.int32)
     p_tok = np.zeros((n, K), np.float64)
     diag = np.empty((n, 2), np.float64)
-    st = lib().oracle_verify(n, K, V, r, ydt, _ptr(y), _ptr(toks), _ptr(qt), _ptr(ql), zdt,
-                             _ptr(z), udt, _ptr(u), _ptr(w), _ptr(prev), _ptr(vl), _ptr(temp),
-                             _ptr(req), C.c_uint64(seed), _ptr(sub_rows), n, _ptr(acc),
-                             _ptr(nxt), _ptr(p_tok), _ptr(diag))
+    hs = None
+    if head_state is not None:
+        hs, hdt = _as_logits(_subset(head_state, rows))
+        assert hdt == BF16 and hs.shape == (n, K, r), "head_state is [B,K,r] bfloat16"
+    st = lib().oracle_verify_head(n, K, V, r, ydt, _ptr(y), _ptr(toks), _ptr(qt), _ptr(ql), zdt,
+                                  _ptr(z), udt, _ptr(u), _ptr(w), _ptr(hs), _ptr(prev), _ptr(vl),
+                                  _ptr(temp), _ptr(req), C.c_uint64(seed), _ptr(sub_rows), n,
+                                  _ptr(acc), _ptr(nxt), _ptr(p_tok), _ptr(diag))
     if st != 0:
         raise ValueError("oracle_verify: token index out of range")
     return dict(accept_len=acc, next_token=nxt, p_tok=p_tok, accept_margin=diag[:, 0],

@@ -223,6 +223,76 @@ int oracle_two_level_sample(int n, const double *a, uint64_t seed, uint32_t req,
 /* Markov sequential head                                                                 */
 /* ------------------------------------------------------------------------------------ */
 
+/* ------------------------------------------------------------------------------------ */
+/* Recurrent sequential head (optional)                                                   */
+/* ------------------------------------------------------------------------------------ */
+/*
+ * Besides the default Markov head the pages mention an optional RNN head that follows the
+ * whole prefix of the draft block; its gain was small and it is off by default (QbitAI, "DSpark
+ * in 10 concepts", section "Cheaper serial module: the Markov head"; 10100.com commentary,
+ * section "Parallel drafts are fast but may turn 'of course' into 'of problem'"; wangjunjian.com
+ * tag page, DeepSpec overview: a light serial module at the output, the low-rank Markov head by
+ * default or an RNN head).  The pages give no form for it.  The reading implemented:
+ *   e_k    = U[prev_k]              the previous token's left factor (prev_0 = t0)
+ *   h_{-1} = 0,  h_k = GRU(h_{k-1}, e_k), kept in float32 (rounded once per step)
+ *   a_k    = h_k rounded to bfloat16 (nearest, ties to even): the contraction's left operand
+ *   c_v    = Z_v + sum_i a_k[i] * W[v][i]
+ * GRU: the gated recurrent unit of Cho et al. (EMNLP 2014) in the usual gate order (reset,
+ * update, new) with separate input and hidden biases,
+ *   g  = sigmoid(Wi_g e + bi_g + Wh_g h + bh_g)        reset gate
+ *   z  = sigmoid(Wi_z e + bi_z + Wh_z h + bh_z)        update gate
+ *   n  = tanh(Wi_n e + bi_n + g * (Wh_n h + bh_n))     candidate
+ *   h' = (1 - z) * n + z * h
+ * Wi, Wh: [3r][r] float32, rows 0..r-1 the reset units, r..2r-1 update, 2r..3r-1 new;
+ * bi, bh: [3r].  The cell is evaluated in double from the float32 state.
+ */
+void oracle_gru_cell(int r, const float *wi, const float *wh, const float *bi, const float *bh,
+                     const double *e, const double *h, double *h_out)
+{
+    for (int u = 0; u < r; ++u) {
+        double a_g = (double)bi[u] + (double)bh[u];
+        double a_z = (double)bi[r + u] + (double)bh[r + u];
+        double a_ni = (double)bi[2 * r + u];
+        double a_nh = (double)bh[2 * r + u];
+        for (int i = 0; i < r; ++i) {
+            a_g += (double)wi[(size_t)u * r + i] * e[i] + (double)wh[(size_t)u * r + i] * h[i];
+            a_z += (double)wi[(size_t)(r + u) * r + i] * e[i] +
+                   (double)wh[(size_t)(r + u) * r + i] * h[i];
+            a_ni += (double)wi[(size_t)(2 * r + u) * r + i] * e[i];
+            a_nh += (double)wh[(size_t)(2 * r + u) * r + i] * h[i];
+        }
+        double g = 1.0 / (1.0 + exp(-a_g));
+        double z = 1.0 / (1.0 + exp(-a_z));
+        double n = tanh(a_ni + g * a_nh);
+        h_out[u] = (1.0 - z) * n + z * h[u];
+    }
+}
+
+/* float -> bfloat16 bits, rounding to nearest with ties to even (NaN stays a NaN). */
+uint16_t oracle_float_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* Corrected logits from an explicit left operand (bfloat16 bits, length r):
+ * c_v = Z_v + sum_i a[i] * W[v][i], accumulated in double and rounded once to float. */
+void oracle_corrected_row_operand(int V, int r, int z_dtype, const void *z_row,
+                                  const uint16_t *a, int uw_dtype, const void *W, float *c_out)
+{
+    for (int v = 0; v < V; ++v) {
+        double bias = 0.0;
+        for (int i = 0; i < r; ++i)
+            bias += bf16_bits_to_double(a[i]) * load_elem(uw_dtype, W, (size_t)v * r + i);
+        c_out[v] = (float)(load_elem(z_dtype, z_row, (size_t)v) + bias);
+    }
+}
+
 /* Corrected logits of one draft row: c_v = Z_v + sum_i U[prev][i] * W[v][i].
  * The sum is accumulated in double; the result is rounded once to float, which is the
  * value the argmax and the softmax below start from. */
@@ -275,7 +345,8 @@ static double log_sum_exp(const double *s, int n)
  * Draft tokens for the requests listed in rows[0..n_rows).  For request b and position
  * k = 0..K_b-1 (K_b = draft_len[b], or K when draft_len is NULL):
  *   prev = t0_b for k = 0, else x_{b,k-1};
- *   c = corrected row (above);
+ *   c = corrected row (above): the Markov head from U[prev], or, when the GRU weights are
+ *       given (gru_wi non-NULL, all four then required), the recurrent head's operand a_k;
  *   T = 0: x = argmax c, q_tok = 1, q_lse = 0;
  *   T > 0: s = c / T, lse = log sum exp s, x = two-level Gumbel-max draw from s (draft
  *          streams), q_tok = exp(s_x - lse), q_lse = lse.
@@ -285,13 +356,18 @@ static double log_sum_exp(const double *s, int n)
  * gap (optional, [B][K]) receives the winning score's margin over the runner-up
  * (c for greedy; the smaller margin of the sampler's two decisions) so that near-ties can be
  * recognised by the tests.
+ * state_out (optional, recurrent head only, [B][K][r] bfloat16 bits) receives a_k for the
+ * drafted positions (other positions are left as they are).
  * Returns 0, or -1 when a token index is out of range.
  */
-int oracle_draft_block(int B, int K, int V, int r, int z_dtype, const void *Z, int uw_dtype,
-                       const void *U, const void *W, const int32_t *prev_token,
-                       const int32_t *draft_len, const float *temperature, const uint32_t *req_id,
-                       uint64_t seed, const int32_t *rows, int n_rows, int32_t *draft_tokens,
-                       double *q_tok, double *q_lse, float *corrected, double *gap)
+int oracle_draft_block_head(int B, int K, int V, int r, int z_dtype, const void *Z,
+                            int uw_dtype, const void *U, const void *W, const float *gru_wi,
+                            const float *gru_wh, const float *gru_bi, const float *gru_bh,
+                            const int32_t *prev_token, const int32_t *draft_len,
+                            const float *temperature, const uint32_t *req_id, uint64_t seed,
+                            const int32_t *rows, int n_rows, int32_t *draft_tokens,
+                            double *q_tok, double *q_lse, float *corrected, double *gap,
+                            uint16_t *state_out)
 {
     (void)B; /* arrays are [B][...]; only the listed rows are touched */
     int status = 0;
@@ -300,6 +376,11 @@ int oracle_draft_block(int B, int K, int V, int r, int z_dtype, const void *Z, i
         int b = rows[ri];
         float *c = (float *)malloc(sizeof(float) * (size_t)V);
         double *s = (double *)malloc(sizeof(double) * (size_t)V);
+        /* recurrent head: input, state (starts at zero), next state, operand */
+        double *e = (double *)malloc(sizeof(double) * (size_t)r);
+        double *h = (double *)calloc((size_t)r, sizeof(double));
+        double *hn = (double *)malloc(sizeof(double) * (size_t)r);
+        uint16_t *a = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)r);
         int Kb = draft_len ? draft_len[b] : K;
         uint32_t req = req_id ? req_id[b] : (uint32_t)b;
         double T = (double)temperature[b];
@@ -321,7 +402,20 @@ int oracle_draft_block(int B, int K, int V, int r, int z_dtype, const void *Z, i
             const void *z_row = (z_dtype == ORACLE_BF16)
                                     ? (const void *)((const uint16_t *)Z + bk * (size_t)V)
                                     : (const void *)((const float *)Z + bk * (size_t)V);
-            oracle_corrected_row(V, r, z_dtype, z_row, uw_dtype, U, W, prev, c);
+            if (gru_wi) {
+                for (int i = 0; i < r; ++i)
+                    e[i] = load_elem(uw_dtype, U, (size_t)prev * r + i);
+                oracle_gru_cell(r, gru_wi, gru_wh, gru_bi, gru_bh, e, h, hn);
+                for (int i = 0; i < r; ++i) {
+                    h[i] = (double)(float)hn[i];
+                    a[i] = oracle_float_to_bf16((float)h[i]);
+                }
+                if (state_out)
+                    memcpy(state_out + bk * (size_t)r, a, sizeof(uint16_t) * (size_t)r);
+                oracle_corrected_row_operand(V, r, z_dtype, z_row, a, uw_dtype, W, c);
+            } else {
+                oracle_corrected_row(V, r, z_dtype, z_row, uw_dtype, U, W, prev, c);
+            }
             if (corrected)
                 memcpy(corrected + bk * (size_t)V, c, sizeof(float) * (size_t)V);
             int x;
@@ -348,8 +442,24 @@ int oracle_draft_block(int B, int K, int V, int r, int z_dtype, const void *Z, i
         }
         free(c);
         free(s);
+        free(e);
+        free(h);
+        free(hn);
+        free(a);
     }
     return status;
+}
+
+/* The Markov head alone (no recurrent state). */
+int oracle_draft_block(int B, int K, int V, int r, int z_dtype, const void *Z, int uw_dtype,
+                       const void *U, const void *W, const int32_t *prev_token,
+                       const int32_t *draft_len, const float *temperature, const uint32_t *req_id,
+                       uint64_t seed, const int32_t *rows, int n_rows, int32_t *draft_tokens,
+                       double *q_tok, double *q_lse, float *corrected, double *gap)
+{
+    return oracle_draft_block_head(B, K, V, r, z_dtype, Z, uw_dtype, U, W, NULL, NULL, NULL,
+                                   NULL, prev_token, draft_len, temperature, req_id, seed, rows,
+                                   n_rows, draft_tokens, q_tok, q_lse, corrected, gap, NULL);
 }
 
 /* ------------------------------------------------------------------------------------ */
@@ -582,7 +692,9 @@ double oracle_ece(int n, const double *s, const double *y, int n_bins)
  *     On the first rejection at k = j: accept_len = j and the correction is
  *       T = 0: argmax Y[b][j];
  *       T > 0: q_j(v) = exp(c_{j,v} / T - q_lse[b][j]) with c_j the corrected row of position j
- *              (previous token t0 for j = 0, else x_{j-1}); r = max(0, p - q_j);
+ *              (previous token t0 for j = 0, else x_{j-1}; with head_state, [B][K][r]
+ *              bfloat16 bits from a recurrent-head draft, its operand head_state[b][j]);
+ *              r = max(0, p - q_j);
  *              two-level Gumbel-max draw from log r (residual streams, position j);
  *              if r is identically zero, the same draw from log p.
  *   If all L pass: accept_len = L and the bonus token is argmax Y[b][L] (T = 0) or the
@@ -593,12 +705,13 @@ double oracle_ece(int n, const double *s, const double *y, int n_bins)
  * or bonus over its runner-up}.
  * Returns 0, or -1 when a token index is out of range.
  */
-int oracle_verify(int B, int K, int V, int r, int y_dtype, const void *Y,
-                  const int32_t *draft_tokens, const float *q_tok, const float *q_lse,
-                  int z_dtype, const void *Z, int uw_dtype, const void *U, const void *W,
-                  const int32_t *prev_token, const int32_t *verify_len, const float *temperature,
-                  const uint32_t *req_id, uint64_t seed, const int32_t *rows, int n_rows,
-                  int32_t *accept_len, int32_t *next_token, double *p_tok, double *diag)
+int oracle_verify_head(int B, int K, int V, int r, int y_dtype, const void *Y,
+                       const int32_t *draft_tokens, const float *q_tok, const float *q_lse,
+                       int z_dtype, const void *Z, int uw_dtype, const void *U, const void *W,
+                       const uint16_t *head_state, const int32_t *prev_token,
+                       const int32_t *verify_len, const float *temperature,
+                       const uint32_t *req_id, uint64_t seed, const int32_t *rows, int n_rows,
+                       int32_t *accept_len, int32_t *next_token, double *p_tok, double *diag)
 {
     (void)B; /* arrays are [B][...]; only the listed rows are touched */
     int status = 0;
@@ -658,7 +771,12 @@ int oracle_verify(int B, int K, int V, int r, int y_dtype, const void *Y,
                         (z_dtype == ORACLE_BF16)
                             ? (const void *)((const uint16_t *)Z + zrow * (size_t)V)
                             : (const void *)((const float *)Z + zrow * (size_t)V);
-                    oracle_corrected_row(V, r, z_dtype, z_row, uw_dtype, U, W, prev, c);
+                    if (head_state)
+                        oracle_corrected_row_operand(V, r, z_dtype, z_row,
+                                                     head_state + zrow * (size_t)r, uw_dtype, W,
+                                                     c);
+                    else
+                        oracle_corrected_row(V, r, z_dtype, z_row, uw_dtype, U, W, prev, c);
                     double lq = (double)q_lse[(size_t)b * K + k];
                     int any = 0;
                     for (int v = 0; v < V; ++v) {
@@ -710,6 +828,19 @@ int oracle_verify(int B, int K, int V, int r, int y_dtype, const void *Y,
         free(c);
     }
     return status;
+}
+
+/* Verification of a Markov-head draft (the recompute takes U[prev]). */
+int oracle_verify(int B, int K, int V, int r, int y_dtype, const void *Y,
+                  const int32_t *draft_tokens, const float *q_tok, const float *q_lse,
+                  int z_dtype, const void *Z, int uw_dtype, const void *U, const void *W,
+                  const int32_t *prev_token, const int32_t *verify_len, const float *temperature,
+                  const uint32_t *req_id, uint64_t seed, const int32_t *rows, int n_rows,
+                  int32_t *accept_len, int32_t *next_token, double *p_tok, double *diag)
+{
+    return oracle_verify_head(B, K, V, r, y_dtype, Y, draft_tokens, q_tok, q_lse, z_dtype, Z,
+                              uw_dtype, U, W, NULL, prev_token, verify_len, temperature, req_id,
+                              seed, rows, n_rows, accept_len, next_token, p_tok, diag);
 }
 
 /* Number of threads the parallel loops above use (1 without OpenMP). */
