@@ -41,6 +41,9 @@ def parse():
                     help="override every request's temperature (0 = greedy)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
+    ap.add_argument("--head", choices=("markov", "rnn"), default="markov",
+                    help="sequential head: the default Markov head, or the optional recurrent "
+                         "(GRU) head with seeded weights")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, run a plain device copy of BYTES bytes five "
                          "times (scales the HBM byte counters of the profiler)")
@@ -88,6 +91,8 @@ def algorithmic_bytes(name, w, inp, acc_host, n_resid, zb, ub, yb):
         return int(sum((int(a) + 1) for a in acc_host)) * V * yb
     if name == "verify_residual":
         return n_resid * V * (zb + yb) + (V * r * ub if n_resid else 0) + n_resid * r * ub
+    if name == "rnn_step":  # GRU weights (float32) + per request: U row, state in/out, operands
+        return K * (2 * 3 * r * r * 4 + B * r * (ub + 4 + 4 + 2 + 2))
     return None
 
 
@@ -166,12 +171,16 @@ def main():
     ws_d = torch.empty(D.dspark_draft_workspace_size(B, K, V, r), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(max(256, D.dspark_schedule_workspace_size(B, K)), dtype=torch.uint8, device=dev)
     ws_v = torch.empty(D.dspark_verify_workspace_size(B, K, V, r), dtype=torch.uint8, device=dev)
+    gru = hs = None
+    if args.head == "rnn":
+        gru = tuple(t.contiguous() for t in synth.make_gru(r, seed=w.data_seed + 1000, device=dev))
+        hs = torch.zeros(B, K, r, dtype=torch.bfloat16, device=dev)
 
     # one untimed draft gives the chain the target logits are built around
     corrected = torch.empty(B, K, V, device=dev)
     D.dspark_draft_block(Z, inp["U"], inp["W"], inp["prev_token"], inp["temperature"], inp["seed"],
                          toks, q_tok, q_lse, draft_len=inp["draft_len"], req_id=inp["req_id"],
-                         corrected=corrected, workspace=ws_d)
+                         corrected=corrected, workspace=ws_d, gru=gru, head_state=hs)
     Y = build_targets_on_gpu(inp, toks, corrected, w)
     del corrected
     torch.cuda.empty_cache()
@@ -179,13 +188,14 @@ def main():
     def step(trace=None):
         D.dspark_draft_block(Z, inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
                              inp["seed"], toks, q_tok, q_lse, draft_len=inp["draft_len"],
-                             req_id=inp["req_id"], workspace=ws_d, trace=trace)
+                             req_id=inp["req_id"], workspace=ws_d, trace=trace, gru=gru,
+                             head_state=hs)
         D.dspark_schedule(inp["conf_logits"], vlen, inp["knot_tokens"], inp["knot_tps"],
                           w.schedule, draft_len=inp["draft_len"], expected_tokens=exp_tok,
                           workspace=ws_s, trace=trace)
         D.dspark_verify(Y, toks, q_tok, q_lse, Z, inp["U"], inp["W"], inp["prev_token"], vlen,
                         inp["temperature"], inp["seed"], acc, nxt, req_id=inp["req_id"],
-                        workspace=ws_v, trace=trace)
+                        workspace=ws_v, trace=trace, head_state=hs)
 
     for _ in range(args.warmup):
         step()
@@ -249,7 +259,7 @@ def main():
     step_bytes = sum((k["algorithmic_bytes_per_launch"] or 0) * k["launches_per_step"] for k in kernels)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.head == "markov":
         cpu = cpu_baseline(inp, w, None)
 
     out = {
@@ -260,7 +270,8 @@ def main():
         "config": {"workload": f"{w.name}: B={B} K={K} V={V} r={r} base/factors "
                                f"{'bf16' if zb == 2 else 'fp32'}, target {'bf16' if yb == 2 else 'fp32'}, "
                                f"T={args.temperature if args.temperature is not None else ','.join(str(t) for t in w.temperature)}, "
-                               f"schedule {'on' if w.schedule else 'off'}",
+                               f"schedule {'on' if w.schedule else 'off'}"
+                               + (", recurrent (GRU) head" if args.head == "rnn" else ""),
                    "B": B, "K": K, "V": V, "r": r, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -48,7 +48,8 @@ bool head_sizes_ok(int32_t B, int32_t K, int32_t V, int32_t r) {
            r <= kMaxRank;
 }
 
-// draft workspace: status | prev_cur[B] | a_rows[B][r] (bf16) | partials[B][n_slabs]
+// draft workspace: status | prev_cur[B] | a_rows[B][r] (bf16) | h_state[2][B][r] (f32) |
+// partials[B][n_slabs]
 size_t draft_layout(int32_t B, int32_t K, int32_t V, int32_t r, DraftWs *ws, char *base) {
     (void)K;
     const int ns = num_vslabs(V, B);
@@ -59,6 +60,8 @@ size_t draft_layout(int32_t B, int32_t K, int32_t V, int32_t r, DraftWs *ws, cha
     off += align256((size_t)B * sizeof(int32_t));
     if (ws) ws->a_rows = reinterpret_cast<uint16_t *>(base + off);
     off += align256((size_t)B * r * sizeof(uint16_t));
+    if (ws) ws->h_state = reinterpret_cast<float *>(base + off);
+    off += align256((size_t)2 * B * r * sizeof(float));
     if (ws) ws->partials = reinterpret_cast<Partial *>(base + off);
     off += align256((size_t)B * ns * sizeof(Partial));
     if (ws) ws->n_slabs = ns;
@@ -140,6 +143,12 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
     if (!a->Z || !a->U || !a->W || !a->prev_token || !a->temperature || !a->draft_tokens ||
         !a->q_tok || !a->q_lse)
         return DSPARK_EINVAL;
+    // recurrent head: all four GRU arrays, matrix-core factors; head_state is its output
+    const bool rnn = a->gru_wi || a->gru_wh || a->gru_bi || a->gru_bh;
+    if (rnn && (!a->gru_wi || !a->gru_wh || !a->gru_bi || !a->gru_bh ||
+                !matrix_core_factors(a->uw_dtype, a->r)))
+        return DSPARK_EINVAL;
+    if (a->head_state && !rnn) return DSPARK_EINVAL;
     if (!check_ws(ws, ws_bytes, dspark_draft_workspace_size(a->B, a->K, a->V, a->r)))
         return DSPARK_EWORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -149,6 +158,12 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
     hipError_t e = traced(a->trace, "draft_prepare", s,
                           [&] { return launch_draft_prepare(*a, w, s); });
     if (e != hipSuccess) return DSPARK_EHIP;
+    // recurrent head: the state of each position is computed from the previous token (which
+    // the preceding reduce step wrote) before the position's head step reads its operand
+    auto rnn_step = [&](int k) {
+        return traced(a->trace, "rnn_step", s, [&] { return launch_rnn_step(*a, w, k, s); });
+    };
+    if (rnn && rnn_step(0) != hipSuccess) return DSPARK_EHIP;
     DraftStepParams p{};
     p.B = a->B;
     p.K = a->K;
@@ -175,6 +190,7 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
         if (e != hipSuccess) return DSPARK_EHIP;
         e = traced(a->trace, "draft_reduce", s, [&] { return launch_draft_reduce(*a, w, k, s); });
         if (e != hipSuccess) return DSPARK_EHIP;
+        if (rnn && k + 1 < a->K && rnn_step(k + 1) != hipSuccess) return DSPARK_EHIP;
     }
     return DSPARK_OK;
 }
@@ -227,6 +243,8 @@ dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_byt
     if (!a->Y || !a->draft_tokens || !a->q_tok || !a->q_lse || !a->Z || !a->U || !a->W ||
         !a->prev_token || !a->verify_len || !a->temperature || !a->accept_len || !a->next_token)
         return DSPARK_EINVAL;
+    // a recurrent-head draft's operands are recomputed on the matrix-core path only
+    if (a->head_state && !matrix_core_factors(a->uw_dtype, a->r)) return DSPARK_EINVAL;
     if (!check_ws(ws, ws_bytes, dspark_verify_workspace_size(a->B, a->K, a->V, a->r)))
         return DSPARK_EWORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

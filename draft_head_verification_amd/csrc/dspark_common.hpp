@@ -29,6 +29,12 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// float -> bfloat16 bits, nearest with ties to even (a NaN stays a quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -443,7 +449,8 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct DraftWs {
     uint32_t *status;    // [1] device status bits
     int32_t *prev_cur;   // [B] previous token of the current step
-    uint16_t *a_rows;    // [B][r] bf16: U row of that token (matrix-core path), or null
+    uint16_t *a_rows;    // [B][r] bf16: left operand of the current position (matrix-core path)
+    float *h_state;      // [2][B][r] recurrent head: state of the last two positions
     Partial *partials;   // [B][n_slabs]
     int n_slabs;
 };
@@ -502,10 +509,16 @@ struct DraftStepParams {
 // Whether the drafting steps run on the matrix cores, which take each request's U row from a
 // gathered copy that the prepare and reduce kernels keep up to date.
 bool draft_gathers_rows(const dspark_draft_args &a);
+// Recurrent head: the GRU update of position k for every live request (k = 0 starts from a
+// zero state), writing the float32 state, the bfloat16 operand and, when asked, head_state.
+hipError_t launch_rnn_step(const dspark_draft_args &a, const DraftWs &ws, int k, hipStream_t s);
 hipError_t launch_draft_prepare(const dspark_draft_args &a, const DraftWs &ws, hipStream_t s);
 hipError_t launch_draft_step(const DraftStepParams &p, int z_dtype, int uw_dtype, hipStream_t s);
 hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, int k,
                                hipStream_t s);
+bool draft_uses_rnn(const dspark_draft_args &a);
+// bfloat16 factors of a rank the matrix-core kernels take (64, 128 or 256)
+bool matrix_core_factors(int uw_dtype, int r);
 
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, hipStream_t s);
 hipError_t launch_calibrate(const dspark_calibrate_args &a, uint32_t *status, hipStream_t s);

@@ -51,7 +51,8 @@ struct HeadParams {
     const uint32_t *req_id;         // [B] or null
     uint32_t key0, key1;
     const int32_t *prev_cur;        // draft: [B]
-    const uint16_t *A;              // draft, matrix-core path: [B][r] U rows of prev_cur
+    const uint16_t *A;              // draft, matrix-core path: [B][r] left operands
+    const uint16_t *S;              // residual: [B][K][r] recurrent-head operands, or null
     const int32_t *resid_rows;      // residual: packed rows
     const int32_t *prev_token;      // residual: [B]
     const int32_t *draft_tokens;    // residual: [B][K]
@@ -553,9 +554,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             zr[q] = ri[q].zrow;
             yr[q] = ri[q].yrow;
         }
-        // (rows past the batch read token 0's row; their results are dropped)
+        // U[prev] (Markov head) or the stored operand of a recurrent-head draft (rows past the
+        // batch read request 0's first row; their results are dropped)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) load_u(q, p.U + (size_t)ri[q].prev * R + 8 * g);
+        for (int q = 0; q < 2; ++q)
+            load_u(q, p.S ? p.S + ((size_t)ri[q].b * p.K + ri[q].pos) * R + 8 * g
+                          : p.U + (size_t)ri[q].prev * R + 8 * g);
     }
     SampleState st[2] = {sample_state_init(), sample_state_init()};
     ResidState rs[2] = {resid_init(), resid_init()};
@@ -963,7 +967,8 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
     int B, int K, int V, int r, int k, int z_dtype, int uw_dtype, const void *Z, const void *U,
     const void *W, const int32_t *draft_len, const float *temperature, const uint32_t *req_id,
     uint32_t key0, uint32_t key1, const Partial *partials, int n_slabs, int32_t *prev_cur,
-    uint16_t *a_rows, int32_t *tokens, float *q_tok, float *q_lse, uint32_t *status) {
+    uint16_t *a_rows, const uint16_t *op_rows, int32_t *tokens, float *q_tok, float *q_lse,
+    uint32_t *status) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (b >= B) return;  // uniform per wave
@@ -1023,7 +1028,10 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
         } else {
             const int e = lane & 15;
             const bool in = v0 + e < V;
-            const float c = wave_corrected16(Z, z_dtype, o, U, W, uw_dtype, r, V, prev, v0);
+            // left operand: U[prev] (Markov head) or the recurrent head's current operand
+            const void *op = op_rows ? static_cast<const void *>(op_rows + (size_t)b * r) : U;
+            const float c = wave_corrected16(Z, z_dtype, o, op, W, uw_dtype, r, V,
+                                             op_rows ? 0 : prev, v0);
             const float s2 = c * (kLog2e / T);
             const uint32_t req = req_id ? req_ld : (uint32_t)b;
             const uint32_t w = token_word((uint32_t)(v0 + e), (uint32_t)k, req, kStreamDraftWithin,
@@ -1114,13 +1122,17 @@ static void set_factors(HeadParams &hp, const void *U, const void *W, int uw_dty
 }
 
 bool draft_gathers_rows(const dspark_draft_args &a) { return use_mfma(a.uw_dtype, a.r); }
+bool draft_uses_rnn(const dspark_draft_args &a) { return a.gru_wi != nullptr; }
+bool matrix_core_factors(int uw_dtype, int r) { return use_mfma(uw_dtype, r); }
 
 hipError_t launch_draft_prepare(const dspark_draft_args &a, const DraftWs &ws, hipStream_t s) {
-    const int chunks = ws.a_rows ? a.B * (a.r / 8) : 0;
+    // (the recurrent head's first operand comes from its own kernel instead)
+    uint16_t *gather = draft_uses_rnn(a) ? nullptr : ws.a_rows;
+    const int chunks = gather ? a.B * (a.r / 8) : 0;
     const int grid = std::max(1, (chunks + 255) / 256);
     draft_prepare_kernel<<<grid, 256, 0, s>>>(a.B, a.V, a.r, a.prev_token,
                                             reinterpret_cast<const uint16_t *>(a.U), ws.prev_cur,
-                                            ws.a_rows, ws.status);
+                                            gather, ws.status);
     return hipGetLastError();
 }
 
@@ -1155,7 +1167,8 @@ hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, in
     draft_reduce_kernel<<<(a.B + per_block - 1) / per_block, 64 * per_block, 0, s>>>(
         a.B, a.K, a.V, a.r, k, a.z_dtype, a.uw_dtype, a.Z, a.U, a.W, a.draft_len, a.temperature,
         a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu), (uint32_t)(a.seed >> 32), ws.partials,
-        ws.n_slabs, ws.prev_cur, ws.a_rows, a.draft_tokens, a.q_tok, a.q_lse, ws.status);
+        ws.n_slabs, ws.prev_cur, draft_uses_rnn(a) ? nullptr : ws.a_rows,
+        draft_uses_rnn(a) ? ws.a_rows : nullptr, a.draft_tokens, a.q_tok, a.q_lse, ws.status);
     return hipGetLastError();
 }
 
@@ -1182,6 +1195,7 @@ hipError_t launch_verify_residual(const dspark_verify_args &a, const VerifyWs &w
     hp.Y = a.Y;
     hp.rowstats = ws.rowstats;
     hp.q_lse = a.q_lse;
+    hp.S = a.head_state;
     hp.partials = ws.partials;
     hp.corrected = nullptr;
     hp.status = ws.status;

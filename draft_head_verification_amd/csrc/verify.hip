@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
     const int32_t *draft_tokens, const float *q_lse, const float *temperature,
     const uint32_t *req_id, uint32_t key0, uint32_t key1, const float4 *rowstats,
     const int32_t *n_resid, const int32_t *resid_rows, const Partial *partials, int n_slabs,
-    int32_t *next_token, uint32_t *status) {
+    const uint16_t *head_state, int32_t *next_token, uint32_t *status) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (row >= *n_resid) return;  // uniform per wave
@@ -451,7 +451,10 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
         if (prev < 0 || prev >= V) prev = 0;  // flagged by the rows / finish kernels
         const float lse2p = rs.x + fast_log2(rs.y);
         const float qlse2 = ql * kLog2e;
-        const float c = wave_corrected16(Z, z_dtype, zrow, U, W, uw_dtype, r, V, prev, v0);
+        // the left operand: U[prev] (Markov head) or the stored recurrent-head operand
+        const void *op = head_state ? static_cast<const void *>(head_state + zrow * (size_t)r) : U;
+        const float c = wave_corrected16(Z, z_dtype, zrow, op, W, uw_dtype, r, V,
+                                         head_state ? 0 : prev, v0);
         const int e = lane & 15;
         const int v = min(v0 + e, V - 1);
         const bool in = v0 + e < V;
@@ -586,7 +589,7 @@ hipError_t launch_verify_residual_reduce(const dspark_verify_args &a, const Veri
         a.K, a.V, a.r, a.y_dtype, a.z_dtype, a.uw_dtype, a.Y, a.Z, a.U, a.W, a.prev_token,
         a.draft_tokens, a.q_lse, a.temperature, a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu),
         (uint32_t)(a.seed >> 32), ws.rowstats, ws.n_resid, ws.resid_rows, ws.partials,
-        ws.n_slabs, a.next_token, ws.status);
+        ws.n_slabs, a.head_state, a.next_token, ws.status);
     return hipGetLastError();
 }
 

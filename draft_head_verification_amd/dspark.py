@@ -44,7 +44,8 @@ class DraftArgs(C.Structure):
                 ("prev_token", _p), ("draft_len", _p), ("temperature", _p), ("req_id", _p),
                 ("seed", C.c_uint64),
                 ("draft_tokens", _p), ("q_tok", _p), ("q_lse", _p), ("corrected", _p),
-                ("trace", _p)]
+                ("trace", _p), ("gru_wi", _p), ("gru_wh", _p), ("gru_bi", _p), ("gru_bh", _p),
+                ("head_state", _p)]
 
 
 class ScheduleArgs(C.Structure):
@@ -65,7 +66,8 @@ class VerifyArgs(C.Structure):
                 ("Y", _p), ("draft_tokens", _p), ("q_tok", _p), ("q_lse", _p),
                 ("Z", _p), ("U", _p), ("W", _p), ("prev_token", _p), ("verify_len", _p),
                 ("temperature", _p), ("req_id", _p), ("seed", C.c_uint64),
-                ("accept_len", _p), ("next_token", _p), ("p_tok", _p), ("trace", _p)]
+                ("accept_len", _p), ("next_token", _p), ("p_tok", _p), ("trace", _p),
+                ("head_state", _p)]
 
 
 _lib.dspark_draft_workspace_size.restype = C.c_size_t
@@ -196,9 +198,11 @@ def dspark_schedule_workspace_size(B, K) -> int:
 
 def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok, q_lse,
                        draft_len=None, req_id=None, corrected=None, workspace=None, stream=None,
-                       trace=None):
+                       trace=None, gru=None, head_state=None):
     """Draft one block (see dspark_draft_block in include/dspark.h).  Returns the workspace
-    (reusable; it also carries the device status word)."""
+    (reusable; it also carries the device status word).  gru: None (Markov head) or the
+    recurrent head's (Wi [3r,r], Wh [3r,r], bi [3r], bh [3r]) float32 device tensors;
+    head_state: optional [B,K,r] bfloat16 output of the recurrent head's operands."""
     B, K, V = Z.shape
     r = U.shape[1]
     _dev(Z, "Z", _LOGIT)
@@ -215,12 +219,20 @@ def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_t
         _dev(req_id, "req_id", _INT, (B,))
     if corrected is not None:
         _dev(corrected, "corrected", _F32, (B, K, V))
+    g = (None,) * 4
+    if gru is not None:
+        g = tuple(gru)
+        for t, n, shape in zip(g, ("gru_wi", "gru_wh", "gru_bi", "gru_bh"),
+                               ((3 * r, r), (3 * r, r), (3 * r,), (3 * r,))):
+            _dev(t, n, _F32, shape)
+    if head_state is not None:
+        _dev(head_state, "head_state", (torch.bfloat16,), (B, K, r))
     need = dspark_draft_workspace_size(B, K, V, r)
     ws = _ws(workspace, need, Z.device)
     a = DraftArgs(B, K, V, r, _DT[Z.dtype], _DT[U.dtype], _ptr(Z), _ptr(U), _ptr(W),
                   _ptr(prev_token), _ptr(draft_len), _ptr(temperature), _ptr(req_id),
                   int(seed) & (2**64 - 1), _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse),
-                  _ptr(corrected), _trace(trace))
+                  _ptr(corrected), _trace(trace), *(_ptr(t) for t in g), _ptr(head_state))
     st = _lib.dspark_draft_block(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_draft_block")
@@ -280,8 +292,9 @@ def dspark_calibrate(conf_logits, verify_len, accept_len, inv_temp, step=1.0, ri
 
 def dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature,
                   seed, accept_len, next_token, req_id=None, p_tok=None, workspace=None,
-                  stream=None, trace=None):
-    """Rejection-sampling verification (see dspark_verify in include/dspark.h)."""
+                  stream=None, trace=None, head_state=None):
+    """Rejection-sampling verification (see dspark_verify in include/dspark.h).  head_state:
+    the [B,K,r] bfloat16 operands of a recurrent-head draft, or None (Markov head)."""
     B, K, V = Z.shape
     r = U.shape[1]
     _dev(Y, "Y", _LOGIT, (B, K + 1, V))
@@ -300,12 +313,14 @@ def dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len
         _dev(req_id, "req_id", _INT, (B,))
     if p_tok is not None:
         _dev(p_tok, "p_tok", _F32, (B, K))
+    if head_state is not None:
+        _dev(head_state, "head_state", (torch.bfloat16,), (B, K, r))
     ws = _ws(workspace, dspark_verify_workspace_size(B, K, V, r), Z.device)
     a = VerifyArgs(B, K, V, r, _DT[Y.dtype], _DT[Z.dtype], _DT[U.dtype], _ptr(Y),
                    _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse), _ptr(Z), _ptr(U), _ptr(W),
                    _ptr(prev_token), _ptr(verify_len), _ptr(temperature), _ptr(req_id),
                    int(seed) & (2**64 - 1), _ptr(accept_len), _ptr(next_token), _ptr(p_tok),
-                   _trace(trace))
+                   _trace(trace), _ptr(head_state))
     st = _lib.dspark_verify(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_verify")
@@ -326,18 +341,24 @@ def dspark_query_device_status(workspace: torch.Tensor, stream=None) -> int:
 # ----------------------------------------------------------------------------------------
 
 def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=None,
-                want_corrected=False, workspace=None, trace=None):
+                want_corrected=False, workspace=None, trace=None, gru=None):
+    """gru: None (Markov head) or (Wi, Wh, bi, bh) for the recurrent head, whose operands are
+    returned as head_state [B,K,r] bfloat16 (positions past a draft are zero)."""
     B, K, V = Z.shape
+    r = U.shape[1]
     dev = Z.device
     out = dict(tokens=torch.empty(B, K, dtype=torch.int32, device=dev),
                q_tok=torch.empty(B, K, dtype=torch.float32, device=dev),
                q_lse=torch.empty(B, K, dtype=torch.float32, device=dev),
                corrected=(torch.empty(B, K, V, dtype=torch.float32, device=dev)
-                          if want_corrected else None))
+                          if want_corrected else None),
+               head_state=(torch.zeros(B, K, r, dtype=torch.bfloat16, device=dev)
+                           if gru is not None else None))
     out["workspace"] = dspark_draft_block(Z, U, W, prev_token, temperature, seed, out["tokens"],
                                           out["q_tok"], out["q_lse"], draft_len=draft_len,
                                           req_id=req_id, corrected=out["corrected"],
-                                          workspace=workspace, trace=trace)
+                                          workspace=workspace, trace=trace, gru=gru,
+                                          head_state=out["head_state"])
     return out
 
 
@@ -362,7 +383,7 @@ def calibrate(conf_logits, verify_len, accept_len, inv_temp, step=1.0, ridge=1e-
 
 
 def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature, seed,
-           req_id=None, want_p=True, workspace=None, trace=None):
+           req_id=None, want_p=True, workspace=None, trace=None, head_state=None):
     B, K = draft_tokens.shape
     dev = Y.device
     out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
@@ -371,5 +392,5 @@ def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, tempe
     out["workspace"] = dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token,
                                      verify_len, temperature, seed, out["accept_len"],
                                      out["next_token"], req_id=req_id, p_tok=out["p_tok"],
-                                     workspace=workspace, trace=trace)
+                                     workspace=workspace, trace=trace, head_state=head_state)
     return out

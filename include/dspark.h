@@ -92,7 +92,8 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 typedef struct dspark_trace dspark_trace;
 
 /*
- * dspark_draft_block -- draft one block with the Markov sequential head.
+ * dspark_draft_block -- draft one block with the Markov sequential head (default) or the
+ * optional recurrent head.
  *
  * For request b and position k = 0 .. K_b - 1 (K_b = draft_len[b], or K):
  *   prev   = prev_token[b] for k = 0, else x[b][k-1]          (previous token only)
@@ -110,6 +111,21 @@ typedef struct dspark_trace dspark_trace;
  * Outputs: draft_tokens [B][K] int32, q_tok [B][K] float32, q_lse [B][K] float32; corrected
  * [B][K][V] float32 is optional (NULL skips it) and receives c.
  * req_id [B] (NULL: the request index) keys the random streams of each request.
+ *
+ * Recurrent head (QbitAI "DSpark in 10 concepts", section "Cheaper serial module: the Markov
+ * head", and 10100.com, section "Parallel drafts are fast but may turn 'of course' into 'of
+ * problem'": an optional RNN head that follows the whole draft prefix, of limited gain and
+ * off by default; the pages give no form).  When gru_wi is non-NULL (then gru_wh, gru_bi and
+ * gru_bh are required too) the left operand U[prev] above is replaced by a_k, the state of a
+ * GRU (Cho et al., EMNLP 2014) over the previous tokens' factors rounded to bfloat16:
+ *   e_k = U[prev_k];  h_{-1} = 0;  h_k = GRU(h_{k-1}, e_k) in float32
+ *   g = sigmoid(Wi_g e + bi_g + Wh_g h + bh_g), z = sigmoid(Wi_z e + bi_z + Wh_z h + bh_z),
+ *   n = tanh(Wi_n e + bi_n + g * (Wh_n h + bh_n)), h' = (1 - z) * n + z * h
+ *   a_k = bfloat16(h_k) (nearest, ties to even);  c[v] = Z[b][k][v] + sum_i a_k[i] W[v][i]
+ * gru_wi, gru_wh [3r][r] float32 (rows: reset units, update units, new units), gru_bi,
+ * gru_bh [3r].  Requires bfloat16 factors with r = 64, 128 or 256 (else DSPARK_EINVAL).
+ * head_state (optional, [B][K][r] bfloat16) receives a_k for every drafted position (other
+ * positions are not written); dspark_verify needs it to recompute a rejected position.
  */
 typedef struct {
     int32_t B, K, V, r;
@@ -127,6 +143,11 @@ typedef struct {
     float *q_lse;          /* out [B][K]                 */
     float *corrected;      /* optional out [B][K][V]     */
     dspark_trace *trace;   /* optional                   */
+    const float *gru_wi;   /* recurrent head: [3r][r], or NULL (Markov head) */
+    const float *gru_wh;   /* [3r][r]                    */
+    const float *gru_bi;   /* [3r]                       */
+    const float *gru_bh;   /* [3r]                       */
+    uint16_t *head_state;  /* optional out [B][K][r] bfloat16 (recurrent head) */
 } dspark_draft_args;
 
 /*
@@ -205,7 +226,8 @@ typedef struct {
  *   First rejection at k = j: accept_len = j and next_token is
  *     T = 0: argmax_v Y[b][j][v];
  *     T > 0: q_j(v) = exp(c_j[v] / T - q_lse[b][j]) with c_j recomputed by the Markov head
- *            (previous token prev_token[b] for j = 0, else draft_tokens[b][j-1]);
+ *            (previous token prev_token[b] for j = 0, else draft_tokens[b][j-1]), or, when
+ *            head_state is given (a recurrent-head draft), from its operand head_state[b][j];
  *            r = max(0, p - q_j); the two-level draw from the weights r on the residual
  *            streams at position j; if r is identically zero, the same draw from p.
  *   No rejection: accept_len = L and next_token is argmax_v Y[b][L][v] (T = 0) or the
@@ -215,6 +237,8 @@ typedef struct {
  * the ones the draft used.  Y may be float32 or bfloat16.
  * Outputs: accept_len [B], next_token [B]; p_tok [B][K] optional: p(x_k) for each tested
  * position (1 / 0 for a greedy match / mismatch), 0 for untested positions.
+ * head_state [B][K][r] bfloat16 (as written by dspark_draft_block's recurrent head) requires
+ * bfloat16 factors with r = 64, 128 or 256 (else DSPARK_EINVAL).
  */
 typedef struct {
     int32_t B, K, V, r;
@@ -235,6 +259,7 @@ typedef struct {
     int32_t *next_token;         /* out [B]               */
     float *p_tok;                /* optional out [B][K]   */
     dspark_trace *trace;
+    const uint16_t *head_state;  /* [B][K][r] bfloat16 from a recurrent-head draft, or NULL */
 } dspark_verify_args;
 
 /* Workspace bytes each call needs for the given sizes (0 on invalid sizes). */

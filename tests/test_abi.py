@@ -94,6 +94,18 @@ def test_host_validation_without_gpu():
     assert lib.dspark_draft_block(C.byref(a), None, 0, None) == D.DSPARK_EWORKSPACE
     assert lib.dspark_draft_block(C.byref(a), fake + 8, 1 << 30, None) == D.DSPARK_EWORKSPACE
     assert lib.dspark_draft_block(C.byref(a), fake, 16, None) == D.DSPARK_EWORKSPACE
+    # recurrent head: all four GRU arrays, bfloat16 factors of a matrix-core rank; head_state
+    # only with it (a has float32 factors of rank 16)
+    rnn = D.DraftArgs(*[getattr(a, f) for f, _ in a._fields_])
+    rnn.gru_wi = fake
+    assert lib.dspark_draft_block(C.byref(rnn), fake, 1 << 30, None) == D.DSPARK_EINVAL
+    rnn.gru_wh = rnn.gru_bi = rnn.gru_bh = fake
+    assert lib.dspark_draft_block(C.byref(rnn), fake, 1 << 30, None) == D.DSPARK_EINVAL
+    rnn.uw_dtype, rnn.r = 1, 100
+    assert lib.dspark_draft_block(C.byref(rnn), fake, 1 << 30, None) == D.DSPARK_EINVAL
+    hs = D.DraftArgs(*[getattr(a, f) for f, _ in a._fields_])
+    hs.head_state = fake
+    assert lib.dspark_draft_block(C.byref(hs), fake, 1 << 30, None) == D.DSPARK_EINVAL
     # B = 0 is a no-op
     empty = D.DraftArgs(*[getattr(a, f) for f, _ in a._fields_])
     empty.B = 0
@@ -115,6 +127,8 @@ def test_host_validation_without_gpu():
     assert lib.dspark_verify(C.byref(v), None, 0, None) == D.DSPARK_EDTYPE
     v.y_dtype, v.Y = 0, None
     assert lib.dspark_verify(C.byref(v), None, 0, None) == D.DSPARK_EINVAL
+    v.Y, v.head_state = fake, fake  # recurrent-head operands need matrix-core factors
+    assert lib.dspark_verify(C.byref(v), fake, 1 << 30, None) == D.DSPARK_EINVAL
 
     c = D.CalibrateArgs(4, 4, fake, fake, fake, fake, 1.0, 1e-3, None)
     assert lib.dspark_calibrate(None, None, 0, None) == D.DSPARK_EINVAL
