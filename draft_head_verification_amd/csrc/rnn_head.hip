@@ -13,12 +13,13 @@
 //
 // Work: per request 6 r x r products (input and hidden weights of three gates), B * 6 r^2
 // multiply-adds per position (0.1 GFLOP at B = r = 256), float32 throughout: about 3 us of the
-// vector ALUs over 256 CUs, plus one round of loads.  A workgroup takes 16 requests x 16
-// hidden units (256 workgroups at B = r = 256); every load it needs -- the 16 input rows
-// (bfloat16, widened), the 16 state rows and the 6 x 16 weight rows -- goes out at once into
-// shared memory (120 KB at r = 256), and each thread then keeps the four pre-activations
-// (reset, update, new-input, new-hidden) of one request and one unit, reading four inputs
-// at a time.
+// vector ALUs over 256 CUs, about half that on the matrix cores.  A workgroup takes 16
+// requests x 16 hidden units (256 workgroups at B = r = 256); every load it needs -- the 16
+// input rows (bfloat16, widened), the 16 state rows and the 6 x 16 weight rows -- goes out at
+// once into shared memory (133 KB at r = 256).  The four pre-activations (reset, update,
+// new-input, new-hidden) are 16 x 16 float32 matrix-core products, each wave summing a
+// quarter of the inputs; the quarters are added in shared memory and one thread per
+// (request, unit) finishes the gates.
 #include "dspark_common.hpp"
 
 namespace dspark {
@@ -124,34 +125,62 @@ __global__ __launch_bounds__(kRnnThreads) void rnn_step_kernel(
     if constexpr (W_DIRECT) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // ---- pre-activations of request row0 + rq, unit unit0 + u
-    const int rq = t / kRnnUnits, u = t % kRnnUnits;
-    const float *er = es + rq * RS, *hr = hs + rq * RS;
-    const float *w_ig = ws + (0 * kRnnUnits + u) * RS, *w_iz = ws + (1 * kRnnUnits + u) * RS;
-    const float *w_in = ws + (2 * kRnnUnits + u) * RS, *w_hg = ws + (3 * kRnnUnits + u) * RS;
-    const float *w_hz = ws + (4 * kRnnUnits + u) * RS, *w_hn = ws + (5 * kRnnUnits + u) * RS;
-    float a_g = 0.f, a_z = 0.f, a_ni = 0.f, a_nh = 0.f;
-#pragma unroll 4
-    for (int j = 0; j < R; j += 4) {
-        const float4 e = *reinterpret_cast<const float4 *>(er + j);
-        const float4 h = *reinterpret_cast<const float4 *>(hr + j);
-        const float4 ig = *reinterpret_cast<const float4 *>(w_ig + j);
-        const float4 iz = *reinterpret_cast<const float4 *>(w_iz + j);
-        const float4 in = *reinterpret_cast<const float4 *>(w_in + j);
-        const float4 hg = *reinterpret_cast<const float4 *>(w_hg + j);
-        const float4 hz = *reinterpret_cast<const float4 *>(w_hz + j);
-        const float4 hn = *reinterpret_cast<const float4 *>(w_hn + j);
-        a_g = fmaf(ig.x, e.x, fmaf(hg.x, h.x, a_g));
-        a_g = fmaf(ig.y, e.y, fmaf(hg.y, h.y, a_g));
-        a_g = fmaf(ig.z, e.z, fmaf(hg.z, h.z, a_g));
-        a_g = fmaf(ig.w, e.w, fmaf(hg.w, h.w, a_g));
-        a_z = fmaf(iz.x, e.x, fmaf(hz.x, h.x, a_z));
-        a_z = fmaf(iz.y, e.y, fmaf(hz.y, h.y, a_z));
-        a_z = fmaf(iz.z, e.z, fmaf(hz.z, h.z, a_z));
-        a_z = fmaf(iz.w, e.w, fmaf(hz.w, h.w, a_z));
-        a_ni = fmaf(in.x, e.x, fmaf(in.y, e.y, fmaf(in.z, e.z, fmaf(in.w, e.w, a_ni))));
-        a_nh = fmaf(hn.x, h.x, fmaf(hn.y, h.y, fmaf(hn.z, h.z, fmaf(hn.w, h.w, a_nh))));
+    // ---- pre-activations on the matrix cores (v_mfma_f32_16x16x4_f32): D[request][unit] +=
+    // A[request][input] * B[input][unit], B[i][j] = weight row (unit j), column i.  Wave w
+    // takes the inputs [w R/4, (w+1) R/4) in blocks of 16, where lane group g = lane / 16
+    // supplies inputs 4g .. 4g+3 of the block over four steps (any order of the sum is the
+    // sum).  Lane l holds D[4g + r][l % 16], r = 0..3.
+    const int lane = t & 63, wave = t >> 6, m = lane & 15, g4 = 4 * (lane >> 4);
+    const float *er = es + m * RS + g4, *hr = hs + m * RS + g4;
+    const float *wrow = ws + m * RS + g4;  // + part * kRnnUnits * RS: weight row of unit m
+    floatx4 acc_g = {0.f, 0.f, 0.f, 0.f}, acc_z = acc_g, acc_ni = acc_g, acc_nh = acc_g;
+    for (int kb = wave * (R / 4); kb < (wave + 1) * (R / 4); kb += 16) {
+        const float4 e = *reinterpret_cast<const float4 *>(er + kb);
+        const float4 h = *reinterpret_cast<const float4 *>(hr + kb);
+        float4 w[6];
+#pragma unroll
+        for (int part = 0; part < 6; ++part)
+            w[part] = *reinterpret_cast<const float4 *>(wrow + part * kRnnUnits * RS + kb);
+        const float ev4[4] = {e.x, e.y, e.z, e.w}, hv4[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const float wc[6] = {st == 0 ? w[0].x : st == 1 ? w[0].y : st == 2 ? w[0].z : w[0].w,
+                                 st == 0 ? w[1].x : st == 1 ? w[1].y : st == 2 ? w[1].z : w[1].w,
+                                 st == 0 ? w[2].x : st == 1 ? w[2].y : st == 2 ? w[2].z : w[2].w,
+                                 st == 0 ? w[3].x : st == 1 ? w[3].y : st == 2 ? w[3].z : w[3].w,
+                                 st == 0 ? w[4].x : st == 1 ? w[4].y : st == 2 ? w[4].z : w[4].w,
+                                 st == 0 ? w[5].x : st == 1 ? w[5].y : st == 2 ? w[5].z : w[5].w};
+            acc_g = __builtin_amdgcn_mfma_f32_16x16x4f32(ev4[st], wc[0], acc_g, 0, 0, 0);
+            acc_g = __builtin_amdgcn_mfma_f32_16x16x4f32(hv4[st], wc[3], acc_g, 0, 0, 0);
+            acc_z = __builtin_amdgcn_mfma_f32_16x16x4f32(ev4[st], wc[1], acc_z, 0, 0, 0);
+            acc_z = __builtin_amdgcn_mfma_f32_16x16x4f32(hv4[st], wc[4], acc_z, 0, 0, 0);
+            acc_ni = __builtin_amdgcn_mfma_f32_16x16x4f32(ev4[st], wc[2], acc_ni, 0, 0, 0);
+            acc_nh = __builtin_amdgcn_mfma_f32_16x16x4f32(hv4[st], wc[5], acc_nh, 0, 0, 0);
+        }
     }
+    // the four waves' partial sums meet in shared memory, over the weights (no longer read;
+    // 96 rows of at least 68 floats hold the 4 x 4 x 64 x 4 sums)
+    __syncthreads();
+    float *red = ws;  // [wave][4 sums][64 lanes][4]
+    static_assert(6 * kRnnUnits * RS >= 4 * 4 * 64 * 4, "reduction space");
+    const floatx4 accs[4] = {acc_g, acc_z, acc_ni, acc_nh};
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<floatx4 *>(red + ((wave * 4 + a) * 64 + lane) * 4) = accs[a];
+    __syncthreads();
+    // thread t finishes request rq = t / 16, unit u = t % 16 (held by lane 16 (rq / 4) + u,
+    // element rq % 4)
+    const int rq = t / kRnnUnits, u = t % kRnnUnits;
+    const int src_lane = 16 * (rq / 4) + u, src_el = rq % 4;
+    float pre[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) sum += red[((w2 * 4 + a) * 64 + src_lane) * 4 + src_el];
+        pre[a] = sum;
+    }
+    const float a_g = pre[0], a_z = pre[1], a_ni = pre[2], a_nh = pre[3];
 
     const int b = row0 + rq, unit = unit0 + u;
     if (b >= B) return;
