@@ -57,6 +57,48 @@ def _bf16_values(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def compare_rnn_draft(g, o, rows, temps, dlen, wmax, tally, tag):
+    """g: GPU outputs indexed by request (tokens, q_tok, q_lse, corrected, state bits) or, for
+    corrected / state, by position in `rows`; o: oracle outputs indexed by position in rows."""
+    B_rows = len(rows)
+    K = o["tokens"].shape[1]
+    r = o["state"].shape[2]
+    flipped = compared = 0
+    for i, b in enumerate(rows):
+        Tb = float(temps[b])
+        ci = i if g["corrected"].shape[0] == B_rows else b
+        for k in range(int(dlen[b])):
+            # operands: equal, or apart by one bfloat16 rounding step of the value (at most
+            # 2^-7 of it) plus the float32 evaluation error of the state (which matters near
+            # zero, where a step is tiny)
+            av, ov_ = _bf16_values(g["state"][ci, k]), _bf16_values(o["state"][i, k])
+            diff = np.abs(av - ov_)
+            assert np.all(diff <= 2.0 ** -7 * np.abs(ov_) + STATE_ABS), (b, k, diff.max())
+            flipped += int((diff != 0).sum())
+            compared += r
+            bound = float(diff.sum()) * wmax
+            oc = o["corrected"][i, k].astype(np.float64)
+            err = np.abs(g["corrected"][ci, k].astype(np.float64) - oc)
+            assert np.all(err <= TOL_C_TIGHT_ABS + TOL_C_TIGHT_REL * np.abs(oc) + bound), (b, k)
+            tally.compared_positions += 1
+            if g["tokens"][b, k] != o["tokens"][i, k]:
+                limit = max(TIE_GREEDY if Tb == 0 else TIE_SAMPLE, 2.0 * bound / max(Tb, 1e-30))
+                assert o["gap"][i, k] < limit, (b, k, g["tokens"][b, k], o["tokens"][i, k],
+                                                o["gap"][i, k])
+                tally.diverged_requests += 1
+                break  # the chains differ from here on
+            if Tb > 0:
+                assert abs(g["q_lse"][b, k] - o["q_lse"][i, k]) <= TOL_LSE + bound / Tb, (b, k)
+                assert abs(g["q_tok"][b, k] - o["q_tok"][i, k]) <= TOL_Q + 2.0 * bound / Tb, (b, k)
+            else:
+                assert g["q_tok"][b, k] == 1 and g["q_lse"][b, k] == 0
+        for k in range(int(dlen[b]), K):
+            assert g["tokens"][b, k] == -1
+    tally.report(tag)
+    print(f"  operand elements apart: {flipped} of {compared}", flush=True)
+    assert flipped <= max(4, compared // 1000)
+
+
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 def test_rnn_round_parity(case):
     from draft_head_verification_amd import dspark as D
@@ -80,47 +122,14 @@ def test_rnn_round_parity(case):
                             inp["seed"], draft_len=inp["draft_len"], req_id=inp["req_id"])
     live = od["tokens"] >= 0
     assert (od["tokens"][live] != om["tokens"][live]).mean() > 0.1
-    gt, gq, gl = (gd[k].cpu().numpy() for k in ("tokens", "q_tok", "q_lse"))
-    gc = gd["corrected"].cpu().numpy()
-    gs = _bits(gd["head_state"])
-    wmax = float(inp["W"].float().abs().max())
+    gnp = {k: gd[k].cpu().numpy() for k in ("tokens", "q_tok", "q_lse")}
+    gnp["corrected"] = gd["corrected"].cpu().numpy()
+    gnp["state"] = _bits(gd["head_state"])
     temps = inp["temperature"].numpy()
     dlen = inp["draft_len"].numpy()
     tally = Tally()
-    flipped_elems = compared_elems = 0
-    for b in range(B):
-        Tb = float(temps[b])
-        for k in range(int(dlen[b])):
-            # operands: equal, or apart by one bfloat16 rounding step of the value plus the
-            # float32 evaluation error of the state (which matters near zero, where a step is
-            # tiny)
-            av, ov_ = _bf16_values(gs[b, k]), _bf16_values(od["state"][b, k])
-            diff = np.abs(av - ov_)
-            # (one bfloat16 step of x is at most 2^-7 |x|)
-            assert np.all(diff <= 2.0 ** -7 * np.abs(ov_) + STATE_ABS), (b, k, diff.max())
-            flipped_elems += int((diff != 0).sum())
-            compared_elems += r
-            bound = float(diff.sum()) * wmax
-            oc = od["corrected"][b, k].astype(np.float64)
-            err = np.abs(gc[b, k].astype(np.float64) - oc)
-            assert np.all(err <= TOL_C_TIGHT_ABS + TOL_C_TIGHT_REL * np.abs(oc) + bound), (b, k)
-            tally.compared_positions += 1
-            if gt[b, k] != od["tokens"][b, k]:
-                limit = max(TIE_GREEDY if Tb == 0 else TIE_SAMPLE, 2.0 * bound / max(Tb, 1e-30))
-                assert od["gap"][b, k] < limit, (b, k, gt[b, k], od["tokens"][b, k], od["gap"][b, k])
-                tally.diverged_requests += 1
-                break  # the chains differ from here on
-            if Tb > 0:
-                assert abs(gl[b, k] - od["q_lse"][b, k]) <= TOL_LSE + bound / Tb, (b, k)
-                assert abs(gq[b, k] - od["q_tok"][b, k]) <= TOL_Q + 2.0 * bound / Tb, (b, k)
-            else:
-                assert gq[b, k] == 1 and gl[b, k] == 0
-        for k in range(int(dlen[b]), K):
-            assert gt[b, k] == -1
-    tally.report(f"rnn draft {_ids(case)}")
-    print(f"  operand elements one bfloat16 step apart: {flipped_elems} of {compared_elems}",
-          flush=True)
-    assert flipped_elems <= max(4, compared_elems // 1000)
+    compare_rnn_draft(gnp, od, list(range(B)), temps, dlen, float(inp["W"].float().abs().max()),
+                      tally, f"rnn draft {_ids(case)}")
 
     # ---- verify, on the oracle's draft: target rows = oracle corrected rows (+ noise)
     corr = inp["Z_ext"].float().clone()
@@ -169,3 +178,77 @@ def test_rnn_draft_is_deterministic_and_feeds_its_verify():
     a = v["accept_len"].cpu()
     assert bool(((a >= 0) & (a <= w.K)).all())
     assert bool(((v["next_token"].cpu() >= 0) & (v["next_token"].cpu() < w.V)).all())
+
+
+def _sample_rows(B):
+    return sorted({0, max(0, B // 2 - 1), B // 2, B - 1} & set(range(B)))
+
+
+@pytest.mark.parametrize("name", ["headline", "ragged"])
+def test_rnn_full_size_round(name):
+    """The recurrent head at a workload's full size in the benchmark's launch shape: the whole
+    batch on the GPU, a sample of requests recomputed by the oracle from the generator's inputs
+    (draft, then verify on the oracle's draft with targets built from its corrected rows; the
+    other requests keep the GPU's own chain and are checked through properties)."""
+    from draft_head_verification_amd import dspark as D
+    w = synth.WORKLOADS[name]
+    B, K, V, r = w.B, w.K, w.V, w.r
+    print(f"[rnn full {name}] B={B} K={K} V={V} r={r}", flush=True)
+    g = synth.make_inputs(w, device="cuda")
+    Z = g["Z_ext"][:, :K].contiguous()
+    gru = _gru(w)
+    gru_d = tuple(t.cuda() for t in gru)
+    rows = _sample_rows(B)
+    idx = torch.tensor(rows, device="cuda")
+    host = {k: g[k].cpu() for k in ("prev_token", "temperature", "draft_len", "req_id")}
+    temps, dlen = host["temperature"].numpy(), host["draft_len"].numpy()
+    U_cpu, W_cpu = g["U"].cpu(), g["W"].cpu()
+    gd = D.draft_block(Z, g["U"], g["W"], g["prev_token"], g["temperature"], g["seed"],
+                       draft_len=g["draft_len"], req_id=g["req_id"], want_corrected=True,
+                       gru=gru_d)
+    assert D.dspark_query_device_status(gd["workspace"]) == 0
+    toks = gd["tokens"].cpu().numpy()
+    for b in range(B):
+        kb = int(dlen[b])
+        assert np.all((toks[b, :kb] >= 0) & (toks[b, :kb] < V)) and np.all(toks[b, kb:] == -1)
+    od = oracle.draft_block(Z, U_cpu, W_cpu, host["prev_token"], host["temperature"], g["seed"],
+                            draft_len=host["draft_len"], req_id=host["req_id"], rows=rows,
+                            want_corrected=True, gru=gru)
+    gnp = {"tokens": toks, "q_tok": gd["q_tok"].cpu().numpy(), "q_lse": gd["q_lse"].cpu().numpy(),
+           "corrected": gd["corrected"][idx].cpu().numpy(), "state": _bits(gd["head_state"][idx])}
+    tally = Tally()
+    compare_rnn_draft(gnp, od, rows, temps, dlen, float(W_cpu.float().abs().max()), tally,
+                      f"rnn full draft {name}")
+
+    # verify: the sampled requests carry the oracle's draft, operands and targets
+    corr = gd["corrected"]
+    hs = gd["head_state"].clone()
+    toks_v, qt_v, ql_v = gd["tokens"].clone(), gd["q_tok"].clone(), gd["q_lse"].clone()
+    o_hs = torch.from_numpy(od["state"].view(np.int16)).view(torch.bfloat16)
+    for i, b in enumerate(rows):
+        kb = int(dlen[b])
+        corr[b, :kb] = torch.from_numpy(od["corrected"][i, :kb]).cuda()
+        hs[b] = o_hs[i].cuda()
+        toks_v[b] = torch.from_numpy(od["tokens"][i]).cuda()
+        qt_v[b] = torch.from_numpy(od["q_tok"][i].astype(np.float32)).cuda()
+        ql_v[b] = torch.from_numpy(od["q_lse"][i].astype(np.float32)).cuda()
+    ext = torch.cat([corr, g["Z_ext"][:, K:].float()], dim=1)
+    Y = synth.target_logits(ext, g["noise"], w.y_dtype)
+    del corr, ext
+    vlen = g["draft_len"].clone()
+    gv = D.verify(Y, toks_v, qt_v, ql_v, Z, g["U"], g["W"], g["prev_token"], vlen,
+                  g["temperature"], g["seed"], req_id=g["req_id"], head_state=hs)
+    assert D.dspark_query_device_status(gv["workspace"]) == 0
+    acc, nxt = gv["accept_len"].cpu().numpy(), gv["next_token"].cpu().numpy()
+    assert np.all((acc >= 0) & (acc <= dlen)) and np.all((nxt >= 0) & (nxt < V))
+    Yrows = Y[idx].cpu()
+    ov = oracle.verify(Yrows, od["tokens"], od["q_tok"].astype(np.float32),
+                       od["q_lse"].astype(np.float32), Z[idx].cpu(), U_cpu, W_cpu,
+                       host["prev_token"][rows], host["draft_len"][rows],
+                       host["temperature"][rows], g["seed"], req_id=host["req_id"][rows],
+                       head_state=o_hs)
+    gvn = {"accept_len": acc[rows], "next_token": nxt[rows],
+           "p_tok": gv["p_tok"][idx].cpu().numpy()}
+    vt = Tally()
+    compare_verify(gvn, ov, list(range(len(rows))), temps[rows], vt)
+    vt.report(f"rnn full verify {name}")
