@@ -31,6 +31,7 @@ CASES = [
     ("headline", {"V": 2392, "B": 64}, None),
     ("ragged", {"V": 1208, "r": 128, "B": 96}, None),
     ("single", {"V": 1208}, 0.0),
+    ("moderate", {"V": 1208, "r": 64, "B": 37, "K": 5}, 0.7),  # a ragged last row tile
 ]
 
 
