@@ -232,7 +232,8 @@ def main():
         s[0] += 1
         s[1] += ms
     acc_host = acc.cpu().numpy()
-    n_resid = int(torch.from_numpy(ws_v[256:260].cpu().numpy().copy()).view(torch.int32)[0])
+    # requests whose round ended in a rejection at T > 0 (the residual pass's rows)
+    n_resid = int(((acc < vlen) & (inp["temperature"] > 0)).sum().item())
     kernels = []
     for name, (cnt, tot) in sorted(per.items(), key=lambda kv: -kv[1][1]):
         avg_us = tot / cnt * 1e3

@@ -474,11 +474,11 @@ inline int num_row_slabs(int V, int B) {
 
 struct VerifyWs {
     uint32_t *status;      // [1]
-    int32_t *n_resid;      // [1] number of rows needing a residual draw
+    int32_t *n_resid;      // [1] nonzero when some request needs a residual draw
     int32_t *n_alive;      // [kMaxChunks] requests listed for each chunk
     int4 *alive;           // [kMaxChunks][B] records {b, L, T bits, req} of the listed requests
     int32_t *first_reject; // [B] first rejected position (K + 1: none so far)
-    int32_t *resid_rows;   // [B] packed (b * 128 + j)
+    int32_t *resid_rows;   // [B] packed (b * 128 + j) of request b's residual row, or -1
     float4 *rowstats;      // [B][K+1] {m2, l, idx-as-bits, g}
     Partial *row_partials; // [B][K+1][n_row_slabs]
     Partial *partials;     // [B][n_slabs] residual candidates

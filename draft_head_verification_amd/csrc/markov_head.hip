@@ -41,7 +41,7 @@ enum class HeadMode { Draft, Residual };
 struct HeadParams {
     int B, K, V, r;
     int n_rows_max;                 // grid is sized for this many GEMM rows
-    const int32_t *n_rows_dev;      // residual mode: actual row count (device)
+    const int32_t *n_rows_dev;      // residual mode: nonzero when any row needs the pass
     int k;                          // draft mode: the position of this step
     const void *Z;                  // [B][K][V]
     const uint16_t *U, *W;          // [V][r] bf16 (matrix-core path)
@@ -126,10 +126,13 @@ __device__ __forceinline__ RowInfo row_info(const HeadParams &p, int row, int n_
     if constexpr (MODE == HeadMode::Draft) {
         return draft_row_resolve(p, row, n_rows, draft_row_load(p, row));
     } else {
+        // row b of the batch: its packed (b, j), or -1 when request b needs no residual draw
+        // (such rows read request 0's first rows, shared and cached, and are dropped)
         const int raw = p.resid_rows[rc];
-        const int packed = in ? raw : 0;
+        const bool live = in && raw >= 0;
+        const int packed = live ? raw : 0;
         const int b = packed >> 7, j = packed & 127;
-        ri.valid = in;
+        ri.valid = live;
         ri.b = b;
         ri.pos = j;
         const int pt = p.prev_token[b];
@@ -473,7 +476,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
     const int group = slot % n_groups;
     const int slab = (slot / n_groups) * 8 + xcd;
-    const int n_rows = kResid ? *p.n_rows_dev : p.n_rows_max;
+    // residual mode: every request has its row (B rows) as soon as one needs a residual draw
+    const int n_rows = kResid ? (*p.n_rows_dev ? p.n_rows_max : 0) : p.n_rows_max;
     if (group * kRowsPerGroup >= n_rows || slab >= p.n_slabs) return;  // uniform exit
 
     const int n_tiles = (p.V + kTileV - 1) / kTileV;
@@ -861,7 +865,9 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
     __shared__ ResidState red_rs[kValuThreads / 64];
     const int slab = (int)(blockIdx.x % (unsigned)p.n_slabs);
     const int row = (int)(blockIdx.x / (unsigned)p.n_slabs);
-    const int n_rows = (MODE == HeadMode::Residual) ? *p.n_rows_dev : p.n_rows_max;
+    // residual mode: row b is request b's residual row, when it has one (the flag is set)
+    const int n_rows = (MODE == HeadMode::Residual) ? (*p.n_rows_dev ? p.n_rows_max : 0)
+                                                    : p.n_rows_max;
     const RowInfo ri = row_info<MODE>(p, row, n_rows);
     if (!ri.valid) return;  // uniform per block
     const void *Ub = p.Uf ? (const void *)p.Uf : (const void *)p.U;

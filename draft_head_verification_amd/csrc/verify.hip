@@ -326,6 +326,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
     }
     const ReqInfo ri = req_info(b, K, verify_len, temperature, req_id);
     const size_t rbase = (size_t)b * (K + 1);
+    if (lane == 0) resid_rows[b] = -1;  // replaced below when the request needs a residual draw
     int fr = first_reject[b];
     bool here = false;  // the deciding row is in the last chunk, merged by this wave
     float4 rs = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -345,9 +346,11 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
         accept_len[b] = a;
     }
     if (rejected && !ri.greedy) {
+        // row b of the residual pass (no compaction: a shared counter would serialise the
+        // waves' atomics); the flag only tells the residual launches that there is work
         if (lane == 0) {
-            const int slot = atomicAdd(n_resid, 1);
-            resid_rows[slot] = b * 128 + a;
+            resid_rows[b] = b * 128 + a;
+            *n_resid = 1;
             next_token[b] = -1;  // written by the residual reduction
         }
         return;
@@ -390,25 +393,27 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
     const int32_t *draft_tokens, const float *q_lse, const float *temperature,
     const uint32_t *req_id, uint32_t key0, uint32_t key1, const float4 *rowstats,
     const int32_t *n_resid, const int32_t *resid_rows, const Partial *partials, int n_slabs,
-    const uint16_t *head_state, int32_t *next_token, uint32_t *status) {
+    const uint16_t *head_state, int32_t *next_token, uint32_t *status, int B) {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (row >= *n_resid) return;  // uniform per wave
-    // the row's record and its slab partials (four per lane) go out together
+    const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);  // = request b
+    if (row >= B || *n_resid == 0) return;  // uniform per wave
+    // the row's record, its slab partials (four per lane) and the request's values go out
+    // together (absent optional arrays are read at a stand-in address and replaced)
     const int packed = resid_rows[row];
     constexpr int kPer = 4;
     const Partial *prow = partials + (size_t)row * n_slabs;
     Partial pp[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) pp[i] = prow[min(lane + 64 * i, n_slabs - 1)];
-    // the request's values: loads that need only the record, issued before the merge needs
-    // the partials (absent optional arrays are read at a stand-in address and replaced)
-    const int b = packed >> 7, j = packed & 127;
-    const size_t zrow = (size_t)b * K + j, yrow = (size_t)b * (K + 1) + j;
+    const int b = row;
     const uint32_t *rq = req_id ? req_id : reinterpret_cast<const uint32_t *>(prev_token);
     const float T = temperature[b];  // > 0: greedy rows never need a residual
     const uint32_t req_ld = rq[b];
     const int pt = prev_token[b];
+    if (packed < 0) return;  // no residual draw for this request
+    // then the loads that need the record's position
+    const int j = packed & 127;
+    const size_t zrow = (size_t)b * K + j, yrow = (size_t)b * (K + 1) + j;
     const int dt = draft_tokens[(size_t)b * K + (j > 0 ? j - 1 : 0)];
     const float4 rs = rowstats[yrow];
     const float ql = q_lse[zrow];
@@ -589,7 +594,7 @@ hipError_t launch_verify_residual_reduce(const dspark_verify_args &a, const Veri
         a.K, a.V, a.r, a.y_dtype, a.z_dtype, a.uw_dtype, a.Y, a.Z, a.U, a.W, a.prev_token,
         a.draft_tokens, a.q_lse, a.temperature, a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu),
         (uint32_t)(a.seed >> 32), ws.rowstats, ws.n_resid, ws.resid_rows, ws.partials,
-        ws.n_slabs, a.head_state, a.next_token, ws.status);
+        ws.n_slabs, a.head_state, a.next_token, ws.status, a.B);
     return hipGetLastError();
 }
 
