@@ -253,3 +253,31 @@ def test_rnn_full_size_round(name):
     vt = Tally()
     compare_verify(gvn, ov, list(range(len(rows))), temps[rows], vt)
     vt.report(f"rnn full verify {name}")
+
+
+def test_rnn_zero_and_short_drafts():
+    """Requests with draft length 0 (nothing drafted, nothing written), 1 and the full K in one
+    batch: the recurrent state of a request stops with its draft, the others go on."""
+    from draft_head_verification_amd import dspark as D
+    w = synth.shrink(synth.WORKLOADS["moderate"], V=1208, r=128, B=24, K=6)
+    inp = synth.make_inputs(w, strong_bias=True)
+    inp["draft_len"] = torch.tensor([0, 1, 6, 3, 0, 2] * 4, dtype=torch.int32)
+    g = to_device(inp)
+    gru = _gru(w)
+    gd = D.draft_block(g["Z"], g["U"], g["W"], g["prev_token"], g["temperature"], inp["seed"],
+                       draft_len=g["draft_len"], req_id=g["req_id"], want_corrected=True,
+                       gru=tuple(t.cuda() for t in gru))
+    assert D.dspark_query_device_status(gd["workspace"]) == 0
+    Zc = inp["Z_ext"][:, :w.K].contiguous()
+    od = oracle.draft_block(Zc, inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
+                            inp["seed"], draft_len=inp["draft_len"], req_id=inp["req_id"],
+                            want_corrected=True, gru=tuple(t.numpy() for t in gru))
+    gnp = {k: gd[k].cpu().numpy() for k in ("tokens", "q_tok", "q_lse")}
+    gnp["corrected"] = gd["corrected"].cpu().numpy()
+    gnp["state"] = _bits(gd["head_state"])
+    dlen = inp["draft_len"].numpy()
+    compare_rnn_draft(gnp, od, list(range(w.B)), inp["temperature"].numpy(), dlen,
+                      float(inp["W"].float().abs().max()), Tally(), "rnn short drafts")
+    # positions past a draft keep the output's initial zeros
+    for b in range(w.B):
+        assert not gnp["state"][b, dlen[b]:].any()
