@@ -251,8 +251,6 @@ dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_byt
     VerifyWs w;
     verify_layout(a->B, a->K, a->V, &w, reinterpret_cast<char *>(ws));
     hipError_t e;
-    e = traced(a->trace, "verify_prepare", s, [&] { return launch_verify_prepare(*a, w, s); });
-    if (e != hipSuccess) return DSPARK_EHIP;
     int bounds[kMaxChunks + 1];
     const int n_chunks = verify_chunks(a->K, bounds);
     for (int c = 0; c < n_chunks; ++c) {

@@ -523,7 +523,6 @@ bool matrix_core_factors(int uw_dtype, int r);
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, hipStream_t s);
 hipError_t launch_calibrate(const dspark_calibrate_args &a, uint32_t *status, hipStream_t s);
 
-hipError_t launch_verify_prepare(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s);
 // Target rows are verified in chunks (one launch each, and a decide launch after every chunk
 // but the last); verify_chunks fills the chunk edges for K and returns their count.
 int verify_chunks(int K, int bounds[kMaxChunks + 1]);

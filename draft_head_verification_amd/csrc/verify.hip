@@ -9,10 +9,11 @@
 // tag page, post "Speculative Decoding", steps 3-4).
 //
 // Kernels, in launch order:
-//   verify_prepare   clear the status word, the residual-row counter, the per-chunk request
-//                    counts and the per-request first rejection
 //   verify_rows      one launch per chunk of target rows ([0,2), [2,5), [5,9), [9,17), ...),
-//                    over the requests still being verified there: a fixed grid takes the
+//                    over the requests still being verified there (the first launch also
+//                    clears the status word, the residual flag, the per-chunk request counts
+//                    and the per-request first rejection, and lists every request for the
+//                    first decide launch): a fixed grid takes the
 //                    (request, row of the chunk, vocabulary slab) items in turn and streams
 //                    each slab of Y[b][k] once: softmax max / sum-exp of Y/T in log2 units,
 //                    the argmax for greedy rows, and the bonus row's block race.  Rows after
@@ -23,7 +24,7 @@
 //                    request for the next chunk if it is still being verified
 //   verify_finish    one wave per request: decides the last chunk, then the accepted length,
 //                    the greedy correction / the bonus draw inside its winning block, or
-//                    enqueues the first rejected row for a residual draw
+//                    marks the first rejected row for a residual draw
 //   (markov_head.hip) the residual rows: recompute q_j with the Markov head on the matrix
 //                    cores and run the block race of max(0, p - q_j)
 //   verify_residual_reduce  merge the race, draw the token inside the winning block
@@ -42,18 +43,28 @@ __device__ __forceinline__ int4 make_req_rec(int b, int K, const int32_t *verify
     return make_int4(b, L < 0 ? 0 : (L > K ? K : L), __float_as_int(T), (int)req);
 }
 
-__global__ __launch_bounds__(256) void verify_prepare_kernel(
-    int B, int K, const int32_t *verify_len, const float *temperature, const uint32_t *req_id,
-    uint32_t *status, int32_t *n_resid, int32_t *first_reject, int32_t *n_alive, int4 *list0) {
+// The first chunk lists every request: its row launch also sets up the verification state
+// (status word, residual flag, per-chunk counts, first rejections, chunk 0's records) for the
+// launches after it, and takes its own requests' records straight from the arguments.
+struct FirstChunk {
+    int B;  // > 0: this launch is the first chunk
+    const int32_t *verify_len;
+    const float *temperature;
+    const uint32_t *req_id;
+    uint32_t *status;
+    int32_t *n_resid, *first_reject, *n_alive;
+    int4 *list0;
+};
+__device__ __forceinline__ void first_chunk_setup(const FirstChunk &fc, int K) {
     const int i0 = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
     if (i0 == 0) {
-        *status = 0u;
-        *n_resid = 0;
+        *fc.status = 0u;
+        *fc.n_resid = 0;
     }
-    if (i0 < kMaxChunks) n_alive[i0] = i0 == 0 ? B : 0;  // chunk 0 lists every request
-    for (int i = i0; i < B; i += stride) {
-        first_reject[i] = K + 1;
-        list0[i] = make_req_rec(i, K, verify_len, temperature, req_id);
+    if (i0 < kMaxChunks) fc.n_alive[i0] = i0 == 0 ? fc.B : 0;
+    for (int i = i0; i < fc.B; i += stride) {
+        fc.first_reject[i] = K + 1;
+        fc.list0[i] = make_req_rec(i, K, fc.verify_len, fc.temperature, fc.req_id);
     }
 }
 
@@ -237,11 +248,13 @@ __device__ __forceinline__ long long row_groups(long long T, int grid) {
 template <typename YT>
 __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     int K, int V, const void *Y, uint32_t key0, uint32_t key1, int S, int k_lo, int k_hi,
-    const int32_t *n_alive, const int4 *alive, Partial *row_partials) {
+    const int32_t *n_alive, const int4 *alive, Partial *row_partials, FirstChunk fc) {
     __shared__ SampleState red[kRowThreads / 64];
+    const bool first = fc.B > 0;
+    if (first) first_chunk_setup(fc, K);
     const int R = k_hi - k_lo;
     const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
-    const long long T = (long long)*n_alive * R * n_blk;
+    const long long T = (long long)(first ? fc.B : *n_alive) * R * n_blk;
     if (T == 0) return;
     const long long G = row_groups(T, gridDim.x);
     const long long w = blockIdx.x;
@@ -251,7 +264,9 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     for (long long gb = w * T / G; gb < g1;) {  // uniform: one row segment per pass
         const long long ri = gb / n_blk, row_begin = ri * n_blk;
         const long long seg_end = g1 < row_begin + n_blk ? g1 : row_begin + n_blk;
-        const int4 rec = alive[ri / R];
+        const int4 rec = first ? make_req_rec((int)(ri / R), K, fc.verify_len, fc.temperature,
+                                              fc.req_id)
+                               : alive[ri / R];
         const int k = k_lo + (int)(ri % R);
         const ReqInfo info = req_info(rec);
         if (k <= info.L) {  // rows past L are not verified
@@ -494,14 +509,6 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
 // launchers
 // ---------------------------------------------------------------------------------------
 
-hipError_t launch_verify_prepare(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s) {
-    const int blocks = (a.B + 255) / 256 < 1024 ? (a.B + 255) / 256 : 1024;
-    verify_prepare_kernel<<<blocks < 1 ? 1 : blocks, 256, 0, s>>>(
-        a.B, a.K, a.verify_len, a.temperature, a.req_id, ws.status, ws.n_resid,
-        ws.first_reject, ws.n_alive, ws.alive);
-    return hipGetLastError();
-}
-
 int verify_chunks(int K, int bounds[kMaxChunks + 1]) {
     // rows 0 .. K (K + 1 target rows) in chunks of 2, 3, 4, 8, 16, ... rows
     static const int edges[] = {0, 2, 5, 9, 17, 33, 65};
@@ -532,12 +539,16 @@ hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, i
     grid = grid < 1 ? 1 : (grid > kRowGrid ? kRowGrid : grid);
     const int4 *list = alive_list(ws, chunk, a.B);
     const int32_t *cnt = ws.n_alive + chunk;
+    FirstChunk fc{};
+    if (chunk == 0)
+        fc = FirstChunk{a.B,       a.verify_len,     a.temperature, a.req_id,  ws.status,
+                        ws.n_resid, ws.first_reject, ws.n_alive,    ws.alive};
     if (a.y_dtype == DSPARK_BF16)
         verify_rows_kernel<uint16_t><<<(unsigned)grid, kRowThreads, 0, s>>>(
-            a.K, a.V, a.Y, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials);
+            a.K, a.V, a.Y, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials, fc);
     else
         verify_rows_kernel<float><<<(unsigned)grid, kRowThreads, 0, s>>>(
-            a.K, a.V, a.Y, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials);
+            a.K, a.V, a.Y, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials, fc);
     return hipGetLastError();
 }
 
