@@ -14,7 +14,6 @@ struct dspark_trace {
 
 namespace {
 
-constexpr int kMaxK = 64;
 constexpr int kMaxRank = 1024;
 constexpr int kMaxV = 1 << 30;
 
@@ -129,9 +128,16 @@ size_t dspark_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r) 
     return verify_layout(B, K, V, nullptr, nullptr);
 }
 
+// status word, then (scheduling on) the items' prefix products and ranks
+static size_t schedule_items(int32_t B, int32_t K) {
+    const long long n = (long long)B * K;
+    return (size_t)(n < 8192 ? n : 8192);
+}
+
 size_t dspark_schedule_workspace_size(int32_t B, int32_t K) {
     if (B < 0 || B > 8192 || K < 1 || K > kMaxK) return 0;
-    return 256;
+    const size_t n = schedule_items(B, K);
+    return 256 + align256(n * sizeof(long long)) + align256(n * sizeof(int));
 }
 
 dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws_bytes,
@@ -209,8 +215,13 @@ dspark_status dspark_schedule(const dspark_schedule_args *a, void *ws, size_t ws
     if (!check_ws(ws, ws_bytes, dspark_schedule_workspace_size(a->B, a->K)))
         return DSPARK_EWORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    uint32_t *status = reinterpret_cast<uint32_t *>(ws);
-    hipError_t e = traced(a->trace, "schedule", s, [&] { return launch_schedule(*a, status, s); });
+    char *base = reinterpret_cast<char *>(ws);
+    uint32_t *status = reinterpret_cast<uint32_t *>(base);
+    long long *key = reinterpret_cast<long long *>(base + 256);
+    int *rank = reinterpret_cast<int *>(
+        base + 256 + align256(schedule_items(a->B, a->K) * sizeof(long long)));
+    hipError_t e = traced(a->trace, "schedule", s,
+                          [&] { return launch_schedule(*a, status, key, rank, s); });
     return e == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
 

@@ -423,6 +423,7 @@ __device__ __forceinline__ int checked_token(int t, int V, uint32_t *status) {
 // Launch geometry shared by host and device code
 // ---------------------------------------------------------------------------------------
 
+constexpr int kMaxK = 64;            // draft positions per request
 constexpr int kTileV = 64;           // vocabulary rows per W tile (4 MFMA row blocks)
 constexpr int kMfmaWaves = 8;        // waves per matrix-core workgroup
 constexpr int kRowsPerWave = 32;     // requests per wave (two 16-wide MFMA column blocks)
@@ -520,7 +521,8 @@ bool draft_uses_rnn(const dspark_draft_args &a);
 // bfloat16 factors of a rank the matrix-core kernels take (64, 128 or 256)
 bool matrix_core_factors(int uw_dtype, int r);
 
-hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, hipStream_t s);
+hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, long long *key,
+                           int *rank, hipStream_t s);
 hipError_t launch_calibrate(const dspark_calibrate_args &a, uint32_t *status, hipStream_t s);
 
 // Target rows are verified in chunks (one launch each, and a decide launch after every chunk

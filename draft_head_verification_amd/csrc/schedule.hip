@@ -14,9 +14,11 @@
 // maximise expected emitted tokens per unit of verify time, E(n) * T(N(n)) / N(n), over the
 // n most probable prefix items; see include/dspark.h for the exact statement.
 //
-// One workgroup of 1024 threads: survival products in float64, an LDS bitonic sort of up to
-// 8192 (P, position, request) keys, a block prefix sum, a parallel argmax over n and an
-// LDS count per request.
+// Survival products in float64; every item ranked against every request's run across the
+// whole GPU (a request's prefix products never increase along its draft, each factor being
+// at most 1, so its items form one sorted run and an item's place in it is a binary search);
+// then one workgroup takes the items in rank order, forms E(n) by a block prefix sum, takes
+// the argmax over n, and counts each request's items ranked below n*.
 #include "dspark_common.hpp"
 
 namespace dspark {
@@ -45,19 +47,97 @@ __device__ __forceinline__ double profile_at(const double *kt, const double *kp,
     return kp[lo] + (kp[lo + 1] - kp[lo]) * t;
 }
 
-// (key desc, id asc) is "a before b"
-__device__ __forceinline__ bool sched_before(unsigned long long ka, int ia, unsigned long long kb,
-                                             int ib) {
-    return ka > kb || (ka == kb && ia < ib);
+// "a before b": (P desc, k asc, b asc), with P as its float64 bits (P >= 0; -1 marks a slot
+// past the request's draft, after every item) and t = k * B + b (unique per item)
+__device__ __forceinline__ bool sched_before(long long ka, int ta, long long kb, int tb) {
+    return ka > kb || (ka == kb && ta < tb);
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
+// the request's draft length, clamped to [0, K] (out-of-range values are flagged by the select
+// kernel)
+__device__ __forceinline__ int sched_len(const int32_t *draft_len, int b, int K) {
+    const int kb = draft_len ? draft_len[b] : K;
+    return kb < 0 ? 0 : (kb > K ? K : kb);
+}
+
+// Ranking runs in three launches: prepare (one thread per request: its prefix products into
+// key[b*K + k], rank counters cleared), rank (every item against every request's run), and
+// select (one workgroup: items in rank order, the objective over n, lengths).
+constexpr int kPrepThreads = 256;
+constexpr int kRankThreads = 256;
+constexpr int kRankRuns = 32;  // request runs staged per rank workgroup
+
+__global__ __launch_bounds__(kPrepThreads) void schedule_prepare_kernel(
+    int B, int K, const float *conf, const int32_t *draft_len, const double *inv_temp,
+    long long *key, int *rank) {
+    const int b = blockIdx.x * kPrepThreads + threadIdx.x;
+    if (b >= B) return;
+    const int kb = sched_len(draft_len, b, K);
+    double run_p = 1.0;
+    for (int k = 0; k < K; ++k) {
+        if (k < kb)
+            run_p = run_p * survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0);
+        key[(size_t)b * K + k] = k < kb ? __double_as_longlong(run_p) : -1ll;
+        rank[(size_t)b * K + k] = 0;
+    }
+}
+
+// Item i's rank is the number of items before it.  A request's items are sorted along its
+// draft (P never increases, k rises; empty slots last), so those before item i form a prefix
+// of each run, found by binary lifting.  Workgroup (x, y) ranks items [256x, 256x + 256)
+// against the runs of requests [32y, 32y + 32), staged in LDS; the counts of all y add up.
+__global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(int B, int K,
+                                                                     const long long *key,
+                                                                     int *rank) {
+    __shared__ long long rk[kRankRuns * kMaxK];
+    const int tid = threadIdx.x;
+    const int r0 = blockIdx.y * kRankRuns;
+    const int nr = min(kRankRuns, B - r0);
+    for (int i = tid; i < nr * K; i += kRankThreads) rk[i] = key[(size_t)r0 * K + i];
+    __syncthreads();
+    const int n_total = B * K;
+    const int i = blockIdx.x * kRankThreads + tid;
+    if (i >= n_total) return;
+    const long long mk = key[i];
+    if (mk < 0) return;  // a slot past the draft has no rank
+    const int mt = (i % K) * B + i / K;
+    int top = 1;
+    while (top * 2 <= K) top <<= 1;
+    int lo[kRankRuns];
+#pragma unroll
+    for (int rr = 0; rr < kRankRuns; ++rr) lo[rr] = 0;
+    for (int step = top; step > 0; step >>= 1) {
+        long long km[kRankRuns];
+        // (all reads of a step first, clamped inside the staged runs; bitwise logic after)
+#pragma unroll
+        for (int rr = 0; rr < kRankRuns; ++rr)
+            km[rr] = rk[min(rr, nr - 1) * K + min(lo[rr] + step, K) - 1];
+#pragma unroll
+        for (int rr = 0; rr < kRankRuns; ++rr) {
+            const int cand = lo[rr] + step;
+            const int tm = (cand - 1) * B + r0 + rr;
+            const int ok = (int)(cand <= K) & (int)(rr < nr) &
+                           ((int)(km[rr] > mk) | ((int)(km[rr] == mk) & (int)(tm < mt)));
+            lo[rr] += ok * step;
+        }
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int rr = 0; rr < kRankRuns; ++rr) cnt += lo[rr];
+    if (cnt) atomicAdd(rank + i, cnt);
+}
+
+// One workgroup: validation, then (scheduling on) the items in rank order, E(n) by a block
+// prefix sum, the argmax of G(n), and each request's length = its items ranked below n*.
+// With scheduling off every request verifies its draft and nothing else was launched: the
+// products are formed here.
+__global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     int B, int K, const float *conf, const int32_t *draft_len, int n_knots,
     const double *knot_tokens, const double *knot_tps, int enabled, const double *inv_temp,
-    int32_t *verify_len, double *expected_tokens, uint32_t *status) {
-    __shared__ unsigned long long key[kSchedMaxItems];  // float64 bits of P (P >= 0)
-    __shared__ int ids[kSchedMaxItems];                 // k * B + b; sentinel 0x7FFFFFFF
-    __shared__ int len[kSchedMaxItems];                 // per-request length being built
+    const long long *key, const int *rank, int32_t *verify_len, double *expected_tokens,
+    uint32_t *status) {
+    __shared__ long long sorted[kSchedMaxItems];  // products in rank order
+    __shared__ int ranks[kSchedMaxItems];         // rank of item b*K + k
     __shared__ double kt[kSchedMaxKnots], kp[kSchedMaxKnots];
     __shared__ double wsum[kSchedThreads / 64];
     __shared__ double best_g[kSchedThreads / 64];
@@ -70,15 +150,13 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
         s_items = 0;
     }
     __syncthreads();
+    int my_items = 0;
     for (int b = tid; b < B; b += kSchedThreads) {
-        int kb = draft_len ? draft_len[b] : K;
-        if (kb < 0 || kb > K) {
-            atomicOr(status, DSPARK_DEV_BAD_LENGTH);
-            kb = kb < 0 ? 0 : K;
-        }
-        len[b] = kb;  // the answer when scheduling is off
-        atomicAdd(&s_items, kb);
+        const int raw = draft_len ? draft_len[b] : K;
+        if (raw < 0 || raw > K) atomicOr(status, DSPARK_DEV_BAD_LENGTH);
+        my_items += sched_len(draft_len, b, K);
     }
+    if (my_items) atomicAdd(&s_items, my_items);
     if (enabled)
         for (int i = tid; i < n_knots; i += kSchedThreads) {
             kt[i] = knot_tokens[i];
@@ -95,51 +173,21 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
             if (!ok) atomicOr(status, DSPARK_DEV_BAD_PROFILE);
         }
         s_ok = ok ? 1 : 0;
+        s_nstar = -1;  // no schedule: every request verifies its whole draft
     }
     __syncthreads();
     const int n_items = s_items;
 
     if (s_ok) {
-        // slot b*K + k holds (P[b][k], k*B + b) for k < K_b and a sentinel otherwise;
-        // "before" order = (P desc, k asc, b asc), sentinels last
-        int n_slots = 1;
-        while (n_slots < B * K) n_slots <<= 1;
-        for (int b = tid; b < B; b += kSchedThreads) {
-            const int kb = len[b];
-            double run_p = 1.0;
-            for (int k = 0; k < K; ++k) {
-                run_p = run_p * survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0);
-                const bool real = k < kb;
-                key[b * K + k] = real ? (unsigned long long)__double_as_longlong(run_p) : 0ull;
-                ids[b * K + k] = real ? k * B + b : 0x7FFFFFFF;
-            }
-        }
-        for (int i = B * K + tid; i < n_slots; i += kSchedThreads) {
-            key[i] = 0ull;
-            ids[i] = 0x7FFFFFFF;
+        // ranks of the items are a permutation of 0 .. n_items - 1
+        for (int i = tid; i < B * K; i += kSchedThreads) {
+            const long long k = key[i];
+            const int r = rank[i];
+            const bool item = k >= 0 && r >= 0 && r < n_items;
+            if (item) sorted[r] = k;
+            ranks[i] = item ? r : -1;
         }
         __syncthreads();
-        for (int size = 2; size <= n_slots; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < n_slots; i += kSchedThreads) {
-                    const int j = i ^ stride;
-                    if (j > i) {
-                        const unsigned long long ki = key[i], kj = key[j];
-                        const int ii = ids[i], ij = ids[j];
-                        const bool forward = (i & size) == 0;
-                        const bool swap = forward ? sched_before(kj, ij, ki, ii)
-                                                  : sched_before(ki, ii, kj, ij);
-                        if (swap) {
-                            key[i] = kj;
-                            key[j] = ki;
-                            ids[i] = ij;
-                            ids[j] = ii;
-                        }
-                    }
-                }
-                __syncthreads();
-            }
-        }
         // thread t evaluates G(n) for n in [n0, n1), a tiling of 0..n_items; its item range
         // [n0, min(n1, n_items)) tiles the sorted items, so E(n0) = B + (sum over earlier
         // threads' item ranges)
@@ -147,7 +195,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
         const int n0 = min(tid * per, n_items + 1), n1 = min(n0 + per, n_items + 1);
         const int i1 = min(n1, n_items);
         double own = 0.0;
-        for (int i = n0; i < i1; ++i) own += __longlong_as_double((long long)key[i]);
+        for (int i = n0; i < i1; ++i) own += __longlong_as_double(sorted[i]);
         double incl = own;
         for (int d = 1; d < 64; d <<= 1) {
             const double o = __shfl_up(incl, d);
@@ -167,7 +215,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
                 bg = g;
                 bn = n;
             }
-            if (n < n_items) e += __longlong_as_double((long long)key[n]);
+            if (n < n_items) e += __longlong_as_double(sorted[n]);
         }
         for (int mask = 1; mask < 64; mask <<= 1) {
             const double og = __shfl_xor(bg, mask);
@@ -192,32 +240,45 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(
                 }
             s_nstar = n;
         }
-        for (int b = tid; b < B; b += kSchedThreads) len[b] = 0;
-        __syncthreads();
-        // the top n* items of each request form a prefix of its draft: count them
-        const int nstar = s_nstar;
-        for (int i = tid; i < nstar; i += kSchedThreads) atomicAdd(&len[ids[i] % B], 1);
         __syncthreads();
     }
+    // request b verifies its items ranked below n* (a prefix of its draft: ranks rise along
+    // it); expected tokens add up the same float64 products that were ranked
+    const int nstar = s_nstar;
     for (int b = tid; b < B; b += kSchedThreads) {
-        const int L = len[b];
-        verify_len[b] = L;
-        if (expected_tokens) {
-            double run_p = 1.0, e = 1.0;
-            for (int k = 0; k < L; ++k) {
+        const int kb = sched_len(draft_len, b, K);
+        double run_p = 1.0, e = 1.0;
+        int L = 0;
+        for (int k = 0; k < kb; ++k) {
+            if (s_ok) {
+                const int r = ranks[b * K + k];
+                if (r < 0 || r >= nstar) break;
+                run_p = __longlong_as_double(sorted[r]);
+            } else if (enabled) {  // (a bad profile: the products were still formed)
+                run_p = __longlong_as_double(key[(size_t)b * K + k]);
+            } else {
                 run_p = run_p * survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0);
-                e += run_p;
             }
-            expected_tokens[b] = e;
+            L = k + 1;
+            e += run_p;
         }
+        verify_len[b] = L;
+        if (expected_tokens) expected_tokens[b] = e;
     }
 }
 
-hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, hipStream_t s) {
-    schedule_kernel<<<1, kSchedThreads, 0, s>>>(a.B, a.K, a.conf_logits, a.draft_len, a.n_knots,
-                                                 a.knot_tokens, a.knot_tps, a.enabled,
-                                                 a.conf_inv_temp, a.verify_len,
-                                                 a.expected_tokens, status);
+hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, long long *key,
+                           int *rank, hipStream_t s) {
+    if (a.enabled) {
+        schedule_prepare_kernel<<<(a.B + kPrepThreads - 1) / kPrepThreads, kPrepThreads, 0, s>>>(
+            a.B, a.K, a.conf_logits, a.draft_len, a.conf_inv_temp, key, rank);
+        const dim3 grid((unsigned)((a.B * a.K + kRankThreads - 1) / kRankThreads),
+                        (unsigned)((a.B + kRankRuns - 1) / kRankRuns));
+        schedule_rank_kernel<<<grid, kRankThreads, 0, s>>>(a.B, a.K, key, rank);
+    }
+    schedule_select_kernel<<<1, kSchedThreads, 0, s>>>(
+        a.B, a.K, a.conf_logits, a.draft_len, a.n_knots, a.knot_tokens, a.knot_tps, a.enabled,
+        a.conf_inv_temp, key, rank, a.verify_len, a.expected_tokens, status);
     return hipGetLastError();
 }
 

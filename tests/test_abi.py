@@ -59,7 +59,10 @@ def test_workspace_queries_and_strings(lib):
     lib.dspark_status_string.restype = C.c_char_p
     assert lib.dspark_draft_workspace_size(256, 16, 151936, 256) > 256 * 4
     assert lib.dspark_verify_workspace_size(256, 16, 151936, 256) > 256 * 17 * 16
-    assert lib.dspark_schedule_workspace_size(512, 16) == 256
+    # status word, then 8-byte products and 4-byte ranks of up to 8192 items
+    assert lib.dspark_schedule_workspace_size(512, 16) == 256 + 8192 * 8 + 8192 * 4
+    assert lib.dspark_schedule_workspace_size(8192, 64) == 256 + 8192 * 8 + 8192 * 4
+    assert lib.dspark_schedule_workspace_size(3, 5) == 256 + 256 + 256
     # invalid sizes give 0
     assert lib.dspark_draft_workspace_size(4, 0, 1024, 16) == 0
     assert lib.dspark_draft_workspace_size(4, 4, 1020, 16) == 0  # V % 8 != 0
