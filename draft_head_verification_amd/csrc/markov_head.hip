@@ -749,6 +749,23 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         epilogue(H1{}, t_end - 1, acc_hi, w);
     };
 
+    // A wave whose rows are all empty (past the batch, or past their drafts) keeps only its
+    // share of the workgroup's W pipeline: the same W loads into the same stages and the same
+    // barriers as `run` (one before tile t0's work, one per later tile), and no logit loads,
+    // matrix-core work or sampling.  Its wait after each issue leaves W(t+2), W(t+3) pending,
+    // so W(t+1) has landed before the barrier that opens tile t+1 (the live waves force it no
+    // later), and the barrier before each issue retires every read of the stage it refills.
+    auto run_loader = [&](auto mask_tag) {
+        tile_barrier();
+        issue_w(t0 + 3, 3, mask_tag);
+        DSPARK_WAIT_VMCNT(2 * LPW);
+        for (int t = t0 + 1; t < t_end; ++t) {
+            tile_barrier();
+            issue_w(t + 3, (t + 3 - t0) & 3, mask_tag);
+            DSPARK_WAIT_VMCNT(2 * LPW);
+        }
+    };
+
     using I0 = std::integral_constant<int, kEpiGreedy>;
     using I1 = std::integral_constant<int, kEpiSampled>;
     using I2 = std::integral_constant<int, kEpiMixed>;
@@ -786,7 +803,10 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         // only the slab holding a partial last tile needs the masked (and clamped) variant;
         // writing the corrected logits out is rare and always takes it
         const bool partial = t_end == n_tiles && p.V % kTileV != 0;
-        if constexpr (kResid) {
+        if (!wave_active) {
+            if (partial) run_loader(B1{});
+            else run_loader(B0{});
+        } else if constexpr (kResid) {
             if (partial) run(I3{}, B0{}, B1{});
             else run(I3{}, B0{}, B0{});
         } else if (p.corrected) {
