@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 METRIC = "draft+verify positions/s at V=151936,K=16,B=256; HBM GB/s vs peak"
 
 
@@ -245,18 +246,26 @@ def main():
                         "algorithmic_bytes_per_launch": (int(per_launch) if per_launch else per_launch),
                         "achieved_GBs": (round(per_launch / (avg_us * 1e-6) / 1e9, 1) if per_launch else None)})
     dom = next(k for k in kernels if k["algorithmic_bytes_per_launch"])
-    traffic = None
+    traffic = mfma_util = None
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
             ent = tj.get(args.workload, {}).get(dom["kernel"])
             if ent and ent.get("source_hash") == _kernel_source_hash():
                 traffic = ent["hbm_bytes_per_launch"]
+                mfma_util = ent.get("mfma_util_pct")
         except Exception:
-            traffic = None
+            traffic = mfma_util = None
     roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["achieved_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": traffic}
+    # the matrix cores' share of the dominant kernel when it is the bias contraction:
+    # 2 B r V bf16 flops per drafting step over the same live launch duration
+    if dom["kernel"] == "markov_head_step" and ub == 2 and r in (64, 128, 256):
+        tflops = 2.0 * B * r * V / (dom["avg_us"] * 1e-6) / 1e12
+        roofline["mfma"] = {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "rocprof_mfma_util_pct": mfma_util}
     step_bytes = sum((k["algorithmic_bytes_per_launch"] or 0) * k["launches_per_step"] for k in kernels)
 
     cpu = None

@@ -24,6 +24,8 @@ traffic the articles describe, with a vocabulary of 151936 or 262144 and rank-25
               verify length = draft length.
   headline    B=256 K=16 V=151936 r=256 bf16 base/factors, fp32 target; Zipf; noise 0.6;
               T=1; confidence as moderate; scheduling off.
+  headline_sched  the headline inputs with scheduling on against the concurrent workload's
+              knee profile.
 
 Factor entries are N(0, sd) with sd = 0.5/sqrt(r) ("std" reading).  ``strong_bias=True`` uses
 sd = sqrt(0.5/sqrt(r)) instead (the "variance" reading), which makes the Markov bias large
@@ -77,6 +79,10 @@ WORKLOADS = {
                        (1.5, 1.0, 0.15), (0.0, 0.7, 1.0), True, False, (), 105, 0xD5A0000000000005),
     "headline": Workload("headline", 256, 16, 151936, 256, BF16, BF16, F32, "zipf", (0.6, 0.6),
                          (1.5, 1.0, 0.15), (1.0,), False, False, (), 106, 0xD5A0000000000006),
+    # the headline inputs with the confidence schedule on, against the knee profile
+    "headline_sched": Workload("headline_sched", 256, 16, 151936, 256, BF16, BF16, F32, "zipf",
+                               (0.6, 0.6), (1.5, 1.0, 0.15), (1.0,), False, True, KNEE_PROFILE,
+                               106, 0xD5A0000000000006),
 }
 
 

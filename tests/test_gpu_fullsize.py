@@ -18,7 +18,7 @@ from parity import Tally, compare_draft, compare_verify, oracle_targets, TOL_EXP
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["single", "moderate", "concurrent", "ragged", "headline"]
+FULL = ["single", "moderate", "concurrent", "ragged", "headline", "headline_sched"]
 
 
 def _sample_rows(B):
