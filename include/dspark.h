@@ -164,8 +164,10 @@ typedef struct {
  * token per request, N one target position per verified token plus one per request.
  * enabled = 0: verify_len = draft_len (or K).
  * expected_tokens [B] (optional, float64) = 1 + sum_{k < verify_len[b]} P[b][k].
- * Limits: K in [1, 64]; when enabled, sum_b K_b <= 8192 and n_knots in [1, 64]; knot tokens
+ * Limits: K in [1, 64]; when enabled, B * K <= 8192 and n_knots in [1, 64]; knot tokens
  * strictly increasing and positive, throughputs positive (checked on the device).
+ * Workspace: dspark_schedule_workspace_size(B, K): the status word, then, for up to 8192
+ * items, each item's float64 prefix product and int32 rank (filled when enabled).
  */
 typedef struct {
     int32_t B, K;
