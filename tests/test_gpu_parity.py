@@ -31,13 +31,24 @@ CASES = [
     ("moderate", {"V": 2392, "r": 64}, None, True),
     ("ragged", {"V": 1208, "r": 128}, None, True),
     ("single", {"V": 1208, "r": 96}, None, True),
+    # the largest draft length (65 target rows: every verification chunk), greedy with long
+    # accepted prefixes and sampled
+    ("single", {"V": 1208, "K": 64, "B": 6}, 0.0, False),
+    ("single", {"V": 1208, "K": 64, "B": 6}, 1.0, False),
+    # targets equal to the drafter's logits (p = q): every position passes, the bonus comes
+    # from row 64 after all eight chunks
+    ("single", {"V": 1208, "K": 64, "B": 6, "noise": (0.0, 0.0)}, 0.0, False),
+    ("single", {"V": 1208, "K": 64, "B": 6, "noise": (0.0, 0.0)}, 1.0, False),
+    # two request groups of the matrix-core kernel, the second one partial
+    ("concurrent", {"V": 1208, "B": 300}, None, False),
 ]
 
 
 def _ids(c):
     name, kw, T, strong = c
     return (f"{name}-V{kw.get('V', 'full')}-T{T}-{'strong' if strong else 'std'}"
-            + (f"-K{kw['K']}" if "K" in kw else "") + (f"-r{kw['r']}" if "r" in kw else ""))
+            + (f"-K{kw['K']}" if "K" in kw else "") + (f"-r{kw['r']}" if "r" in kw else "")
+            + (f"-B{kw['B']}" if "B" in kw else "") + ("-exact" if "noise" in kw else ""))
 
 
 def run_round(w, T, strong, tally, tag, draft_len_override=None):

@@ -79,3 +79,21 @@ def test_schedule_matches_oracle(case):
     np.testing.assert_array_equal(g0["verify_len"].cpu().numpy(), dlen.numpy())
     print(f"[schedule] n*={o['n_star']} of {int(dlen.sum())} items, margin {o['margin']:.3g}",
           flush=True)
+
+
+def test_schedule_off_beyond_the_item_limit():
+    """With scheduling off the batch may exceed the 8192 ranked items (B = 2000, K = 64):
+    every request verifies its draft and the expected tokens are formed in the select
+    kernel alone."""
+    from draft_head_verification_amd import dspark as D
+    B, K = 2000, 64
+    conf, dlen = _inputs(B, K, True, "normal", seed=11)
+    kt = torch.tensor([p[0] for p in PROFILES["knee"]], dtype=torch.float64)
+    kp = torch.tensor([p[1] for p in PROFILES["knee"]], dtype=torch.float64)
+    o = oracle.schedule(conf, kt, kp, False, draft_len=dlen)
+    g = D.schedule(conf.cuda(), kt.cuda(), kp.cuda(), False, draft_len=dlen.cuda())
+    assert D.dspark_query_device_status(g["workspace"]) == 0
+    np.testing.assert_array_equal(g["verify_len"].cpu().numpy(), dlen.numpy())
+    np.testing.assert_array_equal(o["verify_len"], dlen.numpy())
+    np.testing.assert_allclose(g["expected_tokens"].cpu().numpy(), o["expected_tokens"],
+                               rtol=1e-12, atol=0)
