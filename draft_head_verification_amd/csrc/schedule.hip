@@ -67,16 +67,25 @@ constexpr int kPrepThreads = 256;
 constexpr int kRankThreads = 256;
 constexpr int kRankRuns = 32;  // request runs staged per rank workgroup
 
+// Workgroup g takes requests [g*R, g*R + R), R = 256 / K (K <= 64): every thread forms one
+// item's survival factor, then one thread per request multiplies its factors in order.
+static_assert(kMaxK <= kPrepThreads, "a request's factors fit one workgroup");
 __global__ __launch_bounds__(kPrepThreads) void schedule_prepare_kernel(
     int B, int K, const float *conf, const int32_t *draft_len, const double *inv_temp,
     long long *key, int *rank) {
-    const int b = blockIdx.x * kPrepThreads + threadIdx.x;
-    if (b >= B) return;
+    __shared__ double sv[kPrepThreads];
+    const int R = kPrepThreads / K;
+    const int t = threadIdx.x;
+    const int b0 = blockIdx.x * R;
+    if (t < R * K && b0 + t / K < B)
+        sv[t] = survival(conf[(size_t)(b0 + t / K) * K + t % K], inv_temp ? inv_temp[t % K] : 1.0);
+    __syncthreads();
+    const int b = b0 + t;
+    if (t >= R || b >= B) return;
     const int kb = sched_len(draft_len, b, K);
     double run_p = 1.0;
     for (int k = 0; k < K; ++k) {
-        if (k < kb)
-            run_p = run_p * survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0);
+        if (k < kb) run_p = run_p * sv[t * K + k];
         key[(size_t)b * K + k] = k < kb ? __double_as_longlong(run_p) : -1ll;
         rank[(size_t)b * K + k] = 0;
     }
@@ -145,23 +154,43 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     __shared__ int s_ok, s_items, s_nstar;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+    // Everything that depends on no other load goes out first and is held in registers
+    // across the barrier that orders the status word's reset before its flags: the draft
+    // lengths, the knots and (scheduling on) the items' products and ranks.
+    constexpr int kPer = kSchedMaxItems / kSchedThreads;  // B <= 8192; B*K <= 8192 when on
+    int raw_len[kPer];
+    long long ik[kPer];
+    int ir[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int b = tid + j * kSchedThreads;
+        raw_len[j] = b < B ? (draft_len ? draft_len[b] : K) : 0;
+        const int i = tid + j * kSchedThreads;
+        const bool has = enabled && i < B * K;
+        ik[j] = has ? key[i] : -1ll;
+        ir[j] = has ? rank[i] : -1;
+    }
+    const bool knot = enabled && tid < n_knots;
+    const double ktv = knot ? knot_tokens[tid] : 0.0, kpv = knot ? knot_tps[tid] : 0.0;
     if (tid == 0) {
         *status = 0u;
         s_items = 0;
     }
     __syncthreads();
     int my_items = 0;
-    for (int b = tid; b < B; b += kSchedThreads) {
-        const int raw = draft_len ? draft_len[b] : K;
-        if (raw < 0 || raw > K) atomicOr(status, DSPARK_DEV_BAD_LENGTH);
-        my_items += sched_len(draft_len, b, K);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int raw = raw_len[j];
+        if (tid + j * kSchedThreads < B) {
+            if (raw < 0 || raw > K) atomicOr(status, DSPARK_DEV_BAD_LENGTH);
+            my_items += raw < 0 ? 0 : (raw > K ? K : raw);
+        }
     }
     if (my_items) atomicAdd(&s_items, my_items);
-    if (enabled)
-        for (int i = tid; i < n_knots; i += kSchedThreads) {
-            kt[i] = knot_tokens[i];
-            kp[i] = knot_tps[i];
-        }
+    if (knot) {
+        kt[tid] = ktv;
+        kp[tid] = kpv;
+    }
     __syncthreads();
     if (tid == 0) {
         bool ok = enabled != 0;
@@ -180,12 +209,12 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
 
     if (s_ok) {
         // ranks of the items are a permutation of 0 .. n_items - 1
-        for (int i = tid; i < B * K; i += kSchedThreads) {
-            const long long k = key[i];
-            const int r = rank[i];
-            const bool item = k >= 0 && r >= 0 && r < n_items;
-            if (item) sorted[r] = k;
-            ranks[i] = item ? r : -1;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = tid + j * kSchedThreads;
+            const bool item = ik[j] >= 0 && ir[j] >= 0 && ir[j] < n_items;
+            if (item) sorted[ir[j]] = ik[j];
+            if (i < B * K) ranks[i] = item ? ir[j] : -1;
         }
         __syncthreads();
         // thread t evaluates G(n) for n in [n0, n1), a tiling of 0..n_items; its item range
@@ -245,8 +274,19 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     // request b verifies its items ranked below n* (a prefix of its draft: ranks rise along
     // it); expected tokens add up the same float64 products that were ranked
     const int nstar = s_nstar;
-    for (int b = tid; b < B; b += kSchedThreads) {
-        const int kb = sched_len(draft_len, b, K);
+    // scheduling off, with the items fitting the (otherwise unused) rank-order array: every
+    // thread forms survival factors, one per item, first
+    const bool par = !enabled && B * K <= kSchedMaxItems;
+    if (par) {
+        for (int i = tid; i < B * K; i += kSchedThreads)
+            sorted[i] = __double_as_longlong(survival(conf[i], inv_temp ? inv_temp[i % K] : 1.0));
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int b = tid + j * kSchedThreads;
+        if (b >= B) break;
+        const int kb = raw_len[j] < 0 ? 0 : (raw_len[j] > K ? K : raw_len[j]);
         double run_p = 1.0, e = 1.0;
         int L = 0;
         for (int k = 0; k < kb; ++k) {
@@ -257,7 +297,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
             } else if (enabled) {  // (a bad profile: the products were still formed)
                 run_p = __longlong_as_double(key[(size_t)b * K + k]);
             } else {
-                run_p = run_p * survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0);
+                run_p = run_p * (par ? __longlong_as_double(sorted[b * K + k])
+                                     : survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0));
             }
             L = k + 1;
             e += run_p;
@@ -270,7 +311,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, long long *key,
                            int *rank, hipStream_t s) {
     if (a.enabled) {
-        schedule_prepare_kernel<<<(a.B + kPrepThreads - 1) / kPrepThreads, kPrepThreads, 0, s>>>(
+        const int per = kPrepThreads / a.K;
+        schedule_prepare_kernel<<<(a.B + per - 1) / per, kPrepThreads, 0, s>>>(
             a.B, a.K, a.conf_logits, a.draft_len, a.conf_inv_temp, key, rank);
         const dim3 grid((unsigned)((a.B * a.K + kRankThreads - 1) / kRankThreads),
                         (unsigned)((a.B + kRankRuns - 1) / kRankRuns));
