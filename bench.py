@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--head", choices=("markov", "rnn"), default="markov",
                     help="sequential head: the default Markov head, or the optional recurrent "
                          "(GRU) head with seeded weights")
+    ap.add_argument("--flush", action="store_true",
+                    help="time every round on its own, after writing a 512 MB buffer (untimed) so "
+                         "that no input is left in L2 or the Infinity Cache; reports the median")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, run a plain device copy of BYTES bytes five "
                          "times (scales the HBM byte counters of the profiler)")
@@ -213,6 +216,22 @@ def main():
     wall = time.perf_counter() - t0
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
+    if args.flush:
+        # cold caches: each round timed alone after a 512 MB write (outside its events)
+        junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(args.steps):
+            junk.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del junk
+        times.sort()
+        ms_per_step = times[len(times) // 2]
+        ms_total = ms_per_step * args.steps
     # the same steps again with HIP events around every kernel, on the stream the kernels
     # run on, for the per-kernel durations (the roofline's launch durations)
     trace = D.Trace(capacity=64 * (args.steps + 1) + 64)
@@ -285,6 +304,7 @@ def main():
                    "B": B, "K": K, "V": V, "r": r, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "caches": "flushed before every round (median round)" if args.flush else "warm",
         "step_algorithmic_GBs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "wall_s": round(wall, 3),
         "mean_accept_len": round(float(acc.float().mean().item()), 3),
