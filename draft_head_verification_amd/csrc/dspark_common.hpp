@@ -456,21 +456,27 @@ struct DraftWs {
     int n_slabs;
 };
 
-// Verification spreads the 16-token blocks of a chunk's target rows evenly over the
-// workgroups of a launch (each takes a contiguous range of at least kRowSweep blocks of the
-// flattened rows), so a chunk keeps every CU streaming to its end whatever the number of
-// requests still being verified.  A row is then covered by at most ceil(n_blk / kRowSweep) + 1
-// workgroups; each leaves one partial in the row's slot (its index mod n_row_slabs), and the
-// workgroup that starts the row fills the slots nobody uses with empty partials.
+// Verification spreads a chunk's target rows evenly over the workgroups of a launch: every
+// row is cut into the same runs of at most kRowSweep blocks, and each workgroup takes a
+// contiguous range of the chunk's runs, so a chunk keeps every CU streaming to its end
+// whatever the number of requests still being verified.
 constexpr int kRowThreads = 256;
 constexpr int kRowBlocks = 4;    // sampler blocks per thread and sweep, loads issued together
 constexpr int kRowSweep = kRowBlocks * kRowThreads;
 constexpr int kRowGrid = 1024;   // workgroups of a row-statistics launch (4 per CU)
 constexpr int kMaxChunks = 8;    // chunks of target rows (K + 1 <= 65 rows)
+// A target row is cut into runs of 16-token blocks at fixed places (ceil(blocks / kRowSweep)
+// runs of equal length but the last), and each wave of the workgroup that takes a run leaves
+// one partial: slot run * (kRowThreads / 64) + wave.  A row's statistics then merge the same
+// partials in the same order whichever workgroups computed them.
+constexpr int kRowWaves = kRowThreads / 64;
+inline int num_row_runs(int V) {
+    const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
+    return (n_blk + kRowSweep - 1) / kRowSweep;
+}
 inline int num_row_slabs(int V, int B) {
     (void)B;
-    const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
-    return (n_blk + kRowSweep - 1) / kRowSweep + 1;
+    return num_row_runs(V) * kRowWaves;
 }
 
 struct VerifyWs {

@@ -234,36 +234,34 @@ __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V,
     }
 }
 
-// Workgroups of a row-statistics launch that share T blocks: at most the launched grid, and
-// at least kRowSweep blocks each.
-__device__ __forceinline__ long long row_groups(long long T, int grid) {
-    long long G = T / kRowSweep;
-    return G < 1 ? 1 : (G > grid ? grid : G);
-}
-
-// Chunk [k_lo, k_hi) of the target rows for the n_alive requests listed for it.  The chunk's
-// rows, flattened into one sequence of 16-token blocks (row i = list entry i / R, row k_lo +
-// i % R), are cut into G equal contiguous ranges, one per workgroup; each row segment of a
-// range leaves one partial in slot (workgroup % S) of its row.
+// Chunk [k_lo, k_hi) of the target rows for the n_alive requests listed for it.  Row i of the
+// chunk (list entry i / R, row k_lo + i % R) is cut into `runs` runs of blocks at fixed places
+// (run s: blocks [s*len, (s+1)*len), len = ceil(blocks / runs)); the chunk's n_alive*R*runs
+// runs are shared out as equal contiguous ranges, one per workgroup, and wave w of the
+// workgroup that takes run s of a row leaves its partial in slot s * kRowWaves + w.  The list
+// order (requests are appended as they survive) thus changes which workgroup computes a run
+// but not the partials, so row statistics are reproducible; and the waves never wait for one
+// another.
 template <typename YT>
 __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     int K, int V, const void *Y, uint32_t key0, uint32_t key1, int S, int k_lo, int k_hi,
     const int32_t *n_alive, const int4 *alive, Partial *row_partials, FirstChunk fc) {
-    __shared__ SampleState red[kRowThreads / 64];
     const bool first = fc.B > 0;
     if (first) first_chunk_setup(fc, K);
     const int R = k_hi - k_lo;
+    const int runs = S / kRowWaves;
     const int n_blk = (V + kSampleBlock - 1) / kSampleBlock;
-    const long long T = (long long)(first ? fc.B : *n_alive) * R * n_blk;
+    const int run_len = (n_blk + runs - 1) / runs;
+    const long long T = (long long)(first ? fc.B : *n_alive) * R * runs;
     if (T == 0) return;
-    const long long G = row_groups(T, gridDim.x);
+    const long long G = T < (long long)gridDim.x ? T : (long long)gridDim.x;
     const long long w = blockIdx.x;
     if (w >= G) return;  // uniform
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const long long g1 = (w + 1) * T / G;
-    for (long long gb = w * T / G; gb < g1;) {  // uniform: one row segment per pass
-        const long long ri = gb / n_blk, row_begin = ri * n_blk;
-        const long long seg_end = g1 < row_begin + n_blk ? g1 : row_begin + n_blk;
+    for (long long gr = w * T / G; gr < g1; ++gr) {  // uniform: one run per pass
+        const long long ri = gr / runs;
+        const int run = (int)(gr % runs);
         const int4 rec = first ? make_req_rec((int)(ri / R), K, fc.verify_len, fc.temperature,
                                               fc.req_id)
                                : alive[ri / R];
@@ -271,33 +269,16 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
         const ReqInfo info = req_info(rec);
         if (k <= info.L) {  // rows past L are not verified
             const size_t row = (size_t)rec.x * (K + 1) + k;
+            const int blk_lo = min(n_blk, run * run_len), blk_hi = min(n_blk, blk_lo + run_len);
             SampleState st = sample_state_init();
-            row_slab_stats<YT>(Y, row, V, (int)(gb - row_begin), (int)(seg_end - row_begin), info,
-                               !info.greedy && k == info.L, k, key0, key1, st);
+            row_slab_stats<YT>(Y, row, V, blk_lo, blk_hi, info, !info.greedy && k == info.L, k,
+                               key0, key1, st);
             for (int mask = 1; mask < 64; mask <<= 1) {
                 const SampleState o = shfl_xor_state(st, mask);
                 merge_into(st, o, info.greedy);
             }
-            if (lane == 0) red[wave] = st;
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                SampleState a = red[0];
-                for (int i = 1; i < kRowThreads / 64; ++i) merge_into(a, red[i], info.greedy);
-                row_partials[row * S + (int)(w % S)] = to_partial(a);
-            }
-            if (gb == row_begin) {
-                // this workgroup starts the row: the row's workgroups are w .. w_last, and the
-                // slots none of them takes get empty partials
-                const long long w_last = ((row_begin + n_blk) * G - 1) / T;
-                const Partial none = to_partial(sample_state_init());
-                for (int sl = threadIdx.x; sl < S; sl += kRowThreads) {
-                    const long long first = w + (((long long)sl - w % S) + S) % S;
-                    if (first > w_last) row_partials[row * S + sl] = none;
-                }
-            }
-            __syncthreads();  // red is reused by the next segment
+            if (lane == 0) row_partials[row * S + run * kRowWaves + wave] = to_partial(st);
         }
-        gb = seg_end;
     }
 }
 
@@ -532,10 +513,9 @@ hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, i
     if (chunk < 0 || chunk >= n) return hipErrorInvalidValue;
     const int k_lo = bounds[chunk], k_hi = bounds[chunk + 1];
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
-    // enough workgroups for every request of the chunk; the kernel uses fewer when fewer are
-    // listed
-    const long long n_blk = (a.V + kSampleBlock - 1) / kSampleBlock;
-    long long grid = (long long)a.B * (k_hi - k_lo) * n_blk / kRowSweep;
+    // enough workgroups for every run of every request of the chunk; the kernel uses fewer
+    // when fewer are listed
+    long long grid = (long long)a.B * (k_hi - k_lo) * (ws.n_row_slabs / kRowWaves);
     grid = grid < 1 ? 1 : (grid > kRowGrid ? kRowGrid : grid);
     const int4 *list = alive_list(ws, chunk, a.B);
     const int32_t *cnt = ws.n_alive + chunk;

@@ -133,6 +133,32 @@ def test_deterministic_across_runs():
         assert torch.equal(a, b)
 
 
+def test_schedule_and_verify_deterministic_across_runs():
+    """The schedule (ranks summed with atomics) and the verification (chunked, with a
+    residual pass) give bit-identical results when run twice on the same inputs."""
+    from draft_head_verification_amd import dspark as D
+    w = synth.shrink(synth.WORKLOADS["concurrent"], V=1208, B=300)
+    inp = synth.make_inputs(w)
+    g = to_device(inp)
+    d = D.draft_block(g["Z"], g["U"], g["W"], g["prev_token"], g["temperature"], inp["seed"],
+                      req_id=g["req_id"], want_corrected=True)
+    Y = d["corrected"].float()
+    Y = torch.cat([Y, Y[:, -1:]], 1)  # a bonus row: any target logits will do here
+    Y = (Y + 0.5 * torch.randn(Y.shape, generator=torch.Generator(device="cuda").manual_seed(5),
+                               device="cuda")).to(torch.bfloat16).contiguous()
+    outs = []
+    for _ in range(2):
+        s = D.schedule(g["conf_logits"], g["knot_tokens"], g["knot_tps"], True)
+        v = D.verify(Y, d["tokens"], d["q_tok"], d["q_lse"], g["Z"], g["U"], g["W"],
+                     g["prev_token"], s["verify_len"], g["temperature"], inp["seed"],
+                     req_id=g["req_id"])
+        outs.append([t.cpu() for t in (s["verify_len"], s["expected_tokens"], v["accept_len"],
+                                       v["next_token"], v["p_tok"])])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    assert int(outs[0][0].sum()) < w.B * w.K  # the schedule cut some suffixes
+
+
 def test_device_status_flags_bad_inputs():
     from draft_head_verification_amd import dspark as D
     w = synth.WORKLOADS["tiny"]
