@@ -259,12 +259,16 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
     if (w >= G) return;  // uniform
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const long long g1 = (w + 1) * T / G;
+    long long rec_i = -1;  // list entry of `rec` (consecutive runs mostly share a row)
+    int4 rec = make_int4(0, 0, 0, 0);
     for (long long gr = w * T / G; gr < g1; ++gr) {  // uniform: one run per pass
         const long long ri = gr / runs;
         const int run = (int)(gr % runs);
-        const int4 rec = first ? make_req_rec((int)(ri / R), K, fc.verify_len, fc.temperature,
-                                              fc.req_id)
-                               : alive[ri / R];
+        if (ri / R != rec_i) {
+            rec_i = ri / R;
+            rec = first ? make_req_rec((int)rec_i, K, fc.verify_len, fc.temperature, fc.req_id)
+                        : alive[rec_i];
+        }
         const int k = k_lo + (int)(ri % R);
         const ReqInfo info = req_info(rec);
         if (k <= info.L) {  // rows past L are not verified
