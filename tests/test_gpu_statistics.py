@@ -48,3 +48,60 @@ def test_gpu_round_output_law_equals_target(T):
     assert stats.chisquare(np.bincount(nt[full], minlength=V), pb * full.sum()).pvalue > 1e-4
     # the draft alone does not follow p_1, so the test has power
     assert stats.chisquare(np.bincount(toks[:, 0], minlength=V), p1 * n).pvalue < 1e-6
+
+
+def _binned(tokens, hot, V):
+    """Counts of the hot tokens, then one bin for every other token."""
+    counts = np.bincount(tokens, minlength=V)
+    return np.append(counts[hot], counts.sum() - counts[hot].sum())
+
+
+def _binned_p(p, hot):
+    return np.append(p[hot], 1.0 - p[hot].sum())
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_gpu_round_output_law_matrix_core_path(T):
+    """The same laws through the matrix-core head (bfloat16 factors, rank 64) on a vocabulary
+    of 2392 tokens: 37 full 64-token tiles and a short one, spread over several vocabulary
+    slabs, so the block race is merged across lanes, tiles, slabs and the reduction.  Forty
+    hot tokens, placed across the tiles (the short one included), carry most of the mass; the
+    other tokens share one bin."""
+    from draft_head_verification_amd import dspark as D
+    n, V, r, K = 1 << 17, 2392, 64, 2
+    g = torch.Generator().manual_seed(77)
+    hot = np.sort(torch.randperm(V - 24, generator=g)[:39].numpy())
+    hot = np.append(hot, V - 5)  # one hot token in the short last tile
+    base = torch.full((K, V), -4.0)
+    base[:, hot] = 2.0 + torch.randn(K, len(hot), generator=g)
+    U = (0.3 * torch.randn(V, r, generator=g)).to(torch.bfloat16)
+    W = (0.3 * torch.randn(V, r, generator=g)).to(torch.bfloat16)
+    # the drafter's logits for every position follow from the committed token 7 and the
+    # draft chain, so the target rows are drawn independently of them
+    Yrow = torch.cat([base, base[-1:]], 0) + 0.8 * torch.randn(K + 1, V, generator=g)
+    dev = "cuda"
+    Z = base.to(torch.bfloat16).to(dev).expand(n, K, V).contiguous()
+    Y = Yrow.float().to(dev).expand(n, K + 1, V).contiguous()
+    U, W = U.to(dev), W.to(dev)
+    prev = torch.full((n,), 7, dtype=torch.int32, device=dev)
+    temp = torch.full((n,), T, device=dev)
+    d = D.draft_block(Z, U, W, prev, temp, 977)
+    v = D.verify(Y, d["tokens"], d["q_tok"], d["q_lse"], Z, U, W, prev,
+                 torch.full((n,), K, dtype=torch.int32, device=dev), temp, 977)
+    a = v["accept_len"].cpu().numpy()
+    nt = v["next_token"].cpu().numpy()
+    toks = d["tokens"].cpu().numpy()
+    T32 = float(np.float32(T))
+    p = [torch.softmax(Yrow[k].double() / T32, 0).numpy() for k in range(K + 1)]
+    first = np.where(a >= 1, toks[:, 0], nt)
+    assert stats.chisquare(_binned(first, hot, V), _binned_p(p[0], hot) * n).pvalue > 1e-4
+    sel = a >= 1
+    second = np.where(a[sel] >= 2, toks[sel, 1], nt[sel])
+    assert stats.chisquare(_binned(second, hot, V),
+                           _binned_p(p[1], hot) * sel.sum()).pvalue > 1e-4
+    full = a == K
+    assert full.sum() > 1000
+    assert stats.chisquare(_binned(nt[full], hot, V),
+                           _binned_p(p[K], hot) * full.sum()).pvalue > 1e-4
+    # the draft alone does not follow p_1, so the test has power
+    assert stats.chisquare(_binned(toks[:, 0], hot, V), _binned_p(p[0], hot) * n).pvalue < 1e-6
