@@ -36,6 +36,9 @@ CASES = [  # B, K, ragged, conf kind, profile
     (512, 16, True, "zeros", "irregular"),
     (8192, 1, False, "ties", "knee"),
     (1000, 8, True, "normal", "linear"),
+    (128, 64, True, "ties", "knee"),   # the largest draft length, 8192 items
+    (1, 64, False, "normal", "irregular"),
+    (300, 3, True, "zeros", "linear"),
 ]
 
 
