@@ -24,6 +24,8 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
 STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESIDUAL, STREAM_BONUS = 0, 1, 2, 3
+# samplers: the per-token Gumbel-max (the definition), and the optional two-level block race
+SAMPLERS = {"token": 0, "block16": 1}
 
 _lib = None
 
@@ -58,10 +60,12 @@ def lib() -> C.CDLL:
         L.oracle_two_level_sample.restype = i32
         L.oracle_two_level_sample.argtypes = [i32, p, u64, C.c_uint32, C.c_uint32, C.c_uint32,
                                               C.c_uint32, p]
+        L.oracle_token_sample.restype = i32
+        L.oracle_token_sample.argtypes = [i32, p, u64, C.c_uint32, C.c_uint32, C.c_uint32, p]
         L.oracle_corrected_row.argtypes = [i32, i32, i32, p, i32, p, p, i32, p]
         L.oracle_draft_block.restype = i32
         L.oracle_draft_block.argtypes = [i32, i32, i32, i32, i32, p, i32, p, p, p, p, p, p, u64,
-                                         p, i32, p, p, p, p, p]
+                                         p, i32, p, p, p, p, p, i32]
         L.oracle_profile.restype = C.c_double
         L.oracle_profile.argtypes = [i32, p, p, C.c_double]
         L.oracle_schedule.restype = i32
@@ -72,17 +76,17 @@ def lib() -> C.CDLL:
         L.oracle_ece.argtypes = [i32, p, p, i32]
         L.oracle_verify.restype = i32
         L.oracle_verify.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, i32, p, i32, p, p, p, p,
-                                    p, p, u64, p, i32, p, p, p, p]
+                                    p, p, u64, p, i32, p, p, p, p, i32]
         L.oracle_gru_cell.argtypes = [i32, p, p, p, p, p, p, p]
         L.oracle_float_to_bf16.restype = C.c_uint16
         L.oracle_float_to_bf16.argtypes = [C.c_float]
         L.oracle_corrected_row_operand.argtypes = [i32, i32, i32, p, p, i32, p, p]
         L.oracle_draft_block_head.restype = i32
         L.oracle_draft_block_head.argtypes = [i32, i32, i32, i32, i32, p, i32, p, p, p, p, p, p,
-                                              p, p, p, p, u64, p, i32, p, p, p, p, p, p]
+                                              p, p, p, p, u64, p, i32, p, p, p, p, p, p, i32]
         L.oracle_verify_head.restype = i32
         L.oracle_verify_head.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, i32, p, i32, p,
-                                         p, p, p, p, p, p, u64, p, i32, p, p, p, p]
+                                         p, p, p, p, p, p, u64, p, i32, p, p, p, p, i32]
         L.oracle_num_threads.restype = i32
         _lib = L
     return _lib
@@ -173,6 +177,14 @@ def block_uniform(seed, req, pos, beta, stream):
     return lib().oracle_block_uniform(C.c_uint64(seed), req, pos, beta, stream)
 
 
+def token_sample(log_w, seed, req, pos, stream):
+    """Per-token Gumbel-max draw argmax_v(log_w_v + G_v) on `stream` -> (token, margin)."""
+    a = _np(log_w, np.float64)
+    gap = np.zeros(1, np.float64)
+    x = lib().oracle_token_sample(len(a), _ptr(a), C.c_uint64(seed), req, pos, stream, _ptr(gap))
+    return int(x), float(gap[0])
+
+
 def two_level_sample(log_w, seed, req, pos, race_stream, within_stream):
     """Two-level Gumbel-max draw from log-weights log_w [n] -> (token, margin)."""
     a = _np(log_w, np.float64)
@@ -230,8 +242,11 @@ def float_to_bf16(x):
 
 
 def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=None, rows=None,
-                want_corrected=False, gru=None):
+                want_corrected=False, gru=None, sampler="token"):
     """Draft tokens for a block (see oracle_draft_block_head in dspark_oracle.c).
+
+    sampler: "token" (the per-token Gumbel-max, the definition) or "block16" (the optional
+    two-level block race).
 
     Z [B,K,V] (float32 or bfloat16), U [V,r], W [V,r] (row v = column v of the r x V factor),
     prev_token [B], temperature [B], draft_len [B] or None (= K), req_id [B] or None (= b).
@@ -268,7 +283,7 @@ def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=N
                                        *(_ptr(x) for x in g), _ptr(prev), _ptr(dlen), _ptr(temp),
                                        _ptr(req), C.c_uint64(seed), _ptr(sub_rows), n,
                                        _ptr(tokens), _ptr(q_tok), _ptr(q_lse), _ptr(corrected),
-                                       _ptr(gap), _ptr(state))
+                                       _ptr(gap), _ptr(state), SAMPLERS[sampler])
     if st != 0:
         raise ValueError("oracle_draft_block: token index out of range")
     return dict(tokens=tokens, q_tok=q_tok, q_lse=q_lse, gap=gap, corrected=corrected,
@@ -327,8 +342,10 @@ def ece(s, y, n_bins=10):
 
 
 def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature, seed,
-           req_id=None, rows=None, head_state=None):
+           req_id=None, rows=None, head_state=None, sampler="token"):
     """Rejection-sampling verification (see oracle_verify_head in dspark_oracle.c).
+
+    sampler: "token" (per-token Gumbel-max draws) or "block16" (the two-level block race).
 
     Y [B,K+1,V] (float32 or bfloat16); draft_tokens [B,K]; q_tok, q_lse [B,K] (taken as
     float32, the precision the draft hands over); Z, U, W, prev_token as for draft_block;
@@ -368,7 +385,8 @@ def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, tempe
     st = lib().oracle_verify_head(n, K, V, r, ydt, _ptr(y), _ptr(toks), _ptr(qt), _ptr(ql), zdt,
                                   _ptr(z), udt, _ptr(u), _ptr(w), _ptr(hs), _ptr(prev), _ptr(vl),
                                   _ptr(temp), _ptr(req), C.c_uint64(seed), _ptr(sub_rows), n,
-                                  _ptr(acc), _ptr(nxt), _ptr(p_tok), _ptr(diag))
+                                  _ptr(acc), _ptr(nxt), _ptr(p_tok), _ptr(diag),
+                                  SAMPLERS[sampler])
     if st != 0:
         raise ValueError("oracle_verify: token index out of range")
     return dict(accept_len=acc, next_token=nxt, p_tok=p_tok, accept_margin=diag[:, 0],

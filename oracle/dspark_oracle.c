@@ -40,20 +40,26 @@
  *  - Random numbers: Philox4x32 with 10 rounds (Salmon et al., SC'11), key = (seed low word,
  *    seed high word), counter = (v >> 2, position, request key, stream), output word v & 3,
  *    uniform = ((word >> 8) + 0.5) * 2^-24, which lies strictly inside (0, 1).
- *    Streams: 0 / 4 draft sampling (block race / within the block), 1 accept test (v = 0),
- *    2 / 5 residual resampling, 3 / 6 bonus.
- *  - Sampling a token from weights w_v = exp(a_v) (the pages fix only the law, not how the
- *    draw is made): a two-level Gumbel-max.  The vocabulary is cut into blocks of 16
- *    consecutive ids (the last one may be shorter); block beta gets the log-weight
- *    A_beta = log sum_{v in beta} w_v and the race score A_beta + G_beta, where G_beta is the
- *    Gumbel draw of block beta on the race stream (block uniforms: see oracle_block_uniform);
- *    the best block wins, and inside it the token with the best a_v + G_v, G_v the Gumbel draw
- *    of token v on the within stream.  The block race picks beta with probability
- *    W_beta / sum W and the second step v with probability w_v / W_beta, so the token has
- *    probability w_v / sum w, the law of one Gumbel-max over all tokens.
+ *    Streams: 0 draft sampling, 1 accept test (v = 0), 2 residual resampling, 3 bonus
+ *    (4 / 5 / 6: within-block draws of the optional two-level sampler).
+ *  - Sampling a token from weights w_v = exp(a_v) (the pages fix the law: the draft token follows
+ *    the drafter's softmax, the emitted token the target's): the plain Gumbel-max draw keyed per
+ *    token, x = argmax_v (a_v + G_v), G_v = -log(-log u_v) with u_v the uniform of token v on the
+ *    draw's stream at its position (streams: 0 draft, 2 residual, 3 bonus).  Tokens of weight 0
+ *    (a_v = -inf) are never drawn; exact ties go to the lowest index.
+ *    Optional second mode (the library's cheaper opt-in sampler, defined here so that it can be
+ *    checked too; it keeps the law but not the per-token keying): a two-level Gumbel-max.  The
+ *    vocabulary is cut into blocks of 16 consecutive ids (the last one may be shorter); block
+ *    beta gets the log-weight A_beta = log sum_{v in beta} w_v and the race score
+ *    A_beta + G_beta, where G_beta is the Gumbel draw of block beta on the race stream (block
+ *    uniforms: see oracle_block_uniform); the best block wins, and inside it the token with the
+ *    best a_v + G_v, G_v the Gumbel draw of token v on the within stream.  The block race picks
+ *    beta with probability W_beta / sum W and the second step v with probability w_v / W_beta,
+ *    so the token has probability w_v / sum w, the law of one Gumbel-max over all tokens.
+ *    Streams of that mode: race 0 / 2 / 3 (draft / residual / bonus), within 4 / 5 / 6.
  *  - Accept test: u * q(x) < p(x)  (equivalent to u < p/q for q > 0; p >= q always accepts).
- *  - Residual: r_v = max(0, p_v - q_v); the correction is the two-level draw from the
- *    weights r (residual streams); if every r_v is 0 it is the same draw from p.
+ *  - Residual: r_v = max(0, p_v - q_v); the correction is the draw from the weights r (residual
+ *    stream); if every r_v is 0 it is the same draw from p.
  *  - Schedule: survival s = 1/(1+exp(-C)); P = running product over positions; rank all
  *    (request, position) items by (P desc, position asc, request asc); for n = 0..sum K_b
  *    E(n) = B + sum of the top-n P, N(n) = B + n, G(n) = E(n) * T(N(n)) / N(n) with T the
@@ -83,6 +89,10 @@
 
 /* tokens per block of the two-level sampler */
 #define ORACLE_SAMPLE_BLOCK 16
+
+/* sampler modes: the per-token Gumbel-max (the definition) and the optional two-level race */
+#define ORACLE_SAMPLER_TOKEN 0
+#define ORACLE_SAMPLER_BLOCK16 1
 
 /* ------------------------------------------------------------------------------------ */
 /* element access                                                                         */
@@ -219,6 +229,40 @@ int oracle_two_level_sample(int n, const double *a, uint64_t seed, uint32_t req,
     return x;
 }
 
+/*
+ * Per-token Gumbel-max draw from log-weights a[0..n) (-inf = weight 0; at least one finite):
+ * x = argmax_v (a_v + G_v), G_v the Gumbel draw of token v on `stream` at position pos, lowest
+ * index on exact ties.  P(x = v) = exp(a_v) / sum exp(a) (Gumbel, 1954; the "Gumbel-max trick").
+ * *gap (optional) receives the winner's margin over the runner-up, so that tests can recognise
+ * near-ties.
+ */
+int oracle_token_sample(int n, const double *a, uint64_t seed, uint32_t req, uint32_t pos,
+                        uint32_t stream, double *gap)
+{
+    double *score = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int v = 0; v < n; ++v)
+        score[v] = (a[v] == -INFINITY) ? -INFINITY
+                                       : a[v] + oracle_gumbel(seed, req, pos, (uint32_t)v, stream);
+    int x = argmax_double(score, n, gap);
+    free(score);
+    return x;
+}
+
+/* One draw of the round (kind 0 draft, 1 residual, 2 bonus) with the selected sampler. */
+static int sample_draw(int sampler, int n, const double *a, uint64_t seed, uint32_t req,
+                       uint32_t pos, int kind, double *gap)
+{
+    static const uint32_t token_stream[3] = {ORACLE_STREAM_DRAFT, ORACLE_STREAM_RESIDUAL,
+                                             ORACLE_STREAM_BONUS};
+    static const uint32_t within_stream[3] = {ORACLE_STREAM_DRAFT_WITHIN,
+                                              ORACLE_STREAM_RESIDUAL_WITHIN,
+                                              ORACLE_STREAM_BONUS_WITHIN};
+    if (sampler == ORACLE_SAMPLER_BLOCK16)
+        return oracle_two_level_sample(n, a, seed, req, pos, token_stream[kind],
+                                       within_stream[kind], gap);
+    return oracle_token_sample(n, a, seed, req, pos, token_stream[kind], gap);
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Markov sequential head                                                                 */
 /* ------------------------------------------------------------------------------------ */
@@ -348,14 +392,15 @@ static double log_sum_exp(const double *s, int n)
  *   c = corrected row (above): the Markov head from U[prev], or, when the GRU weights are
  *       given (gru_wi non-NULL, all four then required), the recurrent head's operand a_k;
  *   T = 0: x = argmax c, q_tok = 1, q_lse = 0;
- *   T > 0: s = c / T, lse = log sum exp s, x = two-level Gumbel-max draw from s (draft
- *          streams), q_tok = exp(s_x - lse), q_lse = lse.
+ *   T > 0: s = c / T, lse = log sum exp s, x = Gumbel-max draw from s on the draft stream
+ *          (per token, or the two-level race when sampler = ORACLE_SAMPLER_BLOCK16),
+ *          q_tok = exp(s_x - lse), q_lse = lse.
  * Positions k >= K_b get x = -1, q_tok = 0, q_lse = 0.
  * Arrays are full-size ([B][K] / [B][K][V]); only the listed requests are written.
  * corrected (optional, [B][K][V]) receives the float corrected logits.
  * gap (optional, [B][K]) receives the winning score's margin over the runner-up
- * (c for greedy; the smaller margin of the sampler's two decisions) so that near-ties can be
- * recognised by the tests.
+ * (c for greedy; the perturbed score for a sampled token, the smaller margin of the two
+ * decisions of the two-level race) so that near-ties can be recognised by the tests.
  * state_out (optional, recurrent head only, [B][K][r] bfloat16 bits) receives a_k for the
  * drafted positions (other positions are left as they are).
  * Returns 0, or -1 when a token index is out of range.
@@ -367,7 +412,7 @@ int oracle_draft_block_head(int B, int K, int V, int r, int z_dtype, const void 
                             const float *temperature, const uint32_t *req_id, uint64_t seed,
                             const int32_t *rows, int n_rows, int32_t *draft_tokens,
                             double *q_tok, double *q_lse, float *corrected, double *gap,
-                            uint16_t *state_out)
+                            uint16_t *state_out, int sampler)
 {
     (void)B; /* arrays are [B][...]; only the listed rows are touched */
     int status = 0;
@@ -430,8 +475,7 @@ int oracle_draft_block_head(int B, int K, int V, int r, int z_dtype, const void 
                 for (int v = 0; v < V; ++v)
                     s[v] = (double)c[v] / T;
                 double lse = log_sum_exp(s, V);
-                x = oracle_two_level_sample(V, s, seed, req, (uint32_t)k, ORACLE_STREAM_DRAFT,
-                                            ORACLE_STREAM_DRAFT_WITHIN, &g);
+                x = sample_draw(sampler, V, s, seed, req, (uint32_t)k, 0, &g);
                 q_tok[bk] = exp(s[x] - lse);
                 q_lse[bk] = lse;
             }
@@ -455,11 +499,12 @@ int oracle_draft_block(int B, int K, int V, int r, int z_dtype, const void *Z, i
                        const void *U, const void *W, const int32_t *prev_token,
                        const int32_t *draft_len, const float *temperature, const uint32_t *req_id,
                        uint64_t seed, const int32_t *rows, int n_rows, int32_t *draft_tokens,
-                       double *q_tok, double *q_lse, float *corrected, double *gap)
+                       double *q_tok, double *q_lse, float *corrected, double *gap, int sampler)
 {
     return oracle_draft_block_head(B, K, V, r, z_dtype, Z, uw_dtype, U, W, NULL, NULL, NULL,
                                    NULL, prev_token, draft_len, temperature, req_id, seed, rows,
-                                   n_rows, draft_tokens, q_tok, q_lse, corrected, gap, NULL);
+                                   n_rows, draft_tokens, q_tok, q_lse, corrected, gap, NULL,
+                                   sampler);
 }
 
 /* ------------------------------------------------------------------------------------ */
@@ -695,10 +740,12 @@ double oracle_ece(int n, const double *s, const double *y, int n_bins)
  *              (previous token t0 for j = 0, else x_{j-1}; with head_state, [B][K][r]
  *              bfloat16 bits from a recurrent-head draft, its operand head_state[b][j]);
  *              r = max(0, p - q_j);
- *              two-level Gumbel-max draw from log r (residual streams, position j);
+ *              Gumbel-max draw from log r (residual stream, position j);
  *              if r is identically zero, the same draw from log p.
  *   If all L pass: accept_len = L and the bonus token is argmax Y[b][L] (T = 0) or the
- *   two-level draw from Y[b][L]/T with the bonus streams at position L.
+ *   Gumbel-max draw from Y[b][L]/T on the bonus stream at position L.
+ * Every draw is the per-token Gumbel-max, or the two-level race when
+ * sampler = ORACLE_SAMPLER_BLOCK16.
  * Outputs: accept_len[b], next_token[b]; p_tok (optional, [B][K]) = p(x_k) for the tested
  * positions (1 for a greedy match, 0 for a greedy mismatch); diag (optional, [B][2]) =
  * {|u - p/q| of the deciding test (inf for greedy / none), margin of the sampled correction
@@ -711,7 +758,8 @@ int oracle_verify_head(int B, int K, int V, int r, int y_dtype, const void *Y,
                        const uint16_t *head_state, const int32_t *prev_token,
                        const int32_t *verify_len, const float *temperature,
                        const uint32_t *req_id, uint64_t seed, const int32_t *rows, int n_rows,
-                       int32_t *accept_len, int32_t *next_token, double *p_tok, double *diag)
+                       int32_t *accept_len, int32_t *next_token, double *p_tok, double *diag,
+                       int sampler)
 {
     (void)B; /* arrays are [B][...]; only the listed rows are touched */
     int status = 0;
@@ -792,9 +840,8 @@ int oracle_verify_head(int B, int K, int V, int r, int y_dtype, const void *Y,
                     if (!any)
                         for (int v = 0; v < V; ++v)
                             score[v] = log(p[v]);
-                    token = oracle_two_level_sample(V, score, seed, req, (uint32_t)k,
-                                                    ORACLE_STREAM_RESIDUAL,
-                                                    ORACLE_STREAM_RESIDUAL_WITHIN, &sample_margin);
+                    token = sample_draw(sampler, V, score, seed, req, (uint32_t)k, 1,
+                                        &sample_margin);
                 }
             }
             if (!accept) {
@@ -811,9 +858,7 @@ int oracle_verify_head(int B, int K, int V, int r, int y_dtype, const void *Y,
             } else {
                 for (int v = 0; v < V; ++v)
                     score[v] = y[v] / T;
-                token = oracle_two_level_sample(V, score, seed, req, (uint32_t)L,
-                                                ORACLE_STREAM_BONUS, ORACLE_STREAM_BONUS_WITHIN,
-                                                &sample_margin);
+                token = sample_draw(sampler, V, score, seed, req, (uint32_t)L, 2, &sample_margin);
             }
         }
         accept_len[b] = a;
@@ -836,11 +881,12 @@ int oracle_verify(int B, int K, int V, int r, int y_dtype, const void *Y,
                   int z_dtype, const void *Z, int uw_dtype, const void *U, const void *W,
                   const int32_t *prev_token, const int32_t *verify_len, const float *temperature,
                   const uint32_t *req_id, uint64_t seed, const int32_t *rows, int n_rows,
-                  int32_t *accept_len, int32_t *next_token, double *p_tok, double *diag)
+                  int32_t *accept_len, int32_t *next_token, double *p_tok, double *diag,
+                  int sampler)
 {
     return oracle_verify_head(B, K, V, r, y_dtype, Y, draft_tokens, q_tok, q_lse, z_dtype, Z,
                               uw_dtype, U, W, NULL, prev_token, verify_len, temperature, req_id,
-                              seed, rows, n_rows, accept_len, next_token, p_tok, diag);
+                              seed, rows, n_rows, accept_len, next_token, p_tok, diag, sampler);
 }
 
 /* Number of threads the parallel loops above use (1 without OpenMP). */

@@ -80,15 +80,16 @@ def _tiny_block(n_req, V, r, K, seed=0, strong=1.0):
     return Z, U, W
 
 
-@pytest.mark.parametrize("T", [1.0, 0.6])
-def test_gumbel_max_sampling_follows_softmax(T):
+@pytest.mark.parametrize("T,sampler", [(1.0, "token"), (0.6, "token"), (1.0, "block16"),
+                                       (0.6, "block16")])
+def test_gumbel_max_sampling_follows_softmax(T, sampler):
     """Across 200k request keys, position 1 is distributed as softmax(c_1 / T) and position 2,
     given x_1 = a, as softmax(c_2(a) / T) -- the chain feeds the sampled token back."""
     n, V, r, K = 200_000, 40, 4, 2  # three sampler blocks, the last one 8 tokens long
     Z, U, W = _tiny_block(n, V, r, K, seed=4, strong=0.8)
     prev = torch.full((n,), 3, dtype=torch.int32)
     temp = torch.full((n,), T)
-    res = oracle.draft_block(Z, U, W, prev, temp, seed=77)
+    res = oracle.draft_block(Z, U, W, prev, temp, seed=77, sampler=sampler)
     x1 = res["tokens"][:, 0]
     T = float(np.float32(T))
     c1 = (Z[0, 0].double() + _bias64(U, W, 3)).float().double()
@@ -105,6 +106,26 @@ def test_gumbel_max_sampling_follows_softmax(T):
     c2_wrong = (Z[0, 1].double() + _bias64(U, W, 3)).float().double()
     p2_wrong = torch.softmax(c2_wrong / T, 0).numpy()
     assert stats.chisquare(obs2, p2_wrong * sel.sum()).pvalue < 1e-6
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_sampled_draft_is_keyed_per_token(T, rocrand_gumbel):
+    """Each sampled draft token is argmax_v (c_v / T + G_v) with G from rocRAND's Philox under
+    the documented keying: stream 0, position k (0-based), the request key, teacher-forced on
+    the oracle's own previous token (its corrected rows are pinned to fp64 matmul above)."""
+    w = synth.shrink(synth.WORKLOADS["tiny"], V=264)
+    inp = synth.make_inputs(w, temperature=T, strong_bias=True)
+    res = oracle.draft_block(inp["Z"], inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
+                             inp["seed"], req_id=inp["req_id"], want_corrected=True)
+    T32 = float(np.float32(T))
+    for b in range(w.B):
+        req = int(inp["req_id"][b])
+        for k in range(w.K):
+            s = res["corrected"][b, k].astype(np.float64) / T32
+            g = rocrand_gumbel(inp["seed"], req, k, w.V, 0)
+            assert res["tokens"][b, k] == int(np.argmax(s + g)), (b, k)
+            lse = np.log(np.exp(s - s.max()).sum()) + s.max()
+            assert abs(res["q_tok"][b, k] - np.exp(s[res["tokens"][b, k]] - lse)) < 1e-12
 
 
 def test_ragged_draft_lengths_mask_tail():

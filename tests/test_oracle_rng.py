@@ -5,34 +5,12 @@ implementation is checked against rocRAND's public host-callable Philox4x32-10 e
 here from its installed header and run as a separate program (nothing is copied from it).
 The uniform / Gumbel conversions are checked by their ranges and distributions.
 """
-import os
-import subprocess
-import tempfile
-
 import numpy as np
-import pytest
 from scipy import stats
 
 import oracle
 
-PIN_SRC = os.path.join(os.path.dirname(__file__), "pins", "rocrand_philox_pin.cpp")
-
-
-@pytest.fixture(scope="module")
-def rocrand_pin():
-    out = os.path.join(tempfile.gettempdir(), "dspark_rocrand_pin")
-    if not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(PIN_SRC):
-        subprocess.run(["hipcc", "-O1", PIN_SRC, "-o", out], check=True,
-                       stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
-
-    def run(keys, ctrs):
-        lines = "".join(
-            f"{k[0]:08x} {k[1]:08x} {c[0]:08x} {c[1]:08x} {c[2]:08x} {c[3]:08x}\n"
-            for k, c in zip(keys, ctrs))
-        res = subprocess.run([out], input=lines, capture_output=True, text=True, check=True)
-        return np.array([[int(w, 16) for w in ln.split()] for ln in res.stdout.strip().splitlines()],
-                        dtype=np.uint64).astype(np.uint32)
-    return run
+# the rocRAND Philox fixture (rocrand_pin) lives in conftest.py
 
 
 def test_philox_matches_rocrand(rocrand_pin):

@@ -1,7 +1,14 @@
-"""Pins for the oracle's two-level Gumbel-max sampler.
+"""Pins for the oracle's samplers.
 
-The sampler draws token v with probability w_v / sum w: a Gumbel race between 16-token
-blocks weighted by their total weight, then a Gumbel-max inside the winning block.  Checked:
+The default draw is the per-token Gumbel-max, x = argmax_v (a_v + G_v), keyed per token on
+(seed, request, position, vocabulary index, stream).  Checked:
+  * the token equals the argmax of a + G with G computed from rocRAND's Philox words under the
+    documented keying (an independent generator and a library argmax), with zero-weight tokens;
+  * the law: chi-squared against w / sum w over 150k request keys, with a power check.
+
+The optional two-level sampler draws token v with probability w_v / sum w: a Gumbel race
+between 16-token blocks weighted by their total weight, then a Gumbel-max inside the winning
+block.  Checked:
   * the block uniforms are the documented words of Philox blocks (Philox itself is pinned to
     rocRAND in test_oracle_rng), and the block -> (counter, word) map is one-to-one;
   * with at most 16 tokens (one block) the draw is the textbook Gumbel-max argmax(a + G);
@@ -16,6 +23,38 @@ import pytest
 from scipy import stats
 
 import oracle
+
+
+@pytest.mark.parametrize("n", [1, 3, 16, 57, 1000])
+def test_token_draw_is_argmax_over_rocrand_gumbels(n, rocrand_gumbel):
+    rng = np.random.default_rng(100 + n)
+    for trial in range(6):
+        seed = int(rng.integers(0, 2**63))
+        req, pos, stream = int(rng.integers(0, 5000)), int(rng.integers(0, 64)), trial % 4
+        a = rng.normal(size=n) * 2.0
+        if n > 3:
+            a[rng.choice(n, size=n // 4, replace=False)] = -np.inf  # weight 0: never drawn
+        g = rocrand_gumbel(seed, req, pos, n, stream)
+        want = int(np.argmax(np.where(np.isfinite(a), a + g, -np.inf)))
+        got, gap = oracle.token_sample(a, seed, req, pos, stream)
+        assert got == want and np.isfinite(a[got]) and gap >= 0
+
+
+def test_token_law_is_normalised_weights():
+    n_draw, V = 150_000, 56
+    rng = np.random.default_rng(6)
+    logw = rng.normal(size=V) * 1.2
+    logw[[3, 20, 21, 40]] = -np.inf
+    w = np.exp(logw)
+    p = w / w.sum()
+    obs = np.zeros(V, np.int64)
+    for req in range(n_draw):
+        obs[oracle.token_sample(logw, 17, req, 2, oracle.STREAM_DRAFT)[0]] += 1
+    assert obs[[3, 20, 21, 40]].sum() == 0
+    live = p > 0
+    assert stats.chisquare(obs[live], p[live] * n_draw).pvalue > 1e-4
+    flat = live / live.sum()
+    assert stats.chisquare(obs[live], flat[live] * n_draw).pvalue < 1e-6
 
 
 def test_block_uniform_is_documented_philox_word():

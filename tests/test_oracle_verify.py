@@ -9,7 +9,10 @@ target's; wangjunjian.com tag page, post "Speculative Decoding", steps 3-4).  Ch
   * with a chain-independent drafter, the mean accepted length is
     sum_k prod_{j<=k} alpha_j, alpha_j = sum_v min(p_j, q_j) (Monte Carlo, 4 sigma);
   * special cases: T = 0 gives the exact-match prefix and an argmax correction; q = p always
-    accepts and takes the bonus; a draft token with p = 0 is rejected at once.
+    accepts and takes the bonus; a draft token with p = 0 is rejected at once;
+  * where the random numbers come from: the per-token residual and bonus draws equal the argmax
+    of log-weight + G with G from rocRAND's Philox on the residual / bonus stream.
+Laws are checked for both samplers (per-token, and the optional two-level race).
 """
 import numpy as np
 import pytest
@@ -35,12 +38,12 @@ def _setup(n, V, r, K, T, seed=0, strong=0.7, noise=0.8, zero_head=False):
     return Z, U, W, Y, prev, temp
 
 
-def _run(Z, U, W, Y, prev, temp, L, seed=1234):
+def _run(Z, U, W, Y, prev, temp, L, seed=1234, sampler="token"):
     n, K, V = Z.shape
-    d = oracle.draft_block(Z, U, W, prev, temp, seed)
+    d = oracle.draft_block(Z, U, W, prev, temp, seed, sampler=sampler)
     vl = torch.full((n,), L, dtype=torch.int32)
     v = oracle.verify(Y, d["tokens"], d["q_tok"].astype(np.float32), d["q_lse"].astype(np.float32),
-                      Z, U, W, prev, vl, temp, seed)
+                      Z, U, W, prev, vl, temp, seed, sampler=sampler)
     return d, v
 
 
@@ -55,11 +58,12 @@ def _emitted(d, v, i):
     return out
 
 
-@pytest.mark.parametrize("T", [1.0, 0.7])
-def test_output_distribution_equals_target(T):
+@pytest.mark.parametrize("T,sampler", [(1.0, "token"), (0.7, "token"), (1.0, "block16"),
+                                       (0.7, "block16")])
+def test_output_distribution_equals_target(T, sampler):
     n, V, r, K = 200_000, 40, 4, 3  # three sampler blocks, the last one 8 tokens long
     Z, U, W, Y, prev, temp = _setup(n, V, r, K, T, seed=11)
-    d, v = _run(Z, U, W, Y, prev, temp, L=K)
+    d, v = _run(Z, U, W, Y, prev, temp, L=K, sampler=sampler)
     T32 = float(np.float32(T))
     p1 = torch.softmax(Y[0, 0].double() / T32, 0).numpy()
     p2 = torch.softmax(Y[0, 1].double() / T32, 0).numpy()
@@ -166,16 +170,47 @@ def test_zero_target_probability_rejects_immediately():
     assert np.all(v["next_token"] != d["tokens"][:, 0])
 
 
-def test_bonus_draw_uses_extra_row_position_and_bonus_streams():
-    """The bonus token is the two-level draw from Y[L] / T at position L on the bonus streams
-    (a convention of where its random numbers come from: the law alone cannot tell)."""
+@pytest.mark.parametrize("sampler", ["token", "block16"])
+def test_bonus_draw_uses_extra_row_position_and_bonus_streams(sampler, rocrand_gumbel):
+    """The bonus token is the draw from Y[L] / T at position L on the bonus stream(s) (a
+    convention of where its random numbers come from: the law alone cannot tell).  Per-token
+    mode: argmax(Y[L] / T + G) with G from rocRAND's Philox on stream 3."""
     n, V, r, K = 64, 40, 4, 3
     Z, U, W, Y, prev, temp = _setup(n, V, r, K, 1.0, seed=21, zero_head=True)
     Y = torch.cat([Z, Z[:, -1:]], 1).contiguous()  # q = p on the drafted rows: always accepted
     for L in (0, 2, 3):
-        d, v = _run(Z, U, W, Y, prev, temp, L=L, seed=99)
+        d, v = _run(Z, U, W, Y, prev, temp, L=L, seed=99, sampler=sampler)
         assert np.all(v["accept_len"] == L)
         for b in range(n):
-            want, _ = oracle.two_level_sample(Y[b, L].double().numpy(), 99, b, L,
-                                              oracle.STREAM_BONUS, oracle.STREAM_BONUS_WITHIN)
+            y = Y[b, L].double().numpy()
+            if sampler == "token":
+                want = int(np.argmax(y + rocrand_gumbel(99, b, L, V, 3)))
+            else:
+                want, _ = oracle.two_level_sample(y, 99, b, L, oracle.STREAM_BONUS,
+                                                  oracle.STREAM_BONUS_WITHIN)
             assert v["next_token"][b] == want
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_residual_draw_is_keyed_per_token(T, rocrand_gumbel):
+    """A rejected position j is resampled as argmax_v (log r_v + G_v), r = max(0, p - q_j),
+    with G from rocRAND's Philox on stream 2 at position j; p from torch's softmax of Y / T and
+    q_j from the corrected row (pinned to fp64 matmul) and the draft's own normaliser."""
+    n, V, r, K = 48, 40, 4, 3
+    Z, U, W, Y, prev, temp = _setup(n, V, r, K, T, seed=23, noise=1.5)
+    d = oracle.draft_block(Z, U, W, prev, temp, 7, want_corrected=True)
+    T32 = float(np.float32(T))
+    vl = torch.full((n,), K, dtype=torch.int32)
+    qt, ql = d["q_tok"].astype(np.float32), d["q_lse"].astype(np.float32)
+    v = oracle.verify(Y, d["tokens"], qt, ql, Z, U, W, prev, vl, temp, 7)
+    rejected = np.flatnonzero(v["accept_len"] < K)
+    assert len(rejected) > 10
+    for b in rejected:
+        j = int(v["accept_len"][b])
+        p = torch.softmax(Y[b, j].double() / T32, 0).numpy()
+        q = np.exp(d["corrected"][b, j].astype(np.float64) / T32 - float(ql[b, j]))
+        res = np.maximum(p - q, 0.0)
+        with np.errstate(divide="ignore"):
+            lw = np.where(res > 0, np.log(res), -np.inf)
+        want = int(np.argmax(lw + rocrand_gumbel(7, b, j, V, 2)))
+        assert v["next_token"][b] == want, (b, j)
