@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--head", choices=("markov", "rnn"), default="markov",
                     help="sequential head: the default Markov head, or the optional recurrent "
                          "(GRU) head with seeded weights")
+    ap.add_argument("--sampler", choices=("token", "block16"), default="token",
+                    help="how sampled tokens are drawn: the per-token Gumbel-max (default) or the "
+                         "optional two-level 16-token block race")
     ap.add_argument("--flush", action="store_true",
                     help="time every round on its own, after writing a 512 MB buffer (untimed) so "
                          "that no input is left in L2 or the Infinity Cache; reports the median")
@@ -100,7 +103,7 @@ def algorithmic_bytes(name, w, inp, acc_host, n_resid, zb, ub, yb):
     return None
 
 
-def cpu_baseline(inp, w, n_threads_hint):
+def cpu_baseline(inp, w, n_threads_hint, sampler="token"):
     """The oracle, as it stands, on a bounded sample of requests of the same workload."""
     import numpy as np
     import torch
@@ -116,7 +119,7 @@ def cpu_baseline(inp, w, n_threads_hint):
     req, dlen = inp["req_id"][:n].cpu(), inp["draft_len"][:n].cpu()
     t0 = time.perf_counter()
     od = oracle.draft_block(Zc, U, W, prev, temp, inp["seed"], draft_len=dlen, req_id=req,
-                            want_corrected=True)
+                            want_corrected=True, sampler=sampler)
     t_draft = time.perf_counter() - t0
     # targets of the sample from the oracle's own chain (not timed)
     corr = inp["Z_ext"][:n].cpu().float().clone()
@@ -128,7 +131,7 @@ def cpu_baseline(inp, w, n_threads_hint):
     Y = synth.target_logits(corr, inp["noise"][:n].cpu(), w.y_dtype)
     t1 = time.perf_counter()
     oracle.verify(Y, od["tokens"], od["q_tok"].astype(np.float32), od["q_lse"].astype(np.float32),
-                  Zc, U, W, prev, dlen, temp, inp["seed"], req_id=req, rows=rows)
+                  Zc, U, W, prev, dlen, temp, inp["seed"], req_id=req, rows=rows, sampler=sampler)
     t_verify = time.perf_counter() - t1
     positions = int(dlen.sum())
     return {"value": positions / (t_draft + t_verify), "unit": "positions/s", "cores": threads,
@@ -184,7 +187,8 @@ def main():
     corrected = torch.empty(B, K, V, device=dev)
     D.dspark_draft_block(Z, inp["U"], inp["W"], inp["prev_token"], inp["temperature"], inp["seed"],
                          toks, q_tok, q_lse, draft_len=inp["draft_len"], req_id=inp["req_id"],
-                         corrected=corrected, workspace=ws_d, gru=gru, head_state=hs)
+                         corrected=corrected, workspace=ws_d, gru=gru, head_state=hs,
+                         sampler=args.sampler)
     Y = build_targets_on_gpu(inp, toks, corrected, w)
     del corrected
     torch.cuda.empty_cache()
@@ -193,13 +197,13 @@ def main():
         D.dspark_draft_block(Z, inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
                              inp["seed"], toks, q_tok, q_lse, draft_len=inp["draft_len"],
                              req_id=inp["req_id"], workspace=ws_d, trace=trace, gru=gru,
-                             head_state=hs)
+                             head_state=hs, sampler=args.sampler)
         D.dspark_schedule(inp["conf_logits"], vlen, inp["knot_tokens"], inp["knot_tps"],
                           w.schedule, draft_len=inp["draft_len"], expected_tokens=exp_tok,
                           workspace=ws_s, trace=trace)
         D.dspark_verify(Y, toks, q_tok, q_lse, Z, inp["U"], inp["W"], inp["prev_token"], vlen,
                         inp["temperature"], inp["seed"], acc, nxt, req_id=inp["req_id"],
-                        workspace=ws_v, trace=trace, head_state=hs)
+                        workspace=ws_v, trace=trace, head_state=hs, sampler=args.sampler)
 
     for _ in range(args.warmup):
         step()
@@ -289,7 +293,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and args.head == "markov":
-        cpu = cpu_baseline(inp, w, None)
+        cpu = cpu_baseline(inp, w, None, args.sampler)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "positions/s", "n_gpus": 1,
@@ -299,8 +303,10 @@ def main():
         "config": {"workload": f"{w.name}: B={B} K={K} V={V} r={r} base/factors "
                                f"{'bf16' if zb == 2 else 'fp32'}, target {'bf16' if yb == 2 else 'fp32'}, "
                                f"T={args.temperature if args.temperature is not None else ','.join(str(t) for t in w.temperature)}, "
-                               f"schedule {'on' if w.schedule else 'off'}"
+                               f"schedule {'on' if w.schedule else 'off'}, "
+                               f"{'per-token Gumbel-max' if args.sampler == 'token' else 'two-level block-race'} sampler"
                                + (", recurrent (GRU) head" if args.head == "rnn" else ""),
+                   "sampler": args.sampler,
                    "B": B, "K": K, "V": V, "r": r, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

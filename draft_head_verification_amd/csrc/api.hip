@@ -18,6 +18,7 @@ constexpr int kMaxRank = 1024;
 constexpr int kMaxV = 1 << 30;
 
 bool valid_dtype(int d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
+bool valid_sampler(int s) { return s == DSPARK_SAMPLER_TOKEN || s == DSPARK_SAMPLER_BLOCK16; }
 
 // Records HIP events around one kernel launch when a trace is attached.
 template <typename F>
@@ -61,8 +62,8 @@ size_t draft_layout(int32_t B, int32_t K, int32_t V, int32_t r, DraftWs *ws, cha
     off += align256((size_t)B * r * sizeof(uint16_t));
     if (ws) ws->h_state = reinterpret_cast<float *>(base + off);
     off += align256((size_t)2 * B * r * sizeof(float));
-    if (ws) ws->partials = reinterpret_cast<Partial *>(base + off);
-    off += align256((size_t)B * ns * sizeof(Partial));
+    if (ws) ws->partials = reinterpret_cast<DraftPartial *>(base + off);
+    off += align256((size_t)B * ns * sizeof(DraftPartial));
     if (ws) ws->n_slabs = ns;
     return off;
 }
@@ -145,6 +146,7 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
     if (!a) return DSPARK_EINVAL;
     if (!head_sizes_ok(a->B, a->K, a->V, a->r)) return DSPARK_EINVAL;
     if (!valid_dtype(a->z_dtype) || !valid_dtype(a->uw_dtype)) return DSPARK_EDTYPE;
+    if (!valid_sampler(a->sampler)) return DSPARK_EINVAL;
     if (a->B == 0) return DSPARK_OK;
     if (!a->Z || !a->U || !a->W || !a->prev_token || !a->temperature || !a->draft_tokens ||
         !a->q_tok || !a->q_lse)
@@ -189,6 +191,7 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
     p.corrected = a->corrected;
     p.status = w.status;
     p.n_slabs = w.n_slabs;
+    p.sampler = a->sampler;
     for (int k = 0; k < a->K; ++k) {
         p.k = k;
         e = traced(a->trace, "markov_head_step", s,
@@ -250,6 +253,7 @@ dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_byt
     if (!head_sizes_ok(a->B, a->K, a->V, a->r) || a->B >= (1 << 24)) return DSPARK_EINVAL;
     if (!valid_dtype(a->y_dtype) || !valid_dtype(a->z_dtype) || !valid_dtype(a->uw_dtype))
         return DSPARK_EDTYPE;
+    if (!valid_sampler(a->sampler)) return DSPARK_EINVAL;
     if (a->B == 0) return DSPARK_OK;
     if (!a->Y || !a->draft_tokens || !a->q_tok || !a->q_lse || !a->Z || !a->U || !a->W ||
         !a->prev_token || !a->verify_len || !a->temperature || !a->accept_len || !a->next_token)

@@ -1,7 +1,8 @@
 // dspark_common.hpp -- device helpers and internal launch interfaces of libdspark.so.
 //
 // Everything here is written for gfx950 (CDNA4, wave64).  The random-number definition, the
-// sampling rule and the tie-break rule are those stated in include/dspark.h.
+// sampling rules (the per-token Gumbel-max, and the optional two-level block race) and the
+// tie-break rule are those stated in include/dspark.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,8 +14,9 @@ namespace dspark {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Philox stream ids: the block race and the within-block draw of each sampled token, and
-// the accept test.
+// Philox stream ids: the per-token draws of the draft, residual and bonus tokens (which are
+// also the race streams of the optional two-level sampler), the accept test, and the
+// within-block draws of the two-level sampler.
 constexpr uint32_t kStreamDraft = 0, kStreamAccept = 1, kStreamResidual = 2, kStreamBonus = 3,
                    kStreamDraftWithin = 4, kStreamResidualWithin = 5, kStreamBonusWithin = 6;
 constexpr int kSampleBlock = 16;  // tokens per block of the two-level sampler
@@ -94,6 +96,109 @@ __device__ __forceinline__ float exp_from_word(uint32_t word) {
 // Gumbel draw of a word in log2 units: -log2(E) = log2(e) * (-ln E).
 __device__ __forceinline__ float gumbel2_from_word(uint32_t word) {
     return -fast_log2(exp_from_word(word));
+}
+
+// E2 = -log2(u) = log2(e) * E for the uniform of `word`, accurate in relative terms (the
+// per-token draws rank tokens by w / E2, which orders them as w / E does): for d = 1 - u below
+// 2^-6 the series log2(e) (d + d^2/2 + d^3/3) (truncation < 2^-19 relative); above, -log2(u)
+// of the float u, whose rounding (at most 2^-25) is then below 2^-18 relative.
+__device__ __forceinline__ float exp2_from_word(uint32_t word) {
+    const float fm = (float)(word >> 8);
+    const float u = fmaf(fm, 0x1p-24f, 0x1p-25f);
+    // d = 1 - u = (2^25 - 2m - 1) 2^-25: 1 - m 2^-24 is exact, and so is the subtraction
+    // whenever d <= 1/2 (the only case in which d is used)
+    const float d = fmaf(fm, -0x1p-24f, 1.0f) - 0x1p-25f;
+    const float series = d * fmaf(d, fmaf(d, kLog2e / 3.0f, kLog2e / 2.0f), kLog2e);
+    return d < 0x1p-6f ? series : -fast_log2(u);
+}
+
+// ---------------------------------------------------------------------------------------
+// Per-token Gumbel-max, streamed.  Token v wins when it maximises a_v + G_v, i.e. w_v / E_v
+// with w_v = exp(a_v - base) for any common base and E_v = -log u_v.  A lane keeps its best
+// candidate as (weight against the lane's running base, E2, token); when the base rises the
+// weight is rescaled with the same factor as the running sum.  At the end the candidate's
+// score in log2 units is base + log2(w) - log2(E2) (the offset -log2(log2 e) from a_v + G_v in
+// log2 units is the same for every token) and its scaled logit a_x in log2 units is
+// base + log2(w).
+// ---------------------------------------------------------------------------------------
+
+struct TokLane {
+    float m, l;   // running base (log2 units; -inf before any live entry) and sum of weights
+    float bw, be; // best candidate: weight against the base, and its E2
+    int bi;       // its token
+};
+
+__device__ __forceinline__ TokLane tok_lane_init() {
+    TokLane t;
+    t.m = -INFINITY;
+    t.l = 0.f;
+    t.bw = 0.f;
+    t.be = 1.f;
+    t.bi = 0x7FFFFFFF;
+    return t;
+}
+
+// Candidate token v with weight w (against the lane's current base) and E2 = e: strict >, so
+// within a lane (tokens visited in increasing order) exact ties keep the lower token.
+__device__ __forceinline__ void tok_take(TokLane &t, float w, float e, int v) {
+    const bool take = w * t.be > t.bw * e;
+    t.bw = take ? w : t.bw;
+    t.be = take ? e : t.be;
+    t.bi = take ? v : t.bi;
+}
+
+// Per-token state of a row for merging: softmax statistics (m, l), the best score g, its
+// token and its scaled logit sx (both in log2 units).
+struct TokState {
+    float m, l, g, sx;
+    int idx;
+};
+
+__device__ __forceinline__ TokState tok_state_init() {
+    TokState s;
+    s.m = -INFINITY;
+    s.l = 0.f;
+    s.g = -INFINITY;
+    s.sx = -INFINITY;
+    s.idx = 0x7FFFFFFF;
+    return s;
+}
+
+__device__ __forceinline__ TokState tok_finish(const TokLane &t) {
+    TokState s;
+    s.m = t.m;
+    s.l = t.l;
+    const bool any = t.bw > 0.f;
+    const float base = (t.m == -INFINITY) ? 0.f : t.m;
+    s.sx = any ? base + fast_log2(t.bw) : -INFINITY;
+    s.g = any ? s.sx - fast_log2(t.be) : -INFINITY;
+    s.idx = any ? t.bi : 0x7FFFFFFF;
+    return s;
+}
+
+__device__ __forceinline__ TokState merge_token(TokState a, TokState b) {
+    const float mn = fmaxf(a.m, b.m);
+    const float l = (mn == -INFINITY) ? 0.f
+                                      : a.l * fast_exp2(a.m - mn) + b.l * fast_exp2(b.m - mn);
+    const bool take_b = (b.g > a.g) || (b.g == a.g && b.idx < a.idx);
+    if (take_b) {
+        a.g = b.g;
+        a.idx = b.idx;
+        a.sx = b.sx;
+    }
+    a.m = mn;
+    a.l = l;
+    return a;
+}
+
+__device__ __forceinline__ TokState shfl_xor_tok(TokState s, int mask) {
+    TokState r;
+    r.m = __shfl_xor(s.m, mask);
+    r.l = __shfl_xor(s.l, mask);
+    r.g = __shfl_xor(s.g, mask);
+    r.sx = __shfl_xor(s.sx, mask);
+    r.idx = __shfl_xor(s.idx, mask);
+    return r;
 }
 
 // Two-level sampler, block uniforms: block beta = 16 a + 4 b + c (b, c in 0..3) takes word b
@@ -238,6 +343,43 @@ __device__ __forceinline__ SampleState from_partial(const Partial &p) {
     s.g = p.g;
     s.idx = p.idx;
     return s;
+}
+
+// Partial record of a drafting row per V-slab: 32 bytes.  Per-token sampler: the TokState
+// (p = {m, l, g, idx}, sx the winner's scaled logit); two-level sampler and greedy rows: the
+// SampleState in p (sx unused).
+struct __align__(16) DraftPartial {
+    Partial p;
+    float sx, pad0, pad1, pad2;
+};
+
+__device__ __forceinline__ DraftPartial to_draft_partial(const TokState &t) {
+    DraftPartial d;
+    d.p.m = t.m;
+    d.p.l = t.l;
+    d.p.g = t.g;
+    d.p.idx = t.idx;
+    d.sx = t.sx;
+    d.pad0 = d.pad1 = d.pad2 = 0.f;
+    return d;
+}
+
+__device__ __forceinline__ DraftPartial to_draft_partial(const SampleState &s) {
+    DraftPartial d;
+    d.p = to_partial(s);
+    d.sx = 0.f;
+    d.pad0 = d.pad1 = d.pad2 = 0.f;
+    return d;
+}
+
+__device__ __forceinline__ TokState tok_from_partial(const DraftPartial &d) {
+    TokState t;
+    t.m = d.p.m;
+    t.l = d.p.l;
+    t.g = d.p.g;
+    t.idx = d.p.idx;
+    t.sx = d.sx;
+    return t;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -452,7 +594,7 @@ struct DraftWs {
     int32_t *prev_cur;   // [B] previous token of the current step
     uint16_t *a_rows;    // [B][r] bf16: left operand of the current position (matrix-core path)
     float *h_state;      // [2][B][r] recurrent head: state of the last two positions
-    Partial *partials;   // [B][n_slabs]
+    DraftPartial *partials;  // [B][n_slabs]
     int n_slabs;
 };
 
@@ -507,10 +649,11 @@ struct DraftStepParams {
     uint32_t key0, key1;
     const int32_t *prev_cur;       // [B]
     const uint16_t *a_rows;        // [B][r] gathered U rows (matrix-core path)
-    Partial *partials;             // [B][n_slabs]
+    DraftPartial *partials;        // [B][n_slabs]
     float *corrected;              // [B][K][V] or null
     uint32_t *status;
     int n_slabs;
+    int sampler;                   // dspark_sampler
 };
 
 // Whether the drafting steps run on the matrix cores, which take each request's U row from a

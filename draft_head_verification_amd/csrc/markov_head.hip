@@ -9,10 +9,13 @@
 // section on parallel drafts and the rank-256 transition correction).  Steps run left to right
 // because position k needs the token sampled at k-1 (QbitAI, section "DSpark = Eagle + DFlash").
 //
-// Sampled rows use the two-level Gumbel-max draw: a race between 16-token blocks weighted by
-// their total softmax weight (one uniform per block), then a Gumbel-max inside the winning
-// block.  The head kernels run the race; the reduction kernels recompute the 16 corrected
-// logits of the winning block and draw the token inside it.
+// Sampled rows use the per-token Gumbel-max draw by default: every token of the row gets its
+// own Philox uniform, and each lane keeps its best token (as weight / E, against the running
+// softmax base) together with the softmax statistics; the reduction kernels merge the slabs'
+// candidates and take the winner, whose scaled logit travels with it.  The optional two-level
+// sampler races 16-token blocks weighted by their total softmax weight (one uniform per block)
+// in the head kernels; its reduction kernels recompute the 16 corrected logits of the winning
+// block and draw the token inside it.
 //
 // Matrix-core path (bf16 factors, r = 64, 128 or 256):
 //   GEMM view: rows = vocabulary (M), columns = requests (N), reduction = r (K).
@@ -59,11 +62,15 @@ struct HeadParams {
     const void *Y;                  // residual: [B][K+1][V]
     const float4 *rowstats;         // residual: [B][K+1]
     const float *q_lse;             // residual: [B][K]
-    Partial *partials;              // [rows][n_slabs]
+    int sampler;                    // dspark_sampler
+    Partial *partials;              // residual: [rows][n_slabs]
+    DraftPartial *dpartials;        // draft: [rows][n_slabs]
     float *corrected;               // draft: optional [B][K][V]
     uint32_t *status;
     int n_slabs;
 };
+
+constexpr int kSampToken = DSPARK_SAMPLER_TOKEN, kSampBlock = DSPARK_SAMPLER_BLOCK16;
 
 // Per-row description resolved on the device.
 struct RowInfo {
@@ -233,13 +240,15 @@ __device__ __forceinline__ void load4(const void *base, size_t row, int V, int v
 }
 
 // Epilogue for four consecutive corrected logits c[0..3] = entries v..v+3 of one row, v a
-// multiple of 4; lanes 4j..4j+3 of the workgroup hold one 16-token sampler block and every
-// lane must call this (the block sums are exchanged between them).  `live` is false past
-// the slab end (no output, weight 0).
-template <HeadMode MODE, typename YT>
+// multiple of 4.  Per-token sampler: the lane draws its four tokens' uniforms (one Philox
+// block, counter v / 4) and keeps its best perturbed score with the token's scaled logit.
+// Two-level sampler: lanes 4j..4j+3 of the workgroup hold one 16-token sampler block and every
+// lane must call this (the block sums are exchanged between them).  `live` is false past the
+// slab end (no output, weight 0).
+template <HeadMode MODE, int SAMP, typename YT>
 __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInfo &ri, int v,
                                                bool live, const float c[4], SampleState &st,
-                                               ResidState &rs) {
+                                               TokState &ts, ResidState &rs) {
     const bool lead = (threadIdx.x & 3) == 0;  // holds the block's first token
     if constexpr (MODE == HeadMode::Draft) {
         if (p.corrected && live) {
@@ -259,6 +268,26 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
         float s[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[i] = live ? c[i] * inv : -INFINITY;
+        if constexpr (SAMP == kSampToken) {
+            SampleState ls;
+            ls.m = ts.m;
+            ls.l = ts.l;
+            lse_update4(ls, s);
+            ts.m = ls.m;
+            ts.l = ls.l;
+            const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
+                                             kStreamDraft, p.key0, p.key1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sc = s[i] - fast_log2(exp2_from_word(ph.w[i]));
+                if (sc > ts.g) {  // increasing tokens inside a lane: ties keep the lower one
+                    ts.g = sc;
+                    ts.sx = s[i];
+                    ts.idx = v + i;
+                }
+            }
+            return;
+        }
         lse_update4(st, s);
         float M = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         M = fmaxf(M, __shfl_xor(M, 1));
@@ -282,6 +311,28 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
             for (int i = 0; i < 4; ++i) y[i] = -INFINITY;
         }
         const float inv = kLog2e / ri.T;
+        if constexpr (SAMP == kSampToken) {
+            const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
+                                             kStreamResidual, p.key0, p.key1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = live ? fast_exp2(y[i] * inv - ri.lse2p) : 0.f;
+                const float rv = pv - fast_exp2(c[i] * inv - ri.qlse2);
+                const float le = fast_log2(exp2_from_word(ph.w[i]));
+                // log2 of a zero weight is -inf: never taken
+                const float sr = (live && rv > 0.f) ? fast_log2(rv) - le : -INFINITY;
+                const float sp = pv > 0.f ? fast_log2(pv) - le : -INFINITY;
+                if (sr > rs.gr) {
+                    rs.gr = sr;
+                    rs.ir = v + i;
+                }
+                if (sp > rs.gp) {
+                    rs.gp = sp;
+                    rs.ip = v + i;
+                }
+            }
+            return;
+        }
         float R = 0.f, P = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -419,6 +470,85 @@ __device__ __forceinline__ void epi_resid_pair(const float c[8], const Raw16<YT>
     race_update(rs.gp, rs.ip, 0.f, P, word, vb);
 }
 
+// Per-token sampled epilogue (drafting map): half H of the lane's 16-entry block, entries
+// v .. v + 7 (v = v0 + 8H) with their Philox words (w0: v .. v + 3, w1: v + 4 .. v + 7).  The
+// base rises to the running maximum of c * inv (taken on c and scaled once: rounding is
+// monotonic and inv > 0); each weight is exp2(c * inv - base) with one fused multiply-add and
+// feeds both the running sum and the lane's candidate.
+template <bool MASK>
+__device__ __forceinline__ void epi_token8(const float c[8], int v, int n_live, float inv,
+                                           const Philox4 &w0, const Philox4 &w1, TokLane &tl) {
+    float cm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cm[e] = (!MASK || e < n_live) ? c[e] : -INFINITY;
+    const float m8 = fmaxf(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])),
+                           fmaxf(fmaxf(cm[4], cm[5]), fmaxf(cm[6], cm[7])));
+    const float mn = fmaxf(tl.m, m8 * inv);
+    const float base = (mn == -INFINITY) ? 0.f : mn;
+    const float f = fast_exp2(tl.m - base);  // 0 before the first live entry
+    float l = tl.l * f;
+    tl.bw *= f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float w = fast_exp2(fmaf(cm[e], inv, -base));
+        l += w;
+        tok_take(tl, w, exp2_from_word(e < 4 ? w0.w[e] : w1.w[e - 4]), v + e);
+    }
+    tl.l = l;
+    tl.m = mn;
+}
+
+// Per-token residual candidates of one lane: best token for the weights r = max(p - q, 0) and,
+// as the fallback when r is identically zero, for p; weights are absolute (p and q normalised
+// by their known log-normalisers), so no running base is needed.
+struct ResTok {
+    float br, er, bp, ep;
+    int ir, ip;
+};
+
+__device__ __forceinline__ ResTok restok_init() {
+    ResTok t;
+    t.br = 0.f;
+    t.er = 1.f;
+    t.bp = 0.f;
+    t.ep = 1.f;
+    t.ir = 0x7FFFFFFF;
+    t.ip = 0x7FFFFFFF;
+    return t;
+}
+
+__device__ __forceinline__ ResidState restok_finish(const ResTok &t) {
+    ResidState s;
+    s.gr = t.br > 0.f ? fast_log2(t.br) - fast_log2(t.er) : -INFINITY;
+    s.ir = t.br > 0.f ? t.ir : 0x7FFFFFFF;
+    s.gp = t.bp > 0.f ? fast_log2(t.bp) - fast_log2(t.ep) : -INFINITY;
+    s.ip = t.bp > 0.f ? t.ip : 0x7FFFFFFF;
+    return s;
+}
+
+// Per-token residual epilogue (residual map): the lane's 8 entries v .. v + 7 of half H.
+template <typename YT, bool MASK, int H>
+__device__ __forceinline__ void epi_resid_token8(const float c[8], const Raw16<YT> &yr, int v,
+                                                 int n_live, const RowInfo &ri, const Philox4 &w0,
+                                                 const Philox4 &w1, ResTok &rt) {
+    const float inv = kLog2e / ri.T;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bool in = !MASK || e < n_live;
+        const float pv = in ? fast_exp2(fmaf(yr.get(8 * H + e), inv, -ri.lse2p)) : 0.f;  // p_v
+        const float rv = in ? fmaxf(pv - fast_exp2(fmaf(c[e], inv, -ri.qlse2)), 0.f) : 0.f;
+        const float E = exp2_from_word(e < 4 ? w0.w[e] : w1.w[e - 4]);
+        const bool tr = rv * rt.er > rt.br * E;
+        rt.br = tr ? rv : rt.br;
+        rt.er = tr ? E : rt.er;
+        rt.ir = tr ? v + e : rt.ir;
+        const bool tp = pv * rt.ep > rt.bp * E;
+        rt.bp = tp ? pv : rt.bp;
+        rt.ep = tp ? E : rt.ep;
+        rt.ip = tp ? v + e : rt.ip;
+    }
+}
+
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
 #define DSPARK_WAIT_VMCNT(n) \
     __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
@@ -433,7 +563,7 @@ __device__ __forceinline__ void tile_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <HeadMode MODE, typename ZT, typename YT, int R>
+template <HeadMode MODE, int SAMP, typename ZT, typename YT, int R>
 __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadParams p) {
     static_assert(R == 64 || R == 128 || R == 256, "matrix-core path: rank 64, 128 or 256");
     constexpr int KS = R / 32;                     // MFMA k-steps of 32
@@ -567,6 +697,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     }
     SampleState st[2] = {sample_state_init(), sample_state_init()};
     ResidState rs[2] = {resid_init(), resid_init()};
+    TokLane tl[2] = {tok_lane_init(), tok_lane_init()};  // per-token sampler, drafting
+    ResTok rt[2] = {restok_init(), restok_init()};      // per-token sampler, residual
     float gm[2] = {-INFINITY, -INFINITY};  // greedy rows of a mixed wave
     int gi[2] = {0x7FFFFFFF, 0x7FFFFFFF};
     BlockPart bp[2] = {{0.f, 0.f}, {0.f, 0.f}};
@@ -654,8 +786,10 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         constexpr int EPI = decltype(epi_tag)::value;
         constexpr bool STORE = decltype(store_tag)::value;
         constexpr bool MASK = decltype(mask_tag)::value;
-        constexpr bool WORDS = EPI != kEpiGreedy;
-        // epilogue of half H of tile t from acc, with the race words w[q] of that tile
+        constexpr bool WORDS = EPI != kEpiGreedy && SAMP == kSampBlock;
+        constexpr bool TOKEN = SAMP == kSampToken;
+        // epilogue of half H of tile t from acc, with the race words w[q] of that tile (two-level
+        // sampler); the per-token sampler draws the words of the half's 8 tokens here
         auto epilogue = [&](auto half_tag, int t, const floatx4 (&acc)[2][2], const uint32_t (&w)[2]) {
             constexpr int H = decltype(half_tag)::value;
             const int v0 = t * kTileV + 16 * g;  // drafting map: the lane's block
@@ -678,16 +812,35 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                                     make_float4(c[4 * hh], c[4 * hh + 1], c[4 * hh + 2], c[4 * hh + 3]);
                     }
                 }
+                // per-token words of the half's 8 tokens: Philox blocks (v >> 2) and (v >> 2) + 1
+                const int vt = kResid ? v8 : v0 + 8 * H;
+                auto tok_words = [&](uint32_t stream, Philox4 &a, Philox4 &b) {
+                    a = philox4x32_10((uint32_t)vt >> 2, (uint32_t)ri[q].pos, ri[q].req, stream,
+                                      p.key0, p.key1);
+                    b = philox4x32_10(((uint32_t)vt >> 2) + 1u, (uint32_t)ri[q].pos, ri[q].req,
+                                      stream, p.key0, p.key1);
+                };
                 if constexpr (EPI == kEpiGreedy) {
                     epi_greedy8<MASK>(c, v0 + 8 * H, live, st[q].m, st[q].idx);
-                } else if constexpr (EPI == kEpiSampled) {
-                    epi_sampled8<H, MASK>(c, v0, live, kLog2e / ri[q].T, w[q], st[q], bp[q]);
-                } else if constexpr (EPI == kEpiMixed) {
-                    const bool samp = ri[q].T > 0.f;
-                    epi_sampled8<H, MASK>(c, v0, live, samp ? kLog2e / ri[q].T : 1.f, w[q], st[q], bp[q]);
-                    epi_greedy8<MASK>(c, v0 + 8 * H, live, gm[q], gi[q]);
+                } else if constexpr (EPI == kEpiSampled || EPI == kEpiMixed) {
+                    const bool samp = EPI == kEpiSampled || ri[q].T > 0.f;
+                    const float inv = samp ? kLog2e / ri[q].T : 1.f;
+                    if constexpr (TOKEN) {
+                        Philox4 wa, wb;
+                        tok_words(kStreamDraft, wa, wb);
+                        epi_token8<MASK>(c, vt, live, inv, wa, wb, tl[q]);
+                    } else {
+                        epi_sampled8<H, MASK>(c, v0, live, inv, w[q], st[q], bp[q]);
+                    }
+                    if constexpr (EPI == kEpiMixed) epi_greedy8<MASK>(c, v0 + 8 * H, live, gm[q], gi[q]);
                 } else {
-                    epi_resid_pair<YT, MASK, H>(c, y[q], vb, live, ri[q], w[q], rs[q]);
+                    if constexpr (TOKEN) {
+                        Philox4 wa, wb;
+                        tok_words(kStreamResidual, wa, wb);
+                        epi_resid_token8<YT, MASK, H>(c, y[q], v8, live, ri[q], wa, wb, rt[q]);
+                    } else {
+                        epi_resid_pair<YT, MASK, H>(c, y[q], vb, live, ri[q], w[q], rs[q]);
+                    }
                 }
             }
         };
@@ -826,7 +979,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     // every global->LDS load has landed before the workgroup can exit
     DSPARK_WAIT_VMCNT(0);
     if (!wave_active) return;
-    // merge the four lanes that share a request (lane, lane^16, lane^32, lane^48)
+    // merge the four lanes that share a request (lane, lane^16, lane^32, lane^48); every lane
+    // runs every shuffle (partners hold the same request and so take the same branches)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         if constexpr (MODE == HeadMode::Draft) {
@@ -835,27 +989,29 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                 st[q].m = gm[q];
                 st[q].idx = gi[q];
             }
+            TokState ts = tok_finish(tl[q]);
 #pragma unroll
             for (int mask = 16; mask <= 32; mask <<= 1) {
                 const SampleState o = shfl_xor_state(st[q], mask);
                 merge_into(st[q], o, greedy);
+                if constexpr (SAMP == kSampToken) ts = merge_token(ts, shfl_xor_tok(ts, mask));
             }
+            if (lane < 16 && ri[q].valid)
+                p.dpartials[(size_t)rowid[q] * p.n_slabs + slab] =
+                    (SAMP == kSampToken && !greedy) ? to_draft_partial(ts) : to_draft_partial(st[q]);
         } else {
+            if constexpr (SAMP == kSampToken) rs[q] = restok_finish(rt[q]);
 #pragma unroll
             for (int mask = 16; mask <= 32; mask <<= 1)
                 rs[q] = resid_merge(rs[q], resid_shfl_xor(rs[q], mask));
-        }
-        if (lane < 16 && ri[q].valid) {
-            Partial out;
-            if constexpr (MODE == HeadMode::Draft) {
-                out = to_partial(st[q]);
-            } else {
+            if (lane < 16 && ri[q].valid) {
+                Partial out;
                 out.g = rs[q].gr;
                 out.idx = rs[q].ir;
                 out.m = rs[q].gp;
                 out.l = __int_as_float(rs[q].ip);
+                p.partials[(size_t)rowid[q] * p.n_slabs + slab] = out;
             }
-            p.partials[(size_t)rowid[q] * p.n_slabs + slab] = out;
         }
     }
 }
@@ -878,10 +1034,11 @@ __device__ __forceinline__ float factor_at<uint16_t>(const void *base, size_t id
 constexpr int kValuThreads = 256;
 constexpr int kMaxValuRank = 1024;
 
-template <HeadMode MODE, typename ZT, typename YT, typename FT>
+template <HeadMode MODE, int SAMP, typename ZT, typename YT, typename FT>
 __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p) {
     __shared__ float urow[kMaxValuRank];
     __shared__ SampleState red_st[kValuThreads / 64];
+    __shared__ TokState red_ts[kValuThreads / 64];
     __shared__ ResidState red_rs[kValuThreads / 64];
     const int slab = (int)(blockIdx.x % (unsigned)p.n_slabs);
     const int row = (int)(blockIdx.x / (unsigned)p.n_slabs);
@@ -902,6 +1059,7 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
     if (v_end > p.V) v_end = p.V;
 
     SampleState st = sample_state_init();
+    TokState ts = tok_state_init();
     ResidState rs = resid_init();
     // every lane runs every iteration: the epilogue exchanges block sums between lanes
     for (int vb = v_begin; vb < v_end; vb += 4 * kValuThreads) {
@@ -919,40 +1077,53 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
                 c[i] = z[i] + acc;
             }
         }
-        head_epilogue4<MODE, YT>(p, ri, v, live, c, st, rs);
+        head_epilogue4<MODE, SAMP, YT>(p, ri, v, live, c, st, ts, rs);
     }
     // block reduction
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool greedy = ri.T == 0.f;
+    const bool token = MODE == HeadMode::Draft && SAMP == kSampToken && !greedy;  // uniform
     for (int mask = 1; mask < 64; mask <<= 1) {
         if constexpr (MODE == HeadMode::Draft) {
-            const SampleState o = shfl_xor_state(st, mask);
-            merge_into(st, o, greedy);
+            if (token) {
+                ts = merge_token(ts, shfl_xor_tok(ts, mask));
+            } else {
+                const SampleState o = shfl_xor_state(st, mask);
+                merge_into(st, o, greedy);
+            }
         } else {
             rs = resid_merge(rs, resid_shfl_xor(rs, mask));
         }
     }
     if (lane == 0) {
         red_st[wave] = st;
+        red_ts[wave] = ts;
         red_rs[wave] = rs;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        Partial out;
         if constexpr (MODE == HeadMode::Draft) {
-            SampleState a = red_st[0];
-            for (int w = 1; w < kValuThreads / 64; ++w)
-                merge_into(a, red_st[w], greedy);
-            out = to_partial(a);
+            DraftPartial out;
+            if (token) {
+                TokState a = red_ts[0];
+                for (int w = 1; w < kValuThreads / 64; ++w) a = merge_token(a, red_ts[w]);
+                out = to_draft_partial(a);
+            } else {
+                SampleState a = red_st[0];
+                for (int w = 1; w < kValuThreads / 64; ++w) merge_into(a, red_st[w], greedy);
+                out = to_draft_partial(a);
+            }
+            p.dpartials[(size_t)row * p.n_slabs + slab] = out;
         } else {
             ResidState a = red_rs[0];
             for (int w = 1; w < kValuThreads / 64; ++w) a = resid_merge(a, red_rs[w]);
+            Partial out;
             out.g = a.gr;
             out.idx = a.ir;
             out.m = a.gp;
             out.l = __int_as_float(a.ip);
+            p.partials[(size_t)row * p.n_slabs + slab] = out;
         }
-        p.partials[(size_t)row * p.n_slabs + slab] = out;
     }
 }
 
@@ -986,15 +1157,16 @@ __global__ __launch_bounds__(256) void draft_prepare_kernel(int B, int V, int r,
     }
 }
 
-// One wave per request: merge the slabs' partials of position k, then (sampled rows) draw the
-// token inside the winning 16-token block from its recomputed corrected logits.  On the
+// One wave per request: merge the slabs' partials of position k.  Per-token sampler: the
+// winning token and its scaled logit come with the merged candidates.  Two-level sampler: draw
+// the token inside the winning 16-token block from its recomputed corrected logits.  On the
 // matrix-core path (a_rows set) it also copies the drawn token's U row for the next position.
 __global__ __launch_bounds__(256) void draft_reduce_kernel(
     int B, int K, int V, int r, int k, int z_dtype, int uw_dtype, const void *Z, const void *U,
     const void *W, const int32_t *draft_len, const float *temperature, const uint32_t *req_id,
-    uint32_t key0, uint32_t key1, const Partial *partials, int n_slabs, int32_t *prev_cur,
-    uint16_t *a_rows, const uint16_t *op_rows, int32_t *tokens, float *q_tok, float *q_lse,
-    uint32_t *status) {
+    uint32_t key0, uint32_t key1, const DraftPartial *partials, int n_slabs, int sampler,
+    int32_t *prev_cur, uint16_t *a_rows, const uint16_t *op_rows, int32_t *tokens, float *q_tok,
+    float *q_lse, uint32_t *status) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (b >= B) return;  // uniform per wave
@@ -1007,8 +1179,8 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
     const int prev = prev_cur[b];
     const uint32_t req_ld = rq[b];
     constexpr int kPer = 4;
-    Partial pp[kPer];
-    const Partial *prow = partials + (size_t)b * n_slabs;
+    DraftPartial pp[kPer];
+    const DraftPartial *prow = partials + (size_t)b * n_slabs;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) pp[i] = prow[min(lane + 64 * i, n_slabs - 1)];
 
@@ -1028,48 +1200,61 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
     }
     const float T = (lane == 0 && k == 0) ? checked_temperature(T_ld, status) : T_ld;
     const bool greedy = !(T > 0.f);
-    SampleState st = sample_state_init();
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-        if (lane + 64 * i < n_slabs) merge_into(st, from_partial(pp[i]), greedy);
-    for (int s = lane + 64 * kPer; s < n_slabs; s += 64) {
-        const SampleState o2 = from_partial(prow[s]);
-        merge_into(st, o2, greedy);
-    }
-    for (int mask = 1; mask < 64; mask <<= 1) {
-        const SampleState o2 = shfl_xor_state(st, mask);
-        merge_into(st, o2, greedy);
-    }
     // a row with no finite score (all -inf / NaN logits) has no winner: token 0, flagged,
     // so that the next step's gather stays inside U
     int x;
     float qt = 1.f, ql = 0.f;
-    if (greedy) {
-        x = st.idx;
-        if (x < 0 || x >= V) x = -1;
+    if (!greedy && sampler == kSampToken) {
+        TokState ts = tok_state_init();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (lane + 64 * i < n_slabs) ts = merge_token(ts, tok_from_partial(pp[i]));
+        for (int s = lane + 64 * kPer; s < n_slabs; s += 64) ts = merge_token(ts, tok_from_partial(prow[s]));
+        for (int mask = 1; mask < 64; mask <<= 1) ts = merge_token(ts, shfl_xor_tok(ts, mask));
+        x = (ts.g > -INFINITY && ts.idx >= 0 && ts.idx < V) ? ts.idx : -1;
+        const float lse2 = ts.m + fast_log2(ts.l);
+        qt = fast_exp2(ts.sx - lse2);
+        ql = lse2 * kLn2;
     } else {
-        const int v0 = st.idx;
-        if (v0 < 0 || v0 >= V || (v0 % kSampleBlock) != 0) {
-            x = -1;
+        SampleState st = sample_state_init();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (lane + 64 * i < n_slabs) merge_into(st, from_partial(pp[i].p), greedy);
+        for (int s = lane + 64 * kPer; s < n_slabs; s += 64) {
+            const SampleState o2 = from_partial(prow[s].p);
+            merge_into(st, o2, greedy);
+        }
+        for (int mask = 1; mask < 64; mask <<= 1) {
+            const SampleState o2 = shfl_xor_state(st, mask);
+            merge_into(st, o2, greedy);
+        }
+        if (greedy) {
+            x = st.idx;
+            if (x < 0 || x >= V) x = -1;
         } else {
-            const int e = lane & 15;
-            const bool in = v0 + e < V;
-            // left operand: U[prev] (Markov head) or the recurrent head's current operand
-            const void *op = op_rows ? static_cast<const void *>(op_rows + (size_t)b * r) : U;
-            const float c = wave_corrected16(Z, z_dtype, o, op, W, uw_dtype, r, V,
-                                             op_rows ? 0 : prev, v0);
-            const float s2 = c * (kLog2e / T);
-            const uint32_t req = req_id ? req_ld : (uint32_t)b;
-            const uint32_t w = token_word((uint32_t)(v0 + e), (uint32_t)k, req, kStreamDraftWithin,
-                                         key0, key1);
-            const float sc = in ? s2 + gumbel2_from_word(w) : -INFINITY;
-            int best = v0 + e;
-            float bsc = sc, bs2 = s2;
-            wave_argmax16(bsc, best, bs2);
-            x = (bsc > -INFINITY) ? best : -1;
-            const float lse2 = st.m + fast_log2(st.l);
-            qt = fast_exp2(bs2 - lse2);
-            ql = lse2 * kLn2;
+            const int v0 = st.idx;
+            if (v0 < 0 || v0 >= V || (v0 % kSampleBlock) != 0) {
+                x = -1;
+            } else {
+                const int e = lane & 15;
+                const bool in = v0 + e < V;
+                // left operand: U[prev] (Markov head) or the recurrent head's current operand
+                const void *op = op_rows ? static_cast<const void *>(op_rows + (size_t)b * r) : U;
+                const float c = wave_corrected16(Z, z_dtype, o, op, W, uw_dtype, r, V,
+                                                 op_rows ? 0 : prev, v0);
+                const float s2 = c * (kLog2e / T);
+                const uint32_t req = req_id ? req_ld : (uint32_t)b;
+                const uint32_t w = token_word((uint32_t)(v0 + e), (uint32_t)k, req,
+                                              kStreamDraftWithin, key0, key1);
+                const float sc = in ? s2 + gumbel2_from_word(w) : -INFINITY;
+                int best = v0 + e;
+                float bsc = sc, bs2 = s2;
+                wave_argmax16(bsc, best, bs2);
+                x = (bsc > -INFINITY) ? best : -1;
+                const float lse2 = st.m + fast_log2(st.l);
+                qt = fast_exp2(bs2 - lse2);
+                ql = lse2 * kLn2;
+            }
         }
     }
     if (lane == 0) {
@@ -1083,7 +1268,8 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
         q_tok[o] = qt;
         q_lse[o] = ql;
     }
-    // the next position's U row (x is the same in every lane; a flagged row takes token 0's)
+    // the next position's U row (a flagged row takes token 0's)
+    x = __shfl(x, 0);
     if (a_rows && k + 1 < kb) {
         const int xs = x < 0 ? 0 : x;
         const uint16_t *src = reinterpret_cast<const uint16_t *>(U) + (size_t)xs * r;
@@ -1101,36 +1287,49 @@ static bool use_mfma(int uw_dtype, int r) {
     return uw_dtype == DSPARK_BF16 && (r == 64 || r == 128 || r == 256);
 }
 
-template <HeadMode MODE, typename ZT, typename YT>
+template <HeadMode MODE, int SAMP, typename ZT, typename YT>
 static hipError_t launch_head_t(const HeadParams &p, int uw_dtype, hipStream_t s) {
     if (use_mfma(uw_dtype, p.r)) {
         const int groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
         const dim3 grid(p.n_slabs * groups), block(kMfmaWaves * 64);
         switch (p.r) {
-            case 64: markov_mfma_kernel<MODE, ZT, YT, 64><<<grid, block, 0, s>>>(p); break;
-            case 128: markov_mfma_kernel<MODE, ZT, YT, 128><<<grid, block, 0, s>>>(p); break;
-            case 256: markov_mfma_kernel<MODE, ZT, YT, 256><<<grid, block, 0, s>>>(p); break;
+            case 64: markov_mfma_kernel<MODE, SAMP, ZT, YT, 64><<<grid, block, 0, s>>>(p); break;
+            case 128: markov_mfma_kernel<MODE, SAMP, ZT, YT, 128><<<grid, block, 0, s>>>(p); break;
+            case 256: markov_mfma_kernel<MODE, SAMP, ZT, YT, 256><<<grid, block, 0, s>>>(p); break;
             default: return hipErrorInvalidValue;
         }
     } else {
         const dim3 grid((unsigned)p.n_slabs * (unsigned)p.n_rows_max), block(kValuThreads);
         if (uw_dtype == DSPARK_F32)
-            markov_valu_kernel<MODE, ZT, YT, float><<<grid, block, 0, s>>>(p);
+            markov_valu_kernel<MODE, SAMP, ZT, YT, float><<<grid, block, 0, s>>>(p);
         else
-            markov_valu_kernel<MODE, ZT, YT, uint16_t><<<grid, block, 0, s>>>(p);
+            markov_valu_kernel<MODE, SAMP, ZT, YT, uint16_t><<<grid, block, 0, s>>>(p);
     }
     return hipGetLastError();
 }
 
+template <HeadMode MODE, typename ZT, typename YT>
+static hipError_t launch_head_s(const HeadParams &p, int uw_dtype, hipStream_t s) {
+    if (p.sampler == kSampBlock) return launch_head_t<MODE, kSampBlock, ZT, YT>(p, uw_dtype, s);
+    return launch_head_t<MODE, kSampToken, ZT, YT>(p, uw_dtype, s);
+}
+
+// (drafting steps read no target logits: one instantiation per base-logit type)
 template <HeadMode MODE>
 static hipError_t launch_head(const HeadParams &p, int z_dtype, int uw_dtype, int y_dtype,
                               hipStream_t s) {
-    if (z_dtype == DSPARK_BF16) {
-        if (y_dtype == DSPARK_BF16) return launch_head_t<MODE, uint16_t, uint16_t>(p, uw_dtype, s);
-        return launch_head_t<MODE, uint16_t, float>(p, uw_dtype, s);
+    if constexpr (MODE == HeadMode::Draft) {
+        (void)y_dtype;
+        if (z_dtype == DSPARK_BF16) return launch_head_s<MODE, uint16_t, float>(p, uw_dtype, s);
+        return launch_head_s<MODE, float, float>(p, uw_dtype, s);
+    } else {
+        if (z_dtype == DSPARK_BF16) {
+            if (y_dtype == DSPARK_BF16) return launch_head_s<MODE, uint16_t, uint16_t>(p, uw_dtype, s);
+            return launch_head_s<MODE, uint16_t, float>(p, uw_dtype, s);
+        }
+        if (y_dtype == DSPARK_BF16) return launch_head_s<MODE, float, uint16_t>(p, uw_dtype, s);
+        return launch_head_s<MODE, float, float>(p, uw_dtype, s);
     }
-    if (y_dtype == DSPARK_BF16) return launch_head_t<MODE, float, uint16_t>(p, uw_dtype, s);
-    return launch_head_t<MODE, float, float>(p, uw_dtype, s);
 }
 
 static void set_factors(HeadParams &hp, const void *U, const void *W, int uw_dtype) {
@@ -1180,7 +1379,9 @@ hipError_t launch_draft_step(const DraftStepParams &d, int z_dtype, int uw_dtype
     hp.key1 = d.key1;
     hp.prev_cur = d.prev_cur;
     hp.A = d.a_rows;
-    hp.partials = d.partials;
+    hp.partials = nullptr;
+    hp.dpartials = d.partials;
+    hp.sampler = d.sampler;
     hp.corrected = d.corrected;
     hp.status = d.status;
     hp.n_slabs = d.n_slabs;
@@ -1193,7 +1394,7 @@ hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, in
     draft_reduce_kernel<<<(a.B + per_block - 1) / per_block, 64 * per_block, 0, s>>>(
         a.B, a.K, a.V, a.r, k, a.z_dtype, a.uw_dtype, a.Z, a.U, a.W, a.draft_len, a.temperature,
         a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu), (uint32_t)(a.seed >> 32), ws.partials,
-        ws.n_slabs, ws.prev_cur, draft_uses_rnn(a) ? nullptr : ws.a_rows,
+        ws.n_slabs, a.sampler, ws.prev_cur, draft_uses_rnn(a) ? nullptr : ws.a_rows,
         draft_uses_rnn(a) ? ws.a_rows : nullptr, a.draft_tokens, a.q_tok, a.q_lse, ws.status);
     return hipGetLastError();
 }
@@ -1223,6 +1424,8 @@ hipError_t launch_verify_residual(const dspark_verify_args &a, const VerifyWs &w
     hp.q_lse = a.q_lse;
     hp.S = a.head_state;
     hp.partials = ws.partials;
+    hp.dpartials = nullptr;
+    hp.sampler = a.sampler;
     hp.corrected = nullptr;
     hp.status = ws.status;
     hp.n_slabs = ws.n_slabs;

@@ -16,18 +16,22 @@
 //                    first decide launch): a fixed grid takes the
 //                    (request, row of the chunk, vocabulary slab) items in turn and streams
 //                    each slab of Y[b][k] once: softmax max / sum-exp of Y/T in log2 units,
-//                    the argmax for greedy rows, and the bonus row's block race.  Rows after
+//                    the argmax for greedy rows, and the bonus row's per-token candidates (or
+//                    its block race with the two-level sampler).  Rows after
 //                    the first rejection are never needed, so only the chunks up to it are
 //                    read; the kernel boundaries order the data between chunks.
 //   verify_decide    after every chunk but the last, one wave per listed request: merges the
 //                    chunk's slab statistics, takes its accept decisions and lists the
 //                    request for the next chunk if it is still being verified
 //   verify_finish    one wave per request: decides the last chunk, then the accepted length,
-//                    the greedy correction / the bonus draw inside its winning block, or
-//                    marks the first rejected row for a residual draw
+//                    the greedy correction / the bonus token (the merged per-token winner, or
+//                    the draw inside the winning block), or marks the first rejected row for a
+//                    residual draw
 //   (markov_head.hip) the residual rows: recompute q_j with the Markov head on the matrix
-//                    cores and run the block race of max(0, p - q_j)
-//   verify_residual_reduce  merge the race, draw the token inside the winning block
+//                    cores and keep the per-token candidates of max(0, p - q_j) and p (or run
+//                    their block races)
+//   verify_residual_reduce  merge the candidates (two-level sampler: draw the token inside
+//                    the winning block)
 #include "dspark_common.hpp"
 
 namespace dspark {
@@ -188,11 +192,16 @@ __device__ int decide_rows(int b, int k0, int k1, const ReqInfo &ri, int K, int 
 }
 
 // Statistics of one vocabulary slab of one target row (whole workgroup).  Each thread takes
-// kRowBlocks sampler blocks per sweep and issues all their loads before using any.
+// kRowBlocks sampler blocks per sweep and issues all their loads before using any.  The bonus
+// row of a sampled request also carries its draw: per-token candidates (weight against the
+// running base, E2, token), or the two-level sampler's block race.
 template <typename YT>
 __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V, int blk_lo,
-                                               int blk_hi, const ReqInfo &ri, bool bonus, int k,
-                                               uint32_t key0, uint32_t key1, SampleState &st) {
+                                               int blk_hi, const ReqInfo &ri, bool bonus,
+                                               int sampler, int k, uint32_t key0, uint32_t key1,
+                                               SampleState &st) {
+    const bool tok_bonus = bonus && sampler == DSPARK_SAMPLER_TOKEN;
+    TokLane tl = tok_lane_init();
     for (int blk = blk_lo + (int)threadIdx.x; blk < blk_hi; blk += kRowBlocks * kRowThreads) {
         Raw16<YT> y[kRowBlocks];
 #pragma unroll
@@ -219,18 +228,44 @@ __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V,
                 for (int e = 1; e < 16; ++e) m16 = fmaxf(m16, s[e]);
                 const float mn = fmaxf(st.m, m16);
                 const float base = (mn == -INFINITY) ? 0.f : mn;
-                float acc = 0.f;
+                const float f = fast_exp2(st.m - base);
+                if (tok_bonus) {  // uniform per wave: one row per workgroup pass
+                    float acc = 0.f;
+                    tl.bw *= f;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc += fast_exp2(s[e] - base);
-                st.l = st.l * fast_exp2(st.m - base) + acc;
-                st.m = mn;
-                if (bonus) {
-                    const uint32_t w = race_word((uint32_t)bb, (uint32_t)k, ri.req, kStreamBonus,
-                                                 key0, key1);
-                    race_update(st.g, st.idx, base, acc, w, v0);
+                    for (int c = 0; c < 4; ++c) {
+                        const Philox4 ph = philox4x32_10(((uint32_t)v0 >> 2) + (uint32_t)c,
+                                                         (uint32_t)k, ri.req, kStreamBonus, key0,
+                                                         key1);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float w = fast_exp2(s[4 * c + i] - base);
+                            acc += w;
+                            tok_take(tl, w, exp2_from_word(ph.w[i]), v0 + 4 * c + i);
+                        }
+                    }
+                    st.l = st.l * f + acc;
+                    st.m = mn;
+                } else {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc += fast_exp2(s[e] - base);
+                    st.l = st.l * f + acc;
+                    st.m = mn;
+                    if (bonus) {
+                        const uint32_t w = race_word((uint32_t)bb, (uint32_t)k, ri.req,
+                                                     kStreamBonus, key0, key1);
+                        race_update(st.g, st.idx, base, acc, w, v0);
+                    }
                 }
             }
         }
+    }
+    if (tok_bonus) {
+        tl.m = st.m;
+        const TokState ts = tok_finish(tl);
+        st.g = ts.g;
+        st.idx = ts.idx;
     }
 }
 
@@ -244,8 +279,8 @@ __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V,
 // another.
 template <typename YT>
 __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
-    int K, int V, const void *Y, uint32_t key0, uint32_t key1, int S, int k_lo, int k_hi,
-    const int32_t *n_alive, const int4 *alive, Partial *row_partials, FirstChunk fc) {
+    int K, int V, const void *Y, uint32_t key0, uint32_t key1, int sampler, int S, int k_lo,
+    int k_hi, const int32_t *n_alive, const int4 *alive, Partial *row_partials, FirstChunk fc) {
     const bool first = fc.B > 0;
     if (first) first_chunk_setup(fc, K);
     const int R = k_hi - k_lo;
@@ -275,8 +310,8 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows_kernel(
             const size_t row = (size_t)rec.x * (K + 1) + k;
             const int blk_lo = min(n_blk, run * run_len), blk_hi = min(n_blk, blk_lo + run_len);
             SampleState st = sample_state_init();
-            row_slab_stats<YT>(Y, row, V, blk_lo, blk_hi, info, !info.greedy && k == info.L, k,
-                               key0, key1, st);
+            row_slab_stats<YT>(Y, row, V, blk_lo, blk_hi, info, !info.greedy && k == info.L,
+                               sampler, k, key0, key1, st);
             for (int mask = 1; mask < 64; mask <<= 1) {
                 const SampleState o = shfl_xor_state(st, mask);
                 merge_into(st, o, info.greedy);
@@ -314,7 +349,7 @@ template <typename YT>
 __global__ __launch_bounds__(256) void verify_finish_kernel(
     int B, int K, int V, const void *Y, const int32_t *draft_tokens, const float *q_tok,
     const int32_t *verify_len, const float *temperature, const uint32_t *req_id, uint32_t key0,
-    uint32_t key1, int S, int c_lo, int c_hi, const Partial *row_partials,
+    uint32_t key1, int sampler, int S, int c_lo, int c_hi, const Partial *row_partials,
     int32_t *first_reject, float4 *rowstats, int32_t *accept_len, int32_t *next_token,
     float *p_tok, int32_t *n_resid, int32_t *resid_rows, uint32_t *status) {
     const int lane = threadIdx.x & 63;
@@ -358,7 +393,10 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
     // row a's statistics: merged just now, or written by an earlier launch
     if (!here) rs = rowstats[rbase + a];
     int t = __float_as_int(rs.z);
-    if (!ri.greedy) {
+    if (!ri.greedy && sampler == DSPARK_SAMPLER_TOKEN) {
+        // bonus: the merged per-token winner of row L (none when the row has no finite logit)
+        if (!(rs.w > -INFINITY)) t = -1;
+    } else if (!ri.greedy) {
         // bonus: the token inside the winning block of row L
         const int v0 = t;
         t = -1;
@@ -393,7 +431,7 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
     const int32_t *draft_tokens, const float *q_lse, const float *temperature,
     const uint32_t *req_id, uint32_t key0, uint32_t key1, const float4 *rowstats,
     const int32_t *n_resid, const int32_t *resid_rows, const Partial *partials, int n_slabs,
-    const uint16_t *head_state, int32_t *next_token, uint32_t *status, int B) {
+    const uint16_t *head_state, int sampler, int32_t *next_token, uint32_t *status, int B) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);  // = request b
     if (row >= B || *n_resid == 0) return;  // uniform per wave
@@ -449,7 +487,10 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
     const bool use_r = gr > -INFINITY;
     const int v0 = use_r ? ir : ip;
     int t = -1;
-    if (v0 >= 0 && v0 < V && v0 % kSampleBlock == 0) {
+    if (sampler == DSPARK_SAMPLER_TOKEN) {
+        // the merged per-token winner over r (or over p when r is identically zero)
+        if ((use_r || gp > -INFINITY) && v0 >= 0 && v0 < V) t = v0;
+    } else if (v0 >= 0 && v0 < V && v0 % kSampleBlock == 0) {
         const float inv = kLog2e / T;
         const uint32_t req = req_id ? req_ld : (uint32_t)b;
         int prev = (j == 0) ? pt : dt;
@@ -529,10 +570,12 @@ hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, i
                         ws.n_resid, ws.first_reject, ws.n_alive,    ws.alive};
     if (a.y_dtype == DSPARK_BF16)
         verify_rows_kernel<uint16_t><<<(unsigned)grid, kRowThreads, 0, s>>>(
-            a.K, a.V, a.Y, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials, fc);
+            a.K, a.V, a.Y, k0, k1, a.sampler, ws.n_row_slabs, k_lo, k_hi, cnt, list,
+            ws.row_partials, fc);
     else
         verify_rows_kernel<float><<<(unsigned)grid, kRowThreads, 0, s>>>(
-            a.K, a.V, a.Y, k0, k1, ws.n_row_slabs, k_lo, k_hi, cnt, list, ws.row_partials, fc);
+            a.K, a.V, a.Y, k0, k1, a.sampler, ws.n_row_slabs, k_lo, k_hi, cnt, list,
+            ws.row_partials, fc);
     return hipGetLastError();
 }
 
@@ -572,12 +615,12 @@ hipError_t launch_verify_finish(const dspark_verify_args &a, const VerifyWs &ws,
     if (a.y_dtype == DSPARK_BF16)
         verify_finish_kernel<uint16_t><<<grid, block, 0, s>>>(
             a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
-            k0, k1, ws.n_row_slabs, c_lo, c_hi, ws.row_partials, ws.first_reject, ws.rowstats,
+            k0, k1, a.sampler, ws.n_row_slabs, c_lo, c_hi, ws.row_partials, ws.first_reject, ws.rowstats,
             a.accept_len, a.next_token, a.p_tok, ws.n_resid, ws.resid_rows, ws.status);
     else
         verify_finish_kernel<float><<<grid, block, 0, s>>>(
             a.B, a.K, a.V, a.Y, a.draft_tokens, a.q_tok, a.verify_len, a.temperature, a.req_id,
-            k0, k1, ws.n_row_slabs, c_lo, c_hi, ws.row_partials, ws.first_reject, ws.rowstats,
+            k0, k1, a.sampler, ws.n_row_slabs, c_lo, c_hi, ws.row_partials, ws.first_reject, ws.rowstats,
             a.accept_len, a.next_token, a.p_tok, ws.n_resid, ws.resid_rows, ws.status);
     return hipGetLastError();
 }
@@ -589,7 +632,7 @@ hipError_t launch_verify_residual_reduce(const dspark_verify_args &a, const Veri
         a.K, a.V, a.r, a.y_dtype, a.z_dtype, a.uw_dtype, a.Y, a.Z, a.U, a.W, a.prev_token,
         a.draft_tokens, a.q_lse, a.temperature, a.req_id, (uint32_t)(a.seed & 0xFFFFFFFFu),
         (uint32_t)(a.seed >> 32), ws.rowstats, ws.n_resid, ws.resid_rows, ws.partials,
-        ws.n_slabs, a.head_state, a.next_token, ws.status, a.B);
+        ws.n_slabs, a.head_state, a.sampler, a.next_token, ws.status, a.B);
     return hipGetLastError();
 }
 

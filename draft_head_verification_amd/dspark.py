@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libdspark.so")
 DSPARK_OK, DSPARK_EINVAL, DSPARK_EDTYPE, DSPARK_EWORKSPACE, DSPARK_EHIP, DSPARK_EDEVICE = \
     0, -1, -2, -3, -4, -5
 DSPARK_F32, DSPARK_BF16 = 0, 1
+# samplers (include/dspark.h): the per-token Gumbel-max (default) and the opt-in block race
+SAMPLERS = {"token": 0, "block16": 1}
 DEV_BAD_TOKEN, DEV_BAD_TEMPERATURE, DEV_BAD_LENGTH, DEV_BAD_PROFILE = 0x1, 0x2, 0x4, 0x8
 
 
@@ -45,7 +47,7 @@ class DraftArgs(C.Structure):
                 ("seed", C.c_uint64),
                 ("draft_tokens", _p), ("q_tok", _p), ("q_lse", _p), ("corrected", _p),
                 ("trace", _p), ("gru_wi", _p), ("gru_wh", _p), ("gru_bi", _p), ("gru_bh", _p),
-                ("head_state", _p)]
+                ("head_state", _p), ("sampler", _i32)]
 
 
 class ScheduleArgs(C.Structure):
@@ -67,7 +69,7 @@ class VerifyArgs(C.Structure):
                 ("Z", _p), ("U", _p), ("W", _p), ("prev_token", _p), ("verify_len", _p),
                 ("temperature", _p), ("req_id", _p), ("seed", C.c_uint64),
                 ("accept_len", _p), ("next_token", _p), ("p_tok", _p), ("trace", _p),
-                ("head_state", _p)]
+                ("head_state", _p), ("sampler", _i32)]
 
 
 _lib.dspark_draft_workspace_size.restype = C.c_size_t
@@ -170,10 +172,20 @@ class Trace:
             out.append((name.value.decode(), float(ms.value)))
         return out
 
+    def close(self):
+        """Release the events now (also done when the object is collected)."""
+        handle, self.handle = getattr(self, "handle", None), None
+        lib = _lib
+        if handle and lib is not None:
+            lib.dspark_trace_destroy(handle)
+
     def __del__(self):
-        if getattr(self, "handle", None):
-            _lib.dspark_trace_destroy(self.handle)
-            self.handle = None
+        # at interpreter exit the module globals may already be gone: then the process is
+        # ending and the events go with it
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _trace(trace):
@@ -196,13 +208,20 @@ def dspark_schedule_workspace_size(B, K) -> int:
     return int(_lib.dspark_schedule_workspace_size(B, K))
 
 
+def _sampler(sampler) -> int:
+    if sampler not in SAMPLERS:
+        raise ValueError(f"sampler must be one of {sorted(SAMPLERS)}")
+    return SAMPLERS[sampler]
+
+
 def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok, q_lse,
                        draft_len=None, req_id=None, corrected=None, workspace=None, stream=None,
-                       trace=None, gru=None, head_state=None):
+                       trace=None, gru=None, head_state=None, sampler="token"):
     """Draft one block (see dspark_draft_block in include/dspark.h).  Returns the workspace
     (reusable; it also carries the device status word).  gru: None (Markov head) or the
     recurrent head's (Wi [3r,r], Wh [3r,r], bi [3r], bh [3r]) float32 device tensors;
-    head_state: optional [B,K,r] bfloat16 output of the recurrent head's operands."""
+    head_state: optional [B,K,r] bfloat16 output of the recurrent head's operands;
+    sampler: "token" (per-token Gumbel-max) or "block16" (the two-level block race)."""
     B, K, V = Z.shape
     r = U.shape[1]
     _dev(Z, "Z", _LOGIT)
@@ -232,7 +251,8 @@ def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_t
     a = DraftArgs(B, K, V, r, _DT[Z.dtype], _DT[U.dtype], _ptr(Z), _ptr(U), _ptr(W),
                   _ptr(prev_token), _ptr(draft_len), _ptr(temperature), _ptr(req_id),
                   int(seed) & (2**64 - 1), _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse),
-                  _ptr(corrected), _trace(trace), *(_ptr(t) for t in g), _ptr(head_state))
+                  _ptr(corrected), _trace(trace), *(_ptr(t) for t in g), _ptr(head_state),
+                  _sampler(sampler))
     st = _lib.dspark_draft_block(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_draft_block")
@@ -292,9 +312,10 @@ def dspark_calibrate(conf_logits, verify_len, accept_len, inv_temp, step=1.0, ri
 
 def dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature,
                   seed, accept_len, next_token, req_id=None, p_tok=None, workspace=None,
-                  stream=None, trace=None, head_state=None):
+                  stream=None, trace=None, head_state=None, sampler="token"):
     """Rejection-sampling verification (see dspark_verify in include/dspark.h).  head_state:
-    the [B,K,r] bfloat16 operands of a recurrent-head draft, or None (Markov head)."""
+    the [B,K,r] bfloat16 operands of a recurrent-head draft, or None (Markov head); sampler:
+    how the residual / bonus tokens are drawn ("token" or "block16")."""
     B, K, V = Z.shape
     r = U.shape[1]
     _dev(Y, "Y", _LOGIT, (B, K + 1, V))
@@ -320,7 +341,7 @@ def dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len
                    _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse), _ptr(Z), _ptr(U), _ptr(W),
                    _ptr(prev_token), _ptr(verify_len), _ptr(temperature), _ptr(req_id),
                    int(seed) & (2**64 - 1), _ptr(accept_len), _ptr(next_token), _ptr(p_tok),
-                   _trace(trace), _ptr(head_state))
+                   _trace(trace), _ptr(head_state), _sampler(sampler))
     st = _lib.dspark_verify(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_verify")
@@ -341,7 +362,7 @@ def dspark_query_device_status(workspace: torch.Tensor, stream=None) -> int:
 # ----------------------------------------------------------------------------------------
 
 def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=None,
-                want_corrected=False, workspace=None, trace=None, gru=None):
+                want_corrected=False, workspace=None, trace=None, gru=None, sampler="token"):
     """gru: None (Markov head) or (Wi, Wh, bi, bh) for the recurrent head, whose operands are
     returned as head_state [B,K,r] bfloat16 (positions past a draft are zero)."""
     B, K, V = Z.shape
@@ -358,7 +379,7 @@ def draft_block(Z, U, W, prev_token, temperature, seed, draft_len=None, req_id=N
                                           out["q_tok"], out["q_lse"], draft_len=draft_len,
                                           req_id=req_id, corrected=out["corrected"],
                                           workspace=workspace, trace=trace, gru=gru,
-                                          head_state=out["head_state"])
+                                          head_state=out["head_state"], sampler=sampler)
     return out
 
 
@@ -383,7 +404,7 @@ def calibrate(conf_logits, verify_len, accept_len, inv_temp, step=1.0, ridge=1e-
 
 
 def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, temperature, seed,
-           req_id=None, want_p=True, workspace=None, trace=None, head_state=None):
+           req_id=None, want_p=True, workspace=None, trace=None, head_state=None, sampler="token"):
     B, K = draft_tokens.shape
     dev = Y.device
     out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
@@ -392,5 +413,6 @@ def verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len, tempe
     out["workspace"] = dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token,
                                      verify_len, temperature, seed, out["accept_len"],
                                      out["next_token"], req_id=req_id, p_tok=out["p_tok"],
-                                     workspace=workspace, trace=trace, head_state=head_state)
+                                     workspace=workspace, trace=trace, head_state=head_state,
+                                     sampler=sampler)
     return out

@@ -49,16 +49,24 @@
  * (0, 1), G = -log(-log u) a standard Gumbel draw.  Token v's draw on stream s at position k
  * uses word v & 3 of the block at counter (v >> 2, k, request key, s).
  *
- * Sampling a token from weights w_v = exp(a_v) (the pages fix only the law, the draw is this
- * library's): a two-level Gumbel-max.  The vocabulary is cut into blocks of 16 consecutive
- * ids (the last one may be shorter); block beta has the log-weight A = log sum_{v in beta} w_v
- * and the race score A + G_beta, where G_beta comes from word b of the Philox block at
- * counter (4 a + c, k, request key, race stream) for beta = 16 a + 4 b + c (b, c in 0..3).
- * The best block wins; inside it the token with the best a_v + G_v (token draws on the
- * within stream) is drawn.  Token v then has probability w_v / sum w.  Streams (race /
- * within): 0 / 4 draft, 2 / 5 residual, 3 / 6 bonus; 1 is the accept test (v = 0).
- * Results therefore depend only on (inputs, seed, request keys), not on launch geometry.
- * Every argmax, and the race, breaks exact ties towards the lowest index.
+ * Sampling a token from weights w_v = exp(a_v) (the pages fix the law: the draft token follows
+ * the drafter's softmax and the emitted token the target's; QbitAI "DSpark in 10 concepts",
+ * section "Speculative decoding"; wangjunjian.com tag page, post "Speculative Decoding", steps
+ * 3-4).  Two samplers, chosen per call by the `sampler` field of the arguments:
+ *   DSPARK_SAMPLER_TOKEN (0, the default): the per-token Gumbel-max, x = argmax_v (a_v + G_v)
+ *     with G_v the draw of token v on the call's stream at its position -- stream 0 for a draft
+ *     token, 2 for a residual correction, 3 for a bonus token.
+ *   DSPARK_SAMPLER_BLOCK16 (1, opt-in, cheaper): a two-level Gumbel-max with the same law but
+ *     one uniform per 16 tokens instead of one per token.  The vocabulary is cut into blocks of
+ *     16 consecutive ids (the last one may be shorter); block beta has the log-weight
+ *     A = log sum_{v in beta} w_v and the race score A + G_beta, where G_beta comes from word b
+ *     of the Philox block at counter (4 a + c, k, request key, race stream) for
+ *     beta = 16 a + 4 b + c (b, c in 0..3).  The best block wins; inside it the token with the
+ *     best a_v + G_v (token draws on the within stream) is drawn.  Token v then has probability
+ *     w_v / sum w.  Streams (race / within): 0 / 4 draft, 2 / 5 residual, 3 / 6 bonus.
+ * Stream 1 is the accept test (v = 0).  Results therefore depend only on (inputs, seed, request
+ * keys, sampler), not on launch geometry.  Every argmax, and the race, breaks exact ties
+ * towards the lowest index.
  */
 #ifndef DSPARK_H
 #define DSPARK_H
@@ -81,6 +89,9 @@ typedef enum {
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 
+/* How sampled tokens are drawn (see "Sampling" above). */
+typedef enum { DSPARK_SAMPLER_TOKEN = 0, DSPARK_SAMPLER_BLOCK16 = 1 } dspark_sampler;
+
 /* Bits of the device status word. */
 #define DSPARK_DEV_BAD_TOKEN 0x1u       /* a token id outside [0, V) was replaced by 0     */
 #define DSPARK_DEV_BAD_TEMPERATURE 0x2u /* a negative / NaN temperature was taken as 0     */
@@ -99,8 +110,8 @@ typedef struct dspark_trace dspark_trace;
  *   prev   = prev_token[b] for k = 0, else x[b][k-1]          (previous token only)
  *   c[v]   = Z[b][k][v] + sum_i U[prev][i] * W[v][i]          (float32 accumulation)
  *   T_b = 0: x = argmax_v c[v],  q_tok = 1, q_lse = 0
- *   T_b > 0: s = c / T_b, q_lse = log sum_v exp(s_v), x = two-level draw from s on the
- *            draft streams at position k, q_tok = exp(s_x - q_lse)
+ *   T_b > 0: s = c / T_b, q_lse = log sum_v exp(s_v), x = the sampler's draw from s on the
+ *            draft stream(s) at position k, q_tok = exp(s_x - q_lse)
  * Positions k >= K_b get x = -1, q_tok = 0, q_lse = 0.
  *
  * Layouts: Z [B][K][V]; U [V][r] (row t is the left factor of token t); W [V][r] -- row v
@@ -148,6 +159,7 @@ typedef struct {
     const float *gru_bi;   /* [3r]                       */
     const float *gru_bh;   /* [3r]                       */
     uint16_t *head_state;  /* optional out [B][K][r] bfloat16 (recurrent head) */
+    int32_t sampler;       /* dspark_sampler; 0 (a zero-initialised struct) = per token */
 } dspark_draft_args;
 
 /*
@@ -230,10 +242,10 @@ typedef struct {
  *     T > 0: q_j(v) = exp(c_j[v] / T - q_lse[b][j]) with c_j recomputed by the Markov head
  *            (previous token prev_token[b] for j = 0, else draft_tokens[b][j-1]), or, when
  *            head_state is given (a recurrent-head draft), from its operand head_state[b][j];
- *            r = max(0, p - q_j); the two-level draw from the weights r on the residual
- *            streams at position j; if r is identically zero, the same draw from p.
+ *            r = max(0, p - q_j); the sampler's draw from the weights r on the residual
+ *            stream(s) at position j; if r is identically zero, the same draw from p.
  *   No rejection: accept_len = L and next_token is argmax_v Y[b][L][v] (T = 0) or the
- *   two-level draw from Y[b][L] / T on the bonus streams at position L (the bonus token).
+ *   sampler's draw from Y[b][L] / T on the bonus stream(s) at position L (the bonus token).
  * Layouts: Y [B][K+1][V] (row K+1 exists for the bonus); draft_tokens, q_tok, q_lse [B][K]
  * as written by dspark_draft_block; Z, U, W, prev_token, req_id, seed and the dtypes must be
  * the ones the draft used.  Y may be float32 or bfloat16.
@@ -262,6 +274,7 @@ typedef struct {
     float *p_tok;                /* optional out [B][K]   */
     dspark_trace *trace;
     const uint16_t *head_state;  /* [B][K][r] bfloat16 from a recurrent-head draft, or NULL */
+    int32_t sampler;             /* dspark_sampler of the residual / bonus draws; 0 = per token */
 } dspark_verify_args;
 
 /* Workspace bytes each call needs for the given sizes (0 on invalid sizes). */

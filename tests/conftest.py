@@ -15,6 +15,25 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long CPU statistics test")
 
 
+def pytest_sessionfinish(session, exitstatus):
+    """Write the parity tallies (near-ties counted by tests/parity.py) as JSON lines into
+    $DSPARK_TALLY_DIR/parity_tallies.jsonl when that variable names a directory."""
+    out_dir = os.environ.get("DSPARK_TALLY_DIR")
+    if not out_dir:
+        return
+    try:
+        import json
+        import parity
+    except Exception:
+        return
+    if not parity.REPORTS:
+        return
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "parity_tallies.jsonl"), "a") as f:
+        for r in parity.REPORTS:
+            f.write(json.dumps(r) + "\n")
+
+
 def _gpu_available() -> bool:
     try:
         import torch

@@ -42,19 +42,32 @@ TIE_SAMPLE = 1e-4
 TIE_ACCEPT = 1e-5
 
 
+# every Tally.report of the session, written out at its end (conftest.py) when a directory
+# for it is given in DSPARK_TALLY_DIR
+REPORTS: list = []
+
+
 @dataclass
 class Tally:
     compared_positions: int = 0
     greedy_near_ties: int = 0
     sample_near_ties: int = 0
     accept_near_ties: int = 0
+    schedule_near_ties: int = 0
     diverged_requests: int = 0
     notes: list = field(default_factory=list)
 
     def report(self, name):
+        REPORTS.append(dict(case=name, positions=self.compared_positions,
+                            greedy_near_ties=self.greedy_near_ties,
+                            sample_near_ties=self.sample_near_ties,
+                            accept_near_ties=self.accept_near_ties,
+                            schedule_near_ties=self.schedule_near_ties,
+                            diverged_requests=self.diverged_requests))
         print(f"[parity {name}] positions={self.compared_positions} "
               f"greedy_ties={self.greedy_near_ties} sample_ties={self.sample_near_ties} "
-              f"accept_ties={self.accept_near_ties} diverged={self.diverged_requests}", flush=True)
+              f"accept_ties={self.accept_near_ties} schedule_ties={self.schedule_near_ties} "
+              f"diverged={self.diverged_requests}", flush=True)
 
 
 def to_device(inp: dict, device="cuda") -> dict:

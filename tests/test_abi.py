@@ -93,6 +93,12 @@ def test_host_validation_without_gpu():
     assert lib.dspark_draft_block(C.byref(bad), None, 0, None) == D.DSPARK_EDTYPE
     bad.z_dtype, bad.Z = 0, None
     assert lib.dspark_draft_block(C.byref(bad), None, 0, None) == D.DSPARK_EINVAL
+    # an unknown sampler
+    bad.Z, bad.sampler = fake, 2
+    assert lib.dspark_draft_block(C.byref(bad), fake, 1 << 30, None) == D.DSPARK_EINVAL
+    bad.sampler = -1
+    assert lib.dspark_draft_block(C.byref(bad), fake, 1 << 30, None) == D.DSPARK_EINVAL
+    assert a.sampler == D.SAMPLERS["token"] == 0  # a zero-initialised field is the default
     # missing / misaligned / short workspace
     assert lib.dspark_draft_block(C.byref(a), None, 0, None) == D.DSPARK_EWORKSPACE
     assert lib.dspark_draft_block(C.byref(a), fake + 8, 1 << 30, None) == D.DSPARK_EWORKSPACE
@@ -131,6 +137,8 @@ def test_host_validation_without_gpu():
     v.y_dtype, v.Y = 0, None
     assert lib.dspark_verify(C.byref(v), None, 0, None) == D.DSPARK_EINVAL
     v.Y, v.head_state = fake, fake  # recurrent-head operands need matrix-core factors
+    assert lib.dspark_verify(C.byref(v), fake, 1 << 30, None) == D.DSPARK_EINVAL
+    v.head_state, v.sampler = None, 5
     assert lib.dspark_verify(C.byref(v), fake, 1 << 30, None) == D.DSPARK_EINVAL
 
     c = D.CalibrateArgs(4, 4, fake, fake, fake, fake, 1.0, 1e-3, None)

@@ -4,8 +4,9 @@ Sizes keep the recipe of each workload but shrink the vocabulary to a few thousa
 which still spans many 64-row W tiles and leaves a ragged last tile (V = 2392 = 37*64 + 24).
 The rank stays 256 (bf16 factors -> matrix-core path) except in the float32 "tiny" workload
 (rank 16 -> vector path) and three cases that change it: ranks 64 and 128 (the other
-matrix-core instantiations) and 96 (bf16 factors on the vector path).  Tolerances and
-near-tie rules: tests/parity.py.
+matrix-core instantiations) and 96 (bf16 factors on the vector path).  Every case runs the
+default per-token sampler; the cases marked block16 run the optional two-level sampler against
+the oracle's same mode.  Tolerances and near-tie rules: tests/parity.py.
 """
 import numpy as np
 import pytest
@@ -41,6 +42,13 @@ CASES = [
     ("single", {"V": 1208, "K": 64, "B": 6, "noise": (0.0, 0.0)}, 1.0, False),
     # two request groups of the matrix-core kernel, the second one partial
     ("concurrent", {"V": 1208, "B": 300}, None, False),
+    # the optional two-level sampler on the vector and matrix-core paths
+    ("tiny", {"sampler": "block16"}, 1.0, True),
+    ("moderate", {"V": 2392, "sampler": "block16"}, None, True),
+    ("ragged", {"V": 1208, "r": 128, "sampler": "block16"}, None, True),
+    ("single", {"V": 1208, "K": 64, "B": 6, "sampler": "block16"}, 1.0, False),
+    ("single", {"V": 1208, "K": 64, "B": 6, "noise": (0.0, 0.0), "sampler": "block16"}, 1.0,
+     False),
 ]
 
 
@@ -48,10 +56,11 @@ def _ids(c):
     name, kw, T, strong = c
     return (f"{name}-V{kw.get('V', 'full')}-T{T}-{'strong' if strong else 'std'}"
             + (f"-K{kw['K']}" if "K" in kw else "") + (f"-r{kw['r']}" if "r" in kw else "")
-            + (f"-B{kw['B']}" if "B" in kw else "") + ("-exact" if "noise" in kw else ""))
+            + (f"-B{kw['B']}" if "B" in kw else "") + ("-exact" if "noise" in kw else "")
+            + (f"-{kw['sampler']}" if "sampler" in kw else ""))
 
 
-def run_round(w, T, strong, tally, tag, draft_len_override=None):
+def run_round(w, T, strong, tally, tag, draft_len_override=None, sampler="token"):
     from draft_head_verification_amd import dspark as D
     inp = synth.make_inputs(w, temperature=T, strong_bias=strong)
     if draft_len_override is not None:
@@ -61,11 +70,12 @@ def run_round(w, T, strong, tally, tag, draft_len_override=None):
     B, K, V = w.B, w.K, w.V
     # ---- draft
     gd = D.draft_block(g["Z"], g["U"], g["W"], g["prev_token"], g["temperature"], inp["seed"],
-                       draft_len=g["draft_len"], req_id=g["req_id"], want_corrected=True)
+                       draft_len=g["draft_len"], req_id=g["req_id"], want_corrected=True,
+                       sampler=sampler)
     Zc = inp["Z_ext"][:, :K].contiguous()
     od = oracle.draft_block(Zc, inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
                             inp["seed"], draft_len=inp["draft_len"], req_id=inp["req_id"],
-                            want_corrected=True)
+                            want_corrected=True, sampler=sampler)
     gnp = {k: gd[k].cpu().numpy() for k in ("tokens", "q_tok", "q_lse")}
     gcorr = gd["corrected"].cpu().numpy()
     rows = list(range(B))
@@ -91,9 +101,10 @@ def run_round(w, T, strong, tally, tag, draft_len_override=None):
     qt = torch.from_numpy(od["q_tok"].astype(np.float32))
     ql = torch.from_numpy(od["q_lse"].astype(np.float32))
     gv = D.verify(Y.cuda(), toks.cuda(), qt.cuda(), ql.cuda(), g["Z"], g["U"], g["W"],
-                  g["prev_token"], vlen.cuda(), g["temperature"], inp["seed"], req_id=g["req_id"])
+                  g["prev_token"], vlen.cuda(), g["temperature"], inp["seed"], req_id=g["req_id"],
+                  sampler=sampler)
     ov = oracle.verify(Y, toks, qt, ql, Zc, inp["U"], inp["W"], inp["prev_token"], vlen,
-                       inp["temperature"], inp["seed"], req_id=inp["req_id"])
+                       inp["temperature"], inp["seed"], req_id=inp["req_id"], sampler=sampler)
     gvn = {k: gv[k].cpu().numpy() for k in ("accept_len", "next_token", "p_tok")}
     compare_verify(gvn, ov, rows, inp["temperature"].numpy(), tally)
     assert D.dspark_query_device_status(gv["workspace"]) == 0
@@ -103,9 +114,11 @@ def run_round(w, T, strong, tally, tag, draft_len_override=None):
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 def test_round_parity(case):
     name, kw, T, strong = case
+    kw = dict(kw)
+    sampler = kw.pop("sampler", "token")
     w = synth.shrink(synth.WORKLOADS[name], **kw)
     tally = Tally()
-    gd, gv, ov = run_round(w, T, strong, tally, _ids(case))
+    gd, gv, ov = run_round(w, T, strong, tally, _ids(case), sampler=sampler)
     tally.report(_ids(case))
     # the round did real work: some acceptances and some rejections overall
     acc = ov["accept_len"]

@@ -4,7 +4,8 @@ token a round emits is distributed as the target p_1, and the second (given the 
 token was accepted) as p_2 -- the guarantee the pages state for rejection-sampling
 verification (QbitAI "DSpark in 10 concepts", section "Speculative decoding"; 10100.com,
 section on speculative decoding, rule of Leviathan et al.).  Chi-squared against the exact
-softmax computed in float64 on the CPU."""
+softmax computed in float64 on the CPU.  Both samplers: the per-token Gumbel-max and the
+optional two-level block race."""
 import numpy as np
 import pytest
 import torch
@@ -13,8 +14,9 @@ from scipy import stats
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("sampler", ["token", "block16"])
 @pytest.mark.parametrize("T", [1.0, 0.7])
-def test_gpu_round_output_law_equals_target(T):
+def test_gpu_round_output_law_equals_target(T, sampler):
     from draft_head_verification_amd import dspark as D
     n, V, r, K = 1 << 17, 40, 8, 3
     g = torch.Generator().manual_seed(21)
@@ -28,9 +30,9 @@ def test_gpu_round_output_law_equals_target(T):
     U, W = U.to(dev), W.to(dev)
     prev = torch.full((n,), 2, dtype=torch.int32, device=dev)
     temp = torch.full((n,), T, device=dev)
-    d = D.draft_block(Z, U, W, prev, temp, 4242)
+    d = D.draft_block(Z, U, W, prev, temp, 4242, sampler=sampler)
     v = D.verify(Y, d["tokens"], d["q_tok"], d["q_lse"], Z, U, W, prev,
-                 torch.full((n,), K, dtype=torch.int32, device=dev), temp, 4242)
+                 torch.full((n,), K, dtype=torch.int32, device=dev), temp, 4242, sampler=sampler)
     a = v["accept_len"].cpu().numpy()
     nt = v["next_token"].cpu().numpy()
     toks = d["tokens"].cpu().numpy()
@@ -60,8 +62,9 @@ def _binned_p(p, hot):
     return np.append(p[hot], 1.0 - p[hot].sum())
 
 
+@pytest.mark.parametrize("sampler", ["token", "block16"])
 @pytest.mark.parametrize("T", [1.0, 0.7])
-def test_gpu_round_output_law_matrix_core_path(T):
+def test_gpu_round_output_law_matrix_core_path(T, sampler):
     """The same laws through the matrix-core head (bfloat16 factors, rank 64) on a vocabulary
     of 2392 tokens: 37 full 64-token tiles and a short one, spread over several vocabulary
     slabs, so the block race is merged across lanes, tiles, slabs and the reduction.  Forty
@@ -85,9 +88,9 @@ def test_gpu_round_output_law_matrix_core_path(T):
     U, W = U.to(dev), W.to(dev)
     prev = torch.full((n,), 7, dtype=torch.int32, device=dev)
     temp = torch.full((n,), T, device=dev)
-    d = D.draft_block(Z, U, W, prev, temp, 977)
+    d = D.draft_block(Z, U, W, prev, temp, 977, sampler=sampler)
     v = D.verify(Y, d["tokens"], d["q_tok"], d["q_lse"], Z, U, W, prev,
-                 torch.full((n,), K, dtype=torch.int32, device=dev), temp, 977)
+                 torch.full((n,), K, dtype=torch.int32, device=dev), temp, 977, sampler=sampler)
     a = v["accept_len"].cpu().numpy()
     nt = v["next_token"].cpu().numpy()
     toks = d["tokens"].cpu().numpy()
