@@ -1,5 +1,7 @@
 // api.hip -- the C ABI of libdspark.so: argument checks, workspace carving and the launch
 // sequence of each call.  See include/dspark.h for the contract of every entry point.
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "dspark_common.hpp"
@@ -115,6 +117,7 @@ const char *dspark_status_string(dspark_status s) {
         case DSPARK_EWORKSPACE: return "workspace missing, misaligned or too small";
         case DSPARK_EHIP: return "HIP runtime error";
         case DSPARK_EDEVICE: return "invalid device data (see device status bits)";
+        case DSPARK_ESCRATCH: return "sizes exceed the static scratch of the allocation-free call";
     }
     return "unknown status";
 }
@@ -141,8 +144,8 @@ size_t dspark_schedule_workspace_size(int32_t B, int32_t K) {
     return 256 + align256(n * sizeof(long long)) + align256(n * sizeof(int));
 }
 
-dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws_bytes,
-                                 void *stream) {
+// Host-side checks of a draft call that do not involve the workspace; DSPARK_OK to go on.
+static dspark_status check_draft_args(const dspark_draft_args *a) {
     if (!a) return DSPARK_EINVAL;
     if (!head_sizes_ok(a->B, a->K, a->V, a->r)) return DSPARK_EINVAL;
     if (!valid_dtype(a->z_dtype) || !valid_dtype(a->uw_dtype)) return DSPARK_EDTYPE;
@@ -157,11 +160,12 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
                 !matrix_core_factors(a->uw_dtype, a->r)))
         return DSPARK_EINVAL;
     if (a->head_state && !rnn) return DSPARK_EINVAL;
-    if (!check_ws(ws, ws_bytes, dspark_draft_workspace_size(a->B, a->K, a->V, a->r)))
-        return DSPARK_EWORKSPACE;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    DraftWs w;
-    draft_layout(a->B, a->K, a->V, a->r, &w, reinterpret_cast<char *>(ws));
+    return DSPARK_OK;
+}
+
+// The launch sequence of a draft call on a carved workspace (arguments already checked).
+static dspark_status run_draft(const dspark_draft_args *a, DraftWs &w, hipStream_t s) {
+    const bool rnn = a->gru_wi != nullptr;
     if (!draft_gathers_rows(*a)) w.a_rows = nullptr;
     hipError_t e = traced(a->trace, "draft_prepare", s,
                           [&] { return launch_draft_prepare(*a, w, s); });
@@ -202,6 +206,70 @@ dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws
         if (rnn && k + 1 < a->K && rnn_step(k + 1) != hipSuccess) return DSPARK_EHIP;
     }
     return DSPARK_OK;
+}
+
+dspark_status dspark_draft_block(const dspark_draft_args *a, void *ws, size_t ws_bytes,
+                                 void *stream) {
+    const dspark_status st = check_draft_args(a);
+    if (st != DSPARK_OK || a->B == 0) return st;
+    if (!check_ws(ws, ws_bytes, dspark_draft_workspace_size(a->B, a->K, a->V, a->r)))
+        return DSPARK_EWORKSPACE;
+    DraftWs w;
+    draft_layout(a->B, a->K, a->V, a->r, &w, reinterpret_cast<char *>(ws));
+    return run_draft(a, w, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// Allocation-free draft: the workspace is a fixed device array of this library, one copy per
+// GPU, whose device address is looked up once per device (hipGetSymbolAddress) with that
+// device current.  Host code only ever uses the looked-up address: the array's own name is a
+// host-side stand-in, not a device address.
+// ---------------------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = DSPARK_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (nullptr on a HIP error).
+void *current_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+dspark_status dspark_draft_block_static(const dspark_draft_args *a, uint32_t *device_status,
+                                        void *stream) {
+    const dspark_status st = check_draft_args(a);
+    if (st != DSPARK_OK || a->B == 0) return st;
+    if (!device_status) return DSPARK_EINVAL;
+    if (dspark_draft_workspace_size(a->B, a->K, a->V, a->r) > kStaticScratchBytes)
+        return DSPARK_ESCRATCH;
+    char *base = reinterpret_cast<char *>(current_scratch());
+    if (!base) return DSPARK_EHIP;
+    DraftWs w;
+    draft_layout(a->B, a->K, a->V, a->r, &w, base);
+    w.status = device_status;  // the caller's word: cleared by the first kernel, read by the caller
+    return run_draft(a, w, reinterpret_cast<hipStream_t>(stream));
 }
 
 dspark_status dspark_schedule(const dspark_schedule_args *a, void *ws, size_t ws_bytes,

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libdspark.so")
 
 DSPARK_OK, DSPARK_EINVAL, DSPARK_EDTYPE, DSPARK_EWORKSPACE, DSPARK_EHIP, DSPARK_EDEVICE = \
     0, -1, -2, -3, -4, -5
+DSPARK_ESCRATCH = -6
+STATIC_SCRATCH_BYTES = 8 << 20  # DSPARK_STATIC_SCRATCH_BYTES
 DSPARK_F32, DSPARK_BF16 = 0, 1
 # samplers (include/dspark.h): the per-token Gumbel-max (default) and the opt-in block race
 SAMPLERS = {"token": 0, "block16": 1}
@@ -84,6 +86,8 @@ _lib.dspark_calibrate.restype = C.c_int
 _lib.dspark_calibrate.argtypes = [C.POINTER(CalibrateArgs), _p, C.c_size_t, _p]
 _lib.dspark_draft_block.restype = C.c_int
 _lib.dspark_draft_block.argtypes = [C.POINTER(DraftArgs), _p, C.c_size_t, _p]
+_lib.dspark_draft_block_static.restype = C.c_int
+_lib.dspark_draft_block_static.argtypes = [C.POINTER(DraftArgs), _p, _p]
 _lib.dspark_schedule.restype = C.c_int
 _lib.dspark_schedule.argtypes = [C.POINTER(ScheduleArgs), _p, C.c_size_t, _p]
 _lib.dspark_verify.restype = C.c_int
@@ -214,14 +218,8 @@ def _sampler(sampler) -> int:
     return SAMPLERS[sampler]
 
 
-def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok, q_lse,
-                       draft_len=None, req_id=None, corrected=None, workspace=None, stream=None,
-                       trace=None, gru=None, head_state=None, sampler="token"):
-    """Draft one block (see dspark_draft_block in include/dspark.h).  Returns the workspace
-    (reusable; it also carries the device status word).  gru: None (Markov head) or the
-    recurrent head's (Wi [3r,r], Wh [3r,r], bi [3r], bh [3r]) float32 device tensors;
-    head_state: optional [B,K,r] bfloat16 output of the recurrent head's operands;
-    sampler: "token" (per-token Gumbel-max) or "block16" (the two-level block race)."""
+def _draft_args(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok, q_lse, draft_len,
+                req_id, corrected, trace, gru, head_state, sampler) -> DraftArgs:
     B, K, V = Z.shape
     r = U.shape[1]
     _dev(Z, "Z", _LOGIT)
@@ -246,17 +244,47 @@ def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_t
             _dev(t, n, _F32, shape)
     if head_state is not None:
         _dev(head_state, "head_state", (torch.bfloat16,), (B, K, r))
+    return DraftArgs(B, K, V, r, _DT[Z.dtype], _DT[U.dtype], _ptr(Z), _ptr(U), _ptr(W),
+                     _ptr(prev_token), _ptr(draft_len), _ptr(temperature), _ptr(req_id),
+                     int(seed) & (2**64 - 1), _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse),
+                     _ptr(corrected), _trace(trace), *(_ptr(t) for t in g), _ptr(head_state),
+                     _sampler(sampler))
+
+
+def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok, q_lse,
+                       draft_len=None, req_id=None, corrected=None, workspace=None, stream=None,
+                       trace=None, gru=None, head_state=None, sampler="token"):
+    """Draft one block (see dspark_draft_block in include/dspark.h).  Returns the workspace
+    (reusable; it also carries the device status word).  gru: None (Markov head) or the
+    recurrent head's (Wi [3r,r], Wh [3r,r], bi [3r], bh [3r]) float32 device tensors;
+    head_state: optional [B,K,r] bfloat16 output of the recurrent head's operands;
+    sampler: "token" (per-token Gumbel-max) or "block16" (the two-level block race)."""
+    B, K, V = Z.shape
+    r = U.shape[1]
+    a = _draft_args(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok, q_lse,
+                    draft_len, req_id, corrected, trace, gru, head_state, sampler)
     need = dspark_draft_workspace_size(B, K, V, r)
     ws = _ws(workspace, need, Z.device)
-    a = DraftArgs(B, K, V, r, _DT[Z.dtype], _DT[U.dtype], _ptr(Z), _ptr(U), _ptr(W),
-                  _ptr(prev_token), _ptr(draft_len), _ptr(temperature), _ptr(req_id),
-                  int(seed) & (2**64 - 1), _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse),
-                  _ptr(corrected), _trace(trace), *(_ptr(t) for t in g), _ptr(head_state),
-                  _sampler(sampler))
     st = _lib.dspark_draft_block(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_draft_block")
     return ws
+
+
+def dspark_draft_block_static(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok,
+                              q_lse, device_status, draft_len=None, req_id=None, corrected=None,
+                              stream=None, trace=None, gru=None, head_state=None,
+                              sampler="token"):
+    """Allocation-free draft (see dspark_draft_block_static in include/dspark.h): the library's
+    static scratch replaces the workspace; device_status is a one-element int32 / uint32
+    device tensor that receives the device status bits (dspark_query_device_status reads it)."""
+    a = _draft_args(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok, q_lse,
+                    draft_len, req_id, corrected, trace, gru, head_state, sampler)
+    _dev(device_status, "device_status", (torch.int32,), (1,))
+    st = _lib.dspark_draft_block_static(C.byref(a), _ptr(device_status), _stream(stream))
+    if st != DSPARK_OK:
+        raise DSparkError(st, "dspark_draft_block_static")
+    return device_status
 
 
 def dspark_schedule(conf_logits, verify_len, knot_tokens=None, knot_tps=None, enabled=True,

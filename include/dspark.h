@@ -84,7 +84,8 @@ typedef enum {
     DSPARK_EDTYPE = -2,     /* unsupported dtype combination                            */
     DSPARK_EWORKSPACE = -3, /* workspace missing, misaligned or smaller than required   */
     DSPARK_EHIP = -4,       /* the HIP runtime reported an error (launch or sync)       */
-    DSPARK_EDEVICE = -5     /* device data was invalid (see dspark_query_device_status) */
+    DSPARK_EDEVICE = -5,    /* device data was invalid (see dspark_query_device_status) */
+    DSPARK_ESCRATCH = -6    /* sizes exceed the static scratch of dspark_draft_block_static */
 } dspark_status;
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
@@ -293,6 +294,28 @@ dspark_status dspark_verify(const dspark_verify_args *args, void *ws, size_t ws_
                             void *stream);
 dspark_status dspark_calibrate(const dspark_calibrate_args *args, void *ws, size_t ws_bytes,
                                void *stream);
+
+/*
+ * dspark_draft_block_static -- dspark_draft_block without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: its scratch (the same layout the
+ * workspace would hold, dspark_draft_workspace_size(B, K, V, r) bytes) is a fixed array of
+ * DSPARK_STATIC_SCRATCH_BYTES inside the library, one copy per GPU, kept until the process
+ * ends; its address on the current device is looked up on the first call on that device.
+ *   args           as for dspark_draft_block (same checks, same results)
+ *   device_status  caller-owned DEVICE pointer to one uint32_t (required): receives the
+ *                  device status bits of the call (cleared by its first kernel), readable with
+ *                  dspark_query_device_status(device_status, stream, &bits)
+ *   stream         a hipStream_t of the CURRENT device
+ * Returns DSPARK_ESCRATCH when dspark_draft_workspace_size(B, K, V, r) exceeds the array
+ * (e.g. B = 256, K = 16, V = 151936, r = 256 needs about 2.6 MB), and the errors of
+ * dspark_draft_block otherwise.  Every call on one GPU shares that GPU's array and nothing is
+ * carried from one call to the next: calls that may overlap on one GPU (two streams, two host
+ * threads) race on it and must be serialised by the caller.
+ */
+#define DSPARK_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+dspark_status dspark_draft_block_static(const dspark_draft_args *args, uint32_t *device_status,
+                                        void *stream);
 
 /* Synchronises `stream`, then reads the device status word of workspace `ws` (written by the
  * last call that used it).  Returns DSPARK_OK, DSPARK_EDEVICE (and the bits in *bits when
