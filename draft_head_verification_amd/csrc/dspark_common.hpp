@@ -43,13 +43,19 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 // ---------------------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  Each round multiplies counter words 0
-// and 2 by the published multipliers (one v_mad_u64_u32 each), xors the high halves into the
-// other two words together with the round key, and the key advances by the Weyl constants.
+// and 2 by the published multipliers (one v_mad_u64_u32 each, full rate on gfx950), xors the
+// high halves into the other two words together with the round key (one three-input
+// v_bitop3_b32 each: truth table 0x96 is a ^ b ^ c), and the key advances by the Weyl
+// constants.
 // ---------------------------------------------------------------------------------------
 
 struct Philox4 {
     uint32_t w[4];
 };
+
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                  uint32_t c3, uint32_t k0, uint32_t k1) {
@@ -57,8 +63,8 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     for (int round = 0; round < 10; ++round) {
         const uint64_t pa = (uint64_t)0xD2511F53u * (uint64_t)c0;
         const uint64_t pb = (uint64_t)0xCD9E8D57u * (uint64_t)c2;
-        const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(pb >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(pa >> 32), c3, k1);
         c1 = (uint32_t)pb;
         c3 = (uint32_t)pa;
         c0 = n0;
