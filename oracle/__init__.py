@@ -68,6 +68,7 @@ def lib() -> C.CDLL:
                                          p, i32, p, p, p, p, p, i32]
         L.oracle_profile.restype = C.c_double
         L.oracle_profile.argtypes = [i32, p, p, C.c_double]
+        L.oracle_prefix_expected.argtypes = [i32, i32, p, p]
         L.oracle_schedule.restype = i32
         L.oracle_schedule.argtypes = [i32, i32, p, p, i32, p, p, i32, p, p, p, p]
         L.oracle_calibrate_step.restype = i32
@@ -294,6 +295,15 @@ def profile(knot_tokens, knot_tps, N):
     kt = _np(knot_tokens, np.float64)
     kp = _np(knot_tps, np.float64)
     return lib().oracle_profile(len(kt), _ptr(kt), _ptr(kp), float(N))
+
+
+def prefix_expected(B, P_sorted):
+    """E(n) = B + sum of the first n of P_sorted, n = 0..len, each rounded once from the exact
+    sum (see oracle_prefix_expected in dspark_oracle.c) -> float64 [len + 1]."""
+    P = _np(P_sorted, np.float64)
+    out = np.empty(len(P) + 1, np.float64)
+    lib().oracle_prefix_expected(int(B), len(P), _ptr(P), _ptr(out))
+    return out
 
 
 def schedule(conf_logits, knot_tokens, knot_tps, enabled=True, draft_len=None, inv_temp=None):

@@ -64,7 +64,9 @@
  *    (request, position) items by (P desc, position asc, request asc); for n = 0..sum K_b
  *    E(n) = B + sum of the top-n P, N(n) = B + n, G(n) = E(n) * T(N(n)) / N(n) with T the
  *    piecewise-linear throughput profile clamped outside its knots; n* = smallest argmax;
- *    L_b = number of request b's items in the top n*.
+ *    L_b = number of request b's items in the top n*.  E(n) is the float64 rounding of the
+ *    exact sum (each P truncated to a multiple of 2^-80, which moves the sum by less than
+ *    2^-67), so that its value does not depend on the order in which the terms are added.
  */
 #include <math.h>
 #include <stdint.h>
@@ -525,6 +527,38 @@ double oracle_profile(int n_knots, const double *knot_tokens, const double *knot
     return knot_tps[i] + (knot_tps[i + 1] - knot_tps[i]) * t;
 }
 
+/*
+ * E(n) = B + P_0 + ... + P_{n-1} for n = 0..n_items, each the float64 rounding (nearest, ties
+ * to even) of the exact sum, with every P in [0, 1] first truncated to a multiple of 2^-80.
+ * The sums are exact 128-bit integers in units of 2^-80 (B <= 2^14 and n_items <= 2^14 keep
+ * them below 2^95); the conversion to float64 is the compiler's unsigned __int128 -> double,
+ * and the scaling by 2^-80 is exact.
+ */
+static unsigned __int128 fixed80(double p)
+{
+    if (!(p > 0.0))
+        return 0;
+    int e;
+    double f = frexp(p, &e);                      /* p = f 2^e, f in [0.5, 1) */
+    uint64_t m = (uint64_t)ldexp(f, 53);          /* 53-bit integer, exact */
+    int sh = e - 53 + 80;                         /* p 2^80 = m 2^sh */
+    if (sh >= 0)
+        return (unsigned __int128)m << sh;
+    if (sh <= -64)
+        return 0;
+    return (unsigned __int128)(m >> (-sh));
+}
+
+void oracle_prefix_expected(int B, int n_items, const double *P, double *E_out)
+{
+    unsigned __int128 acc = (unsigned __int128)(unsigned)B << 80;
+    for (int n = 0; n <= n_items; ++n) {
+        if (n > 0)
+            acc += fixed80(P[n - 1]);
+        E_out[n] = ldexp((double)acc, -80);
+    }
+}
+
 typedef struct {
     double P;
     int k;
@@ -596,14 +630,16 @@ int oracle_schedule(int B, int K, const float *conf_logits, const int32_t *draft
             }
         }
         qsort(items, (size_t)n_items, sizeof(sched_item), sched_item_cmp);
-        double E = (double)B;
+        double *Ps = (double *)malloc(sizeof(double) * (size_t)(n_items > 0 ? n_items : 1));
+        double *Es = (double *)malloc(sizeof(double) * (size_t)(n_items + 1));
+        for (int i = 0; i < n_items; ++i)
+            Ps[i] = items[i].P;
+        oracle_prefix_expected(B, n_items, Ps, Es);
         double best_G = -INFINITY, second_G = -INFINITY;
         int best_n = 0;
         for (int n = 0; n <= n_items; ++n) {
-            if (n > 0)
-                E += items[n - 1].P;
             double N = (double)B + (double)n;
-            double G = E * oracle_profile(n_knots, knot_tokens, knot_tps, N) / N;
+            double G = Es[n] * oracle_profile(n_knots, knot_tokens, knot_tps, N) / N;
             if (G > best_G) {
                 second_G = best_G;
                 best_G = G;
@@ -620,6 +656,8 @@ int oracle_schedule(int B, int K, const float *conf_logits, const int32_t *draft
             diag[0] = (double)best_n;
             diag[1] = (best_G - second_G) / fabs(best_G);
         }
+        free(Ps);
+        free(Es);
         free(items);
     }
     if (expected_tokens) {

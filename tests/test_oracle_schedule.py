@@ -5,9 +5,14 @@ maximises expected emitted tokens per unit of verify time.  It is checked agains
 exhaustive search over every per-request length vector on tiny batches, against library
 routines for the survival products and the profile interpolation, and against the two
 closed-form load regimes the pages describe (10100.com, "letting the GPU decide how much to
-verify": verify longer when load is low, cut low-return suffixes when it is high).
+verify": verify longer when load is low, cut low-return suffixes when it is high).  Its tie
+rules (ranking at equal survival, smallest n at equal objectives) are pinned by hand-derived
+cases (tests/golden/schedule_ties.json); E(n) is pinned to exact rational arithmetic.
 """
 import itertools
+import json
+import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -99,3 +104,42 @@ def test_concurrent_workload_is_ragged():
     thresh_in = min(P[b, vl[b] - 1] for b in range(w.B) if vl[b] > 0)
     thresh_out = max(P[b, vl[b]] for b in range(w.B) if vl[b] < w.K)
     assert thresh_in >= thresh_out
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "schedule_ties.json")
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_tie_rules_hand_derived(case):
+    conf = np.array(case["conf_logits"], np.float32)
+    res = oracle.schedule(conf, case["knot_tokens"], case["knot_tps"], True)
+    np.testing.assert_array_equal(res["verify_len"], case["verify_len"])
+    assert res["n_star"] == case["n_star"]
+    np.testing.assert_array_equal(res["expected_tokens"], case["expected_tokens"])
+
+
+def _exact_prefix(B, P):
+    """B + sum of the first n terms, each truncated to a multiple of 2^-80, in exact rational
+    arithmetic, then rounded to the nearest float64 (Python's correctly rounded conversion)."""
+    out, acc = [], Fraction(B)
+    for n in range(len(P) + 1):
+        if n:
+            acc += Fraction(int(Fraction(P[n - 1]) * 2**80), 2**80)
+        out.append(float(acc))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefix_expected_is_exact_sum_rounded_once(seed):
+    rng = np.random.default_rng(40 + seed)
+    n = int(rng.integers(1, 400))
+    B = int(rng.integers(1, 8192))
+    # prefix products of many sizes, including tiny ones, exact 0 and 1, and subnormals
+    P = np.cumprod(rng.uniform(0.3, 1.0, size=n))
+    P[rng.integers(0, n, size=max(1, n // 10))] = rng.choice([0.0, 1.0, 1e-30, 5e-324, 2.0**-80])
+    got = oracle.prefix_expected(B, P)
+    np.testing.assert_array_equal(got, _exact_prefix(B, P))
+    # order does not matter for the full sum
+    assert oracle.prefix_expected(B, rng.permutation(P))[-1] == got[-1]
+    # and the truncation is far below the float64 rounding of E
+    assert abs(got[-1] - float(Fraction(B) + sum(Fraction(x) for x in P))) <= np.spacing(got[-1])
