@@ -18,7 +18,12 @@
 // whole GPU (a request's prefix products never increase along its draft, each factor being
 // at most 1, so its items form one sorted run and an item's place in it is a binary search);
 // then one workgroup takes the items in rank order, forms E(n) by a block prefix sum, takes
-// the argmax over n, and counts each request's items ranked below n*.
+// the argmax over n, and counts each request's items ranked below n*.  E(n) is the float64
+// rounding of the exact sum (products truncated to multiples of 2^-80, summed as 128-bit
+// integers), so the parallel prefix sum gives the value a sequential one would, bit for bit;
+// the profile interpolation and G(n) are evaluated with separately rounded float64 operations
+// (no fused multiply-add), as written.  With scheduling off a small kernel copies the draft
+// lengths and forms the expected tokens.
 #include "dspark_common.hpp"
 
 namespace dspark {
@@ -33,6 +38,7 @@ __device__ __forceinline__ double survival(float c, double theta) {
 }
 
 __device__ __forceinline__ double profile_at(const double *kt, const double *kp, int n, double N) {
+#pragma clang fp contract(off)
     if (N <= kt[0]) return kp[0];
     if (N >= kt[n - 1]) return kp[n - 1];
     int lo = 0, hi = n - 1;  // kt[lo] <= N < kt[hi]
@@ -45,6 +51,63 @@ __device__ __forceinline__ double profile_at(const double *kt, const double *kp,
     }
     const double t = (N - kt[lo]) / (kt[lo + 1] - kt[lo]);
     return kp[lo] + (kp[lo + 1] - kp[lo]) * t;
+}
+
+// Unsigned 128-bit integers for the exact prefix sums of E(n), in units of 2^-80.
+struct U128 {
+    unsigned long long lo, hi;
+};
+
+__device__ __forceinline__ U128 u128_add(U128 a, U128 b) {
+    U128 r;
+    r.lo = a.lo + b.lo;
+    r.hi = a.hi + b.hi + (r.lo < a.lo ? 1ull : 0ull);
+    return r;
+}
+
+__device__ __forceinline__ U128 u128_sub(U128 a, U128 b) {
+    U128 r;
+    r.lo = a.lo - b.lo;
+    r.hi = a.hi - b.hi - (a.lo < b.lo ? 1ull : 0ull);
+    return r;
+}
+
+// floor(p * 2^80) for p in [0, 1], from the float64 fields: p = m 2^(e - 1075) (normal) or
+// m 2^-1074 (subnormal), so p 2^80 = m 2^sh with sh = e - 995 (or -994) <= 28.
+__device__ __forceinline__ U128 fixed80(double p) {
+    U128 r = {0ull, 0ull};
+    if (!(p > 0.0)) return r;
+    const unsigned long long bits = (unsigned long long)__double_as_longlong(p);
+    const int ex = (int)((bits >> 52) & 0x7FF);
+    unsigned long long m = bits & ((1ull << 52) - 1);
+    int sh;
+    if (ex == 0) {
+        sh = -1074 + 80;
+    } else {
+        m |= 1ull << 52;
+        sh = ex - 1075 + 80;
+    }
+    if (sh >= 0) {
+        r.lo = m << sh;
+        r.hi = sh == 0 ? 0ull : m >> (64 - sh);
+    } else if (sh > -64) {
+        r.lo = m >> (-sh);
+    }
+    return r;
+}
+
+// v 2^-80 rounded to the nearest float64 (ties to even).
+__device__ __forceinline__ double u128_to_double_scaled(U128 v) {
+    if (v.hi == 0) return ldexp(__ull2double_rn(v.lo), -80);
+    const int lz = __clzll((long long)v.hi);  // 0..63
+    // the value is (top + rest / 2^64) 2^(64 - lz) with top its leading 64 bits
+    const unsigned long long top = lz == 0 ? v.hi : (v.hi << lz) | (v.lo >> (64 - lz));
+    const unsigned long long rest = lz == 0 ? v.lo : v.lo << lz;
+    unsigned long long m = top >> 11;  // 53 bits
+    const unsigned long long r = top & 0x7FFull;
+    const bool up = r > 0x400ull || (r == 0x400ull && (rest != 0ull || (m & 1ull)));
+    m += up ? 1ull : 0ull;  // 2^53 at most: exact in float64
+    return ldexp((double)m, 11 + 64 - lz - 80);
 }
 
 // "a before b": (P desc, k asc, b asc), with P as its float64 bits (P >= 0; -1 marks a slot
@@ -148,7 +211,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     __shared__ long long sorted[kSchedMaxItems];  // products in rank order
     __shared__ int ranks[kSchedMaxItems];         // rank of item b*K + k
     __shared__ double kt[kSchedMaxKnots], kp[kSchedMaxKnots];
-    __shared__ double wsum[kSchedThreads / 64];
+    __shared__ unsigned long long wsum_lo[kSchedThreads / 64], wsum_hi[kSchedThreads / 64];
     __shared__ double best_g[kSchedThreads / 64];
     __shared__ int best_n[kSchedThreads / 64];
     __shared__ int s_ok, s_items, s_nstar;
@@ -223,28 +286,34 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
         const int per = (n_items + 1 + kSchedThreads - 1) / kSchedThreads;
         const int n0 = min(tid * per, n_items + 1), n1 = min(n0 + per, n_items + 1);
         const int i1 = min(n1, n_items);
-        double own = 0.0;
-        for (int i = n0; i < i1; ++i) own += __longlong_as_double(sorted[i]);
-        double incl = own;
+        U128 own = {0ull, 0ull};
+        for (int i = n0; i < i1; ++i) own = u128_add(own, fixed80(__longlong_as_double(sorted[i])));
+        U128 incl = own;
         for (int d = 1; d < 64; d <<= 1) {
-            const double o = __shfl_up(incl, d);
-            if (lane >= d) incl += o;
+            U128 o;
+            o.lo = __shfl_up(incl.lo, d);
+            o.hi = __shfl_up(incl.hi, d);
+            if (lane >= d) incl = u128_add(incl, o);
         }
-        if (lane == 63) wsum[wave] = incl;
+        if (lane == 63) {
+            wsum_lo[wave] = incl.lo;
+            wsum_hi[wave] = incl.hi;
+        }
         __syncthreads();
-        double off = 0.0;
-        for (int w = 0; w < wave; ++w) off += wsum[w];
-        double e = (double)B + (off + (incl - own));
+        U128 e = {0ull, (unsigned long long)B << 16};  // B 2^80
+        for (int w = 0; w < wave; ++w) e = u128_add(e, U128{wsum_lo[w], wsum_hi[w]});
+        e = u128_add(e, u128_sub(incl, own));
         double bg = -INFINITY;
         int bn = 0x7FFFFFFF;
         for (int n = n0; n < n1; ++n) {
+#pragma clang fp contract(off)
             const double N = (double)B + (double)n;
-            const double g = e * profile_at(kt, kp, n_knots, N) / N;
+            const double g = u128_to_double_scaled(e) * profile_at(kt, kp, n_knots, N) / N;
             if (g > bg) {
                 bg = g;
                 bn = n;
             }
-            if (n < n_items) e += __longlong_as_double(sorted[n]);
+            if (n < n_items) e = u128_add(e, fixed80(__longlong_as_double(sorted[n])));
         }
         for (int mask = 1; mask < 64; mask <<= 1) {
             const double og = __shfl_xor(bg, mask);
@@ -274,14 +343,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     // request b verifies its items ranked below n* (a prefix of its draft: ranks rise along
     // it); expected tokens add up the same float64 products that were ranked
     const int nstar = s_nstar;
-    // scheduling off, with the items fitting the (otherwise unused) rank-order array: every
-    // thread forms survival factors, one per item, first
-    const bool par = !enabled && B * K <= kSchedMaxItems;
-    if (par) {
-        for (int i = tid; i < B * K; i += kSchedThreads)
-            sorted[i] = __double_as_longlong(survival(conf[i], inv_temp ? inv_temp[i % K] : 1.0));
-        __syncthreads();
-    }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int b = tid + j * kSchedThreads;
@@ -294,11 +355,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
                 const int r = ranks[b * K + k];
                 if (r < 0 || r >= nstar) break;
                 run_p = __longlong_as_double(sorted[r]);
-            } else if (enabled) {  // (a bad profile: the products were still formed)
+            } else {  // a bad profile: the products were still formed
                 run_p = __longlong_as_double(key[(size_t)b * K + k]);
-            } else {
-                run_p = run_p * (par ? __longlong_as_double(sorted[b * K + k])
-                                     : survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0));
             }
             L = k + 1;
             e += run_p;
@@ -308,16 +366,53 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     }
 }
 
+// Scheduling off: every request verifies its whole draft.  One workgroup (it clears the status
+// word before any flag is raised): the survival factors one per thread into LDS (when the
+// expected tokens are asked for and the items fit), then one thread per request forms
+// 1 + sum_{k < L} P in draft order, as the scheduled path does.
+constexpr int kOffThreads = 1024;
+__global__ __launch_bounds__(kOffThreads) void schedule_off_kernel(
+    int B, int K, const float *conf, const int32_t *draft_len, const double *inv_temp,
+    int32_t *verify_len, double *expected_tokens, uint32_t *status) {
+    __shared__ double sv[kSchedMaxItems];
+    const int tid = threadIdx.x;
+    const bool staged = expected_tokens && B * K <= kSchedMaxItems;
+    if (tid == 0) *status = 0u;
+    if (staged)
+        for (int i = tid; i < B * K; i += kOffThreads)
+            sv[i] = survival(conf[i], inv_temp ? inv_temp[i % K] : 1.0);
+    __syncthreads();
+    for (int b = tid; b < B; b += kOffThreads) {
+        const int raw = draft_len ? draft_len[b] : K;
+        if (raw < 0 || raw > K) atomicOr(status, DSPARK_DEV_BAD_LENGTH);
+        const int kb = raw < 0 ? 0 : (raw > K ? K : raw);
+        verify_len[b] = kb;
+        if (expected_tokens) {
+            double run_p = 1.0, e = 1.0;
+            for (int k = 0; k < kb; ++k) {
+                const size_t i = (size_t)b * K + k;
+                run_p = run_p * (staged ? sv[i] : survival(conf[i], inv_temp ? inv_temp[k] : 1.0));
+                e += run_p;
+            }
+            expected_tokens[b] = e;
+        }
+    }
+}
+
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, long long *key,
                            int *rank, hipStream_t s) {
-    if (a.enabled) {
-        const int per = kPrepThreads / a.K;
-        schedule_prepare_kernel<<<(a.B + per - 1) / per, kPrepThreads, 0, s>>>(
-            a.B, a.K, a.conf_logits, a.draft_len, a.conf_inv_temp, key, rank);
-        const dim3 grid((unsigned)((a.B * a.K + kRankThreads - 1) / kRankThreads),
-                        (unsigned)((a.B + kRankRuns - 1) / kRankRuns));
-        schedule_rank_kernel<<<grid, kRankThreads, 0, s>>>(a.B, a.K, key, rank);
+    if (!a.enabled) {
+        schedule_off_kernel<<<1, kOffThreads, 0, s>>>(a.B, a.K, a.conf_logits, a.draft_len,
+                                                      a.conf_inv_temp, a.verify_len,
+                                                      a.expected_tokens, status);
+        return hipGetLastError();
     }
+    const int per = kPrepThreads / a.K;
+    schedule_prepare_kernel<<<(a.B + per - 1) / per, kPrepThreads, 0, s>>>(
+        a.B, a.K, a.conf_logits, a.draft_len, a.conf_inv_temp, key, rank);
+    const dim3 grid((unsigned)((a.B * a.K + kRankThreads - 1) / kRankThreads),
+                    (unsigned)((a.B + kRankRuns - 1) / kRankRuns));
+    schedule_rank_kernel<<<grid, kRankThreads, 0, s>>>(a.B, a.K, key, rank);
     schedule_select_kernel<<<1, kSchedThreads, 0, s>>>(
         a.B, a.K, a.conf_logits, a.draft_len, a.n_knots, a.knot_tokens, a.knot_tps, a.enabled,
         a.conf_inv_temp, key, rank, a.verify_len, a.expected_tokens, status);
