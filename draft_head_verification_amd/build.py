@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdspark.so")
-SOURCES = ["markov_head.hip", "rnn_head.hip", "verify.hip", "schedule.hip", "api.hip"]
+SOURCES = ["markov_head.hip", "rnn_head.hip", "verify.hip", "schedule.hip", "pack.hip", "api.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

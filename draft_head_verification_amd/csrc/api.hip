@@ -354,6 +354,16 @@ dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_byt
     return e == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
 
+dspark_status dspark_pack_w(const void *w_rv, void *w_vr, int32_t r, int32_t V, int32_t dtype,
+                           void *stream) {
+    if (!w_rv || !w_vr || w_rv == w_vr || r < 1 || r > kMaxRank || V < 1 || V > kMaxV)
+        return DSPARK_EINVAL;
+    if (!valid_dtype(dtype)) return DSPARK_EDTYPE;
+    return launch_pack_w(w_rv, w_vr, r, V, dtype, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? DSPARK_OK
+               : DSPARK_EHIP;
+}
+
 dspark_status dspark_query_device_status(const void *ws, void *stream, uint32_t *bits) {
     if (!ws) return DSPARK_EINVAL;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -105,17 +105,19 @@ __device__ __forceinline__ float gumbel2_from_word(uint32_t word) {
 }
 
 // E2 = -log2(u) = log2(e) * E for the uniform of `word`, accurate in relative terms (the
-// per-token draws rank tokens by w / E2, which orders them as w / E does): for d = 1 - u below
-// 2^-6 the series log2(e) (d + d^2/2 + d^3/3) (truncation < 2^-19 relative); above, -log2(u)
-// of the float u, whose rounding (at most 2^-25) is then below 2^-18 relative.
+// per-token draws rank tokens by w / E2, which orders them as w / E does).  u = (m + 1/2) 2^-24
+// is exact in float for u < 1/2 and rounds to the 2^-24 grid above; the rounding
+// e = u - fl(u) (0 or +-2^-25) is recovered exactly (m 2^-24 - fl(u) is exact, then + 2^-25),
+// and -log2(u) = -log2(fl(u)) - log2(e) e / u to first order, with 1/u replaced by 1 (the
+// difference is e (1 - u) / u, below 2^-25 relative to E2).  v_log_f32 keeps its relative
+// accuracy near 1 (measured on gfx950 over every float in [1/2, 1): 1.0e-7), so E2 is within
+// 1.5e-7 relative of -log2(u) for every word -- also where E2 is tiny and the draw is large,
+// i.e. where samples are decided.
 __device__ __forceinline__ float exp2_from_word(uint32_t word) {
     const float fm = (float)(word >> 8);
     const float u = fmaf(fm, 0x1p-24f, 0x1p-25f);
-    // d = 1 - u = (2^25 - 2m - 1) 2^-25: 1 - m 2^-24 is exact, and so is the subtraction
-    // whenever d <= 1/2 (the only case in which d is used)
-    const float d = fmaf(fm, -0x1p-24f, 1.0f) - 0x1p-25f;
-    const float series = d * fmaf(d, fmaf(d, kLog2e / 3.0f, kLog2e / 2.0f), kLog2e);
-    return d < 0x1p-6f ? series : -fast_log2(u);
+    const float e = fmaf(fm, 0x1p-24f, -u) + 0x1p-25f;  // u - fl(u), exact
+    return fmaf(e, -kLog2e, -fast_log2(u));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -675,6 +677,9 @@ hipError_t launch_draft_reduce(const dspark_draft_args &a, const DraftWs &ws, in
 bool draft_uses_rnn(const dspark_draft_args &a);
 // bfloat16 factors of a rank the matrix-core kernels take (64, 128 or 256)
 bool matrix_core_factors(int uw_dtype, int r);
+
+// r x V right factor (row-major) -> [V][r]
+hipError_t launch_pack_w(const void *w_rv, void *w_vr, int r, int V, int dtype, hipStream_t s);
 
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, long long *key,
                            int *rank, hipStream_t s);

@@ -92,6 +92,8 @@ _lib.dspark_schedule.restype = C.c_int
 _lib.dspark_schedule.argtypes = [C.POINTER(ScheduleArgs), _p, C.c_size_t, _p]
 _lib.dspark_verify.restype = C.c_int
 _lib.dspark_verify.argtypes = [C.POINTER(VerifyArgs), _p, C.c_size_t, _p]
+_lib.dspark_pack_w.restype = C.c_int
+_lib.dspark_pack_w.argtypes = [_p, _p, _i32, _i32, _i32, _p]
 _lib.dspark_query_device_status.restype = C.c_int
 _lib.dspark_query_device_status.argtypes = [_p, _p, C.POINTER(C.c_uint32)]
 _lib.dspark_status_string.restype = C.c_char_p
@@ -374,6 +376,20 @@ def dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_verify")
     return ws
+
+
+def dspark_pack_w(w_rv: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """The r x V right factor -> the [V, r] layout the calls read (see dspark_pack_w in
+    include/dspark.h).  Returns the packed tensor (a new one unless `out` is given)."""
+    _dev(w_rv, "w_rv", _LOGIT)
+    r, V = w_rv.shape
+    if out is None:
+        out = torch.empty(V, r, dtype=w_rv.dtype, device=w_rv.device)
+    _dev(out, "out", (w_rv.dtype,), (V, r))
+    st = _lib.dspark_pack_w(_ptr(w_rv), _ptr(out), r, V, _DT[w_rv.dtype], _stream(stream))
+    if st != DSPARK_OK:
+        raise DSparkError(st, "dspark_pack_w")
+    return out
 
 
 def dspark_query_device_status(workspace: torch.Tensor, stream=None) -> int:

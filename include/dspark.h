@@ -116,7 +116,8 @@ typedef struct dspark_trace dspark_trace;
  * Positions k >= K_b get x = -1, q_tok = 0, q_lse = 0.
  *
  * Layouts: Z [B][K][V]; U [V][r] (row t is the left factor of token t); W [V][r] -- row v
- * holds column v of the r x V right factor (the same layout as an output-projection weight).
+ * holds column v of the r x V right factor (the same layout as an output-projection weight;
+ * a factor held as r x V is converted once, when the weights are loaded, by dspark_pack_w).
  * U and W share a dtype.  Z may be float32 or bfloat16.  Supported: r in [1, 1024]; bfloat16
  * factors with r = 64, 128 or 256 run on the matrix cores, anything else on the
  * vector ALUs.  K in [1, 64].  B >= 0 (B = 0 launches nothing).
@@ -316,6 +317,18 @@ dspark_status dspark_calibrate(const dspark_calibrate_args *args, void *ws, size
 #define DSPARK_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
 dspark_status dspark_draft_block_static(const dspark_draft_args *args, uint32_t *device_status,
                                         void *stream);
+
+/*
+ * dspark_pack_w -- convert the Markov head's right factor from r x V (row i = rank component
+ * i over the vocabulary, the factorisation's own shape) to the [V][r] layout every call above
+ * reads (QbitAI "DSpark in 10 concepts", section "Cheaper serial module: the Markov head": the
+ * bias is a rank-r factorisation U . W).  A one-off step when the weights are loaded, not part
+ * of a round.  w_rv [r][V] and w_vr [V][r] are distinct device buffers of dtype DSPARK_F32 or
+ * DSPARK_BF16, caller-owned; 1 <= r <= 1024.  Asynchronous on `stream`.  Returns DSPARK_EINVAL
+ * (null, aliased or bad sizes), DSPARK_EDTYPE or DSPARK_EHIP.
+ */
+dspark_status dspark_pack_w(const void *w_rv, void *w_vr, int32_t r, int32_t V, int32_t dtype,
+                           void *stream);
 
 /* Synchronises `stream`, then reads the device status word of workspace `ws` (written by the
  * last call that used it).  Returns DSPARK_OK, DSPARK_EDEVICE (and the bits in *bits when
