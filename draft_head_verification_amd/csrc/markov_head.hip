@@ -563,13 +563,17 @@ __device__ __forceinline__ void tile_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <HeadMode MODE, int SAMP, typename ZT, typename YT, int R>
-__global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadParams p) {
+template <HeadMode MODE, int SAMP, typename ZT, typename YT, int R, int NQ>
+__global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams p) {
     static_assert(R == 64 || R == 128 || R == 256, "matrix-core path: rank 64, 128 or 256");
+    static_assert(NQ == 1 || NQ == 2, "one or two 16-wide request blocks per wave");
+    constexpr int WAVES = 16 / NQ;                 // waves per workgroup (256 requests)
+    constexpr int RPW = 16 * NQ;                   // requests per wave
     constexpr int KS = R / 32;                     // MFMA k-steps of 32
     constexpr int CPR = R / 8;                     // 16-byte chunks per W row
     constexpr int TILE_CH = kTileV * CPR;          // chunks per W tile
-    constexpr int LPW = TILE_CH / 64 / kMfmaWaves; // direct loads per wave per tile
+    constexpr int LPW = TILE_CH / 64 / WAVES;      // direct loads per wave per tile
+    static_assert(LPW * 64 * WAVES == TILE_CH, "the W tile splits evenly over the waves");
     constexpr int STAGES = 4;
     constexpr bool kResid = MODE == HeadMode::Residual;
     // Software pipeline over half tiles.  Phase A of tile t: W(t+3) goes out to LDS, then the
@@ -588,7 +592,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     // W(t) was thus forced two phases before phase A of tile t in every wave; the barrier
     // there makes all of it visible and retires every read of stage (t-1) % 4 (last used in
     // phase B of tile t - 1), which W(t+3) overwrites.
-    constexpr int NH = 2 * ((int)sizeof(ZT) / 2) + (kResid ? 2 * ((int)sizeof(YT) / 2) : 0);
+    // vector loads per half tile and wave: per request block, one 16-byte load of bfloat16
+    // base logits or two of float32 ones (and the same for the target logits in residual mode)
+    constexpr int NH = NQ * ((int)sizeof(ZT) / 2 + (kResid ? (int)sizeof(YT) / 2 : 0));
     constexpr int NL = NH;
     constexpr int WAIT_A = NL + LPW, WAIT_B = LPW + NH;
     static_assert(WAIT_A <= 63 && WAIT_B <= 63 && NL + 2 * LPW <= 63, "vmcnt range");
@@ -656,24 +662,24 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     // row metadata, U rows, W(t0), the low logits of t0 and W(t0+1), W(t0+2) all go out
     // together, and one explicit count waits for all but the last three.  A residual row's
     // metadata is a two-load chain, then its U gather; its W(t0) goes out first.
-    RowInfo ri[2];
-    bf16x8 ufrag[2][KS];
-    int rowid[2];
-    size_t zr[2] = {0, 0}, yr[2] = {0, 0};  // logit rows of the tile loads
+    RowInfo ri[NQ];
+    bf16x8 ufrag[NQ][KS];
+    int rowid[NQ];
+    size_t zr[NQ] = {}, yr[NQ] = {};  // logit rows of the tile loads
     // (an empty slab issues the same loads, of a valid tile, and never reads them)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) rowid[q] = group * kRowsPerGroup + wave * kRowsPerWave + q * 16 + m;
+    for (int q = 0; q < NQ; ++q) rowid[q] = group * kRowsPerGroup + wave * RPW + q * 16 + m;
     auto load_u = [&](int q, const uint16_t *urow) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
             ufrag[q][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(urow + 32 * kk));
     };
-    DraftRowRaw raw[2];
+    DraftRowRaw raw[NQ];
     if constexpr (!kResid) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) raw[q] = draft_row_load(p, rowid[q]);
+        for (int q = 0; q < NQ; ++q) raw[q] = draft_row_load(p, rowid[q]);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             // rows past the batch (or past their draft) read a valid row; results are dropped
             const int b = min(rowid[q], p.n_rows_max - 1);
             zr[q] = (size_t)b * p.K + p.k;
@@ -683,7 +689,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     } else {
         issue_w(t0, 0, B1{});
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             ri[q] = row_info<MODE>(p, rowid[q], n_rows);
             zr[q] = ri[q].zrow;
             yr[q] = ri[q].yrow;
@@ -691,17 +697,27 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         // U[prev] (Markov head) or the stored operand of a recurrent-head draft (rows past the
         // batch read request 0's first row; their results are dropped)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < NQ; ++q)
             load_u(q, p.S ? p.S + ((size_t)ri[q].b * p.K + ri[q].pos) * R + 8 * g
                           : p.U + (size_t)ri[q].prev * R + 8 * g);
     }
-    SampleState st[2] = {sample_state_init(), sample_state_init()};
-    ResidState rs[2] = {resid_init(), resid_init()};
-    TokLane tl[2] = {tok_lane_init(), tok_lane_init()};  // per-token sampler, drafting
-    ResTok rt[2] = {restok_init(), restok_init()};      // per-token sampler, residual
-    float gm[2] = {-INFINITY, -INFINITY};  // greedy rows of a mixed wave
-    int gi[2] = {0x7FFFFFFF, 0x7FFFFFFF};
-    BlockPart bp[2] = {{0.f, 0.f}, {0.f, 0.f}};
+    SampleState st[NQ];
+    ResidState rs[NQ];
+    TokLane tl[NQ];   // per-token sampler, drafting
+    ResTok rt[NQ];    // per-token sampler, residual
+    float gm[NQ];     // greedy rows of a mixed wave
+    int gi[NQ];
+    BlockPart bp[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        st[q] = sample_state_init();
+        rs[q] = resid_init();
+        tl[q] = tok_lane_init();
+        rt[q] = restok_init();
+        gm[q] = -INFINITY;
+        gi[q] = 0x7FFFFFFF;
+        bp[q] = BlockPart{0.f, 0.f};
+    }
 
     // per-lane A-fragment offsets (in chunks) of the four blocks, and the column key
     int a_off[4];
@@ -712,11 +728,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                              : w_swizzle<CPR>(tile_row(0, m));
 
     // matrix-core work of half h (blocks j = 2h, 2h + 1) of the tile in stage s
-    auto mfma_half = [&](int s, int h, floatx4 (&acc)[2][2]) {
+    auto mfma_half = [&](int s, int h, floatx4 (&acc)[2][NQ]) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) acc[jj][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < NQ; ++q) acc[jj][q] = floatx4{0.f, 0.f, 0.f, 0.f};
         const uint4 *base = wt + s * TILE_CH;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
@@ -725,15 +741,15 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
                 const int j = 2 * h + jj;
                 const bf16x8 a = __builtin_bit_cast(bf16x8, base[a_off[j] + ((4 * kk + g) ^ a_key)]);
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < NQ; ++q)
                     acc[jj][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ufrag[q][kk], acc[jj][q],
                                                                           0, 0, 0);
             }
         }
     };
     // logits (base, and target in residual mode) of half h of tile t; invalid rows read row 0
-    Raw16<ZT> z[2];
-    Raw16<YT> y[2];
+    Raw16<ZT> z[NQ];
+    Raw16<YT> y[NQ];
     // (CLAMP: the tile may be the vocabulary's partial last one)
     auto load_half = [&](int t, int h, auto clamp_tag) {
         constexpr bool CL = decltype(clamp_tag)::value;
@@ -741,7 +757,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         // half h's 8 entries start at lane_v + 8h (the loaders add 8h)
         const int lane_v = kResid ? tc * kTileV + 8 * g + 24 * h : tc * kTileV + 16 * g;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             if constexpr (CL) {
                 z[q].load_half(p.Z, zr[q], p.V, lane_v, h);
                 if constexpr (kResid) y[q].load_half(p.Y, yr[q], p.V, lane_v, h);
@@ -756,11 +772,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     // Philox call at counter 4a + c): the lane's block of tile t is 4t + g (drafting map: one
     // call per row), or 4t + 2h + (g >> 1) in half h (residual map: one call per row and half).
     constexpr int NH_WORDS = kResid ? 2 : 1;
-    uint32_t rw[2][2][4] = {};
+    uint32_t rw[NQ][2][4] = {};
     const uint32_t stream = kResid ? kStreamResidual : kStreamDraft;
     auto race_words = [&](int t) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int hh = 0; hh < NH_WORDS; ++hh) {
                 const uint32_t c = kResid ? (uint32_t)(2 * hh + (g >> 1)) : (uint32_t)g;
@@ -781,7 +797,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         return (rw[q][hh][0] & m0) | (rw[q][hh][1] & m1) | (rw[q][hh][2] & m2) | (rw[q][hh][3] & m3);
     };
 
-    floatx4 acc_lo[2][2], acc_hi[2][2];
+    floatx4 acc_lo[2][NQ], acc_hi[2][NQ];
     auto run = [&](auto epi_tag, auto store_tag, auto mask_tag) {
         constexpr int EPI = decltype(epi_tag)::value;
         constexpr bool STORE = decltype(store_tag)::value;
@@ -790,14 +806,14 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         constexpr bool TOKEN = SAMP == kSampToken;
         // epilogue of half H of tile t from acc, with the race words w[q] of that tile (two-level
         // sampler); the per-token sampler draws the words of the half's 8 tokens here
-        auto epilogue = [&](auto half_tag, int t, const floatx4 (&acc)[2][2], const uint32_t (&w)[2]) {
+        auto epilogue = [&](auto half_tag, int t, const floatx4 (&acc)[2][NQ], const uint32_t (&w)[NQ]) {
             constexpr int H = decltype(half_tag)::value;
             const int v0 = t * kTileV + 16 * g;  // drafting map: the lane's block
             // residual map: the lane's 8 entries and the start of their block
             const int v8 = t * kTileV + 32 * H + 8 * g, vb = t * kTileV + 32 * H + 16 * (g >> 1);
             const int live = MASK ? min(8, p.V - (kResid ? v8 : v0 + 8 * H)) : 8;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
+            for (int q = 0; q < NQ; ++q) {
                 float c[8];
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
@@ -846,7 +862,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         };
         using H0 = std::integral_constant<int, 0>;
         using H1 = std::integral_constant<int, 1>;
-        const uint32_t nw[2] = {0u, 0u};
+        
 
         if constexpr (WORDS) race_words(t0);
         // tile t0: phase A without an epilogue
@@ -858,28 +874,28 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         DSPARK_WAIT_VMCNT(WAIT_B);
         mfma_half(0, 1, acc_hi);
         {
-            uint32_t w[2] = {0u, 0u};
+            uint32_t w[NQ] = {};
             if constexpr (WORDS) {
-                w[0] = word_of(0, t0, 0);
-                w[1] = word_of(1, t0, 0);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) w[q] = word_of(q, t0, 0);
             }
             epilogue(H0{}, t0, acc_lo, w);
         }
         load_half(t0 + 1, 0, mask_tag);
         for (int t = t0 + 1; t < t_end; ++t) {
             const int stg = (t - t0) & 3;
-            uint32_t wp[2] = {0u, 0u}, wc[2] = {0u, 0u};  // race words of tiles t - 1 and t
+            uint32_t wp[NQ] = {}, wc[NQ] = {};  // race words of tiles t - 1 and t
             if constexpr (WORDS) {
-                wp[0] = word_of(0, t - 1, 1);
-                wp[1] = word_of(1, t - 1, 1);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) wp[q] = word_of(q, t - 1, 1);
             }
             // phase A
             tile_barrier();
             issue_w(t + 3, (t + 3 - t0) & 3, mask_tag);
             if constexpr (WORDS) {
                 if ((t & 3) == 0) race_words(t);
-                wc[0] = word_of(0, t, 0);
-                wc[1] = word_of(1, t, 0);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) wc[q] = word_of(q, t, 0);
             }
             DSPARK_WAIT_VMCNT(WAIT_A);
             mfma_half(stg, 0, acc_lo);
@@ -892,13 +908,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
             load_half(t + 1, 0, mask_tag);
         }
         // the high half of the last tile
-        uint32_t w[2] = {0u, 0u};
+        uint32_t w[NQ] = {};
         if constexpr (WORDS) {
-            w[0] = word_of(0, t_end - 1, 1);
-            w[1] = word_of(1, t_end - 1, 1);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) w[q] = word_of(q, t_end - 1, 1);
         }
-        (void)nw;
-        DSPARK_WAIT_VMCNT(0);
+                DSPARK_WAIT_VMCNT(0);
         epilogue(H1{}, t_end - 1, acc_hi, w);
     };
 
@@ -935,7 +950,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
         // wait for every outstanding load.  The clock never reads all ones.
         const bool never = __builtin_amdgcn_s_memtime() == ~0ull;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             raw[q].kb = never ? 0 : raw[q].kb;
             raw[q].T = never ? 0.f : raw[q].T;
             raw[q].req = never ? 0u : raw[q].req;
@@ -943,7 +958,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     }
     bool any_valid = false, any_sampled = false, any_greedy = false;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < NQ; ++q) {
         if constexpr (!kResid) ri[q] = draft_row_resolve(p, rowid[q], n_rows, raw[q]);
         any_valid |= ri[q].valid;
         any_sampled |= ri[q].valid && ri[q].T > 0.f;
@@ -982,7 +997,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64, 1) void markov_mfma_kernel(HeadPar
     // merge the four lanes that share a request (lane, lane^16, lane^32, lane^48); every lane
     // runs every shuffle (partners hold the same request and so take the same branches)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < NQ; ++q) {
         if constexpr (MODE == HeadMode::Draft) {
             const bool greedy = !(ri[q].T > 0.f);
             if (greedy && (wave_sampled || p.corrected)) {  // the mixed epilogue kept it aside
@@ -1291,11 +1306,16 @@ template <HeadMode MODE, int SAMP, typename ZT, typename YT>
 static hipError_t launch_head_t(const HeadParams &p, int uw_dtype, hipStream_t s) {
     if (use_mfma(uw_dtype, p.r)) {
         const int groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
-        const dim3 grid(p.n_slabs * groups), block(kMfmaWaves * 64);
+        // Drafting steps at ranks 128 and 256: 16 waves of 16 requests (four waves per SIMD in
+        // 128 registers: the sampled epilogue is bound by vector-ALU issue and hides its latency
+        // across waves).  Rank 64, whose W tile is too small to split 16 ways, and the residual
+        // pass, whose epilogue needs more registers than four waves leave: 8 waves of 32.
+        const dim3 grid(p.n_slabs * groups);
+        constexpr int NQ = MODE == HeadMode::Draft ? 1 : 2;
         switch (p.r) {
-            case 64: markov_mfma_kernel<MODE, SAMP, ZT, YT, 64><<<grid, block, 0, s>>>(p); break;
-            case 128: markov_mfma_kernel<MODE, SAMP, ZT, YT, 128><<<grid, block, 0, s>>>(p); break;
-            case 256: markov_mfma_kernel<MODE, SAMP, ZT, YT, 256><<<grid, block, 0, s>>>(p); break;
+            case 64: markov_mfma_kernel<MODE, SAMP, ZT, YT, 64, 2><<<grid, 8 * 64, 0, s>>>(p); break;
+            case 128: markov_mfma_kernel<MODE, SAMP, ZT, YT, 128, NQ><<<grid, 16 / NQ * 64, 0, s>>>(p); break;
+            case 256: markov_mfma_kernel<MODE, SAMP, ZT, YT, 256, NQ><<<grid, 16 / NQ * 64, 0, s>>>(p); break;
             default: return hipErrorInvalidValue;
         }
     } else {

@@ -146,6 +146,26 @@ def test_deterministic_across_runs():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("sampler", ["token", "block16"])
+def test_full_batch_draft_deterministic_across_runs(sampler):
+    """Every wave of both request groups live (B = 512), bfloat16 and float32 base logits,
+    mixed temperatures, many tiles per slab: three drafts agree bit for bit.  (A pipeline wait
+    that let a logit load still be in flight when its epilogue ran would show up here.)"""
+    from draft_head_verification_amd import dspark as D
+    for zdt in (torch.bfloat16, torch.float32):
+        w = synth.shrink(synth.WORKLOADS["ragged"], B=512, V=19008, z_dtype=zdt)
+        g = to_device(synth.make_inputs(w, strong_bias=True))
+        outs = []
+        for _ in range(3):
+            d = D.draft_block(g["Z"], g["U"], g["W"], g["prev_token"], g["temperature"],
+                              w.philox_seed, draft_len=g["draft_len"], req_id=g["req_id"],
+                              sampler=sampler)
+            outs.append([d[k].cpu() for k in ("tokens", "q_tok", "q_lse")])
+        for other in outs[1:]:
+            for a, b in zip(outs[0], other):
+                assert torch.equal(a, b), zdt
+
+
 def test_schedule_and_verify_deterministic_across_runs():
     """The schedule (ranks summed with atomics) and the verification (chunked, with a
     residual pass) give bit-identical results when run twice on the same inputs."""
