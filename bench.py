@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--sampler", choices=("token", "block16"), default="token",
                     help="how sampled tokens are drawn: the per-token Gumbel-max (default) or the "
                          "optional two-level 16-token block race")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one round (all its launches) in a HIP graph and time graph "
+                         "replays instead of the launches")
     ap.add_argument("--flush", action="store_true",
                     help="time every round on its own, after writing a 512 MB buffer (untimed) so "
                          "that no input is left in L2 or the Infinity Cache; reports the median")
@@ -208,13 +211,34 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # the whole round as one HIP graph: every call enqueues kernels only (no allocation, no
+        # memset, no host sync), so a capture records exactly the round's launches
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        step()  # eager reference outputs
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in (toks, q_tok, q_lse, vlen, acc, nxt)]
+        for _ in range(max(3, args.warmup)):
+            for t in (toks, q_tok, q_lse, vlen, acc, nxt):
+                t.fill_(-3)
+            graph.replay()
+            torch.cuda.synchronize()
+            assert all(torch.equal(a, b) for a, b in zip(ref, (toks, q_tok, q_lse, vlen, acc, nxt))), \
+                "graph replay differs from the eager round"
+            step()  # eager work between replays
+            torch.cuda.synchronize()
+        run = graph.replay
     # timed region: the steps alone (no per-kernel events inside)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        step()
+        run()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -311,6 +335,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "caches": "flushed before every round (median round)" if args.flush else "warm",
+        "launch": "one HIP graph per round" if args.graph else "kernel launches",
         "step_algorithmic_GBs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "wall_s": round(wall, 3),
         "mean_accept_len": round(float(acc.float().mean().item()), 3),
