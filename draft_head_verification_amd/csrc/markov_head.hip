@@ -318,17 +318,14 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
             for (int i = 0; i < 4; ++i) {
                 const float pv = live ? fast_exp2(y[i] * inv - ri.lse2p) : 0.f;
                 const float rv = pv - fast_exp2(c[i] * inv - ri.qlse2);
-                const float le = fast_log2(exp2_from_word(ph.w[i]));
-                // log2 of a zero weight is -inf: never taken
-                const float sr = (live && rv > 0.f) ? fast_log2(rv) - le : -INFINITY;
-                const float sp = pv > 0.f ? fast_log2(pv) - le : -INFINITY;
+                // log2 of a zero weight is -inf: never taken (a row with no positive residual
+                // is drawn from p by the reduction kernel)
+                const float sr = (live && rv > 0.f)
+                                     ? fast_log2(rv) - fast_log2(exp2_from_word(ph.w[i]))
+                                     : -INFINITY;
                 if (sr > rs.gr) {
                     rs.gr = sr;
                     rs.ir = v + i;
-                }
-                if (sp > rs.gp) {
-                    rs.gp = sp;
-                    rs.ip = v + i;
                 }
             }
             return;
@@ -498,22 +495,21 @@ __device__ __forceinline__ void epi_token8(const float c[8], int v, int n_live, 
     tl.m = mn;
 }
 
-// Per-token residual candidates of one lane: best token for the weights r = max(p - q, 0) and,
-// as the fallback when r is identically zero, for p; weights are absolute (p and q normalised
-// by their known log-normalisers), so no running base is needed.
+// Per-token residual candidate of one lane: the best token for the weights r = max(p - q, 0),
+// which are absolute (p and q normalised by their known log-normalisers), so no running base is
+// needed.  The fallback for a residual that is identically zero (unreachable in exact arithmetic
+// after a rejection) is not carried here: the reduction kernel draws from p itself when no
+// candidate has a positive weight.
 struct ResTok {
-    float br, er, bp, ep;
-    int ir, ip;
+    float br, er;
+    int ir;
 };
 
 __device__ __forceinline__ ResTok restok_init() {
     ResTok t;
     t.br = 0.f;
     t.er = 1.f;
-    t.bp = 0.f;
-    t.ep = 1.f;
     t.ir = 0x7FFFFFFF;
-    t.ip = 0x7FFFFFFF;
     return t;
 }
 
@@ -521,8 +517,8 @@ __device__ __forceinline__ ResidState restok_finish(const ResTok &t) {
     ResidState s;
     s.gr = t.br > 0.f ? fast_log2(t.br) - fast_log2(t.er) : -INFINITY;
     s.ir = t.br > 0.f ? t.ir : 0x7FFFFFFF;
-    s.gp = t.bp > 0.f ? fast_log2(t.bp) - fast_log2(t.ep) : -INFINITY;
-    s.ip = t.bp > 0.f ? t.ip : 0x7FFFFFFF;
+    s.gp = -INFINITY;  // no p candidate (see above)
+    s.ip = 0x7FFFFFFF;
     return s;
 }
 
@@ -535,17 +531,13 @@ __device__ __forceinline__ void epi_resid_token8(const float c[8], const Raw16<Y
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const bool in = !MASK || e < n_live;
-        const float pv = in ? fast_exp2(fmaf(yr.get(8 * H + e), inv, -ri.lse2p)) : 0.f;  // p_v
+        const float pv = fast_exp2(fmaf(yr.get(8 * H + e), inv, -ri.lse2p));             // p_v
         const float rv = in ? fmaxf(pv - fast_exp2(fmaf(c[e], inv, -ri.qlse2)), 0.f) : 0.f;
         const float E = exp2_from_word(e < 4 ? w0.w[e] : w1.w[e - 4]);
         const bool tr = rv * rt.er > rt.br * E;
         rt.br = tr ? rv : rt.br;
         rt.er = tr ? E : rt.er;
         rt.ir = tr ? v + e : rt.ir;
-        const bool tp = pv * rt.ep > rt.bp * E;
-        rt.bp = tp ? pv : rt.bp;
-        rt.ep = tp ? E : rt.ep;
-        rt.ip = tp ? v + e : rt.ip;
     }
 }
 
@@ -1306,12 +1298,13 @@ template <HeadMode MODE, int SAMP, typename ZT, typename YT>
 static hipError_t launch_head_t(const HeadParams &p, int uw_dtype, hipStream_t s) {
     if (use_mfma(uw_dtype, p.r)) {
         const int groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
-        // Drafting steps at ranks 128 and 256: 16 waves of 16 requests (four waves per SIMD in
-        // 128 registers: the sampled epilogue is bound by vector-ALU issue and hides its latency
-        // across waves).  Rank 64, whose W tile is too small to split 16 ways, and the residual
-        // pass, whose epilogue needs more registers than four waves leave: 8 waves of 32.
+        // Ranks 128 and 256: 16 waves of 16 requests (four waves per SIMD in 128 registers: the
+        // per-token epilogues are bound by vector-ALU issue and hide their latency across
+        // waves), except the two-level sampler's residual pass, whose epilogue needs more
+        // registers than four waves leave.  Rank 64, whose W tile is too small to split 16
+        // ways: 8 waves of 32.
         const dim3 grid(p.n_slabs * groups);
-        constexpr int NQ = MODE == HeadMode::Draft ? 1 : 2;
+        constexpr int NQ = (MODE == HeadMode::Residual && SAMP == kSampBlock) ? 2 : 1;
         switch (p.r) {
             case 64: markov_mfma_kernel<MODE, SAMP, ZT, YT, 64, 2><<<grid, 8 * 64, 0, s>>>(p); break;
             case 128: markov_mfma_kernel<MODE, SAMP, ZT, YT, 128, NQ><<<grid, 16 / NQ * 64, 0, s>>>(p); break;

@@ -488,8 +488,44 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
     const int v0 = use_r ? ir : ip;
     int t = -1;
     if (sampler == DSPARK_SAMPLER_TOKEN) {
-        // the merged per-token winner over r (or over p when r is identically zero)
-        if ((use_r || gp > -INFINITY) && v0 >= 0 && v0 < V) t = v0;
+        if (use_r) {
+            // the merged per-token winner over r
+            if (v0 >= 0 && v0 < V) t = v0;
+        } else {
+            // no positive residual anywhere in the row (unreachable in exact arithmetic after a
+            // rejection): this wave draws from p over the whole row, per token, on the residual
+            // stream -- weights p_v = exp2(y_v / T - lse2 of the row), candidates as weight / E2
+            const float inv = kLog2e / T;
+            const float lse2p = rs.x + fast_log2(rs.y);
+            const uint32_t req = req_id ? req_ld : (uint32_t)b;
+            float bw = 0.f, be = 1.f;
+            int bi = 0x7FFFFFFF;
+            for (int v4 = 4 * lane; v4 < V; v4 += 4 * 64) {  // V % 4 == 0: v4 + 3 < V
+                const Philox4 ph = philox4x32_10((uint32_t)v4 >> 2, (uint32_t)j, req,
+                                                 kStreamResidual, key0, key1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pv = fast_exp2(load_value(Y, y_dtype, yrow * (size_t)V + v4 + i) * inv -
+                                               lse2p);
+                    const float E = exp2_from_word(ph.w[i]);
+                    const bool take_v = pv * be > bw * E;
+                    bw = take_v ? pv : bw;
+                    be = take_v ? E : be;
+                    bi = take_v ? v4 + i : bi;
+                }
+            }
+            float sc = bw > 0.f ? fast_log2(bw) - fast_log2(be) : -INFINITY;
+            int tok = bi;
+            for (int mask = 1; mask < 64; mask <<= 1) {
+                const float os = __shfl_xor(sc, mask);
+                const int ot = __shfl_xor(tok, mask);
+                if (os > sc || (os == sc && ot < tok)) {
+                    sc = os;
+                    tok = ot;
+                }
+            }
+            if (sc > -INFINITY && tok >= 0 && tok < V) t = tok;
+        }
     } else if (v0 >= 0 && v0 < V && v0 % kSampleBlock == 0) {
         const float inv = kLog2e / T;
         const uint32_t req = req_id ? req_ld : (uint32_t)b;

@@ -125,6 +125,40 @@ def test_round_parity(case):
     assert acc.min() >= 0
 
 
+@pytest.mark.parametrize("sampler", ["token", "block16"])
+@pytest.mark.parametrize("V,r", [(2392, 256), (1024, 16)])
+def test_identically_zero_residual_draws_from_p(sampler, V, r):
+    """A residual max(0, p - q) that is zero everywhere (here forced by handing the verifier a
+    draft log-normaliser 2 below the true one, so q exceeds p at every token, and q_tok = 1 so
+    that most positions reject): the correction is drawn from p, on the residual stream, on
+    the matrix-core and the vector path."""
+    from draft_head_verification_amd import dspark as D
+    base = "moderate" if r == 256 else "tiny"
+    w = synth.shrink(synth.WORKLOADS[base], V=V, B=24, K=3, r=r)
+    inp = synth.make_inputs(w, temperature=1.0, strong_bias=True)
+    g = to_device(inp)
+    Zc = inp["Z_ext"][:, : w.K].contiguous()
+    od = oracle.draft_block(Zc, inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
+                            inp["seed"], req_id=inp["req_id"], sampler=sampler)
+    rows = list(range(w.B))
+    Y = oracle_targets(inp, rows, od["tokens"], inp["U"], inp["W"])
+    toks = torch.from_numpy(od["tokens"])
+    qt = torch.ones(w.B, w.K)
+    ql = torch.from_numpy(od["q_lse"].astype(np.float32)) - 2.0
+    vlen = torch.full((w.B,), w.K, dtype=torch.int32)
+    gv = D.verify(Y.cuda(), toks.cuda(), qt.cuda(), ql.cuda(), g["Z"], g["U"], g["W"],
+                  g["prev_token"], vlen.cuda(), g["temperature"], inp["seed"], req_id=g["req_id"],
+                  sampler=sampler)
+    ov = oracle.verify(Y, toks, qt, ql, Zc, inp["U"], inp["W"], inp["prev_token"], vlen,
+                       inp["temperature"], inp["seed"], req_id=inp["req_id"], sampler=sampler)
+    assert (ov["accept_len"] < w.K).sum() >= w.B // 2  # the fallback path really ran
+    tally = Tally()
+    compare_verify({k: gv[k].cpu().numpy() for k in ("accept_len", "next_token", "p_tok")}, ov,
+                   rows, inp["temperature"].numpy(), tally)
+    tally.report(f"zero-residual-{sampler}-V{V}-r{r}")
+    assert D.dspark_query_device_status(gv["workspace"]) == 0
+
+
 def test_zero_lengths_and_ragged_tail():
     """draft_len 0 (no draft) and verify_len 0 (one plain decoding step from row 0)."""
     w = synth.WORKLOADS["tiny"]
