@@ -48,6 +48,13 @@ def parse():
     ap.add_argument("--sampler", choices=("token", "block16"), default="token",
                     help="how sampled tokens are drawn: the per-token Gumbel-max (default) or the "
                          "optional two-level 16-token block race")
+    ap.add_argument("--targets", choices=("noisy", "exact"), default="noisy",
+                    help="target logits: the workload's (corrected draft logits plus noise), or "
+                         "exactly the drafter's corrected logits, so that p = q and every verified "
+                         "position is accepted (the verifier reads every target row)")
+    ap.add_argument("--round-model", action="store_true",
+                    help="also measure the verify throughput curve at this workload's shape and "
+                         "report the round cost model built from the measured kernel times")
     ap.add_argument("--graph", action="store_true",
                     help="capture one round (all its launches) in a HIP graph and time graph "
                          "replays instead of the launches")
@@ -71,9 +78,10 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 5}), flush=True)
 
 
-def build_targets_on_gpu(inp, tokens, corrected, w):
+def build_targets_on_gpu(inp, tokens, corrected, w, exact=False):
     """Target logits for the timed GPU path: the drafter's corrected rows plus the workload's
-    noise; the bonus row adds the bias of the last drafted token to the extra base row."""
+    noise (exact: no noise, the target equals the drafter); the bonus row adds the bias of the
+    last drafted token to the extra base row."""
     import torch
     from draft_head_verification_amd import synth
     B, K = w.B, w.K
@@ -82,7 +90,7 @@ def build_targets_on_gpu(inp, tokens, corrected, w):
     last = tokens[:, K - 1].long().clamp(min=0)
     bias = inp["U"][last].float() @ inp["W"].float().T
     corr[:, K] += bias
-    Y = synth.target_logits(corr, inp["noise"], w.y_dtype)
+    Y = synth.target_logits(corr, 0.0 * inp["noise"] if exact else inp["noise"], w.y_dtype)
     del corr, bias
     torch.cuda.empty_cache()
     return Y
@@ -143,6 +151,53 @@ def cpu_baseline(inp, w, n_threads_hint, sampler="token"):
                       f"oracle draft {t_draft:.2f} s + verify {t_verify:.2f} s, OpenMP over requests"}
 
 
+def round_model_report(w, records, steps, inp, vlen, acc, ms_per_step):
+    """The round cost model built from this run: per-position and fixed kernel times from the
+    traced rounds, and the verify throughput curve measured at this workload's vocabulary, rank,
+    draft length and target dtype (every tested position accepted, so every target row is
+    read).  Reports the model's time per emitted token and per-user speed against one-token
+    rounds (one drafting position, its pass probability the first survival probability), the
+    model's expected tokens next to the measured ones, and the drafting cost of K = 4 against
+    K = 16 positions."""
+    import numpy as np
+    import torch
+    from draft_head_verification_amd import profile_builder as PB
+    from draft_head_verification_amd import round_model as RM
+    B, K = w.B, w.K
+    shapes = [(b, l) for b in (1, 8, 32, 64, 128, 256, 512) for l in (0, 3, 7, K - 1)
+              if b <= max(B, 8) and l <= K - 1]
+    kt, kp = PB.measure_verify_curve(shapes, V=w.V, r=w.r, K=K, y_dtype=w.y_dtype, reps=2)
+    m = RM.MeasuredRound.from_trace(records, steps, K, kt, kp)
+    surv = torch.sigmoid(inp["conf_logits"].double()).cpu().numpy()
+    P = np.cumprod(surv, axis=1)
+    L = vlen.cpu().numpy()
+    r, base, ratio = m.against_one_token(P, L, K)
+    a = acc.cpu().numpy().astype(np.float64)
+    r4 = m.round(P[:, :4], np.minimum(L, 4), 4)
+    # A target model's forward of t seconds per round adds t to both rounds:
+    # speed ratio(t) = (E_K / E_1) (T_1 + t) / (T_K + t), above 1 once t exceeds the break-even
+    eK, e1 = float(r["emitted"].mean()), float(base["emitted"].mean())
+    tK, t1 = r["t_round"], base["t_round"]
+    t_even = (e1 * tK - eK * t1) / (eK - e1) if eK > e1 else float("inf")
+    return {
+        "t_position_us": round(m.t_position * 1e6, 2), "t_fixed_us": round(m.t_fixed * 1e6, 2),
+        "verify_curve": {"tokens": [float(x) for x in kt], "tokens_per_s": [round(float(x), 1) for x in kp]},
+        "model_emitted_per_request": round(float(r["emitted"].mean()), 4),
+        "measured_emitted_per_request": round(float((a + 1).mean()), 4),
+        "model_round_ms": round(r["t_round"] * 1e3, 4), "measured_round_ms": round(ms_per_step, 4),
+        "model_time_per_token_us": round(r["time_per_token"] * 1e6, 3),
+        "one_token_round_ms": round(base["t_round"] * 1e3, 4),
+        "per_user_speed_vs_one_token": round(ratio, 4),
+        "target_forward_break_even_ms": round(max(t_even, 0.0) * 1e3, 4),
+        "per_user_speed_limit_large_target": round(eK / e1, 4),
+        "drafting_K4_vs_K16": {"draft_ms_K4": round(m.draft_time(4) * 1e3, 4),
+                               "draft_ms_K16": round(m.draft_time(K) * 1e3, 4),
+                               "model_round_ms_K4": round(r4["t_round"] * 1e3, 4)},
+        "note": "the verify curve is this library's verifier standing in for a target model's "
+                "forward, which the round does not include",
+    }
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -192,7 +247,7 @@ def main():
                          toks, q_tok, q_lse, draft_len=inp["draft_len"], req_id=inp["req_id"],
                          corrected=corrected, workspace=ws_d, gru=gru, head_state=hs,
                          sampler=args.sampler)
-    Y = build_targets_on_gpu(inp, toks, corrected, w)
+    Y = build_targets_on_gpu(inp, toks, corrected, w, exact=args.targets == "exact")
     del corrected
     torch.cuda.empty_cache()
 
@@ -315,6 +370,10 @@ def main():
                             "rocprof_mfma_util_pct": mfma_util}
     step_bytes = sum((k["algorithmic_bytes_per_launch"] or 0) * k["launches_per_step"] for k in kernels)
 
+    model = None
+    if args.round_model:
+        model = round_model_report(w, trace.records(), args.steps, inp, vlen, acc, ms_per_step)
+
     cpu = None
     if not args.no_cpu_baseline and args.head == "markov":
         cpu = cpu_baseline(inp, w, None, args.sampler)
@@ -329,7 +388,8 @@ def main():
                                f"T={args.temperature if args.temperature is not None else ','.join(str(t) for t in w.temperature)}, "
                                f"schedule {'on' if w.schedule else 'off'}, "
                                f"{'per-token Gumbel-max' if args.sampler == 'token' else 'two-level block-race'} sampler"
-                               + (", recurrent (GRU) head" if args.head == "rnn" else ""),
+                               + (", recurrent (GRU) head" if args.head == "rnn" else "")
+                               + (", exact targets (every position accepted)" if args.targets == "exact" else ""),
                    "sampler": args.sampler,
                    "B": B, "K": K, "V": V, "r": r, "parallelism": "single GPU"},
         "roofline": roofline,
@@ -341,6 +401,8 @@ def main():
         "mean_accept_len": round(float(acc.float().mean().item()), 3),
         "kernels": kernels,
     }
+    if model is not None:
+        out["round_model"] = model
     print(json.dumps(out), flush=True)
 
 

@@ -1,10 +1,10 @@
 """Round cost model: time per emitted token of a draft / schedule / verify round.
 
-The pages put the trade-off of speculative decoding in one line: the time per token is the
-drafting time plus the verification time, divided by the number of tokens a round emits
-(Sina thread, section 4 "speculation is not free"; QbitAI "DSpark in 10 concepts", section
-"Speculation is not free"; 10100.com commentary, section "speculative decoding is block
-checking").  This module evaluates that formula for a batch of requests, with
+The pages weigh speculative decoding by the time a round costs (drafting plus verification)
+against the tokens it emits (Sina thread, section 4 "speculation is not free"; QbitAI "DSpark
+in 10 concepts", section "Speculation is not free"; 10100.com commentary, section "speculative
+decoding is block checking").  This module evaluates that trade-off for a batch of requests,
+with
 
   * emitted tokens per request  E_b = 1 + sum_{k < L_b} P[b][k]
     (the accepted prefix plus the one correction or bonus token; P[b][k] is the
@@ -18,9 +18,14 @@ checking").  This module evaluates that formula for a batch of requests, with
     forward, which is not modelled here, plus K drafting steps of the Markov head, which are
     measured).
 
+MeasuredRound builds the model from a measured run: the per-kernel times of a traced round
+(drafting steps, their reductions, the fixed launches) and a measured verify throughput curve.
+
 Everything is host-side float64 arithmetic on small arrays; it drives no GPU work.
 """
 from __future__ import annotations
+
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -60,12 +65,6 @@ def round_cost(P, verify_len, knot_tokens, knot_tps, t_draft):
                 time_per_token=t_round / (tokens / B))
 
 
-def time_per_token(n_drafted, drafter_time, verify_time, n_accepted):
-    """The pages' single-request form: (n_drafted * drafter_time + verify_time) / n_accepted,
-    for a drafter whose cost grows with every drafted token."""
-    return (n_drafted * drafter_time + verify_time) / n_accepted
-
-
 def compare(P, verify_len, knot_tokens, knot_tps, t_draft, P1, t_draft1):
     """Per-user speed of a multi-token round against a one-token (MTP-1 style) round on the
     same requests: P1 [B] is each request's probability of passing its single draft token and
@@ -74,3 +73,47 @@ def compare(P, verify_len, knot_tokens, knot_tps, t_draft, P1, t_draft1):
     P1 = np.asarray(P1, dtype=np.float64).reshape(-1, 1)
     base = round_cost(P1, np.ones(P1.shape[0], np.int64), knot_tokens, knot_tps, t_draft1)
     return r, base, float(np.mean(r["per_user"]) / np.mean(base["per_user"]))
+
+
+# kernels of a drafting position, and the fixed launches of a round's draft and schedule
+_PER_POSITION = ("markov_head_step", "draft_reduce", "rnn_step")
+_FIXED = ("draft_prepare", "schedule", "schedule_prepare", "schedule_rank", "schedule_select")
+
+
+@dataclass
+class MeasuredRound:
+    """Round costs taken from measurement.
+
+    t_position  seconds per drafting position (head step + reduction, and the recurrent
+                head's update when it runs), the mean over the traced positions;
+    t_fixed     seconds of the launches a round pays once (draft set-up, schedule);
+    knot_tokens, knot_tps  the measured verify throughput curve (tokens/s against the tokens
+                in the verify batch), as profile_builder returns it."""
+    t_position: float
+    t_fixed: float
+    knot_tokens: np.ndarray
+    knot_tps: np.ndarray
+
+    @classmethod
+    def from_trace(cls, records, n_rounds, n_positions, knot_tokens, knot_tps):
+        """records: (kernel name, milliseconds) of n_rounds traced rounds that drafted
+        n_positions positions each (dspark Trace.records())."""
+        per = sum(ms for name, ms in records if name in _PER_POSITION) * 1e-3
+        fixed = sum(ms for name, ms in records if name in _FIXED) * 1e-3
+        return cls(per / (n_rounds * n_positions), fixed / n_rounds,
+                   np.asarray(knot_tokens, np.float64), np.asarray(knot_tps, np.float64))
+
+    def draft_time(self, K):
+        return self.t_fixed + K * self.t_position
+
+    def round(self, P, verify_len, K):
+        """round_cost of a round that drafts K positions and verifies verify_len of them."""
+        return round_cost(P, verify_len, self.knot_tokens, self.knot_tps, self.draft_time(K))
+
+    def against_one_token(self, P, verify_len, K):
+        """Per-user speed of this round against a one-token round on the same requests (one
+        drafting position, verified; its pass probability is each request's first survival
+        probability).  Returns (round, one-token round, speed ratio)."""
+        P = np.asarray(P, np.float64)
+        return compare(P, verify_len, self.knot_tokens, self.knot_tps, self.draft_time(K),
+                       P[:, 0], self.draft_time(1))

@@ -46,13 +46,25 @@ def test_matches_the_schedules_expected_tokens():
     assert int(np.argmax(thr)) == int(o["verify_len"].sum())
 
 
-def test_reduces_to_the_pages_single_request_form():
-    # one request, a flat curve (verify time = N / T): t = (n t_d + N/T) / E
-    n, t_d, T = 4, 2e-3, 500.0
+def test_single_request_numbers():
+    """One request, a flat curve: four drafted positions at 2 ms each, five target positions at
+    500 tokens/s (10 ms), 1 + 0.9 + 0.8 + 0.6 + 0.5 = 3.8 expected tokens: 18 ms / 3.8."""
     P = np.array([[0.9, 0.8, 0.6, 0.5]])
-    r = RM.round_cost(P, [n], [1.0, 2.0], [T, T], n * t_d)
-    E = 1 + P.sum()
-    assert r["time_per_token"] == pytest.approx(RM.time_per_token(n, t_d, (n + 1) / T, E))
+    r = RM.round_cost(P, [4], [1.0, 2.0], [500.0, 500.0], 4 * 2e-3)
+    assert r["t_verify"] == pytest.approx(0.010) and r["tokens"] == pytest.approx(3.8)
+    assert r["time_per_token"] == pytest.approx(0.018 / 3.8)
+
+
+def test_measured_round_from_trace():
+    recs = ([("draft_prepare", 0.006)] + [("markov_head_step", 0.04), ("draft_reduce", 0.01)] * 16
+            + [("schedule", 0.008), ("verify_rows", 0.05)]) * 3
+    m = RM.MeasuredRound.from_trace(recs, 3, 16, [1.0, 100.0], [10.0, 1000.0])
+    assert m.t_position == pytest.approx(50e-6) and m.t_fixed == pytest.approx(14e-6)
+    assert m.draft_time(4) == pytest.approx(14e-6 + 4 * 50e-6)
+    P = RM.prefix_survival(np.full((8, 16), 0.9))
+    r, base, ratio = m.against_one_token(P, np.full(8, 16), 16)
+    assert r["t_round"] == pytest.approx(m.draft_time(16) + 8 * 17 / 1000.0)
+    assert base["N"] == 16 and ratio == pytest.approx(np.mean(r["per_user"]) / np.mean(base["per_user"]))
 
 
 def test_profile_is_clamped_and_linear():
