@@ -150,8 +150,12 @@ __device__ int decide_rows(int b, int k0, int k1, const ReqInfo &ri, int K, int 
     for (int g0 = 0; g0 < n; g0 += G) {
         Partial pr[G];
 #pragma unroll
-        for (int j = 0; j < G; ++j)
-            pr[j] = (g0 + j < n && lane < S) ? row_partials[(rbase + k0 + g0 + j) * S + lane] : none;
+        for (int j = 0; j < G; ++j) {
+            // always a valid address (clamped row and slot); entries outside are replaced
+            const int jr = min(g0 + j, n - 1), sl = min(lane, S - 1);
+            const Partial t = row_partials[(rbase + k0 + jr) * S + sl];
+            pr[j] = (g0 + j < n && lane < S) ? t : none;
+        }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             if (g0 + j >= n) break;  // uniform

@@ -249,8 +249,14 @@ typedef struct {
  *   No rejection: accept_len = L and next_token is argmax_v Y[b][L][v] (T = 0) or the
  *   sampler's draw from Y[b][L] / T on the bonus stream(s) at position L (the bonus token).
  * Layouts: Y [B][K+1][V] (row K+1 exists for the bonus); draft_tokens, q_tok, q_lse [B][K]
- * as written by dspark_draft_block; Z, U, W, prev_token, req_id, seed and the dtypes must be
- * the ones the draft used.  Y may be float32 or bfloat16.
+ * as written by dspark_draft_block; Z, U, W, prev_token, req_id, seed, temperature, the
+ * sampler and the dtypes must be the ones the draft used.  Temperature matters for the law,
+ * not only for parity: the residual rebuilds q_j from this call's T and the draft's q_lse, so
+ * a draft taken at another temperature (a greedy draft verified with T > 0 included) gives a
+ * residual that is not max(0, p - q) of the distribution the draft was drawn from, and
+ * next_token no longer has the target's law.  The call cannot detect such a mismatch (q_tok
+ * and q_lse of a sampled draft may equal a greedy draft's 1 and 0).
+ * Y may be float32 or bfloat16.
  * Outputs: accept_len [B], next_token [B]; p_tok [B][K] optional: p(x_k) for each tested
  * position (1 / 0 for a greedy match / mismatch), 0 for untested positions.
  * head_state [B][K][r] bfloat16 (as written by dspark_draft_block's recurrent head) requires
