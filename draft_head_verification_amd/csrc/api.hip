@@ -1,6 +1,7 @@
 // api.hip -- the C ABI of libdspark.so: argument checks, workspace carving and the launch
 // sequence of each call.  See include/dspark.h for the contract of every entry point.
 #include <atomic>
+#include <cstring>
 #include <mutex>
 #include <new>
 
@@ -17,6 +18,7 @@ struct dspark_trace {
 namespace {
 
 constexpr int kMaxRank = 1024;
+constexpr int kMaxBatch = 1 << 24;  // requests per call
 constexpr int kMaxV = 1 << 30;
 
 bool valid_dtype(int d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
@@ -46,7 +48,7 @@ bool check_ws(const void *ws, size_t ws_bytes, size_t need) {
 }
 
 bool head_sizes_ok(int32_t B, int32_t K, int32_t V, int32_t r) {
-    return B >= 0 && K >= 1 && K <= kMaxK && V >= 8 && V <= kMaxV && V % 8 == 0 && r >= 1 &&
+    return B >= 0 && B < kMaxBatch && K >= 1 && K <= kMaxK && V >= 8 && V <= kMaxV && V % 8 == 0 && r >= 1 &&
            r <= kMaxRank;
 }
 
@@ -110,7 +112,11 @@ extern "C" {
 const char *dspark_version(void) { return "dspark-mi355x 0.1 (gfx950)"; }
 
 const char *dspark_status_string(dspark_status s) {
-    switch (s) {
+    // a C caller may pass any int: read the raw value, not the enumeration (whose range in
+    // C++ is only that of its enumerators)
+    int v = 0;
+    std::memcpy(&v, &s, sizeof v < sizeof s ? sizeof v : sizeof s);
+    switch (v) {
         case DSPARK_OK: return "ok";
         case DSPARK_EINVAL: return "invalid argument";
         case DSPARK_EDTYPE: return "unsupported dtype";
@@ -128,7 +134,7 @@ size_t dspark_draft_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r) {
 }
 
 size_t dspark_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t r) {
-    if (!head_sizes_ok(B, K, V, r) || B >= (1 << 24)) return 0;
+    if (!head_sizes_ok(B, K, V, r)) return 0;
     return verify_layout(B, K, V, nullptr, nullptr);
 }
 
@@ -318,7 +324,7 @@ dspark_status dspark_calibrate(const dspark_calibrate_args *a, void *ws, size_t 
 
 dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_bytes, void *stream) {
     if (!a) return DSPARK_EINVAL;
-    if (!head_sizes_ok(a->B, a->K, a->V, a->r) || a->B >= (1 << 24)) return DSPARK_EINVAL;
+    if (!head_sizes_ok(a->B, a->K, a->V, a->r)) return DSPARK_EINVAL;
     if (!valid_dtype(a->y_dtype) || !valid_dtype(a->z_dtype) || !valid_dtype(a->uw_dtype))
         return DSPARK_EDTYPE;
     if (!valid_sampler(a->sampler)) return DSPARK_EINVAL;

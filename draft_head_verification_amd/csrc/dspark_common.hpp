@@ -583,8 +583,8 @@ constexpr int kTargetSlabs = 256;    // aim for this many workgroups per launch 
 // Number of V-slabs (workgroups along the vocabulary) a launch over n_rows rows uses; a
 // multiple of 8 so that the slab -> XCD mapping is a bijection.
 inline int num_vslabs(int V, int n_rows) {
-    const int n_tiles = (V + kTileV - 1) / kTileV;
-    const int groups = (n_rows + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int n_tiles = (int)(((long long)V + kTileV - 1) / kTileV);
+    const int groups = (int)(((long long)n_rows + kRowsPerGroup - 1) / kRowsPerGroup);
     int s = kTargetSlabs / (groups > 0 ? groups : 1);
     if (s > n_tiles) s = n_tiles;
     s = (s + 7) / 8 * 8;

@@ -366,45 +366,44 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_select_kernel(
     }
 }
 
-// Scheduling off: every request verifies its whole draft.  One workgroup (it clears the status
-// word before any flag is raised): the survival factors one per thread into LDS (when the
-// expected tokens are asked for and the items fit), then one thread per request forms
-// 1 + sum_{k < L} P in draft order, as the scheduled path does.
-constexpr int kOffThreads = 1024;
+// Scheduling off: every request verifies its whole draft.  One thread per request, spread
+// over small workgroups: its survival factors (independent, so their exponentials overlap),
+// then 1 + sum_{k < L} P in draft order, as the scheduled path forms it.  Workgroup 0 alone
+// writes the status word -- the OR of every request's length check, as a plain store -- so no
+// workgroup clears a flag another has raised.
+constexpr int kOffThreads = 64;
 __global__ __launch_bounds__(kOffThreads) void schedule_off_kernel(
     int B, int K, const float *conf, const int32_t *draft_len, const double *inv_temp,
     int32_t *verify_len, double *expected_tokens, uint32_t *status) {
-    __shared__ double sv[kSchedMaxItems];
     const int tid = threadIdx.x;
-    const bool staged = expected_tokens && B * K <= kSchedMaxItems;
-    if (tid == 0) *status = 0u;
-    if (staged)
-        for (int i = tid; i < B * K; i += kOffThreads)
-            sv[i] = survival(conf[i], inv_temp ? inv_temp[i % K] : 1.0);
-    __syncthreads();
-    for (int b = tid; b < B; b += kOffThreads) {
-        const int raw = draft_len ? draft_len[b] : K;
-        if (raw < 0 || raw > K) atomicOr(status, DSPARK_DEV_BAD_LENGTH);
-        const int kb = raw < 0 ? 0 : (raw > K ? K : raw);
-        verify_len[b] = kb;
-        if (expected_tokens) {
-            double run_p = 1.0, e = 1.0;
-            for (int k = 0; k < kb; ++k) {
-                const size_t i = (size_t)b * K + k;
-                run_p = run_p * (staged ? sv[i] : survival(conf[i], inv_temp ? inv_temp[k] : 1.0));
-                e += run_p;
-            }
-            expected_tokens[b] = e;
+    if (blockIdx.x == 0) {
+        bool bad = false;
+        if (draft_len)
+            for (int b = tid; b < B; b += kOffThreads) bad |= draft_len[b] < 0 || draft_len[b] > K;
+        bad = __any(bad);
+        if (tid == 0) *status = bad ? DSPARK_DEV_BAD_LENGTH : 0u;
+    }
+    const int b = blockIdx.x * kOffThreads + tid;
+    if (b >= B) return;
+    const int raw = draft_len ? draft_len[b] : K;
+    const int kb = raw < 0 ? 0 : (raw > K ? K : raw);
+    verify_len[b] = kb;
+    if (expected_tokens) {
+        double run_p = 1.0, e = 1.0;
+        for (int k = 0; k < kb; ++k) {
+            run_p = run_p * survival(conf[(size_t)b * K + k], inv_temp ? inv_temp[k] : 1.0);
+            e += run_p;
         }
+        expected_tokens[b] = e;
     }
 }
 
 hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, long long *key,
                            int *rank, hipStream_t s) {
     if (!a.enabled) {
-        schedule_off_kernel<<<1, kOffThreads, 0, s>>>(a.B, a.K, a.conf_logits, a.draft_len,
-                                                      a.conf_inv_temp, a.verify_len,
-                                                      a.expected_tokens, status);
+        schedule_off_kernel<<<(a.B + kOffThreads - 1) / kOffThreads, kOffThreads, 0, s>>>(
+            a.B, a.K, a.conf_logits, a.draft_len, a.conf_inv_temp, a.verify_len,
+            a.expected_tokens, status);
         return hipGetLastError();
     }
     const int per = kPrepThreads / a.K;

@@ -120,7 +120,7 @@ typedef struct dspark_trace dspark_trace;
  * a factor held as r x V is converted once, when the weights are loaded, by dspark_pack_w).
  * U and W share a dtype.  Z may be float32 or bfloat16.  Supported: r in [1, 1024]; bfloat16
  * factors with r = 64, 128 or 256 run on the matrix cores, anything else on the
- * vector ALUs.  K in [1, 64].  B >= 0 (B = 0 launches nothing).
+ * vector ALUs.  K in [1, 64].  B in [0, 2^24) (B = 0 launches nothing).
  * Outputs: draft_tokens [B][K] int32, q_tok [B][K] float32, q_lse [B][K] float32; corrected
  * [B][K][V] float32 is optional (NULL skips it) and receives c.
  * req_id [B] (NULL: the request index) keys the random streams of each request.
