@@ -485,12 +485,22 @@ __device__ __forceinline__ void epi_token8(const float c[8], int v, int n_live, 
     const float f = fast_exp2(tl.m - base);  // 0 before the first live entry
     float l = tl.l * f;
     tl.bw *= f;
+    // the winner's token is formed once per call: the last taken offset e (an immediate in
+    // each select) is all the loop tracks
+    int le = 0;
+    bool any = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float w = fast_exp2(fmaf(cm[e], inv, -base));
         l += w;
-        tok_take(tl, w, exp2_from_word(e < 4 ? w0.w[e] : w1.w[e - 4]), v + e);
+        const float E = exp2_from_word(e < 4 ? w0.w[e] : w1.w[e - 4]);
+        const bool take = w * tl.be > tl.bw * E;  // strict: ties keep the lower token
+        tl.bw = take ? w : tl.bw;
+        tl.be = take ? E : tl.be;
+        le = take ? e : le;
+        any = any || take;
     }
+    tl.bi = any ? v + le : tl.bi;
     tl.l = l;
     tl.m = mn;
 }
@@ -528,6 +538,8 @@ __device__ __forceinline__ void epi_resid_token8(const float c[8], const Raw16<Y
                                                  int n_live, const RowInfo &ri, const Philox4 &w0,
                                                  const Philox4 &w1, ResTok &rt) {
     const float inv = kLog2e / ri.T;
+    int le = 0;  // the last taken offset; the token is formed once per call
+    bool any = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const bool in = !MASK || e < n_live;
@@ -537,8 +549,10 @@ __device__ __forceinline__ void epi_resid_token8(const float c[8], const Raw16<Y
         const bool tr = rv * rt.er > rt.br * E;
         rt.br = tr ? rv : rt.br;
         rt.er = tr ? E : rt.er;
-        rt.ir = tr ? v + e : rt.ir;
+        le = tr ? e : le;
+        any = any || tr;
     }
+    rt.ir = any ? v + le : rt.ir;
 }
 
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
