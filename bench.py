@@ -122,7 +122,9 @@ def cpu_baseline(inp, w, n_threads_hint, sampler="token"):
     import oracle
     from draft_head_verification_amd import synth
     threads = oracle.num_threads()
-    n = max(8, min(w.B, 4 * threads))
+    # up to 16 requests per host thread (about 10 s of oracle work at the headline), never
+    # more than the batch
+    n = min(w.B, max(8, 16 * threads))
     rows = list(range(n))
     U, W = inp["U"].cpu(), inp["W"].cpu()
     Zc = inp["Z_ext"][:n, : w.K].cpu().contiguous()
