@@ -147,10 +147,20 @@ def cpu_baseline(inp, w, n_threads_hint, sampler="token"):
                   Zc, U, W, prev, dlen, temp, inp["seed"], req_id=req, rows=rows, sampler=sampler)
     t_verify = time.perf_counter() - t1
     positions = int(dlen.sum())
+    # one core: the first request alone (OpenMP over one request runs on one thread)
+    one = [0]
+    t2 = time.perf_counter()
+    oracle.draft_block(Zc, U, W, prev, temp, inp["seed"], draft_len=dlen, req_id=req, rows=one,
+                       sampler=sampler)
+    oracle.verify(Y, od["tokens"], od["q_tok"].astype(np.float32), od["q_lse"].astype(np.float32),
+                  Zc, U, W, prev, dlen, temp, inp["seed"], req_id=req, rows=one, sampler=sampler)
+    t_one = time.perf_counter() - t2
     return {"value": positions / (t_draft + t_verify), "unit": "positions/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} of {w.B} requests of the same workload ({positions} drafted positions): "
-                      f"oracle draft {t_draft:.2f} s + verify {t_verify:.2f} s, OpenMP over requests"}
+                      f"oracle draft {t_draft:.2f} s + verify {t_verify:.2f} s, OpenMP over requests",
+            "one_core": {"value": int(dlen[0]) / t_one, "unit": "positions/s",
+                         "sample": f"request 0 alone ({int(dlen[0])} positions, {t_one:.2f} s)"}}
 
 
 def round_model_report(w, records, steps, inp, vlen, acc, ms_per_step):
