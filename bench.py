@@ -28,6 +28,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+# Vector-ALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T 32-bit lane operations
+# per second (a wave64 instruction issues over four cycles; packed FP32 is not used)
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Algorithmic vector operations per vocabulary entry and request of one drafting step:
+# sampled (per-token Gumbel-max) -- Philox4x32-10 (10 rounds of two 32x32->64-bit products and
+# four XORs: 60 per call of four tokens, 15 per token), uniform -> E (conversion, scale,
+# logarithm: 3), weight (scale-and-shift, exponential: 2), running sum and maximum (2),
+# candidate test (two products, a compare, three selects: 6), bias add and base-logit decode
+# (2) = 30; greedy -- bias add, decode, compare and two selects = 5
+ALU_OPS_SAMPLED, ALU_OPS_GREEDY = 30, 5
 METRIC = "draft+verify positions/s at V=151936,K=16,B=256; HBM GB/s vs peak"
 
 
@@ -373,6 +383,29 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["achieved_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": traffic}
+    # A drafting step that runs the per-token sampler for most requests is bound by vector-ALU
+    # issue, not HBM: report it against the ALU peak, keeping its HBM figure alongside.
+    if dom["kernel"] == "markov_head_step" and args.sampler == "token":
+        T_h = inp["temperature"].float().cpu()
+        L_h = inp["draft_len"].cpu().clamp(0, K)
+        sampled = (T_h > 0).float()
+        ops_step = float(V * sum(float(L_h[b]) * (ALU_OPS_SAMPLED * sampled[b] +
+                                                   ALU_OPS_GREEDY * (1 - sampled[b]))
+                                 for b in range(B))) / K
+        if sampled.mean().item() >= 0.5:
+            tops = ops_step / (dom["avg_us"] * 1e-6) / 1e12
+            hbm = {k: roofline[k] for k in ("achieved", "peak", "unit", "frac")}
+            roofline.update({"bound": "alu", "achieved": round(tops, 2), "peak": round(ALU_PEAK_TOPS, 1),
+                             "unit": "Tops/s", "frac": round(tops / ALU_PEAK_TOPS, 4),
+                             "algorithmic_ops_per_launch": int(ops_step), "hbm": hbm})
+            valu = None
+            try:
+                ent = json.load(open(args.traffic_json)).get(args.workload, {}).get(dom["kernel"])
+                if ent and ent.get("source_hash") == _kernel_source_hash():
+                    valu = ent.get("valu_busy_pct")
+            except Exception:
+                valu = None
+            roofline["rocprof_valu_busy_pct"] = valu
     # the matrix cores' share of the dominant kernel when it is the bias contraction:
     # 2 B r V bf16 flops per drafting step over the same live launch duration
     if dom["kernel"] == "markov_head_step" and ub == 2 and r in (64, 128, 256):
