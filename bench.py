@@ -370,11 +370,17 @@ def main():
                         "algorithmic_bytes_per_launch": (int(per_launch) if per_launch else per_launch),
                         "achieved_GBs": (round(per_launch / (avg_us * 1e-6) / 1e9, 1) if per_launch else None)})
     dom = next(k for k in kernels if k["algorithmic_bytes_per_launch"])
+    # counters are kept per measured variant: the workload, plus the sampler, temperature,
+    # target and head options that change the kernels' work
+    variant = (args.workload + ("_block16" if args.sampler == "block16" else "")
+               + (f"_t{args.temperature:g}" if args.temperature is not None else "")
+               + ("_exact" if args.targets == "exact" else "")
+               + ("_rnn" if args.head == "rnn" else ""))
     traffic = mfma_util = None
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
-            ent = tj.get(args.workload, {}).get(dom["kernel"])
+            ent = tj.get(variant, {}).get(dom["kernel"])
             if ent and ent.get("source_hash") == _kernel_source_hash():
                 traffic = ent["hbm_bytes_per_launch"]
                 mfma_util = ent.get("mfma_util_pct")
@@ -383,8 +389,9 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["achieved_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": traffic}
-    # A drafting step that runs the per-token sampler for most requests is bound by vector-ALU
-    # issue, not HBM: report it against the ALU peak, keeping its HBM figure alongside.
+    # A drafting step whose per-token sampling takes longer at the vector-ALU issue peak than
+    # its bytes take at the HBM peak is bound by the ALU: report it against that peak, keeping
+    # its HBM figure alongside.
     if dom["kernel"] == "markov_head_step" and args.sampler == "token":
         T_h = inp["temperature"].float().cpu()
         L_h = inp["draft_len"].cpu().clamp(0, K)
@@ -392,7 +399,7 @@ def main():
         ops_step = float(V * sum(float(L_h[b]) * (ALU_OPS_SAMPLED * sampled[b] +
                                                    ALU_OPS_GREEDY * (1 - sampled[b]))
                                  for b in range(B))) / K
-        if sampled.mean().item() >= 0.5:
+        if ops_step / (ALU_PEAK_TOPS * 1e12) > dom["algorithmic_bytes_per_launch"] / (HBM_PEAK_GBS * 1e9):
             tops = ops_step / (dom["avg_us"] * 1e-6) / 1e12
             hbm = {k: roofline[k] for k in ("achieved", "peak", "unit", "frac")}
             roofline.update({"bound": "alu", "achieved": round(tops, 2), "peak": round(ALU_PEAK_TOPS, 1),
@@ -400,7 +407,7 @@ def main():
                              "algorithmic_ops_per_launch": int(ops_step), "hbm": hbm})
             valu = None
             try:
-                ent = json.load(open(args.traffic_json)).get(args.workload, {}).get(dom["kernel"])
+                ent = json.load(open(args.traffic_json)).get(variant, {}).get(dom["kernel"])
                 if ent and ent.get("source_hash") == _kernel_source_hash():
                     valu = ent.get("valu_busy_pct")
             except Exception:
