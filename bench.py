@@ -458,13 +458,22 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _strip_comments(src: str) -> str:
+    """The code of a C++ source without its comments and whitespace (string literals kept)."""
+    import re
+    token = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|\s+', re.S)
+    return token.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", src).replace(" ", "")
+
+
 def _kernel_source_hash() -> str:
+    """Hash of the library's kernel code (comments and whitespace do not count)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "draft_head_verification_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(f.encode())
+            h.update(_strip_comments(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -19,13 +19,15 @@
 //
 // Matrix-core path (bf16 factors, r = 64, 128 or 256):
 //   GEMM view: rows = vocabulary (M), columns = requests (N), reduction = r (K).
-//   A workgroup of 8 waves owns up to 256 requests (32 per wave, two 16-wide column blocks)
-//   and a contiguous slab of the vocabulary.  Each wave keeps its requests' gathered U rows
-//   in registers as MFMA B fragments for the whole slab.  The slab streams through LDS in
-//   tiles of 64 vocabulary rows of W (direct global->LDS loads, four stages, one barrier per
-//   tile); every wave reads its A fragments from the shared tile, so W leaves HBM once per
-//   256 requests.  The fragment layout leaves each lane 16 consecutive vocabulary entries of
-//   a request per tile: exactly one sampler block, so the block sums need no data exchange.
+//   A workgroup owns up to 256 requests and a contiguous slab of the vocabulary: 16 waves of
+//   16 requests at ranks 128 and 256 (8 waves of 32, two 16-wide column blocks, at rank 64
+//   and in the two-level sampler's residual pass).  Each wave keeps its requests' gathered U
+//   rows in registers as MFMA B fragments for the whole slab.  The slab streams through LDS
+//   in tiles of 64 vocabulary rows of W (direct global->LDS loads, four stages, one barrier
+//   per tile); every wave reads its A fragments from the shared tile, so W leaves HBM once
+//   per 256 requests.  The fragment layout leaves each lane 16 consecutive vocabulary entries
+//   of a request per tile: one Philox call per four of them, and for the two-level sampler
+//   exactly one block, whose sums then need no data exchange.
 //   Workgroups are laid out so that the request groups sharing a vocabulary slab are
 //   dispatched to the same XCD and meet the slab's W tiles in that XCD's L2.
 // Vector-ALU path (any other factor dtype / rank): one workgroup per (request, slab); four
@@ -354,12 +356,14 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
 // ---------------------------------------------------------------------------------------
 // Matrix-core kernel
 //
-// Work split: workgroup = 8 waves = up to 256 GEMM rows (requests); a slab of 64-row W tiles.
+// Work split: workgroup = 16 / NQ waves of 16 NQ requests = up to 256 GEMM rows; a slab of
+// 64-row W tiles.
 // MFMA mapping: block j (0..3) of a tile, MFMA row m (= lane & 15) is tile row
 //   trow(j, m) = 16 (m >> 2) + 4 j + (m & 3),
 // so lane l (g = l >> 4) ends up holding tile rows 16 g .. 16 g + 15 of request (l & 15) across
-// the four blocks: 16 contiguous vocabulary entries, i.e. one sampler block, 16-byte
-// base-logit loads, and one race uniform per lane and request (block 4 t + g of tile t).
+// the four blocks: 16 contiguous vocabulary entries (four Philox calls of the per-token draw,
+// or one block of the two-level sampler with its race uniform: block 4 t + g of tile t) and
+// 16-byte base-logit loads.
 // W tiles reach LDS through direct global->LDS loads into a 4-stage ring (3 tiles ahead, no
 // registers); each 16-byte chunk sits at column (col ^ swz(row)) of its row, which makes the
 // A-fragment reads of the 16 lanes of a row group hit 16 different bank groups.
@@ -391,11 +395,12 @@ __device__ __forceinline__ int w_swizzle_resid(int row) {
 // entries are < V).  All are branch-free, so that the compiler can interleave them with the
 // matrix-core instructions of the other half.
 //   kEpiGreedy   every request of the wave is greedy: running max / argmax of c
-//   kEpiSampled  every request is sampled: online softmax statistics, and the block race
-//                once both halves of a block are in (the block's weight is its sum taken
-//                against the running maximum)
+//   kEpiSampled  every request is sampled: online softmax statistics and the per-token
+//                candidate (two-level sampler: the block race once both halves of a block are
+//                in, the block's weight being its sum against the running maximum)
 //   kEpiMixed    both, with the greedy max / argmax kept in (gm, gi)
-//   kEpiResid    residual mode: block race over max(p - q, 0) and over p
+//   kEpiResid    residual mode: the per-token candidate of max(p - q, 0) (two-level sampler:
+//                block races over max(p - q, 0) and over p)
 enum { kEpiGreedy = 0, kEpiSampled = 1, kEpiMixed = 2, kEpiResid = 3 };
 
 // The low half's contribution to a block's race weight, carried to the high half.
