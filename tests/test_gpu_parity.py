@@ -60,11 +60,16 @@ def _ids(c):
             + (f"-{kw['sampler']}" if "sampler" in kw else ""))
 
 
-def run_round(w, T, strong, tally, tag, draft_len_override=None, sampler="token"):
+def run_round(w, T, strong, tally, tag, draft_len_override=None, sampler="token",
+              mask_z=None, mask_y=None):
+    """mask_z(inp) may edit the generated inputs before they are copied to the device;
+    mask_y(Y, oracle_tokens) may edit the target logits both sides receive."""
     from draft_head_verification_amd import dspark as D
     inp = synth.make_inputs(w, temperature=T, strong_bias=strong)
     if draft_len_override is not None:
         inp["draft_len"] = torch.tensor(draft_len_override, dtype=torch.int32)
+    if mask_z is not None:
+        mask_z(inp)
     print(f"[case {tag}] B={w.B} K={w.K} V={w.V} r={w.r}", flush=True)
     g = to_device(inp)
     B, K, V = w.B, w.K, w.V
@@ -97,6 +102,8 @@ def run_round(w, T, strong, tally, tag, draft_len_override=None, sampler="token"
         vlen = inp["draft_len"].clone()
     # ---- verify: both sides get the oracle's draft and targets built from it
     Y = oracle_targets(inp, rows, od["tokens"], inp["U"], inp["W"])
+    if mask_y is not None:
+        mask_y(Y, od["tokens"])
     toks = torch.from_numpy(od["tokens"])
     qt = torch.from_numpy(od["q_tok"].astype(np.float32))
     ql = torch.from_numpy(od["q_lse"].astype(np.float32))
@@ -123,6 +130,65 @@ def test_round_parity(case):
     # the round did real work: some acceptances and some rejections overall
     acc = ov["accept_len"]
     assert acc.min() >= 0
+
+
+MASKED = [
+    ("headline", {"V": 2392}, None),                            # matrix cores, ragged tile
+    ("ragged", {"V": 1208, "r": 128}, None),                    # mixed temperatures
+    ("tiny", {}, 0.0),                                          # vector path, greedy
+    ("tiny", {}, 1.0),
+    ("moderate", {"V": 2392, "sampler": "block16"}, None),      # the two-level sampler
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=lambda c: f"{c[0]}-V{c[1].get('V', 'full')}-T{c[2]}"
+                         + (f"-r{c[1]['r']}" if "r" in c[1] else "")
+                         + (f"-{c[1]['sampler']}" if "sampler" in c[1] else ""))
+def test_masked_vocabulary(case):
+    """A vocabulary mask: a seeded quarter of every base-logit row (the bonus rows included) is
+    -inf, so the target rows built from them carry the same mask, and 5% more target entries
+    are masked, among them the drafted token at position 1 of every third request (p(x) = 0:
+    that test must reject, and the residual is drawn from the rest).  Masked tokens are never
+    drawn; everything else follows the oracle as in the other cases."""
+    name, kw, T = case
+    kw = dict(kw)
+    sampler = kw.pop("sampler", "token")
+    w = synth.shrink(synth.WORKLOADS[name], **kw)
+    rng = np.random.default_rng(2024)
+    kept = {}
+
+    def mask_z(inp):
+        Z = inp["Z_ext"]
+        m = torch.from_numpy(rng.random(tuple(Z.shape)) < 0.25)
+        Z[m] = float("-inf")
+        kept["zmask"] = m.numpy()
+
+    def mask_y(Y, tokens):
+        m = torch.from_numpy(rng.random(tuple(Y.shape)) < 0.05)
+        Y[m] = float("-inf")
+        for b in range(0, Y.shape[0], 3):
+            if tokens.shape[1] > 1 and tokens[b, 1] >= 0:
+                Y[b, 1, int(tokens[b, 1])] = float("-inf")
+        kept["Y"] = Y
+
+    tally = Tally()
+    gd, gv, ov = run_round(w, T, False, tally, f"masked-{name}", sampler=sampler,
+                           mask_z=mask_z, mask_y=mask_y)
+    tally.report(f"masked-{name}")
+    # no masked token is ever drawn: neither a draft token (its base logit) nor the emitted
+    # correction / bonus token (its target logit in the row it was drawn from)
+    toks = gd["tokens"].cpu().numpy()
+    zmask = kept["zmask"]
+    for b in range(w.B):
+        for k in range(w.K):
+            if toks[b, k] >= 0:
+                assert not zmask[b, k, toks[b, k]], (b, k, toks[b, k])
+    acc = gv["accept_len"].cpu().numpy()
+    nxt = gv["next_token"].cpu().numpy()
+    Y = kept["Y"]
+    for b in range(w.B):
+        assert 0 <= nxt[b] < w.V
+        assert torch.isfinite(Y[b, acc[b], nxt[b]]), (b, acc[b], nxt[b])
 
 
 @pytest.mark.parametrize("sampler", ["token", "block16"])
