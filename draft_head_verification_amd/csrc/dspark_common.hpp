@@ -155,8 +155,10 @@ __device__ __forceinline__ void tok_take(TokLane &t, float w, float e, int v) {
     t.bi = take ? v : t.bi;
 }
 
-// Per-token state of a row for merging: softmax statistics (m, l), the best score g, its
-// token and its scaled logit sx (both in log2 units).
+// Per-token state of a row for merging: softmax statistics (m, l), the best score g (log2
+// units), its token, and its scaled logit sx taken against the base m (log2 of its weight):
+// q(x) = exp2(sx) / l needs no difference of two large numbers, so it stays exact to a few
+// ulps at any temperature (the scaled logits themselves reach the hundreds at small T).
 struct TokState {
     float m, l, g, sx;
     int idx;
@@ -178,8 +180,9 @@ __device__ __forceinline__ TokState tok_finish(const TokLane &t) {
     s.l = t.l;
     const bool any = t.bw > 0.f;
     const float base = (t.m == -INFINITY) ? 0.f : t.m;
-    s.sx = any ? base + fast_log2(t.bw) : -INFINITY;
-    s.g = any ? s.sx - fast_log2(t.be) : -INFINITY;
+    const float lw = any ? fast_log2(t.bw) : -INFINITY;
+    s.sx = lw;
+    s.g = any ? (base + lw) - fast_log2(t.be) : -INFINITY;
     s.idx = any ? t.bi : 0x7FFFFFFF;
     return s;
 }
@@ -189,10 +192,13 @@ __device__ __forceinline__ TokState merge_token(TokState a, TokState b) {
     const float l = (mn == -INFINITY) ? 0.f
                                       : a.l * fast_exp2(a.m - mn) + b.l * fast_exp2(b.m - mn);
     const bool take_b = (b.g > a.g) || (b.g == a.g && b.idx < a.idx);
+    // the kept candidate's sx moves to the merged base (a state with no entry has none)
+    const float sa = (a.m == -INFINITY) ? -INFINITY : a.sx + (a.m - mn);
+    const float sb = (b.m == -INFINITY) ? -INFINITY : b.sx + (b.m - mn);
+    a.sx = take_b ? sb : sa;
     if (take_b) {
         a.g = b.g;
         a.idx = b.idx;
-        a.sx = b.sx;
     }
     a.m = mn;
     a.l = l;
@@ -267,12 +273,17 @@ __device__ __forceinline__ void greedy_update(SampleState &st, float c, int v) {
 
 // Softmax statistics of four consecutive scores (already in log2 units; -inf = masked),
 // branch-free: an all -inf history and group leave l = 0.
-__device__ __forceinline__ void lse_update4(SampleState &st, const float s[4]) {
-    const float m4 = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+// Running max / sum of exp2(c * inv) over four logits c (-inf: no entry).  The base is the
+// largest c scaled once (rounding is monotonic and inv > 0), and every weight is
+// exp2(c * inv - base) with one fused multiply-add, so no scaled logit is rounded before the
+// base is taken off.
+__device__ __forceinline__ void lse_update4(SampleState &st, const float c[4], float inv) {
+    const float m4 = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3])) * inv;
     const float mn = fmaxf(st.m, m4);
     const float base = (mn == -INFINITY) ? 0.f : mn;
-    st.l = st.l * fast_exp2(st.m - base) + fast_exp2(s[0] - base) + fast_exp2(s[1] - base) +
-           fast_exp2(s[2] - base) + fast_exp2(s[3] - base);
+    st.l = st.l * fast_exp2(st.m - base) + fast_exp2(fmaf(c[0], inv, -base)) +
+           fast_exp2(fmaf(c[1], inv, -base)) + fast_exp2(fmaf(c[2], inv, -base)) +
+           fast_exp2(fmaf(c[3], inv, -base));
     st.m = mn;
 }
 

@@ -267,36 +267,36 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
             return;
         }
         const float inv = kLog2e / ri.T;
-        float s[4];
+        float cl[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = live ? c[i] * inv : -INFINITY;
+        for (int i = 0; i < 4; ++i) cl[i] = live ? c[i] : -INFINITY;
         if constexpr (SAMP == kSampToken) {
             SampleState ls;
             ls.m = ts.m;
             ls.l = ts.l;
-            lse_update4(ls, s);
+            lse_update4(ls, cl, inv);
             ts.m = ls.m;
             ts.l = ls.l;
             const Philox4 ph = philox4x32_10((uint32_t)v >> 2, (uint32_t)ri.pos, ri.req,
                                              kStreamDraft, p.key0, p.key1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float sc = s[i] - fast_log2(exp2_from_word(ph.w[i]));
+                const float sc = fmaf(cl[i], inv, -fast_log2(exp2_from_word(ph.w[i])));
                 if (sc > ts.g) {  // increasing tokens inside a lane: ties keep the lower one
                     ts.g = sc;
-                    ts.sx = s[i];
+                    ts.sx = cl[i];  // the logit itself until the row's base is final
                     ts.idx = v + i;
                 }
             }
             return;
         }
-        lse_update4(st, s);
-        float M = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        lse_update4(st, cl, inv);
+        float M = fmaxf(fmaxf(cl[0], cl[1]), fmaxf(cl[2], cl[3])) * inv;
         M = fmaxf(M, __shfl_xor(M, 1));
         M = fmaxf(M, __shfl_xor(M, 2));
         const float ref = (M == -INFINITY) ? 0.f : M;
-        float a = fast_exp2(s[0] - ref) + fast_exp2(s[1] - ref) + fast_exp2(s[2] - ref) +
-                  fast_exp2(s[3] - ref);
+        float a = fast_exp2(fmaf(cl[0], inv, -ref)) + fast_exp2(fmaf(cl[1], inv, -ref)) +
+                  fast_exp2(fmaf(cl[2], inv, -ref)) + fast_exp2(fmaf(cl[3], inv, -ref));
         a += __shfl_xor(a, 1);
         a += __shfl_xor(a, 2);
         if (lead) {
@@ -318,8 +318,8 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
                                              kStreamResidual, p.key0, p.key1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pv = live ? fast_exp2(y[i] * inv - ri.lse2p) : 0.f;
-                const float rv = pv - fast_exp2(c[i] * inv - ri.qlse2);
+                const float pv = live ? fast_exp2(fmaf(y[i], inv, -ri.lse2p)) : 0.f;
+                const float rv = pv - fast_exp2(fmaf(c[i], inv, -ri.qlse2));
                 // log2 of a zero weight is -inf: never taken (a row with no positive residual
                 // is drawn from p by the reduction kernel)
                 const float sr = (live && rv > 0.f)
@@ -335,8 +335,8 @@ __device__ __forceinline__ void head_epilogue4(const HeadParams &p, const RowInf
         float R = 0.f, P = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float pv = fast_exp2(y[i] * inv - ri.lse2p);
-            const float rv = pv - fast_exp2(c[i] * inv - ri.qlse2);
+            const float pv = fast_exp2(fmaf(y[i], inv, -ri.lse2p));
+            const float rv = pv - fast_exp2(fmaf(c[i], inv, -ri.qlse2));
             R += live ? fmaxf(rv, 0.f) : 0.f;
             P += pv;
         }
@@ -1109,6 +1109,8 @@ __global__ __launch_bounds__(kValuThreads) void markov_valu_kernel(HeadParams p)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool greedy = ri.T == 0.f;
     const bool token = MODE == HeadMode::Draft && SAMP == kSampToken && !greedy;  // uniform
+    // the candidate's logit against the lane's final base (see TokState)
+    if (token) ts.sx = ts.g > -INFINITY ? fmaf(ts.sx, kLog2e / ri.T, -ts.m) : -INFINITY;
     for (int mask = 1; mask < 64; mask <<= 1) {
         if constexpr (MODE == HeadMode::Draft) {
             if (token) {
@@ -1238,9 +1240,9 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
         for (int s = lane + 64 * kPer; s < n_slabs; s += 64) ts = merge_token(ts, tok_from_partial(prow[s]));
         for (int mask = 1; mask < 64; mask <<= 1) ts = merge_token(ts, shfl_xor_tok(ts, mask));
         x = (ts.g > -INFINITY && ts.idx >= 0 && ts.idx < V) ? ts.idx : -1;
-        const float lse2 = ts.m + fast_log2(ts.l);
-        qt = fast_exp2(ts.sx - lse2);
-        ql = lse2 * kLn2;
+        const float l2 = fast_log2(ts.l);
+        qt = fast_exp2(ts.sx - l2);  // sx is taken against the base m
+        ql = (ts.m + l2) * kLn2;
     } else {
         SampleState st = sample_state_init();
 #pragma unroll
@@ -1268,18 +1270,19 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(
                 const void *op = op_rows ? static_cast<const void *>(op_rows + (size_t)b * r) : U;
                 const float c = wave_corrected16(Z, z_dtype, o, op, W, uw_dtype, r, V,
                                                  op_rows ? 0 : prev, v0);
-                const float s2 = c * (kLog2e / T);
+                const float inv = kLog2e / T;
                 const uint32_t req = req_id ? req_ld : (uint32_t)b;
                 const uint32_t w = token_word((uint32_t)(v0 + e), (uint32_t)k, req,
                                               kStreamDraftWithin, key0, key1);
-                const float sc = in ? s2 + gumbel2_from_word(w) : -INFINITY;
+                const float sc = in ? c * inv + gumbel2_from_word(w) : -INFINITY;
                 int best = v0 + e;
-                float bsc = sc, bs2 = s2;
-                wave_argmax16(bsc, best, bs2);
+                float bsc = sc, bc = c;
+                wave_argmax16(bsc, best, bc);
                 x = (bsc > -INFINITY) ? best : -1;
-                const float lse2 = st.m + fast_log2(st.l);
-                qt = fast_exp2(bs2 - lse2);
-                ql = lse2 * kLn2;
+                // q from the winner's logit against the row's base (one rounding, any T)
+                const float l2 = fast_log2(st.l);
+                qt = fast_exp2(fmaf(bc, inv, -st.m) - l2);
+                ql = (st.m + l2) * kLn2;
             }
         }
     }

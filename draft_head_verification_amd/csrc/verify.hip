@@ -179,8 +179,8 @@ __device__ int decide_rows(int b, int k0, int k1, const ReqInfo &ri, int K, int 
                 accept = xk == a.idx;
                 p = accept ? 1.f : 0.f;
             } else {
-                const float lse2 = a.m + fast_log2(a.l);
-                p = fast_exp2(__shfl(yx, g0 + j) * ri.inv - lse2);
+                // against the row's base m, with one rounding: exact to a few ulps at any T
+                p = fast_exp2(fmaf(__shfl(yx, g0 + j), ri.inv, -a.m) - fast_log2(a.l));
                 const Philox4 ph = philox4x32_10(0u, (uint32_t)k, ri.req, kStreamAccept, key0, key1);
                 accept = uniform_from_word(ph.w[0]) * __shfl(q, g0 + j) < p;
             }
@@ -224,12 +224,15 @@ __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V,
                 for (int e = 0; e < 16; ++e)
                     greedy_update(st, e < n_live ? y[h].get(e) : -INFINITY, v0 + e);
             } else {
+                // weights exp2(y * inv - base), one fused multiply-add each: the base is the
+                // largest y scaled once (rounding is monotonic), no scaled logit is rounded
                 float s[16];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) s[e] = e < n_live ? y[h].get(e) * ri.inv : -INFINITY;
+                for (int e = 0; e < 16; ++e) s[e] = e < n_live ? y[h].get(e) : -INFINITY;
                 float m16 = s[0];
 #pragma unroll
                 for (int e = 1; e < 16; ++e) m16 = fmaxf(m16, s[e]);
+                m16 *= ri.inv;
                 const float mn = fmaxf(st.m, m16);
                 const float base = (mn == -INFINITY) ? 0.f : mn;
                 const float f = fast_exp2(st.m - base);
@@ -243,7 +246,7 @@ __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V,
                                                          key1);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float w = fast_exp2(s[4 * c + i] - base);
+                            const float w = fast_exp2(fmaf(s[4 * c + i], ri.inv, -base));
                             acc += w;
                             tok_take(tl, w, exp2_from_word(ph.w[i]), v0 + 4 * c + i);
                         }
@@ -253,7 +256,7 @@ __device__ __forceinline__ void row_slab_stats(const void *Y, size_t row, int V,
                 } else {
                     float acc = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) acc += fast_exp2(s[e] - base);
+                    for (int e = 0; e < 16; ++e) acc += fast_exp2(fmaf(s[e], ri.inv, -base));
                     st.l = st.l * f + acc;
                     st.m = mn;
                     if (bonus) {
@@ -509,8 +512,8 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
                                                  kStreamResidual, key0, key1);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float pv = fast_exp2(load_value(Y, y_dtype, yrow * (size_t)V + v4 + i) * inv -
-                                               lse2p);
+                    const float pv = fast_exp2(
+                        fmaf(load_value(Y, y_dtype, yrow * (size_t)V + v4 + i), inv, -lse2p));
                     const float E = exp2_from_word(ph.w[i]);
                     const bool take_v = pv * be > bw * E;
                     bw = take_v ? pv : bw;
@@ -544,8 +547,8 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
         const int e = lane & 15;
         const int v = min(v0 + e, V - 1);
         const bool in = v0 + e < V;
-        const float pv = fast_exp2(load_value(Y, y_dtype, yrow * (size_t)V + v) * inv - lse2p);
-        const float rv = pv - fast_exp2(c * inv - qlse2);
+        const float pv = fast_exp2(fmaf(load_value(Y, y_dtype, yrow * (size_t)V + v), inv, -lse2p));
+        const float rv = pv - fast_exp2(fmaf(c, inv, -qlse2));
         const float g = gumbel2_from_word(token_word((uint32_t)(v0 + e), (uint32_t)j, req,
                                                      kStreamResidualWithin, key0, key1));
         const float lw_r = (in && rv > 0.f) ? fast_log2(rv) : -INFINITY;

@@ -42,6 +42,12 @@ CASES = [
     ("single", {"V": 1208, "K": 64, "B": 6, "noise": (0.0, 0.0)}, 1.0, False),
     # two request groups of the matrix-core kernel, the second one partial
     ("concurrent", {"V": 1208, "B": 300}, None, False),
+    # temperatures far from 1 (scaled logits near 100 / near 0.1) and a one-token draft
+    # (a single verification chunk: no decide launch)
+    ("moderate", {"V": 2392, "K": 6}, 0.05, True),
+    ("moderate", {"V": 2392, "K": 6}, 4.0, True),
+    ("headline", {"V": 1208, "K": 1}, None, False),
+    ("tiny", {"K": 1}, 1.0, True),
     # the optional two-level sampler on the vector and matrix-core paths
     ("tiny", {"sampler": "block16"}, 1.0, True),
     ("moderate", {"V": 2392, "sampler": "block16"}, None, True),
