@@ -147,9 +147,24 @@ def _stream(stream):
 
 
 def _ws(ws: torch.Tensor | None, need: int, device) -> torch.Tensor:
+    """The caller's workspace (a contiguous device tensor on the inputs' device; its size is
+    checked by the library), or a new one of the queried size."""
     if ws is None:
         return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace")
+    if ws.device != torch.device(device):
+        raise ValueError(f"workspace is on {ws.device}, the inputs on {device}")
     return ws
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the first input on {device}")
 
 
 _INT = (torch.int32,)
@@ -246,6 +261,10 @@ def _draft_args(Z, U, W, prev_token, temperature, seed, draft_tokens, q_tok, q_l
             _dev(t, n, _F32, shape)
     if head_state is not None:
         _dev(head_state, "head_state", (torch.bfloat16,), (B, K, r))
+    _same_device(Z.device, U=U, W=W, prev_token=prev_token, temperature=temperature,
+                 draft_tokens=draft_tokens, q_tok=q_tok, q_lse=q_lse, draft_len=draft_len,
+                 req_id=req_id, corrected=corrected, head_state=head_state,
+                 **{n: t for n, t in zip(("gru_wi", "gru_wh", "gru_bi", "gru_bh"), g)})
     return DraftArgs(B, K, V, r, _DT[Z.dtype], _DT[U.dtype], _ptr(Z), _ptr(U), _ptr(W),
                      _ptr(prev_token), _ptr(draft_len), _ptr(temperature), _ptr(req_id),
                      int(seed) & (2**64 - 1), _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse),
@@ -267,7 +286,7 @@ def dspark_draft_block(Z, U, W, prev_token, temperature, seed, draft_tokens, q_t
                     draft_len, req_id, corrected, trace, gru, head_state, sampler)
     need = dspark_draft_workspace_size(B, K, V, r)
     ws = _ws(workspace, need, Z.device)
-    st = _lib.dspark_draft_block(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
+    st = _lib.dspark_draft_block(C.byref(a), _ptr(ws), _nbytes(ws), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_draft_block")
     return ws
@@ -307,12 +326,16 @@ def dspark_schedule(conf_logits, verify_len, knot_tokens=None, knot_tps=None, en
         _dev(draft_len, "draft_len", _INT, (B,))
     if expected_tokens is not None:
         _dev(expected_tokens, "expected_tokens", (torch.float64,), (B,))
+    _same_device(conf_logits.device, verify_len=verify_len, inv_temp=inv_temp,
+                 knot_tokens=knot_tokens if enabled else None,
+                 knot_tps=knot_tps if enabled else None, draft_len=draft_len,
+                 expected_tokens=expected_tokens)
     ws = _ws(workspace, dspark_schedule_workspace_size(B, K), conf_logits.device)
     a = ScheduleArgs(B, K, _ptr(conf_logits), _ptr(draft_len), n_knots,
                      _ptr(knot_tokens) if enabled else None, _ptr(knot_tps) if enabled else None,
                      int(bool(enabled)), _ptr(verify_len), _ptr(expected_tokens), _ptr(inv_temp),
                      _trace(trace))
-    st = _lib.dspark_schedule(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
+    st = _lib.dspark_schedule(C.byref(a), _ptr(ws), _nbytes(ws), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_schedule")
     return ws
@@ -331,10 +354,12 @@ def dspark_calibrate(conf_logits, verify_len, accept_len, inv_temp, step=1.0, ri
     _dev(verify_len, "verify_len", _INT, (B,))
     _dev(accept_len, "accept_len", _INT, (B,))
     _dev(inv_temp, "inv_temp", (torch.float64,), (K,))
+    _same_device(conf_logits.device, verify_len=verify_len, accept_len=accept_len,
+                 inv_temp=inv_temp)
     ws = _ws(workspace, dspark_calibrate_workspace_size(B, K), conf_logits.device)
     a = CalibrateArgs(B, K, _ptr(conf_logits), _ptr(verify_len), _ptr(accept_len), _ptr(inv_temp),
                       float(step), float(ridge), _trace(trace))
-    st = _lib.dspark_calibrate(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
+    st = _lib.dspark_calibrate(C.byref(a), _ptr(ws), _nbytes(ws), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_calibrate")
     return ws
@@ -366,13 +391,17 @@ def dspark_verify(Y, draft_tokens, q_tok, q_lse, Z, U, W, prev_token, verify_len
         _dev(p_tok, "p_tok", _F32, (B, K))
     if head_state is not None:
         _dev(head_state, "head_state", (torch.bfloat16,), (B, K, r))
+    _same_device(Z.device, Y=Y, draft_tokens=draft_tokens, q_tok=q_tok, q_lse=q_lse, U=U, W=W,
+                 prev_token=prev_token, verify_len=verify_len, temperature=temperature,
+                 accept_len=accept_len, next_token=next_token, req_id=req_id, p_tok=p_tok,
+                 head_state=head_state)
     ws = _ws(workspace, dspark_verify_workspace_size(B, K, V, r), Z.device)
     a = VerifyArgs(B, K, V, r, _DT[Y.dtype], _DT[Z.dtype], _DT[U.dtype], _ptr(Y),
                    _ptr(draft_tokens), _ptr(q_tok), _ptr(q_lse), _ptr(Z), _ptr(U), _ptr(W),
                    _ptr(prev_token), _ptr(verify_len), _ptr(temperature), _ptr(req_id),
                    int(seed) & (2**64 - 1), _ptr(accept_len), _ptr(next_token), _ptr(p_tok),
                    _trace(trace), _ptr(head_state), _sampler(sampler))
-    st = _lib.dspark_verify(C.byref(a), _ptr(ws), ws.numel(), _stream(stream))
+    st = _lib.dspark_verify(C.byref(a), _ptr(ws), _nbytes(ws), _stream(stream))
     if st != DSPARK_OK:
         raise DSparkError(st, "dspark_verify")
     return ws
@@ -394,6 +423,7 @@ def dspark_pack_w(w_rv: torch.Tensor, out: torch.Tensor | None = None, stream=No
 
 def dspark_query_device_status(workspace: torch.Tensor, stream=None) -> int:
     """Synchronise and return the device status bits of a workspace (0 = clean)."""
+    _dev(workspace, "workspace")
     bits = C.c_uint32(0)
     st = _lib.dspark_query_device_status(_ptr(workspace), _stream(stream), C.byref(bits))
     if st not in (DSPARK_OK, DSPARK_EDEVICE):

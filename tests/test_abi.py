@@ -153,3 +153,22 @@ def test_host_validation_without_gpu():
     empty.B = 0
     assert lib.dspark_calibrate(C.byref(empty), None, 0, None) == D.DSPARK_OK
     assert D.dspark_calibrate_workspace_size(8, 16) == 256 and D.dspark_calibrate_workspace_size(8, 0) == 0
+
+
+def test_binding_rejects_host_workspaces_and_counts_bytes():
+    """The binding hands the library device pointers only: a host tensor as workspace (or as
+    the workspace whose status is queried) is refused before any call, and a workspace's size
+    is passed in bytes whatever its element type."""
+    import pytest
+    import torch
+    from draft_head_verification_amd import dspark as D
+    with pytest.raises(TypeError, match="workspace must be a device tensor"):
+        D._ws(torch.zeros(1024, dtype=torch.uint8), 256, torch.device("cuda", 0))
+    with pytest.raises(TypeError, match="workspace must be a device tensor"):
+        D.dspark_query_device_status(torch.zeros(256, dtype=torch.uint8))
+    assert D._nbytes(torch.zeros(64, dtype=torch.float32)) == 256
+    assert D._nbytes(torch.zeros(64, dtype=torch.uint8)) == 64
+    # tensors on another device than the first input are refused
+    with pytest.raises(ValueError, match="is on cpu"):
+        D._same_device(torch.device("cuda", 0), U=torch.zeros(1))
+    D._same_device(torch.device("cpu"), U=torch.zeros(1), W=None)
