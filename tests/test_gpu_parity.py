@@ -46,6 +46,8 @@ CASES = [
     # (a single verification chunk: no decide launch)
     ("moderate", {"V": 2392, "K": 6}, 0.05, True),
     ("moderate", {"V": 2392, "K": 6}, 4.0, True),
+    ("moderate", {"V": 2392, "K": 6, "sampler": "block16"}, 0.05, True),
+    ("tiny", {}, 0.05, True),
     ("headline", {"V": 1208, "K": 1}, None, False),
     ("tiny", {"K": 1}, 1.0, True),
     # the optional two-level sampler on the vector and matrix-core paths
