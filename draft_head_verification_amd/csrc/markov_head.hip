@@ -574,9 +574,14 @@ __device__ __forceinline__ void tile_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <HeadMode MODE, int SAMP, typename ZT, typename YT, int R, int NQ>
+template <HeadMode MODE, int SAMP, typename ZT, typename YT, int R, int NQ, bool SPLIT>
 __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams p) {
     static_assert(R == 64 || R == 128 || R == 256, "matrix-core path: rank 64, 128 or 256");
+    // SPLIT (drafting with the per-token sampler, at most 128 requests): the two waves of a
+    // pair take one request block, one half of every tile each, so a small batch keeps twice
+    // as many waves busy; the pair's candidates merge through LDS at the end.
+    static_assert(!SPLIT || (NQ == 1 && MODE == HeadMode::Draft && SAMP == kSampToken),
+                  "split pairs: drafting, per-token sampler, one request block per wave");
     static_assert(NQ == 1 || NQ == 2, "one or two 16-wide request blocks per wave");
     constexpr int WAVES = 16 / NQ;                 // waves per workgroup (256 requests)
     constexpr int RPW = 16 * NQ;                   // requests per wave
@@ -619,13 +624,16 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
     const int m = lane & 15, g = lane >> 4;
-    const int n_groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
+    constexpr int ROWS_PER_GROUP = SPLIT ? kRowsPerGroup / 2 : kRowsPerGroup;
+    const int hw = SPLIT ? (wave & 1) : 0;       // split: the half of every tile this wave takes
+    const int rblk = SPLIT ? (wave >> 1) : wave;  // its request block
+    const int n_groups = (p.n_rows_max + ROWS_PER_GROUP - 1) / ROWS_PER_GROUP;
     const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
     const int group = slot % n_groups;
     const int slab = (slot / n_groups) * 8 + xcd;
     // residual mode: every request has its row (B rows) as soon as one needs a residual draw
     const int n_rows = kResid ? (*p.n_rows_dev ? p.n_rows_max : 0) : p.n_rows_max;
-    if (group * kRowsPerGroup >= n_rows || slab >= p.n_slabs) return;  // uniform exit
+    if (group * ROWS_PER_GROUP >= n_rows || slab >= p.n_slabs) return;  // uniform exit
 
     const int n_tiles = (p.V + kTileV - 1) / kTileV;
     const int t_begin = (int)((long long)slab * n_tiles / p.n_slabs);
@@ -679,7 +687,7 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
     size_t zr[NQ] = {}, yr[NQ] = {};  // logit rows of the tile loads
     // (an empty slab issues the same loads, of a valid tile, and never reads them)
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) rowid[q] = group * kRowsPerGroup + wave * RPW + q * 16 + m;
+    for (int q = 0; q < NQ; ++q) rowid[q] = group * ROWS_PER_GROUP + rblk * RPW + q * 16 + m;
     auto load_u = [&](int q, const uint16_t *urow) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
@@ -817,7 +825,8 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
         constexpr bool TOKEN = SAMP == kSampToken;
         // epilogue of half H of tile t from acc, with the race words w[q] of that tile (two-level
         // sampler); the per-token sampler draws the words of the half's 8 tokens here
-        auto epilogue = [&](auto half_tag, int t, const floatx4 (&acc)[2][NQ], const uint32_t (&w)[NQ]) {
+        auto epilogue = [&](auto half_tag, int t, const floatx4 (&acc)[2][NQ], const uint32_t (&w)[NQ],
+                            const Raw16<ZT> (&zz)[NQ]) {
             constexpr int H = decltype(half_tag)::value;
             const int v0 = t * kTileV + 16 * g;  // drafting map: the lane's block
             // residual map: the lane's 8 entries and the start of their block
@@ -829,7 +838,7 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) c[4 * jj + i] = z[q].get(8 * H + 4 * jj + i) + acc[jj][q][i];
+                    for (int i = 0; i < 4; ++i) c[4 * jj + i] = zz[q].get(8 * H + 4 * jj + i) + acc[jj][q][i];
                 if constexpr (STORE) {
                     if (ri[q].valid) {
 #pragma unroll
@@ -873,7 +882,67 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
         };
         using H0 = std::integral_constant<int, 0>;
         using H1 = std::integral_constant<int, 1>;
-        
+
+        if constexpr (SPLIT) {
+            // Half H of every tile; its base logits go out one tile ahead, into two buffers
+            // taken in turn (tile t0 + i in zs[i & 1]).  Tile t0: its logits, the barrier,
+            // W(t0+3), the logits of t0+1, then a wait that forces W(t0+1), W(t0+2), and the
+            // matrix-core work of tile t0.  Tile t: the barrier, W(t+3), then once at most
+            // 2 LPW + NH operations are pending (W(t+2), the logits of t, W(t+3)) the logits
+            // of t-1 have landed, and with them W(t+1): the epilogue of t-1, the logits of
+            // t+1 into the buffer it freed, and the matrix-core work of tile t, whose results
+            // the next tile's epilogue takes.
+            Raw16<ZT> zs[2][NQ];
+            auto load_z = [&](int t, int h, auto clamp_tag, Raw16<ZT> (&zd)[NQ]) {
+                constexpr bool CL = decltype(clamp_tag)::value;
+                const int tc = max(t < t_end ? t : t_end - 1, 0);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    if constexpr (CL)
+                        zd[q].load_half(p.Z, zr[q], p.V, tc * kTileV + 16 * g, h);
+                    else
+                        zd[q].load_half_nc(p.Z, zr[q], p.V, tc * kTileV + 16 * g, h);
+                }
+            };
+            auto split_run = [&](auto half_tag) {
+                constexpr int H = decltype(half_tag)::value;
+                const uint32_t w0[NQ] = {};
+                load_z(t0, H, mask_tag, zs[0]);
+                tile_barrier();
+                issue_w(t0 + 3, 3, mask_tag);
+                load_z(t0 + 1, H, mask_tag, zs[1]);
+                DSPARK_WAIT_VMCNT(LPW + 2 * NH);
+                mfma_half(0, H, acc_lo);
+                auto step = [&](int t, Raw16<ZT> (&zp)[NQ]) {  // zp: the logits of t - 1
+                    tile_barrier();
+                    issue_w(t + 3, (t + 3 - t0) & 3, mask_tag);
+                    DSPARK_WAIT_VMCNT(2 * LPW + NH);
+                    epilogue(half_tag, t - 1, acc_lo, w0, zp);
+                    load_z(t + 1, H, mask_tag, zp);
+                    mfma_half((t - t0) & 3, H, acc_lo);
+                };
+                int t = t0 + 1;
+                for (; t + 1 < t_end; t += 2) {
+                    step(t, zs[0]);
+                    step(t + 1, zs[1]);
+                }
+                if (t < t_end) {
+                    step(t, zs[0]);
+                    ++t;
+                }
+                DSPARK_WAIT_VMCNT(0);
+                // the last tile, t_end - 1 = t - 1, sits in zs[(t - 1 - t0) & 1]
+                if (((t - 1 - t0) & 1) == 0)
+                    epilogue(half_tag, t - 1, acc_lo, w0, zs[0]);
+                else
+                    epilogue(half_tag, t - 1, acc_lo, w0, zs[1]);
+            };
+            if (hw == 0)
+                split_run(H0{});
+            else
+                split_run(H1{});
+            return;
+        }
 
         if constexpr (WORDS) race_words(t0);
         // tile t0: phase A without an epilogue
@@ -890,7 +959,7 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
 #pragma unroll
                 for (int q = 0; q < NQ; ++q) w[q] = word_of(q, t0, 0);
             }
-            epilogue(H0{}, t0, acc_lo, w);
+            epilogue(H0{}, t0, acc_lo, w, z);
         }
         load_half(t0 + 1, 0, mask_tag);
         for (int t = t0 + 1; t < t_end; ++t) {
@@ -910,12 +979,12 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
             }
             DSPARK_WAIT_VMCNT(WAIT_A);
             mfma_half(stg, 0, acc_lo);
-            epilogue(H1{}, t - 1, acc_hi, wp);
+            epilogue(H1{}, t - 1, acc_hi, wp, z);
             // phase B (the high logit registers are free again)
             load_half(t, 1, mask_tag);
             DSPARK_WAIT_VMCNT(WAIT_B);
             mfma_half(stg, 1, acc_hi);
-            epilogue(H0{}, t, acc_lo, wc);
+            epilogue(H0{}, t, acc_lo, wc, z);
             load_half(t + 1, 0, mask_tag);
         }
         // the high half of the last tile
@@ -924,8 +993,8 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
 #pragma unroll
             for (int q = 0; q < NQ; ++q) w[q] = word_of(q, t_end - 1, 1);
         }
-                DSPARK_WAIT_VMCNT(0);
-        epilogue(H1{}, t_end - 1, acc_hi, w);
+        DSPARK_WAIT_VMCNT(0);
+        epilogue(H1{}, t_end - 1, acc_hi, w, z);
     };
 
     // A wave whose rows are all empty (past the batch, or past their drafts) keeps only its
@@ -951,10 +1020,16 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
     using I3 = std::integral_constant<int, kEpiResid>;
     // the low logits of t0, then W(t0+1), W(t0+2); the metadata, the U fragments and W(t0)
     // have landed once only those are pending (phase B of t0 waits for the rest)
-    load_half(t0, 0, B1{});
-    issue_w(t0 + 1, 1, B1{});
-    issue_w(t0 + 2, 2, B1{});
-    DSPARK_WAIT_VMCNT(NL + 2 * LPW);
+    if constexpr (SPLIT) {  // a split wave loads its half's logits in tile t0
+        issue_w(t0 + 1, 1, B1{});
+        issue_w(t0 + 2, 2, B1{});
+        DSPARK_WAIT_VMCNT(2 * LPW);
+    } else {
+        load_half(t0, 0, B1{});
+        issue_w(t0 + 1, 1, B1{});
+        issue_w(t0 + 2, 2, B1{});
+        DSPARK_WAIT_VMCNT(NL + 2 * LPW);
+    }
     if constexpr (!kResid) {
         // Every use of the metadata is made to depend on a clock read that stays after the
         // wait (both have side effects), so none is moved above it, where the compiler would
@@ -1004,6 +1079,35 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
 
     // every global->LDS load has landed before the workgroup can exit
     DSPARK_WAIT_VMCNT(0);
+    TokState tsq[NQ];
+    if constexpr (MODE == HeadMode::Draft) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            if (!(ri[q].T > 0.f) && (wave_sampled || p.corrected)) {  // the mixed epilogue kept it aside
+                st[q].m = gm[q];
+                st[q].idx = gi[q];
+            }
+            tsq[q] = tok_finish(tl[q]);
+        }
+    }
+    if constexpr (SPLIT) {
+        // The high-half wave of each pair hands its lanes' states to the low-half wave through
+        // LDS (the W stages, free once every wave has passed the first barrier); the low-half
+        // wave merges them and writes the partials.  Every wave meets both barriers.
+        struct PairState {
+            SampleState st;
+            TokState ts;
+        };
+        static_assert(sizeof(PairState) * 64 * (16 / 2) <= sizeof(wt), "pair states fit the stages");
+        PairState *ps = reinterpret_cast<PairState *>(wt);
+        tile_barrier();
+        if (wave_active && hw == 1) ps[rblk * 64 + lane] = PairState{st[0], tsq[0]};
+        tile_barrier();
+        if (!wave_active || hw == 1) return;
+        const PairState o = ps[rblk * 64 + lane];
+        merge_into(st[0], o.st, !(ri[0].T > 0.f));
+        tsq[0] = merge_token(tsq[0], o.ts);
+    }
     if (!wave_active) return;
     // merge the four lanes that share a request (lane, lane^16, lane^32, lane^48); every lane
     // runs every shuffle (partners hold the same request and so take the same branches)
@@ -1011,11 +1115,7 @@ __global__ __launch_bounds__(16 / NQ * 64, 1) void markov_mfma_kernel(HeadParams
     for (int q = 0; q < NQ; ++q) {
         if constexpr (MODE == HeadMode::Draft) {
             const bool greedy = !(ri[q].T > 0.f);
-            if (greedy && (wave_sampled || p.corrected)) {  // the mixed epilogue kept it aside
-                st[q].m = gm[q];
-                st[q].idx = gi[q];
-            }
-            TokState ts = tok_finish(tl[q]);
+            TokState ts = tsq[q];
 #pragma unroll
             for (int mask = 16; mask <= 32; mask <<= 1) {
                 const SampleState o = shfl_xor_state(st[q], mask);
@@ -1319,6 +1419,20 @@ static bool use_mfma(int uw_dtype, int r) {
 template <HeadMode MODE, int SAMP, typename ZT, typename YT>
 static hipError_t launch_head_t(const HeadParams &p, int uw_dtype, hipStream_t s) {
     if (use_mfma(uw_dtype, p.r)) {
+        // Drafting at most 128 requests with the per-token sampler (ranks 128, 256, bfloat16
+        // base logits): split pairs, so that a small batch has two waves per request block
+        // (one per half tile).
+        if constexpr (MODE == HeadMode::Draft && SAMP == kSampToken &&
+                      std::is_same<ZT, uint16_t>::value) {
+            if (p.n_rows_max <= kRowsPerGroup / 2 && (p.r == 128 || p.r == 256)) {
+                const dim3 grid(p.n_slabs);
+                if (p.r == 128)
+                    markov_mfma_kernel<MODE, SAMP, ZT, YT, 128, 1, true><<<grid, 16 * 64, 0, s>>>(p);
+                else
+                    markov_mfma_kernel<MODE, SAMP, ZT, YT, 256, 1, true><<<grid, 16 * 64, 0, s>>>(p);
+                return hipGetLastError();
+            }
+        }
         const int groups = (p.n_rows_max + kRowsPerGroup - 1) / kRowsPerGroup;
         // Ranks 128 and 256: 16 waves of 16 requests (four waves per SIMD in 128 registers: the
         // per-token epilogues are bound by vector-ALU issue and hide their latency across
@@ -1328,9 +1442,9 @@ static hipError_t launch_head_t(const HeadParams &p, int uw_dtype, hipStream_t s
         const dim3 grid(p.n_slabs * groups);
         constexpr int NQ = (MODE == HeadMode::Residual && SAMP == kSampBlock) ? 2 : 1;
         switch (p.r) {
-            case 64: markov_mfma_kernel<MODE, SAMP, ZT, YT, 64, 2><<<grid, 8 * 64, 0, s>>>(p); break;
-            case 128: markov_mfma_kernel<MODE, SAMP, ZT, YT, 128, NQ><<<grid, 16 / NQ * 64, 0, s>>>(p); break;
-            case 256: markov_mfma_kernel<MODE, SAMP, ZT, YT, 256, NQ><<<grid, 16 / NQ * 64, 0, s>>>(p); break;
+            case 64: markov_mfma_kernel<MODE, SAMP, ZT, YT, 64, 2, false><<<grid, 8 * 64, 0, s>>>(p); break;
+            case 128: markov_mfma_kernel<MODE, SAMP, ZT, YT, 128, NQ, false><<<grid, 16 / NQ * 64, 0, s>>>(p); break;
+            case 256: markov_mfma_kernel<MODE, SAMP, ZT, YT, 256, NQ, false><<<grid, 16 / NQ * 64, 0, s>>>(p); break;
             default: return hipErrorInvalidValue;
         }
     } else {
