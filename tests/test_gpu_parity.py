@@ -254,6 +254,35 @@ def test_deterministic_across_runs():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("B", [100, 33, 1])
+def test_small_batch_mixed_temperatures_without_corrected_output(B):
+    """Up to 128 requests the drafting step runs split wave pairs; with mixed temperatures and
+    no corrected-logit output it takes the mixed epilogue without stores, which the round cases
+    (they always ask for the corrected logits) do not reach.  Every request against the
+    oracle, and two runs bit for bit."""
+    from draft_head_verification_amd import dspark as D
+    w = synth.shrink(synth.WORKLOADS["ragged"], B=B, V=2392)
+    inp = synth.make_inputs(w, strong_bias=True)
+    g = to_device(inp)
+    outs = []
+    for _ in range(2):
+        d = D.draft_block(g["Z"], g["U"], g["W"], g["prev_token"], g["temperature"],
+                          inp["seed"], draft_len=g["draft_len"], req_id=g["req_id"])
+        outs.append({k: d[k].cpu().numpy() for k in ("tokens", "q_tok", "q_lse")})
+        assert D.dspark_query_device_status(d["workspace"]) == 0
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+    Zc = inp["Z_ext"][:, : w.K].contiguous()
+    od = oracle.draft_block(Zc, inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
+                            inp["seed"], draft_len=inp["draft_len"], req_id=inp["req_id"])
+    temps = inp["temperature"].numpy()
+    if B > 8:  # a wave with greedy and sampled rows
+        assert (temps == 0).any() and (temps > 0).any()
+    tally = Tally()
+    compare_draft(outs[0], od, list(range(B)), temps, tally)
+    tally.report(f"split-mixed-B{B}")
+
+
 @pytest.mark.parametrize("sampler", ["token", "block16"])
 def test_full_batch_draft_deterministic_across_runs(sampler):
     """Every wave of both request groups live (B = 512), bfloat16 and float32 base logits,
