@@ -58,7 +58,7 @@ def test_greedy_chain_matches_torch_argmax_chain():
 
 def test_softmax_normaliser_and_q_tok_match_torch():
     w = synth.WORKLOADS["tiny"]
-    for T in (1.0, 0.7):
+    for T in (1.0, 0.7, 0.05, 4.0):  # the GPU cases' temperatures, far from 1 included
         inp = synth.make_inputs(w, temperature=T)
         res = oracle.draft_block(inp["Z"], inp["U"], inp["W"], inp["prev_token"], inp["temperature"],
                                  inp["seed"], req_id=inp["req_id"], want_corrected=True)
