@@ -30,6 +30,7 @@ CASES = [
     ("ragged", {"V": 2392}, None, False),
     ("headline", {"V": 2392}, None, False),
     ("moderate", {"V": 2392, "r": 64}, None, True),
+    ("moderate", {"V": 2392, "r": 128}, None, True),  # split pairs at rank 128
     ("ragged", {"V": 1208, "r": 128}, None, True),
     ("single", {"V": 1208, "r": 96}, None, True),
     # the largest draft length (65 target rows: every verification chunk), greedy with long
@@ -142,6 +143,7 @@ def test_round_parity(case):
 
 MASKED = [
     ("headline", {"V": 2392}, None),                            # matrix cores, ragged tile
+    ("moderate", {"V": 2392}, None),                            # split pairs (B = 64)
     ("ragged", {"V": 1208, "r": 128}, None),                    # mixed temperatures
     ("tiny", {}, 0.0),                                          # vector path, greedy
     ("tiny", {}, 1.0),
@@ -254,14 +256,14 @@ def test_deterministic_across_runs():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("B", [100, 33, 1])
-def test_small_batch_mixed_temperatures_without_corrected_output(B):
+@pytest.mark.parametrize("B,r", [(100, 256), (33, 256), (1, 256), (100, 128)])
+def test_small_batch_mixed_temperatures_without_corrected_output(B, r):
     """Up to 128 requests the drafting step runs split wave pairs; with mixed temperatures and
     no corrected-logit output it takes the mixed epilogue without stores, which the round cases
     (they always ask for the corrected logits) do not reach.  Every request against the
     oracle, and two runs bit for bit."""
     from draft_head_verification_amd import dspark as D
-    w = synth.shrink(synth.WORKLOADS["ragged"], B=B, V=2392)
+    w = synth.shrink(synth.WORKLOADS["ragged"], B=B, V=2392, r=r)
     inp = synth.make_inputs(w, strong_bias=True)
     g = to_device(inp)
     outs = []
@@ -280,7 +282,7 @@ def test_small_batch_mixed_temperatures_without_corrected_output(B):
         assert (temps == 0).any() and (temps > 0).any()
     tally = Tally()
     compare_draft(outs[0], od, list(range(B)), temps, tally)
-    tally.report(f"split-mixed-B{B}")
+    tally.report(f"split-mixed-B{B}-r{r}")
 
 
 @pytest.mark.parametrize("sampler", ["token", "block16"])
