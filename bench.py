@@ -66,8 +66,10 @@ def parse():
                     help="also measure the verify throughput curve at this workload's shape and "
                          "report the round cost model built from the measured kernel times")
     ap.add_argument("--graph", action="store_true",
-                    help="capture one round (all its launches) in a HIP graph and time graph "
-                         "replays instead of the launches")
+                    help="(the default) capture one round (all its launches) in a HIP graph and "
+                         "time graph replays, each checked against an eager round first")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the round as plain kernel launches instead of graph replays")
     ap.add_argument("--flush", action="store_true",
                     help="time every round on its own, after writing a 512 MB buffer (untimed) so "
                          "that no input is left in L2 or the Infinity Cache; reports the median")
@@ -289,13 +291,23 @@ def main():
         step()
     torch.cuda.synchronize()
     run = step
-    if args.graph:
+    launch = "kernel launches"
+    graph = None
+    if not args.eager:
         # the whole round as one HIP graph: every call enqueues kernels only (no allocation, no
-        # memset, no host sync), so a capture records exactly the round's launches
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
+        # memset, no host sync), so a capture records exactly the round's launches -- the way
+        # a serving loop runs its rounds; a capture that fails leaves the launches timed
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+        except RuntimeError as e:
+            print(f"graph capture failed ({e}); timing kernel launches", file=sys.stderr)
+            graph = None
+            launch = "kernel launches (graph capture failed)"
+            torch.cuda.synchronize()
+    if graph is not None:
         step()  # eager reference outputs
         torch.cuda.synchronize()
         ref = [t.clone() for t in (toks, q_tok, q_lse, vlen, acc, nxt)]
@@ -309,6 +321,7 @@ def main():
             step()  # eager work between replays
             torch.cuda.synchronize()
         run = graph.replay
+        launch = "one HIP graph per round"
     # timed region: the steps alone (no per-kernel events inside)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -447,7 +460,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "caches": "flushed before every round (median round)" if args.flush else "warm",
-        "launch": "one HIP graph per round" if args.graph else "kernel launches",
+        "launch": launch,
         "step_algorithmic_GBs": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "wall_s": round(wall, 3),
         "mean_accept_len": round(float(acc.float().mean().item()), 3),
