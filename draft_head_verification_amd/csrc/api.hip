@@ -341,7 +341,7 @@ dspark_status dspark_verify(const dspark_verify_args *a, void *ws, size_t ws_byt
     verify_layout(a->B, a->K, a->V, &w, reinterpret_cast<char *>(ws));
     hipError_t e;
     int bounds[kMaxChunks + 1];
-    const int n_chunks = verify_chunks(a->K, bounds);
+    const int n_chunks = verify_chunks(*a, bounds);
     for (int c = 0; c < n_chunks; ++c) {
         e = traced(a->trace, "verify_rows", s, [&] { return launch_verify_rows(*a, w, c, s); });
         if (e != hipSuccess) return DSPARK_EHIP;

@@ -697,8 +697,8 @@ hipError_t launch_schedule(const dspark_schedule_args &a, uint32_t *status, long
 hipError_t launch_calibrate(const dspark_calibrate_args &a, uint32_t *status, hipStream_t s);
 
 // Target rows are verified in chunks (one launch each, and a decide launch after every chunk
-// but the last); verify_chunks fills the chunk edges for K and returns their count.
-int verify_chunks(int K, int bounds[kMaxChunks + 1]);
+// but the last); verify_chunks fills the chunk edges of a call and returns their count.
+int verify_chunks(const dspark_verify_args &a, int bounds[kMaxChunks + 1]);
 hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
                               hipStream_t s);
 hipError_t launch_verify_decide(const dspark_verify_args &a, const VerifyWs &ws, int chunk,

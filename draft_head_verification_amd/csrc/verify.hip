@@ -578,15 +578,26 @@ __global__ __launch_bounds__(256) void verify_residual_reduce_kernel(
 // launchers
 // ---------------------------------------------------------------------------------------
 
-int verify_chunks(int K, int bounds[kMaxChunks + 1]) {
-    // rows 0 .. K (K + 1 target rows) in chunks of 2, 3, 4, 8, 16, ... rows
+// Chunk plan of a call.  Rows 0 .. K go in chunks of 2, 3, 4, 8, 16, ... rows: short first
+// chunks, since most requests stop within a few rows.  When the whole target stream is small
+// (at most kOneChunkBytes, a few microseconds of reading) the launches dominate -- a row
+// launch and a decide launch cost ~6 us each -- and all rows go in one chunk, read for every
+// request.  A chunk holds at most 64 rows (one decide wave has a lane per row).
+int verify_chunks(const dspark_verify_args &a, int bounds[kMaxChunks + 1]) {
+    constexpr double kOneChunkBytes = 32.0 * (1 << 20);
+    const int rows = a.K + 1;
+    const double bytes = (double)a.B * a.V * (a.y_dtype == DSPARK_BF16 ? 2 : 4) * rows;
+    bounds[0] = 0;
+    if (rows <= 64 && bytes <= kOneChunkBytes) {
+        bounds[1] = rows;
+        return 1;
+    }
     static const int edges[] = {0, 2, 5, 9, 17, 33, 65};
     int n = 0;
-    bounds[0] = 0;
     for (int i = 1; i < (int)(sizeof(edges) / sizeof(edges[0])); ++i) {
-        const int e = edges[i] < K + 1 ? edges[i] : K + 1;
+        const int e = edges[i] < rows ? edges[i] : rows;
         if (e > bounds[n]) bounds[++n] = e;
-        if (e == K + 1) break;
+        if (e == rows) break;
     }
     return n;
 }
@@ -597,7 +608,7 @@ static int4 *alive_list(const VerifyWs &ws, int c, int B) { return ws.alive + (s
 hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
                               hipStream_t s) {
     int bounds[kMaxChunks + 1];
-    const int n = verify_chunks(a.K, bounds);
+    const int n = verify_chunks(a, bounds);
     if (chunk < 0 || chunk >= n) return hipErrorInvalidValue;
     const int k_lo = bounds[chunk], k_hi = bounds[chunk + 1];
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
@@ -625,7 +636,7 @@ hipError_t launch_verify_rows(const dspark_verify_args &a, const VerifyWs &ws, i
 hipError_t launch_verify_decide(const dspark_verify_args &a, const VerifyWs &ws, int chunk,
                                 hipStream_t s) {
     int bounds[kMaxChunks + 1];
-    const int n = verify_chunks(a.K, bounds);
+    const int n = verify_chunks(a, bounds);
     if (chunk < 0 || chunk + 1 >= n) return hipErrorInvalidValue;  // not the last chunk
     const int k_lo = bounds[chunk], k_hi = bounds[chunk + 1];
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
@@ -650,7 +661,7 @@ hipError_t launch_verify_decide(const dspark_verify_args &a, const VerifyWs &ws,
 
 hipError_t launch_verify_finish(const dspark_verify_args &a, const VerifyWs &ws, hipStream_t s) {
     int bounds[kMaxChunks + 1];
-    const int n = verify_chunks(a.K, bounds);
+    const int n = verify_chunks(a, bounds);
     const uint32_t k0 = (uint32_t)(a.seed & 0xFFFFFFFFu), k1 = (uint32_t)(a.seed >> 32);
     const int per_block = 1;  // one wave per request and workgroup: spread over the CUs
     const dim3 grid((a.B + per_block - 1) / per_block), block(64 * per_block);

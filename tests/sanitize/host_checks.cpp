@@ -17,7 +17,7 @@
 extern "C" const char *stub_log();
 extern "C" void stub_reset();
 namespace dspark {
-int verify_chunks(int K, int *bounds);  // the stand-ins' copy of the library's chunk table
+int verify_chunks(const dspark_verify_args &a, int *bounds);  // the stand-ins' chunk plan
 }
 
 static int failures = 0;
@@ -294,7 +294,7 @@ static void verify_cases() {
             CHECK(dspark_verify(&a, ws.p, need, nullptr) == DSPARK_OK);
             // one row launch per chunk of rows, a decide launch between chunks, then the tail
             int bounds[16];
-            const int n = dspark::verify_chunks(c.K, bounds);
+            const int n = dspark::verify_chunks(a, bounds);
             std::string want;
             for (int ch = 0; ch < n; ++ch)
                 want += ch + 1 < n ? "verify_rows;verify_decide;" : "verify_rows;";

@@ -64,7 +64,9 @@ bool matrix_core_factors(int uw_dtype, int r) {
 }
 bool draft_gathers_rows(const dspark_draft_args &a) { return matrix_core_factors(a.uw_dtype, a.r); }
 bool draft_uses_rnn(const dspark_draft_args &a) { return a.gru_wi != nullptr; }
-int verify_chunks(int K, int bounds[kMaxChunks + 1]) {
+int verify_chunks(const dspark_verify_args &a, int bounds[kMaxChunks + 1]) {
+    // one of the library's plans (any valid plan exercises the same workspace regions)
+    const int K = a.K;
     static const int edges[] = {0, 2, 5, 9, 17, 33, 65};
     int n = 0;
     bounds[0] = 0;
