@@ -33,7 +33,9 @@
  *     from the caller's workspace (size from the *_workspace_size queries, 256-byte aligned).
  *     Calls on distinct workspaces may run concurrently.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is asynchronous on
- *     that stream and never synchronises the host, except dspark_query_device_status.
+ *     that stream and never synchronises the host, except dspark_query_device_status.  The
+ *     three round calls only enqueue kernels (no allocation, memset or copy), so a whole round
+ *     can be captured into a HIP graph and replayed.
  *   - Host-visible argument errors (null pointers, sizes, dtypes, workspace) are returned
  *     before anything is launched.  A failed launch returns DSPARK_EHIP.  Errors in device
  *     data (a token id outside [0, V), a negative or NaN temperature, a bad verify length,
