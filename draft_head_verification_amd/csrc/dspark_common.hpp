@@ -80,30 +80,44 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     return r;
 }
 
-// Uniform u = ((word >> 9) + 1/2) 2^-23: the word's top 23 bits on the midpoints of a 2^-23
-// grid.  u 2^24 = 2 (word >> 9) + 1 is an odd integer below 2^24, so u is a float and the
-// multiply-add below is exact: every uniform is the same number here and in double precision.
+// Uniform u = ((word >> 8) + 0.5) / 2^24 as float.  Exact for u < 1/2; above that the float
+// rounds to the 2^-24 grid (the accept test tolerates it; the samplers use exp_from_word).
 __device__ __forceinline__ float uniform_from_word(uint32_t word) {
-    return fmaf((float)(word >> 9), 0x1p-23f, 0x1p-24f);
+    return fmaf((float)(word >> 8), 0x1p-24f, 0x1p-25f);
 }
 
-// E2 = -log2(u) for the uniform of `word`.  u is exact and v_log_f32 keeps its relative
-// accuracy near 1 (measured on gfx950 over every float in [1/2, 1): 1.0e-7), so E2 is within
-// about 1e-7 relative of -log2(u) for every word -- also where E2 is tiny and the Gumbel draw
-// is large, i.e. where samples are decided.  The per-token draws rank tokens by w / E2, which
-// orders them as w / E with E = -ln u does.
-__device__ __forceinline__ float exp2_from_word(uint32_t word) {
-    return -fast_log2(uniform_from_word(word));
-}
-
-// E = -ln(u) = ln(2) E2.
+// E = -ln(u) for the uniform of `word`, accurate in relative terms over the whole range:
+// for u < 1/2 the float u is exact; for u >= 1/2 the complement d = 1 - u is exact in float
+// and, when d < 2^-8, E = d + d^2/2 + d^3/3 (truncation < 2^-26 relative) -- this is the
+// region where E is tiny and the Gumbel draw -ln E is large, i.e. where samples are decided.
 __device__ __forceinline__ float exp_from_word(uint32_t word) {
-    return exp2_from_word(word) * kLn2;
+    const uint32_t m = word >> 8;
+    const float u = fmaf((float)m, 0x1p-24f, 0x1p-25f);
+    const float d = fmaf((float)(0xFFFFFFu - m), 0x1p-24f, 0x1p-25f);
+    const float series = d * fmaf(d, fmaf(d, 0.33333334f, 0.5f), 1.0f);
+    const float direct = -fast_log2(u) * kLn2;
+    return d < 0x1p-8f ? series : direct;
 }
 
 // Gumbel draw of a word in log2 units: -log2(E) = log2(e) * (-ln E).
 __device__ __forceinline__ float gumbel2_from_word(uint32_t word) {
     return -fast_log2(exp_from_word(word));
+}
+
+// E2 = -log2(u) = log2(e) * E for the uniform of `word`, accurate in relative terms (the
+// per-token draws rank tokens by w / E2, which orders them as w / E does).  u = (m + 1/2) 2^-24
+// is exact in float for u < 1/2 and rounds to the 2^-24 grid above; the rounding
+// e = u - fl(u) (0 or +-2^-25) is recovered exactly (m 2^-24 - fl(u) is exact, then + 2^-25),
+// and -log2(u) = -log2(fl(u)) - log2(e) e / u to first order, with 1/u replaced by 1 (the
+// difference is e (1 - u) / u, below 2^-25 relative to E2).  v_log_f32 keeps its relative
+// accuracy near 1 (measured on gfx950 over every float in [1/2, 1): 1.0e-7), so E2 is within
+// 1.5e-7 relative of -log2(u) for every word -- also where E2 is tiny and the draw is large,
+// i.e. where samples are decided.
+__device__ __forceinline__ float exp2_from_word(uint32_t word) {
+    const float fm = (float)(word >> 8);
+    const float u = fmaf(fm, 0x1p-24f, 0x1p-25f);
+    const float e = fmaf(fm, 0x1p-24f, -u) + 0x1p-25f;  // u - fl(u), exact
+    return fmaf(e, -kLog2e, -fast_log2(u));
 }
 
 // ---------------------------------------------------------------------------------------

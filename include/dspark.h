@@ -47,8 +47,8 @@
  *   - Vocabulary size V must be a multiple of 8 (vectorised row loads).
  *
  * Randomness (all three calls): Philox4x32-10 (Salmon et al., SC'11) keyed by `seed`
- * (low word, high word); a draw takes one output word w and u = ((w >> 9) + 0.5) / 2^23 in
- * (0, 1) (a float in single precision too), G = -log(-log u) a standard Gumbel draw.  Token v's draw on stream s at position k
+ * (low word, high word); a draw takes one output word w and u = ((w >> 8) + 0.5) / 2^24 in
+ * (0, 1), G = -log(-log u) a standard Gumbel draw.  Token v's draw on stream s at position k
  * uses word v & 3 of the block at counter (v >> 2, k, request key, s).
  *
  * Sampling a token from weights w_v = exp(a_v) (the pages fix the law: the draft token follows

@@ -39,9 +39,7 @@
  *    means greedy (argmax).  Ties in every argmax go to the lowest vocabulary index.
  *  - Random numbers: Philox4x32 with 10 rounds (Salmon et al., SC'11), key = (seed low word,
  *    seed high word), counter = (v >> 2, position, request key, stream), output word v & 3,
- *    uniform = ((word >> 9) + 0.5) * 2^-23, which lies strictly inside (0, 1): the top 23 bits
- *    of the word on the midpoints of a 2^-23 grid, so that every uniform is a float (24
- *    significant bits) and single precision holds it without rounding.
+ *    uniform = ((word >> 8) + 0.5) * 2^-24, which lies strictly inside (0, 1).
  *    Streams: 0 draft sampling, 1 accept test (v = 0), 2 residual resampling, 3 bonus
  *    (4 / 5 / 6: within-block draws of the optional two-level sampler).
  *  - Sampling a token from weights w_v = exp(a_v) (the pages fix the law: the draft token follows
@@ -157,12 +155,6 @@ void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t
     out[3] = c[3];
 }
 
-/* The uniform of one output word (see the readings above). */
-static double word_uniform(uint32_t w)
-{
-    return ((double)(w >> 9) + 0.5) * (1.0 / 8388608.0);
-}
-
 /* Uniform in (0,1) for vocabulary index v at (request key, position, stream). */
 double oracle_uniform(uint64_t seed, uint32_t req, uint32_t pos, uint32_t v, uint32_t stream)
 {
@@ -170,7 +162,8 @@ double oracle_uniform(uint64_t seed, uint32_t req, uint32_t pos, uint32_t v, uin
     uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
     uint32_t out[4];
     oracle_philox4x32_10(ctr, key, out);
-    return word_uniform(out[v & 3u]);
+    uint32_t w = out[v & 3u];
+    return ((double)(w >> 8) + 0.5) * (1.0 / 16777216.0);
 }
 
 /* Standard Gumbel draw from the uniform above. */
@@ -192,7 +185,7 @@ double oracle_block_uniform(uint64_t seed, uint32_t req, uint32_t pos, uint32_t 
     uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
     uint32_t out[4];
     oracle_philox4x32_10(ctr, key, out);
-    return word_uniform(out[b]);
+    return ((double)(out[b] >> 8) + 0.5) * (1.0 / 16777216.0);
 }
 
 static int argmax_double(const double *a, int n, double *gap);

@@ -79,7 +79,7 @@ def rocrand_gumbel(rocrand_pin):
     """Gumbel draws of tokens 0..n-1 at (seed, request key, position, stream) computed from
     rocRAND's Philox words with the documented keying: word v & 3 of the block at counter
     (v >> 2, position, request key, stream) under key (seed low, seed high),
-    u = ((word >> 9) + 0.5) 2^-23, G = -log(-log u)."""
+    u = ((word >> 8) + 0.5) 2^-24, G = -log(-log u)."""
     import numpy as np
 
     def gumbel(seed, req, pos, n, stream):
@@ -88,6 +88,6 @@ def rocrand_gumbel(rocrand_pin):
         ctrs = np.stack([v >> 2, np.full(n, pos), np.full(n, req), np.full(n, stream)],
                         1).astype(np.uint32)
         words = rocrand_pin(np.repeat(key[None], n, 0), ctrs)[v, v & 3]
-        u = ((words >> 9).astype(np.float64) + 0.5) / 2.0**23
+        u = ((words >> 8).astype(np.float64) + 0.5) / 2.0**24
         return -np.log(-np.log(u))
     return gumbel

