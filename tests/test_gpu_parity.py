@@ -58,6 +58,12 @@ CASES = [
     ("single", {"V": 1208, "K": 64, "B": 6, "sampler": "block16"}, 1.0, False),
     ("single", {"V": 1208, "K": 64, "B": 6, "noise": (0.0, 0.0), "sampler": "block16"}, 1.0,
      False),
+    # a vocabulary below one 64-row tile on the matrix-core path: one partial tile, held by the
+    # last of eight slabs, the other seven empty; one sampler block partial
+    ("moderate", {"V": 40, "B": 20, "K": 3}, 1.0, True),          # split pairs
+    ("headline", {"V": 56, "B": 300, "K": 2}, 1.0, True),         # two request groups
+    ("single", {"V": 40, "B": 3, "K": 4}, None, True),            # greedy
+    ("moderate", {"V": 40, "B": 20, "K": 3, "sampler": "block16"}, 1.0, True),
 ]
 
 
