@@ -3,8 +3,9 @@
 Sizes keep the recipe of each workload but shrink the vocabulary to a few thousand entries,
 which still spans many 64-row W tiles and leaves a ragged last tile (V = 2392 = 37*64 + 24).
 The rank stays 256 (bf16 factors -> matrix-core path) except in the float32 "tiny" workload
-(rank 16 -> vector path) and three cases that change it: ranks 64 and 128 (the other
-matrix-core instantiations) and 96 (bf16 factors on the vector path).  Every case runs the
+(rank 16 -> vector path) and the cases that change it: ranks 64 and 128 (the other
+matrix-core instantiations), 96 (bf16 factors on the vector path) and the rank limits 1 and
+1024 (vector path).  Every case runs the
 default per-token sampler; the cases marked block16 run the optional two-level sampler against
 the oracle's same mode.  Tolerances and near-tie rules: tests/parity.py.
 """
@@ -64,6 +65,10 @@ CASES = [
     ("headline", {"V": 56, "B": 300, "K": 2}, 1.0, True),         # two request groups
     ("single", {"V": 40, "B": 3, "K": 4}, None, True),            # greedy
     ("moderate", {"V": 40, "B": 20, "K": 3, "sampler": "block16"}, 1.0, True),
+    # the rank limits of the vector-ALU head (r = 1 and r = 1024, float32 and bfloat16 factors)
+    ("tiny", {"r": 1024}, 1.0, True),
+    ("tiny", {"r": 1}, 0.0, True),
+    ("moderate", {"V": 1208, "r": 1024, "B": 6, "K": 3}, 1.0, True),
 ]
 
 
