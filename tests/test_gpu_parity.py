@@ -379,3 +379,83 @@ def test_empty_batch_is_noop():
                          torch.empty(0, 4, dtype=torch.int32, device="cuda"),
                          torch.empty(0, 4, device="cuda"), torch.empty(0, 4, device="cuda"))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("moderate", {"V": 2392, "B": 20, "K": 3}),    # matrix cores, split pairs
+    ("headline", {"V": 2392, "B": 300, "K": 3}),   # matrix cores, two request groups
+    ("tiny", {"K": 3}),                            # vector path
+])
+def test_greedy_exact_ties_take_the_lowest_index(name, kw):
+    """Exact ties in every greedy argmax go to the lowest vocabulary index.  With zero factors
+    the corrected logit is the base logit itself; each base row and each target row holds its
+    maximum at four indices spread over lanes, tiles and slabs.  The drafted tokens, accepted
+    lengths and next tokens must be exactly those of the lowest tied indices (checked directly:
+    the parity helpers' near-tie allowance would pass a wrong tie order at a gap of zero)."""
+    from draft_head_verification_amd import dspark as D
+    w = synth.shrink(synth.WORKLOADS[name], **kw)
+    inp = synth.make_inputs(w, temperature=0.0)
+    B, K, V = w.B, w.K, w.V
+    print(f"[ties {name}] B={B} K={K} V={V} r={w.r}", flush=True)
+    inp["U"].zero_()
+    inp["W"].zero_()
+    rng = np.random.default_rng(11)
+    top = 32.0  # exact in bfloat16, above every generated logit
+    Zx = inp["Z_ext"]
+    assert float(Zx.float().max()) < top
+    z_ties = np.sort(np.stack([rng.choice(V, 4, replace=False) for _ in range(B * (K + 1))]),
+                     axis=1).reshape(B, K + 1, 4)
+    for b in range(B):
+        for k in range(K + 1):
+            Zx[b, k, torch.from_numpy(z_ties[b, k])] = top
+    g = to_device(inp)
+    gd = D.draft_block(g["Z"], g["U"], g["W"], g["prev_token"], g["temperature"], inp["seed"],
+                       draft_len=g["draft_len"], req_id=g["req_id"])
+    assert D.dspark_query_device_status(gd["workspace"]) == 0
+    toks = gd["tokens"].cpu().numpy()
+    dl = inp["draft_len"].numpy()
+    for b in range(B):
+        for k in range(K):
+            assert toks[b, k] == (z_ties[b, k, 0] if k < dl[b] else -1), (b, k, toks[b, k])
+    # targets: row k's maximum at four indices; a third of the rows put the drafted token
+    # first among them (accept), a third put a lower index before it, a third leave it out
+    ydt = w.y_dtype
+    Y = torch.from_numpy(rng.normal(0.0, 1.0, (B, K + 1, V)).astype(np.float32))
+    for b in range(B):
+        for k in range(K + 1):
+            x = int(toks[b, k]) if k < K and toks[b, k] >= 0 else -1
+            mode = (b + k) % 3
+            if x >= 0 and mode == 0:
+                others = rng.choice(np.arange(x + 1, V), 3, replace=False)
+                idx = np.concatenate([[x], others])
+            elif x > 0 and mode == 1:
+                lower = rng.integers(0, x)
+                others = rng.choice(np.setdiff1d(np.arange(V), [x, lower]), 2, replace=False)
+                idx = np.concatenate([[lower, x], others])
+            else:
+                idx = rng.choice(np.setdiff1d(np.arange(V), [x]), 4, replace=False)
+            Y[b, k, torch.from_numpy(np.asarray(idx, dtype=np.int64))] = top
+    Y = Y.to(ydt)
+    vlen = inp["draft_len"].clone()
+    qt = torch.from_numpy((toks >= 0).astype(np.float32))
+    ql = torch.zeros(B, K)
+    gv = D.verify(Y.cuda(), torch.from_numpy(toks).cuda(), qt.cuda(), ql.cuda(), g["Z"], g["U"],
+                  g["W"], g["prev_token"], vlen.cuda(), g["temperature"], inp["seed"],
+                  req_id=g["req_id"])
+    assert D.dspark_query_device_status(gv["workspace"]) == 0
+    acc = gv["accept_len"].cpu().numpy()
+    nxt = gv["next_token"].cpu().numpy()
+    Yf = Y.float().numpy()
+    for b in range(B):
+        L = int(vlen[b])
+        a = 0
+        while a < L and int(np.argmax(Yf[b, a])) == toks[b, a]:  # np.argmax: first maximum
+            a += 1
+        assert acc[b] == a, (b, acc[b], a)
+        assert nxt[b] == int(np.argmax(Yf[b, a])), (b, nxt[b], int(np.argmax(Yf[b, a])))
+    # and the oracle agrees on the same inputs
+    ov = oracle.verify(Y, torch.from_numpy(toks), qt, ql, inp["Z_ext"][:, :K].contiguous(),
+                       inp["U"], inp["W"], inp["prev_token"], vlen, inp["temperature"],
+                       inp["seed"], req_id=inp["req_id"])
+    np.testing.assert_array_equal(acc, ov["accept_len"])
+    np.testing.assert_array_equal(nxt, ov["next_token"])
