@@ -117,10 +117,13 @@ __device__ __forceinline__ ReqInfo req_info(int b, int K, const int32_t *verify_
 // One wave: merge the slab statistics of rows [k0, k1) of request b (rows past L are not
 // verified) and take their accept decisions in order.  Returns the first rejected row, or -1.
 // The writer records row statistics, p(x_k) and the rejection; every caller computes the same.
-// *last receives the statistics of the last row merged (the rejected row, or row L).
-// Everything a decision reads is fetched up front (lane j holds row k0 + j's draft token,
-// target logit and q; the slab partials of eight rows at a time), so a chunk costs a couple of
-// memory round trips rather than a few per row.
+// *last receives the statistics of the deciding row (the rejected row, or row L).
+// Rows go eight at a time, one group of eight lanes per row: lane i of group j folds slots
+// i, i + 8, i + 16, ... of its row in that order, then the group merges over xor masks 1, 2, 4
+// -- a fixed order, so a row's statistics are the same in every caller.  Each group takes its
+// row's accept decision; the first deciding row of the eight (a rejection, or row L) is found
+// with one ballot.  Everything a pass reads goes out together (the slab partials, and each
+// row's draft token, q and target logit), so eight rows cost one or two memory round trips.
 template <typename YT>
 __device__ int decide_rows(int b, int k0, int k1, const ReqInfo &ri, int K, int V, int S,
                            const void *Y, const int32_t *draft_tokens, const float *q_tok,
@@ -130,66 +133,70 @@ __device__ int decide_rows(int b, int k0, int k1, const ReqInfo &ri, int K, int 
     const int lane = threadIdx.x & 63;
     const int n = min(k1, ri.L + 1) - k0;  // rows to merge (at most 64)
     if (n <= 0) return -1;
+    constexpr int G = 8, LPR = 64 / G, PF = 8;  // rows per pass, lanes per row, slots in flight
+    const int j = lane / LPR, i = lane % LPR;
     const size_t rbase = (size_t)b * (K + 1);
-    int x = 0;
-    float yx = 0.f, q = 0.f;
-    if (lane < n && k0 + lane < ri.L) {
-        const int k = k0 + lane;
-        x = draft_tokens[(size_t)b * K + k];
-        if (x < 0 || x >= V) {
-            if (writer) atomicOr(status, DSPARK_DEV_BAD_TOKEN);
-            x = 0;
-        }
-        if (!ri.greedy) {
-            q = q_tok[(size_t)b * K + k];
-            yx = load1<YT>(Y, (rbase + k) * (size_t)V + x);
-        }
-    }
-    const Partial none = to_partial(sample_state_init());
-    constexpr int G = 8;
     for (int g0 = 0; g0 < n; g0 += G) {
-        Partial pr[G];
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            // always a valid address (clamped row and slot); entries outside are replaced
-            const int jr = min(g0 + j, n - 1), sl = min(lane, S - 1);
-            const Partial t = row_partials[(rbase + k0 + jr) * S + sl];
-            pr[j] = (g0 + j < n && lane < S) ? t : none;
-        }
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            if (g0 + j >= n) break;  // uniform
-            const int k = k0 + g0 + j;
-            const size_t row = rbase + k;
-            SampleState a = from_partial(pr[j]);
-            for (int s = lane + 64; s < S; s += 64)
-                merge_into(a, from_partial(row_partials[row * S + s]), ri.greedy);
-            for (int mask = 1; mask < 64; mask <<= 1) {
-                const SampleState o = shfl_xor_state(a, mask);
-                merge_into(a, o, ri.greedy);
+        const bool valid = g0 + j < n;
+        const int k = k0 + min(g0 + j, n - 1);  // rows past the pass's end repeat its last row
+        const size_t row = rbase + k;
+        const bool tested = k < ri.L;
+        int x = 0;
+        float yx = 0.f, q = 0.f;
+        if (tested) {
+            x = draft_tokens[(size_t)b * K + k];
+            if (x < 0 || x >= V) {
+                if (writer && i == 0) atomicOr(status, DSPARK_DEV_BAD_TOKEN);
+                x = 0;
             }
-            const float4 stats = make_float4(a.m, a.l, __int_as_float(a.idx), a.g);
-            if (writer && lane == 0) rowstats[row] = stats;
-            if (last) *last = stats;
-            if (k == ri.L) return -1;  // the bonus row: nothing to test
-            const int xk = __shfl(x, g0 + j);
-            bool accept;
-            float p;
+            if (!ri.greedy) {
+                q = q_tok[(size_t)b * K + k];
+                yx = load1<YT>(Y, row * (size_t)V + x);
+            }
+        }
+        Partial pr[PF];
+#pragma unroll
+        for (int t = 0; t < PF; ++t) pr[t] = row_partials[row * S + min(i + LPR * t, S - 1)];
+        SampleState a = sample_state_init();
+#pragma unroll
+        for (int t = 0; t < PF; ++t)
+            if (i + LPR * t < S) merge_into(a, from_partial(pr[t]), ri.greedy);
+        for (int sl = i + LPR * PF; sl < S; sl += LPR)
+            merge_into(a, from_partial(row_partials[row * S + sl]), ri.greedy);
+#pragma unroll
+        for (int mask = 1; mask < LPR; mask <<= 1) {
+            const SampleState o = shfl_xor_state(a, mask);
+            merge_into(a, o, ri.greedy);
+        }
+        bool accept = true;
+        float p = 0.f;
+        if (tested) {
             if (ri.greedy) {
-                accept = xk == a.idx;
+                accept = x == a.idx;
                 p = accept ? 1.f : 0.f;
             } else {
                 // against the row's base m, with one rounding: exact to a few ulps at any T
-                p = fast_exp2(fmaf(__shfl(yx, g0 + j), ri.inv, -a.m) - fast_log2(a.l));
+                p = fast_exp2(fmaf(yx, ri.inv, -a.m) - fast_log2(a.l));
                 const Philox4 ph = philox4x32_10(0u, (uint32_t)k, ri.req, kStreamAccept, key0, key1);
-                accept = uniform_from_word(ph.w[0]) * __shfl(q, g0 + j) < p;
+                accept = uniform_from_word(ph.w[0]) * q < p;
             }
-            if (writer && lane == 0) {
-                if (p_tok) p_tok[(size_t)b * K + k] = p;
-                if (!accept)
-                    __hip_atomic_store(first_reject + b, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            if (!accept) return k;
+        }
+        // the first deciding row of the pass: a rejection, or row L (nothing to test there)
+        const unsigned long long dec = __ballot(valid && i == 0 && (k == ri.L || !accept));
+        const int jd = dec ? (int)(__builtin_ctzll(dec) / LPR) : G;  // uniform
+        if (writer && valid && i == 0 && j <= jd) {
+            rowstats[row] = make_float4(a.m, a.l, __int_as_float(a.idx), a.g);
+            if (tested && p_tok) p_tok[(size_t)b * K + k] = p;
+            if (j == jd && tested && !accept)
+                __hip_atomic_store(first_reject + b, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (jd < G) {
+            const int src = jd * LPR;
+            if (last)
+                *last = make_float4(__shfl(a.m, src), __shfl(a.l, src),
+                                    __int_as_float(__shfl(a.idx, src)), __shfl(a.g, src));
+            const int kd = k0 + g0 + jd;
+            return kd == ri.L ? -1 : kd;
         }
     }
     return -1;
