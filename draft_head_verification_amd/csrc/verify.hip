@@ -389,11 +389,9 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
     // every position before the first rejection was decided
     const bool rejected = fr < ri.L;
     const int a = rejected ? fr : ri.L;
-    if (lane == 0) {
-        if (p_tok)  // positions after the deciding one were not tested
-            for (int k = a + (rejected ? 1 : 0); k < K; ++k) p_tok[(size_t)b * K + k] = 0.f;
-        accept_len[b] = a;
-    }
+    if (p_tok)  // positions after the deciding one were not tested
+        for (int k = a + (rejected ? 1 : 0) + lane; k < K; k += 64) p_tok[(size_t)b * K + k] = 0.f;
+    if (lane == 0) accept_len[b] = a;
     if (rejected && !ri.greedy) {
         // row b of the residual pass (no compaction: a shared counter would serialise the
         // waves' atomics); the flag only tells the residual launches that there is work
