@@ -69,6 +69,8 @@ CASES = [
     ("tiny", {"r": 1024}, 1.0, True),
     ("tiny", {"r": 1}, 0.0, True),
     ("moderate", {"V": 1208, "r": 1024, "B": 6, "K": 3}, 1.0, True),
+    # target rows with more slab partials than the decide step folds from registers (148 > 64)
+    ("single", {"V": 600000, "B": 2, "K": 2}, 1.0, True),
 ]
 
 
