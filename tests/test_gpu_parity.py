@@ -71,6 +71,12 @@ CASES = [
     ("moderate", {"V": 1208, "r": 1024, "B": 6, "K": 3}, 1.0, True),
     # target rows with more slab partials than the decide step folds from registers (148 > 64)
     ("single", {"V": 600000, "B": 2, "K": 2}, 1.0, True),
+    # float32 base logits with bfloat16 factors: the matrix-core kernels' float32-logit
+    # instantiations (drafting and the residual pass, both samplers, one and two request groups)
+    ("headline", {"V": 2392, "B": 40, "K": 4, "z_dtype": torch.float32}, 1.0, True),
+    ("single", {"V": 2392, "B": 3, "z_dtype": torch.float32}, None, True),
+    ("concurrent", {"V": 1208, "B": 300, "z_dtype": torch.float32}, None, False),
+    ("moderate", {"V": 2392, "K": 6, "z_dtype": torch.float32, "sampler": "block16"}, 1.0, True),
 ]
 
 
@@ -79,6 +85,7 @@ def _ids(c):
     return (f"{name}-V{kw.get('V', 'full')}-T{T}-{'strong' if strong else 'std'}"
             + (f"-K{kw['K']}" if "K" in kw else "") + (f"-r{kw['r']}" if "r" in kw else "")
             + (f"-B{kw['B']}" if "B" in kw else "") + ("-exact" if "noise" in kw else "")
+            + ("-z32" if "z_dtype" in kw else "")
             + (f"-{kw['sampler']}" if "sampler" in kw else ""))
 
 
