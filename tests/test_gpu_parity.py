@@ -77,6 +77,8 @@ CASES = [
     ("single", {"V": 2392, "B": 3, "z_dtype": torch.float32}, None, True),
     ("concurrent", {"V": 1208, "B": 300, "z_dtype": torch.float32}, None, False),
     ("moderate", {"V": 2392, "K": 6, "z_dtype": torch.float32, "sampler": "block16"}, 1.0, True),
+    # rank 64 (eight waves of two request blocks) with the two-level sampler
+    ("moderate", {"V": 2392, "r": 64, "sampler": "block16"}, 1.0, True),
 ]
 
 
