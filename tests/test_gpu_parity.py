@@ -79,6 +79,10 @@ CASES = [
     ("moderate", {"V": 2392, "K": 6, "z_dtype": torch.float32, "sampler": "block16"}, 1.0, True),
     # rank 64 (eight waves of two request blocks) with the two-level sampler
     ("moderate", {"V": 2392, "r": 64, "sampler": "block16"}, 1.0, True),
+    # bfloat16 factors on the vector path with the two-level sampler; float32 base logits at
+    # rank 128 on the matrix cores
+    ("moderate", {"V": 1208, "r": 96, "K": 5, "sampler": "block16"}, 1.0, True),
+    ("ragged", {"V": 1208, "r": 128, "z_dtype": torch.float32}, None, True),
 ]
 
 
