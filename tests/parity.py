@@ -178,4 +178,7 @@ def compare_verify(g: dict, o: dict, rows, temps, tally: Tally):
         if g.get("p_tok") is not None:
             np.testing.assert_allclose(g["p_tok"][b, :tested], o["p_tok"][i, :tested], rtol=0,
                                        atol=TOL_Q)
+            # positions after the deciding one were not tested: p is 0 there (the output is
+            # allocated uninitialised, so a position left unwritten shows)
+            assert np.all(g["p_tok"][b, tested:] == 0), (b, g["p_tok"][b, tested:])
         tally.compared_positions += tested
